@@ -1,0 +1,207 @@
+"""fp64 CPU oracle of the fused GEMM + epilogue computation.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the package's smoke check and the
+benchmark's CPU-baseline leg may import this module; the product path never
+calls it and has no CPU fallback.
+
+What it computes is the plain definition, in the order the pages state it:
+
+  1. optional RMS normalisation of the rows of A, with the gain gamma applied
+     per feature (the row-wise norm of the "augment_me" comment on the zeli.app
+     page, and the Transformer operators listed in section 3.1 / Fig. 4 of the
+     d9bl.com page);
+  2. the GEMM  C = alpha * Y @ B  (section 3.1 of the d9bl.com page, where the
+     GEMM is written C = alpha*A*B + beta*C_prev and the epilogue D = f(C));
+  3. the epilogue f as an ordered list of primitives, each statement acting on
+     the previous value (section 3.2 of the d9bl.com page, the EPILOGUE
+     example), drawn from the four primitive families of the agentlenshq.com
+     page ("How it works": scaling, reductions, pairwise transformations,
+     accumulation).
+
+Everything runs in fp64 on the exact values of the stored inputs; nothing is
+rounded.  The GEMM uses numpy's matmul as a library primitive; all other steps
+are written out elementwise-vectorised with no blocking or reordering.
+
+Readings of points the pages leave open (each also listed in the design notes):
+  * GELU is the tanh approximation, 0.5 v (1 + tanh(sqrt(2/pi)(v + 0.044715 v^3)))
+    (Hendrycks & Gimpel 2016); its derivative is the exact derivative of that form.
+  * SiLU(v) = v * sigmoid(v) (Elfwing et al. 2017); SwiGLU pairs column 2j
+    (gate) with column 2j+1 (up): out_j = SiLU(v_2j) * v_2j+1 (Shazeer 2020).
+  * rms(x) = sqrt(mean_k x_k^2 + eps), the mean over the K features of a row,
+    eps inside the square root.
+  * The RMS row scale precedes every other epilogue op (it is a property of A's
+    rows and only commutes past the matmul, not past a nonlinearity).
+  * A reduction observes the running value at its position in the list, over
+    the current width (half the GEMM width after swiglu_pair).
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Sequence, Tuple
+
+import numpy as np
+
+SQRT_2_OVER_PI = math.sqrt(2.0 / math.pi)
+GELU_CUBIC = 0.044715
+
+# op names understood by the oracle (its own vocabulary; the HIP path has its own enum)
+ELEMENTWISE_OPS = ("scale", "scale_row", "scale_col", "add_col", "add_row", "add_mat",
+                   "gelu_tanh", "silu", "swiglu_pair", "mul_dgelu_tanh")
+REDUCTION_OPS = ("row_sum", "row_sumsq", "row_mean")
+
+
+# --- pairwise / elementwise transforms (agentlenshq.com, "How it works": pairwise) ---
+
+def gelu_tanh(v: np.ndarray) -> np.ndarray:
+    """tanh-approximated GELU (Hendrycks & Gimpel 2016)."""
+    v = np.asarray(v, dtype=np.float64)
+    return 0.5 * v * (1.0 + np.tanh(SQRT_2_OVER_PI * (v + GELU_CUBIC * v ** 3)))
+
+
+def gelu_tanh_grad(p: np.ndarray) -> np.ndarray:
+    """Exact derivative of ``gelu_tanh`` at p (product rule on 0.5 p (1 + t(p)))."""
+    p = np.asarray(p, dtype=np.float64)
+    t = np.tanh(SQRT_2_OVER_PI * (p + GELU_CUBIC * p ** 3))
+    dinner = SQRT_2_OVER_PI * (1.0 + 3.0 * GELU_CUBIC * p ** 2)
+    return 0.5 * (1.0 + t) + 0.5 * p * (1.0 - t * t) * dinner
+
+
+def sigmoid(v: np.ndarray) -> np.ndarray:
+    v = np.asarray(v, dtype=np.float64)
+    out = np.empty_like(v)
+    pos = v >= 0
+    out[pos] = 1.0 / (1.0 + np.exp(-v[pos]))
+    e = np.exp(v[~pos])
+    out[~pos] = e / (1.0 + e)
+    return out
+
+
+def silu(v: np.ndarray) -> np.ndarray:
+    """SiLU / Swish with beta = 1: v * sigmoid(v)."""
+    v = np.asarray(v, dtype=np.float64)
+    return v * sigmoid(v)
+
+
+def swiglu_pair(v: np.ndarray) -> np.ndarray:
+    """Column-interleaved SwiGLU: out[:, j] = SiLU(v[:, 2j]) * v[:, 2j+1]."""
+    if v.shape[1] % 2:
+        raise ValueError("swiglu_pair needs an even width")
+    gate = v[:, 0::2]
+    up = v[:, 1::2]
+    return silu(gate) * up
+
+
+# --- row-wise norm (zeli.app comment; d9bl.com section 3.1 / Fig. 4) ---
+
+def rms(X: np.ndarray, eps: float) -> np.ndarray:
+    """Per-row root mean square over the K features, eps inside the root."""
+    X = np.asarray(X, dtype=np.float64)
+    K = X.shape[1]
+    if K == 0:
+        raise ValueError("rms of an empty row is undefined")
+    ms = np.sum(X * X, axis=1) / K
+    return np.sqrt(ms + eps)
+
+
+def rmsnorm(X: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+    """Normalise-first form: Y[i,k] = X[i,k] / rms_i * gamma[k]."""
+    X = np.asarray(X, dtype=np.float64)
+    r = rms(X, eps)
+    return (X / r[:, None]) * np.asarray(gamma, dtype=np.float64)[None, :]
+
+
+def deferred_rmsnorm_gemm(X: np.ndarray, gamma: np.ndarray, B: np.ndarray, eps: float) -> np.ndarray:
+    """The rewritten form: ((X * gamma) @ B) with each row divided by rms(X) afterwards.
+
+    The zeli.app comment states that a per-row scale of a row-wise norm can be
+    pulled past the following projection; this is that form, used only to check
+    the oracle's normalise-first form against the identity.
+    """
+    X = np.asarray(X, dtype=np.float64)
+    C = (X * np.asarray(gamma, dtype=np.float64)[None, :]) @ np.asarray(B, dtype=np.float64)
+    return C / rms(X, eps)[:, None]
+
+
+# --- the GEMM (d9bl.com section 3.1) ---
+
+def logical_b(B_stored: np.ndarray, b_layout: str) -> np.ndarray:
+    """Logical [K x N] operand from its storage: 'KN' as stored, 'NK' transposed."""
+    B_stored = np.asarray(B_stored, dtype=np.float64)
+    if b_layout == "KN":
+        return B_stored
+    if b_layout == "NK":
+        return B_stored.T
+    raise ValueError(b_layout)
+
+
+def gemm(Y: np.ndarray, B: np.ndarray, alpha: float = 1.0) -> np.ndarray:
+    return alpha * (np.asarray(Y, dtype=np.float64) @ np.asarray(B, dtype=np.float64))
+
+
+# --- the ordered epilogue (d9bl.com section 3.2; agentlenshq.com "How it works") ---
+
+def apply_epilogue(C: np.ndarray, ops: Sequence[Tuple[str, Dict]]) -> Tuple[np.ndarray, List[Tuple[str, Dict, np.ndarray]]]:
+    """Apply ``ops`` in order to the running value v = C.
+
+    Returns the final value and, for each reduction op in list order, a tuple
+    (op name, its args, the fp64 per-row result).  ``rms_rowscale`` is not an
+    epilogue op here: the oracle applies it to A before the GEMM.
+    """
+    v = np.array(C, dtype=np.float64, copy=True)
+    reductions = []
+    for name, args in ops:
+        if name == "scale":
+            v = v * float(args["alpha"])
+        elif name == "scale_row":
+            v = v * np.asarray(args["vec"], dtype=np.float64)[:, None]
+        elif name == "scale_col":
+            v = v * np.asarray(args["vec"], dtype=np.float64)[None, :]
+        elif name == "add_col":
+            v = v + np.asarray(args["vec"], dtype=np.float64)[None, :]
+        elif name == "add_row":
+            v = v + np.asarray(args["vec"], dtype=np.float64)[:, None]
+        elif name == "add_mat":
+            v = v + float(args.get("beta", 1.0)) * np.asarray(args["mat"], dtype=np.float64)
+        elif name == "gelu_tanh":
+            v = gelu_tanh(v)
+        elif name == "silu":
+            v = silu(v)
+        elif name == "swiglu_pair":
+            v = swiglu_pair(v)
+        elif name == "mul_dgelu_tanh":
+            v = v * gelu_tanh_grad(np.asarray(args["mat"], dtype=np.float64))
+        elif name == "row_sum":
+            reductions.append((name, args, np.sum(v, axis=1)))
+        elif name == "row_sumsq":
+            reductions.append((name, args, np.sum(v * v, axis=1)))
+        elif name == "row_mean":
+            width = v.shape[1]
+            if width == 0:
+                raise ValueError("row_mean over an empty row is undefined")
+            reductions.append((name, args, np.sum(v, axis=1) / width))
+        elif name == "rms_rowscale":
+            raise ValueError("rms_rowscale is applied to A by forward(); it must come first")
+        else:
+            raise ValueError(f"unknown op {name}")
+    return v, reductions
+
+
+def forward(A: np.ndarray, B_stored: np.ndarray, ops: Sequence[Tuple[str, Dict]],
+            b_layout: str = "KN", alpha: float = 1.0):
+    """Normalise (if the list starts with rms_rowscale) -> GEMM -> ordered epilogue.
+
+    ``ops`` items are (name, args) with array-valued args already resolved.
+    Returns (D fp64, list of (name, args, fp64 per-row result)).
+    """
+    A = np.asarray(A, dtype=np.float64)
+    ops = list(ops)
+    Y = A
+    if ops and ops[0][0] == "rms_rowscale":
+        args = ops[0][1]
+        Y = rmsnorm(A, args["gamma"], float(args["eps"]))
+        ops = ops[1:]
+    for name, _ in ops:
+        if name == "rms_rowscale":
+            raise ValueError("rms_rowscale must be the first op")
+    C = gemm(Y, logical_b(B_stored, b_layout), alpha)
+    return apply_epilogue(C, ops)

@@ -1,0 +1,368 @@
+"""Pins of the fp64 oracle against things other than itself.
+
+Each test ties one part of the oracle to brute force on tiny inputs, a closed
+form, an exact algebraic identity, or an independent library routine, so that
+a dropped term, a wrong sign or index, or a transposed operand fails.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import coda_oracle as co
+import workloads as w
+
+
+# ----------------------------------------------------------------------------
+# brute force: scalar pure-Python loops, written without numpy
+# ----------------------------------------------------------------------------
+
+def _bf_gelu(v):
+    return 0.5 * v * (1.0 + math.tanh(math.sqrt(2.0 / math.pi) * (v + 0.044715 * v * v * v)))
+
+
+def _bf_sigmoid(v):
+    return 1.0 / (1.0 + math.exp(-v)) if v >= 0 else math.exp(v) / (1.0 + math.exp(v))
+
+
+def brute_force(A, B_logical, ops):
+    """Scalar loops over lists: normalise -> triple-loop GEMM -> ops per element."""
+    M, K = len(A), len(A[0]) if A else 0
+    N = len(B_logical[0]) if B_logical else 0
+    Y = [list(row) for row in A]
+    ops = list(ops)
+    if ops and ops[0][0] == "rms_rowscale":
+        g, eps = ops[0][1]["gamma"], ops[0][1]["eps"]
+        for i in range(M):
+            ss = 0.0
+            for k in range(K):
+                ss += A[i][k] * A[i][k]
+            r = math.sqrt(ss / K + eps)
+            for k in range(K):
+                Y[i][k] = A[i][k] / r * g[k]
+        ops = ops[1:]
+    V = [[0.0] * N for _ in range(M)]
+    for i in range(M):
+        for j in range(N):
+            s = 0.0
+            for k in range(K):
+                s += Y[i][k] * B_logical[k][j]
+            V[i][j] = s
+    reds = []
+    for name, a in ops:
+        width = len(V[0]) if V else 0
+        if name == "scale":
+            V = [[x * a["alpha"] for x in row] for row in V]
+        elif name == "scale_row":
+            V = [[x * a["vec"][i] for x in row] for i, row in enumerate(V)]
+        elif name == "scale_col":
+            V = [[x * a["vec"][j] for j, x in enumerate(row)] for row in V]
+        elif name == "add_col":
+            V = [[x + a["vec"][j] for j, x in enumerate(row)] for row in V]
+        elif name == "add_row":
+            V = [[x + a["vec"][i] for x in row] for i, row in enumerate(V)]
+        elif name == "add_mat":
+            V = [[x + a.get("beta", 1.0) * a["mat"][i][j] for j, x in enumerate(row)] for i, row in enumerate(V)]
+        elif name == "gelu_tanh":
+            V = [[_bf_gelu(x) for x in row] for row in V]
+        elif name == "silu":
+            V = [[x * _bf_sigmoid(x) for x in row] for row in V]
+        elif name == "swiglu_pair":
+            V = [[row[2 * j] * _bf_sigmoid(row[2 * j]) * row[2 * j + 1] for j in range(width // 2)] for row in V]
+        elif name == "mul_dgelu_tanh":
+            h = 1e-5
+            out = []
+            for i, row in enumerate(V):
+                out.append([x * (_bf_gelu(a["mat"][i][j] + h) - _bf_gelu(a["mat"][i][j] - h)) / (2 * h)
+                            for j, x in enumerate(row)])
+            V = out
+        elif name == "row_sum":
+            reds.append([sum(row) for row in V])
+        elif name == "row_sumsq":
+            reds.append([sum(x * x for x in row) for row in V])
+        elif name == "row_mean":
+            reds.append([sum(row) / len(row) for row in V])
+    return V, reds
+
+
+def _tiny_case(rng, M, N, K, ints=False):
+    if ints:
+        A = rng.integers(-3, 4, size=(M, K)).astype(np.float64)
+        B = rng.integers(-3, 4, size=(K, N)).astype(np.float64)
+    else:
+        A = rng.standard_normal((M, K))
+        B = rng.standard_normal((K, N)) / math.sqrt(K)
+    return A, B
+
+
+def _lists(x):
+    return [list(map(float, r)) for r in np.atleast_2d(x)]
+
+
+def test_empty_list_is_textbook_gemm_exact_integers():
+    rng = np.random.default_rng(1)
+    for (M, N, K) in [(4, 4, 4), (3, 5, 4), (5, 2, 7)]:
+        A, B = _tiny_case(rng, M, N, K, ints=True)
+        D, reds = oracle.forward(A, B, [], "KN")
+        V, _ = brute_force(_lists(A), _lists(B), [])
+        assert reds == []
+        assert np.array_equal(D, np.array(V))  # integer sums are exact in fp64
+
+
+def test_b_layout_nk_is_transposed_storage():
+    rng = np.random.default_rng(2)
+    A, B = _tiny_case(rng, 3, 5, 4, ints=True)   # non-square, catches a transposed operand
+    D_kn, _ = oracle.forward(A, B, [], "KN")
+    D_nk, _ = oracle.forward(A, np.ascontiguousarray(B.T), [], "NK")
+    V, _ = brute_force(_lists(A), _lists(B), [])
+    assert np.array_equal(D_kn, np.array(V))
+    assert np.array_equal(D_nk, np.array(V))
+    with pytest.raises(ValueError):
+        oracle.forward(A, B, [], "KK")
+
+
+PROGRAMS = {
+    "cfg1": lambda r, M, N, K: [("rms_rowscale", {"gamma": 1 + 0.1 * r.standard_normal(K), "eps": 1e-6}),
+                                ("add_col", {"vec": 0.1 * r.standard_normal(N)}), ("gelu_tanh", {}),
+                                ("add_mat", {"mat": r.standard_normal((M, N)), "beta": 1.0})],
+    "cfg3": lambda r, M, N, K: [("add_col", {"vec": r.standard_normal(N)}),
+                                ("add_mat", {"mat": r.standard_normal((M, N)), "beta": 0.5}),
+                                ("row_sum", {}), ("row_sumsq", {})],
+    "cfg4": lambda r, M, N, K: [("rms_rowscale", {"gamma": 1 + 0.1 * r.standard_normal(K), "eps": 1e-6}),
+                                ("swiglu_pair", {}), ("row_mean", {})],
+    "cfg5": lambda r, M, N, K: [("mul_dgelu_tanh", {"mat": r.standard_normal((M, N))}), ("row_sum", {})],
+    "scales": lambda r, M, N, K: [("scale", {"alpha": -1.5}), ("scale_row", {"vec": r.standard_normal(M)}),
+                                  ("scale_col", {"vec": r.standard_normal(N)}), ("add_row", {"vec": r.standard_normal(M)}),
+                                  ("silu", {}), ("row_sum", {})],
+}
+
+
+@pytest.mark.parametrize("prog", sorted(PROGRAMS))
+def test_oracle_matches_brute_force(prog):
+    rng = np.random.default_rng(7)
+    M, N, K = 3, 6, 5
+    A, B = _tiny_case(rng, M, N, K)
+    ops = PROGRAMS[prog](rng, M, N, K)
+    bf_ops = [(n, {k: (_lists(v) if isinstance(v, np.ndarray) and v.ndim == 2 else
+                       (list(map(float, v)) if isinstance(v, np.ndarray) else v)) for k, v in a.items()})
+              for n, a in ops]
+    D, reds = oracle.forward(A, B, ops, "KN")
+    V, bred = brute_force(_lists(A), _lists(B), bf_ops)
+    # mul_dgelu_tanh's brute force uses a finite difference (error ~1e-10)
+    tol = 1e-8 if prog == "cfg5" else 1e-12
+    assert np.allclose(D, np.array(V), rtol=tol, atol=tol)
+    assert len(reds) == len(bred)
+    for (_, _, r1), r2 in zip(reds, bred):
+        assert np.allclose(r1, np.array(r2), rtol=tol, atol=tol)
+
+
+# ----------------------------------------------------------------------------
+# the deferred-scale identity (zeli.app comment: the row scale commutes past
+# the following projection)
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("idx", [1, 2, 4])
+def test_deferred_equals_normalise_first_at_config_shapes(idx):
+    spec = w.get_config(idx)
+    M = min(spec.M, 512)       # rows are independent; a row block suffices for the identity
+    rng = np.random.default_rng(spec.seed)
+    X = rng.standard_normal((M, spec.K))
+    g = 1 + 0.1 * rng.standard_normal(spec.K)
+    W = rng.standard_normal((spec.K, spec.N)) / math.sqrt(spec.K)
+    eps = 1e-6
+    C_first = oracle.gemm(oracle.rmsnorm(X, g, eps), W)
+    C_def = oracle.deferred_rmsnorm_gemm(X, g, W, eps)
+    scale = np.abs(C_first).max()
+    assert np.abs(C_first - C_def).max() <= 1e-12 * scale
+
+
+def test_deferred_identity_small_exact_rows():
+    # a row scaled by 2 has half the normalised output; the identity holds per row
+    X = np.array([[1.0, 2.0, 2.0], [2.0, 4.0, 4.0]])
+    g = np.array([1.0, 1.0, 1.0])
+    W = np.eye(3)
+    Y = oracle.rmsnorm(X, g, 0.0)
+    assert np.allclose(Y[0], Y[1])
+    assert np.allclose(Y[0], np.array([1, 2, 2]) / math.sqrt(3.0))   # rms([1,2,2]) = sqrt(9/3)
+    assert np.allclose(oracle.deferred_rmsnorm_gemm(X, g, W, 0.0), Y)
+
+
+# ----------------------------------------------------------------------------
+# closed forms
+# ----------------------------------------------------------------------------
+
+def test_rms_constant_row_closed_form():
+    K, eps = 16, 1e-6
+    for c in (0.0, 1e-4, 0.5, -3.0, 100.0):
+        X = np.full((1, K), c)
+        r = oracle.rms(X, eps)
+        assert r[0] == pytest.approx(math.sqrt(c * c + eps), rel=1e-15)
+        D, _ = oracle.forward(X, np.eye(K), [("rms_rowscale", {"gamma": np.ones(K), "eps": eps})])
+        assert np.allclose(D, c / math.sqrt(c * c + eps), rtol=1e-14, atol=0)
+
+
+def test_rms_mean_square_invariant_pins_mean_over_k_and_eps_inside_root():
+    rng = np.random.default_rng(3)
+    K, eps = 24, 0.25
+    X = rng.standard_normal((5, K))
+    D, _ = oracle.forward(X, np.eye(K), [("rms_rowscale", {"gamma": np.ones(K), "eps": eps})])
+    ms = (X * X).mean(axis=1)
+    assert np.allclose((D * D).mean(axis=1), ms / (ms + eps), rtol=1e-13)
+
+
+def test_rms_gamma_scales_feature_not_row():
+    K = 4
+    X = np.array([[1.0, 1.0, 1.0, 1.0]])
+    g = np.array([1.0, 2.0, 3.0, 4.0])
+    D, _ = oracle.forward(X, np.eye(K), [("rms_rowscale", {"gamma": g, "eps": 0.0})])
+    assert np.allclose(D[0], g)
+
+
+def test_activation_closed_forms():
+    assert oracle.gelu_tanh(np.array([0.0]))[0] == 0.0
+    assert oracle.gelu_tanh_grad(np.array([0.0]))[0] == pytest.approx(0.5, abs=1e-15)
+    assert oracle.silu(np.array([0.0]))[0] == 0.0
+    assert oracle.gelu_tanh(np.array([10.0]))[0] == pytest.approx(10.0, abs=1e-12)
+    assert abs(oracle.gelu_tanh(np.array([-10.0]))[0]) <= 1e-12
+    # SiLU(+-1) = +-1 * e^{+-1} / (1 + e^{+-1})
+    e = math.e
+    assert oracle.silu(np.array([1.0]))[0] == pytest.approx(e / (1 + e), rel=1e-15)
+    assert oracle.silu(np.array([-1.0]))[0] == pytest.approx(-1.0 / (1 + e), rel=1e-15)
+    # symmetry: GELU(x) - GELU(-x) = x for the tanh form (tanh is odd)
+    x = np.linspace(-6, 6, 241)
+    assert np.allclose(oracle.gelu_tanh(x) - oracle.gelu_tanh(-x), x, atol=1e-14)
+
+
+def test_gelu_tanh_close_to_erf_gelu():
+    # the tanh form approximates x * Phi(x) to within ~4.7e-4 everywhere
+    x = np.linspace(-8, 8, 4001)
+    exact = np.array([v * 0.5 * (1 + math.erf(v / math.sqrt(2))) for v in x])
+    dexact = np.array([0.5 * (1 + math.erf(v / math.sqrt(2))) + v * math.exp(-v * v / 2) / math.sqrt(2 * math.pi)
+                       for v in x])
+    assert np.abs(oracle.gelu_tanh(x) - exact).max() < 5e-4
+    assert np.abs(oracle.gelu_tanh_grad(x) - dexact).max() < 1e-3
+
+
+def test_gelu_grad_matches_central_difference():
+    x = np.linspace(-6, 6, 1201)
+    h = 1e-5
+    fd = (oracle.gelu_tanh(x + h) - oracle.gelu_tanh(x - h)) / (2 * h)
+    assert np.abs(oracle.gelu_tanh_grad(x) - fd).max() <= 1e-8
+
+
+def test_silu_matches_library_expit():
+    from scipy.special import expit
+    x = np.linspace(-40, 40, 2001)
+    assert np.allclose(oracle.silu(x), x * expit(x), rtol=1e-14, atol=1e-300)
+
+
+def test_swiglu_pair_hand_case():
+    v = np.array([[1.0, 2.0, -1.0, 3.0]])      # columns g0, u0, g1, u1
+    e = math.e
+    expect = [e / (1 + e) * 2.0, -1.0 / (1 + e) * 3.0]
+    assert np.allclose(oracle.swiglu_pair(v)[0], expect, rtol=1e-15)
+    with pytest.raises(ValueError):
+        oracle.swiglu_pair(np.ones((1, 3)))
+
+
+def test_reductions_constant_rows():
+    c, N = 0.75, 12
+    C = np.full((3, N), c)
+    _, reds = oracle.apply_epilogue(C, [("row_sum", {}), ("row_sumsq", {}), ("row_mean", {})])
+    assert np.allclose(reds[0][2], N * c) and np.allclose(reds[1][2], N * c * c) and np.allclose(reds[2][2], c)
+
+
+def test_reduction_sees_value_at_its_position():
+    C = np.full((1, 4), 1.0)
+    _, reds = oracle.apply_epilogue(C, [("row_sum", {}), ("scale", {"alpha": 3.0}), ("row_sum", {}),
+                                        ("swiglu_pair", {}), ("row_mean", {})])
+    assert reds[0][2][0] == 4.0 and reds[1][2][0] == 12.0
+    assert reds[2][2][0] == pytest.approx(3.0 * (3.0 * e_sig(3.0)))
+
+
+def e_sig(x):
+    return 1.0 / (1.0 + math.exp(-x))
+
+
+def test_rms_must_come_first():
+    X = np.ones((2, 4))
+    with pytest.raises(ValueError):
+        oracle.forward(X, np.eye(4), [("add_col", {"vec": np.zeros(4)}),
+                                      ("rms_rowscale", {"gamma": np.ones(4), "eps": 1e-6})])
+    with pytest.raises(ValueError):
+        oracle.rms(np.ones((2, 0)), 1e-6)
+
+
+# ----------------------------------------------------------------------------
+# planted mistakes: each one is caught by a pin above's check
+# ----------------------------------------------------------------------------
+
+def _plant(monkeypatch, name, replacement):
+    """Replace an oracle function in its module and in the package namespace."""
+    monkeypatch.setattr(co, name, replacement)
+    monkeypatch.setattr(oracle, name, replacement)
+
+
+def test_planted_wrong_gelu_constant_is_caught(monkeypatch):
+    monkeypatch.setattr(co, "GELU_CUBIC", 0.04715)
+    with pytest.raises(AssertionError):
+        test_gelu_tanh_close_to_erf_gelu()
+
+
+def test_planted_eps_outside_root_is_caught(monkeypatch):
+    def bad_rms(X, eps):
+        X = np.asarray(X, dtype=np.float64)
+        return np.sqrt(np.sum(X * X, axis=1) / X.shape[1]) + eps
+    _plant(monkeypatch, "rms", bad_rms)
+    with pytest.raises(AssertionError):
+        test_rms_mean_square_invariant_pins_mean_over_k_and_eps_inside_root()
+
+
+def test_planted_swapped_gate_up_is_caught(monkeypatch):
+    def bad_pair(v):
+        return co.silu(v[:, 1::2]) * v[:, 0::2]
+    _plant(monkeypatch, "swiglu_pair", bad_pair)
+    with pytest.raises(AssertionError):
+        test_swiglu_pair_hand_case()
+
+
+def test_planted_transposed_b_is_caught(monkeypatch):
+    _plant(monkeypatch, "logical_b", lambda B, lay: np.asarray(B, dtype=np.float64).T if lay == "KN" else np.asarray(B, dtype=np.float64))
+    with pytest.raises((AssertionError, ValueError)):
+        test_b_layout_nk_is_transposed_storage()
+
+
+def test_planted_dropped_derivative_term_is_caught(monkeypatch):
+    def bad_grad(p):
+        p = np.asarray(p, dtype=np.float64)
+        t = np.tanh(co.SQRT_2_OVER_PI * (p + co.GELU_CUBIC * p ** 3))
+        return 0.5 * (1.0 + t)
+    _plant(monkeypatch, "gelu_tanh_grad", bad_grad)
+    with pytest.raises(AssertionError):
+        test_gelu_grad_matches_central_difference()
+
+
+def _read_golden(path):
+    vals, lines = {}, [l.split() for l in open(path) if l.strip() and not l.startswith("#")]
+    i = 0
+    while i < len(lines):
+        key = lines[i][0]
+        if key in ("A", "B"):
+            r, c = int(lines[i][1]), int(lines[i][2])
+            vals[key] = np.array([[float(x) for x in lines[i + 1 + k]] for k in range(r)])
+            i += 1 + r
+        else:
+            vals[key] = np.array([float(x) for x in lines[i][1:]])
+            i += 1
+    return vals
+
+
+def test_hand_worked_golden_case():
+    import os
+    g = _read_golden(os.path.join(os.path.dirname(__file__), "golden", "hand_rmsnorm_gemm_epilogue.txt"))
+    ops = [("rms_rowscale", {"gamma": g["gamma"], "eps": 0.0}), ("add_col", {"vec": np.array([1.0, 2.0])}),
+           ("row_sum", {}), ("scale", {"alpha": 2.0}), ("row_sumsq", {})]
+    D, reds = oracle.forward(g["A"], g["B"], ops, "KN")
+    assert np.allclose(D[0], g["D0"], rtol=1e-14) and np.allclose(D[1], g["D1"], rtol=1e-14)
+    assert np.allclose(reds[0][2], g["sum"], rtol=1e-14) and np.allclose(reds[1][2], g["sumsq"], rtol=1e-14)

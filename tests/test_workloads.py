@@ -1,0 +1,82 @@
+"""Seeded input generator: determinism, shapes, distributions, bf16 rounding."""
+import math
+import struct
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import workloads as w
+
+
+def _bf16_value(bits):
+    return struct.unpack(">f", struct.pack(">I", int(bits) << 16))[0]
+
+
+def _rne_bf16_bruteforce(x):
+    """Nearest bf16 by exhaustive comparison over the two neighbours (exact rationals)."""
+    f32 = np.float32(x)
+    bits = int(np.array([f32]).view(np.uint32)[0]) >> 16
+    cands = [bits - 1, bits, bits + 1]
+    best = None
+    for b in cands:
+        v = Fraction(_bf16_value(b))
+        d = abs(v - Fraction(x))
+        key = (d, b & 1)   # ties go to the even mantissa
+        if best is None or key < best[0]:
+            best = (key, b)
+    return best[1]
+
+
+def test_bf16_rounding_against_exact_bruteforce():
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal(3000) * np.exp(rng.uniform(-30, 30, 3000))
+    # add exact ties and near-ties
+    ties = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -46720.0, 49.875, 49.875 - 1e-9, 49.875 + 1e-9])
+    x = np.concatenate([x, ties])
+    got = w.bf16_bits_from_f64(x)
+    for xi, gi in zip(x, got):
+        assert int(gi) == _rne_bf16_bruteforce(float(xi)) & 0xFFFF, xi
+
+
+def test_bf16_roundtrip_is_exact():
+    bits = np.arange(0, 0x7F80, 7, dtype=np.uint16)
+    assert np.array_equal(w.bf16_bits_from_f64(w.bf16_bits_to_f64(bits)), bits)
+    neg = bits | np.uint16(0x8000)
+    assert np.array_equal(w.bf16_bits_from_f64(w.bf16_bits_to_f64(neg)), neg)
+
+
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
+def test_generator_deterministic_and_shaped(idx):
+    spec = w.scaled_config(idx, 64, 96, 48) if idx != 1 else w.get_config(1)
+    a = w.make_inputs(spec)
+    b = w.make_inputs(spec)
+    c = w.make_inputs(spec, seed=spec.seed + 1)
+    for t in spec.tensors:
+        assert a[t.name].shape == t.shape
+        assert a[t.name].dtype == (np.uint16 if t.dtype == "bf16" else np.float32)
+        assert np.array_equal(a[t.name], b[t.name])
+    assert any(not np.array_equal(a[t.name], c[t.name]) for t in spec.tensors)
+
+
+def test_distributions_match_recipe():
+    spec = w.scaled_config(3, 2048, 512, 512)
+    x = w.make_inputs(spec)
+    H = w.bf16_bits_to_f64(x["H"])
+    assert H.min() >= 0.0                                   # |N(0,1)|
+    assert abs(H.mean() - math.sqrt(2 / math.pi)) < 0.01
+    W = w.bf16_bits_to_f64(x["W"])
+    assert abs(W.var() * spec.K - 1.0) < 0.02              # N(0, 1/K): variance is the second argument
+    bias = w.bf16_bits_to_f64(x["bias"])
+    assert abs(bias.var() / 0.02 - 1.0) < 0.2
+    s2 = w.scaled_config(2, 256, 512, 4096)
+    g = w.bf16_bits_to_f64(w.make_inputs(s2)["gamma"])
+    assert abs(g.mean() - 1.0) < 0.01 and abs(g.std() - 0.1) < 0.01
+
+
+def test_full_config_table():
+    shapes = {i: (w.CONFIGS[i].M, w.CONFIGS[i].N, w.CONFIGS[i].K, w.CONFIGS[i].out_width) for i in w.CONFIGS}
+    assert shapes == {1: (256, 256, 256, 256), 2: (8192, 3072, 768, 3072), 3: (8192, 1024, 4096, 1024),
+                      4: (4096, 22016, 4096, 11008), 5: (8192, 4096, 1024, 4096)}
+    assert w.CONFIGS[5].b_layout == "NK" and w.CONFIGS[1].ab_dtype == "f32"
+    assert [op for op, _ in w.CONFIGS[4].program] == ["rms_rowscale", "swiglu_pair"]
