@@ -1,0 +1,216 @@
+"""Benchmark of the fused GEMM + epilogue path on one MI355X.
+
+One step = one fused call (operand staging, in-loop sum of squares and gain,
+MFMA main loop, ordered epilogue, one store of D) on the LLaMA-7B-shaped
+SwiGLU gate/up layer: M = 4096 tokens, K = 4096, [W_gate | W_up] column
+interleaved, N = 2 x 11008, deferred RMSNorm row scale then SiLU(gate) * up,
+bf16 storage and fp32 accumulation.  Inputs are seeded synthetic tensors with
+the layer's shapes and value distributions, resident in HBM before timing.
+
+Prints one JSON line: fused TFLOP/s (2 M N K / kernel time), the share of the
+bf16 dense MFMA peak, the speedup over the in-run unfused HIP sequence (same
+main loop, one kernel per operator, bf16 intermediates), the roofline object
+and the CPU-oracle baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0        # MI355X published dense bf16 MFMA peak
+PEAK_HBM_GBPS = 8000.0
+WORKLOAD_INDEX = 4               # LLaMA-7B SwiGLU gate/up
+FLUSH_BYTES = 512 << 20          # larger than L2 (8 x 4 MB) plus the 256 MB Infinity Cache
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gemm_epilogue_transformer_bf16_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_hash: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "fused_llama7b_gate_up_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_hash:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(spec, inputs, budget_s: float = 10.0):
+    """The fp64 oracle on a bounded row sample of the same workload."""
+    import contextlib
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+    except ImportError:       # pragma: no cover
+        threadpool_info = threadpool_limits = None
+    cores = len(os.sched_getaffinity(0))
+    ctx = threadpool_limits(limits=cores) if threadpool_limits else contextlib.nullcontext()
+    with ctx:
+        threads = cores
+        if threadpool_info:
+            info = threadpool_info()
+            if info:
+                threads = max(i.get("num_threads", cores) for i in info)
+        rows_done = 0
+        elapsed = 0.0
+        chunk = 64
+        order = np.random.default_rng(0).permutation(spec.M)
+        oracle.run_workload(spec, inputs, order[:8])   # warm-up
+        while elapsed < budget_s and rows_done < spec.M:
+            rows = order[rows_done:rows_done + chunk]
+            t0 = time.perf_counter()
+            oracle.run_workload(spec, inputs, rows)
+            elapsed += time.perf_counter() - t0
+            rows_done += len(rows)
+            chunk = min(chunk * 2, 1024)
+    flops = 2.0 * rows_done * spec.N * spec.K
+    return {
+        "value": round(flops / elapsed / 1e12, 5),
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{rows_done} of {spec.M} rows of the same layer (fp64 numpy: RMS normalise, matmul, SwiGLU), "
+                  f"{elapsed:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--tile", type=int, default=0, help="force a tile configuration (0 = automatic)")
+    ap.add_argument("--no-flush", action="store_true", help="do not evict L2 / Infinity Cache between steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-unfused", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
+              "the fused GEMM + epilogue path is single-GPU in this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as w
+    from gemm_epilogue_transformer_bf16_amd import coda, runner
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    spec = w.get_config(WORKLOAD_INDEX)
+    print(f"[bench] generating {spec.name} inputs", file=sys.stderr, flush=True)
+    inputs = w.make_inputs(spec)
+    call = runner.WorkloadCall(spec, inputs, tile=args.tile)
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+
+    def step(fn):
+        if not args.no_flush:
+            flush.zero_()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record()
+        coda.check(fn(), "launch")
+        end.record()
+        return start, end
+
+    print(f"[bench] fused warm-up {args.warmup}, timed {args.steps}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step(call.fused)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    evs = [step(call.fused) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    fused_ms = np.array([s.elapsed_time(e) for s, e in evs])
+    ms = float(fused_ms.mean())
+
+    unfused_ms = None
+    if not args.no_unfused:
+        print("[bench] unfused sequence", file=sys.stderr, flush=True)
+        for _ in range(max(2, args.warmup // 2)):
+            step(call.unfused)
+        torch.cuda.synchronize()
+        uevs = [step(call.unfused) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        unfused_ms = float(np.mean([s.elapsed_time(e) for s, e in uevs]))
+
+    flops = float(spec.flops)
+    tflops = flops / (ms * 1e-3) / 1e12
+    # fused algorithmic bytes: read X, W, gamma once, write D once
+    alg_bytes = 2.0 * (spec.M * spec.K + spec.K * spec.N + spec.K + spec.M * spec.out_width)
+    khash = kernel_source_hash()
+    traffic = load_traffic(khash)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(spec, inputs)
+
+    tile = call.desc.tile or 0
+    line = {
+        "metric": "fused GEMM+epilogue TFLOP/s, % bf16 MFMA peak; speedup vs unfused HIP",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "llama7b_swiglu_gate_up: deferred RMSNorm + SwiGLU(gate,up), M=4096 tokens, K=4096, "
+                        "N=2x11008 column-interleaved, bf16 in/out, fp32 accumulate",
+            "M": spec.M, "N": spec.N, "K": spec.K,
+            "cache_flush_between_steps": not args.no_flush,
+            "tile": args.tile,
+        },
+        "pct_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "unfused_ms_per_step": None if unfused_ms is None else round(unfused_ms, 4),
+        "speedup_vs_unfused": None if unfused_ms is None else round(unfused_ms / ms, 3),
+        "effective_GBps": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
+        "fused_ms_p10_p90": [round(float(np.percentile(fused_ms, 10)), 4),
+                             round(float(np.percentile(fused_ms, 90)), 4)],
+        "wall_s_timed_region": round(wall, 4),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+        },
+        "cpu_baseline": cpu,
+        "kernel_source_hash": khash,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

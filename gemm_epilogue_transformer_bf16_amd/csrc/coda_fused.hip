@@ -1,0 +1,95 @@
+// Host side of the fused kernel: argument packing and dispatch to the
+// compiled tile configurations.
+#include "coda_fused_impl.h"
+#include "coda_launch.h"
+
+namespace coda {
+
+
+namespace {
+
+dev::FusedArgs make_args(const Plan& p) {
+  dev::FusedArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.A = p.A;
+  a.B = p.B;
+  a.D = p.D;
+  a.gamma = p.gamma;
+  a.lda = p.lda;
+  a.ldb = p.ldb;
+  a.ldd = p.ldd;
+  a.M = (int)p.M;
+  a.N = (int)p.N;
+  a.K = (int)p.K;
+  a.d_dtype = p.d_dtype;
+  a.out_width = (int)p.out_width;
+  a.n_ops = p.n_ops;
+  a.n_red = p.n_red;
+  a.grid_m = (int)p.grid_m;
+  a.grid_n = (int)p.grid_n;
+  a.eps = p.eps;
+  for (int i = 0; i < p.n_ops; ++i) {
+    const Op& q = p.ops[i];
+    dev::DevOp& d = a.ops[i];
+    d.kind = q.kind;
+    d.dtype = q.dtype;
+    d.in = q.in;
+    d.ld = q.ld;
+    d.scalar = q.scalar;
+    d.width = (int)q.width;
+    d.out = static_cast<float*>(q.out);
+    d.out_stride = q.out_stride;
+    d.red_slot = q.red_slot;
+  }
+  if (p.n_red > 0 && p.grid_n > 1) {
+    char* ws = static_cast<char*>(p.workspace);
+    a.partials = reinterpret_cast<float*>(ws + fused_partials_offset(p));
+    a.counters = reinterpret_cast<unsigned*>(ws + fused_counters_offset(p));
+  }
+  return a;
+}
+
+int launch_args(const Plan& p, const dev::FusedArgs& a, hipStream_t stream) {
+  const int64_t nwg = p.grid_m * p.grid_n;
+  const bool bkn = p.b_layout == CODA_B_KN;
+  const bool rms = p.has_rms;
+  if (p.ab_dtype == CODA_F32) {
+    return dev::launch_tile_f32(a, nwg, bkn, rms, stream);
+  }
+  switch (p.tile) {
+    case 1: return dev::launch_tile1(a, nwg, bkn, rms, stream);
+    case 2: return dev::launch_tile2(a, nwg, bkn, rms, stream);
+    case 3: return dev::launch_tile3(a, nwg, bkn, rms, stream);
+    case 4: return dev::launch_tile4(a, nwg, bkn, rms, stream);
+    default:
+      set_error("no kernel for tile config %d", p.tile);
+      return CODA_ERR_UNSUPPORTED;
+  }
+}
+
+}  // namespace
+
+int launch_fused(const Plan& p, hipStream_t stream) {
+  if (p.M == 0 || p.N == 0) return CODA_OK;
+  dev::FusedArgs a = make_args(p);
+  return launch_args(p, a, stream);
+}
+
+int launch_plain_gemm(const Plan& p, const void* A, int64_t lda, void* out, int64_t ldo, hipStream_t stream) {
+  if (p.M == 0 || p.N == 0) return CODA_OK;
+  Plan q = p;
+  q.A = A;
+  q.lda = lda;
+  q.D = out;
+  q.ldd = ldo;
+  q.has_rms = false;
+  q.gamma = nullptr;
+  q.n_ops = 0;
+  q.n_red = 0;
+  q.has_swiglu = false;
+  q.out_width = p.N;
+  dev::FusedArgs a = make_args(q);
+  return launch_args(q, a, stream);
+}
+
+}  // namespace coda

@@ -1,0 +1,14 @@
+// Instantiations of the fused kernel for bf16 tile configuration 1.
+#include "coda_fused_impl.h"
+#include "coda_plan.h"
+
+namespace coda {
+namespace dev {
+
+int launch_tile1(const FusedArgs& a, int64_t nwg, bool bkn, bool rms, hipStream_t s) {
+  constexpr TileCfg t = kTileCfgs[0];
+  return launch_variants<t.bm, t.bn, t.bk, t.wm, t.wn, false>(a, nwg, bkn, rms, s);
+}
+
+}  // namespace dev
+}  // namespace coda

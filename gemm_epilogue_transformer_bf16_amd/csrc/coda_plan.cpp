@@ -1,0 +1,437 @@
+// Host-side validation, tile choice and workspace sizing for the C ABI.
+// No HIP calls: this file also builds into the host-only test binary.
+#include "coda_plan.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+namespace coda {
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+// Tile-relative byte offsets of A and B loads are 32-bit: 256 rows x ld x 4 bytes < 2^31.
+constexpr int64_t kMaxLd = int64_t(1) << 21;
+
+bool is_reduction(int kind) {
+  return kind == CODA_OP_ROW_SUM || kind == CODA_OP_ROW_SUMSQ || kind == CODA_OP_ROW_MEAN;
+}
+
+bool needs_vector(int kind) {
+  return kind == CODA_OP_SCALE_ROW || kind == CODA_OP_SCALE_COL || kind == CODA_OP_ADD_COL ||
+         kind == CODA_OP_ADD_ROW;
+}
+
+bool needs_matrix(int kind) { return kind == CODA_OP_ADD_MAT || kind == CODA_OP_MUL_DGELU_TANH; }
+
+bool valid_dtype(int dt) { return dt == CODA_BF16 || dt == CODA_F32; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Extent {
+  uintptr_t lo, hi;  // [lo, hi)
+  bool empty() const { return hi <= lo; }
+};
+
+Extent matrix_extent(const void* p, int64_t rows, int64_t cols, int64_t ld, size_t es) {
+  if (rows <= 0 || cols <= 0) return {0, 0};
+  uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  return {lo, lo + static_cast<uintptr_t>(((rows - 1) * ld + cols) * static_cast<int64_t>(es))};
+}
+
+bool overlap(const Extent& a, const Extent& b) {
+  if (a.empty() || b.empty()) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+// Tile count cost model for the automatic choice: waves of 256 workgroups
+// times the per-tile work, weighted by how well each shape keeps MFMA fed.
+int choose_tile(int64_t M, int64_t N) {
+  static const double kEff[kNumTileCfgs] = {1.0, 0.93, 0.80, 0.97};
+  int best = 1;
+  double best_cost = 0;
+  for (int i = 0; i < kNumTileCfgs; ++i) {
+    const TileCfg& c = kTileCfgs[i];
+    int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
+    int64_t waves = (tiles + 255) / 256;
+    double cost = double(waves) * c.bm * c.bn / kEff[i];
+    if (i == 0 || cost < best_cost) {
+      best = i + 1;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+void clear_error() { g_err[0] = 0; }
+
+const char* last_error() { return g_err; }
+
+size_t fused_partials_offset(const Plan&) { return 0; }
+
+size_t fused_counters_offset(const Plan& p) {
+  return align256(size_t(p.n_red) * size_t(p.grid_n) * size_t(p.M) * sizeof(float));
+}
+
+size_t fused_workspace_bytes(const Plan& p) {
+  if (p.n_red == 0 || p.grid_n <= 1 || p.M == 0 || p.N == 0) return 0;
+  return fused_counters_offset(p) + align256(size_t(p.grid_m) * sizeof(uint32_t));
+}
+
+int64_t unfused_ld(const Plan& p) { return (p.N + 7) / 8 * 8; }
+
+size_t unfused_workspace_bytes(const Plan& p) {
+  if (p.M == 0 || p.N == 0) return 0;
+  size_t bytes = 0;
+  if (p.has_rms) bytes += align256(size_t(p.M) * size_t(p.K) * dtype_size(p.ab_dtype));
+  bytes += 2 * align256(size_t(p.M) * size_t(unfused_ld(p)) * dtype_size(p.d_dtype));
+  return bytes;
+}
+
+int build_plan(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
+               const coda_epi_desc* d, int unfused, bool check_pointers, Plan* p) {
+  clear_error();
+  if (!d || !p) {
+    set_error("descriptor is NULL");
+    return CODA_ERR_INVALID_ARG;
+  }
+  std::memset(p, 0, sizeof(*p));
+  if (M < 0 || N < 0 || K < 0) {
+    set_error("negative size M=%lld N=%lld K=%lld", (long long)M, (long long)N, (long long)K);
+    return CODA_ERR_INVALID_ARG;
+  }
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) {
+    set_error("size above 2^31-1");
+    return CODA_ERR_UNSUPPORTED;
+  }
+  if (!valid_dtype(d->ab_dtype) || !valid_dtype(d->d_dtype)) {
+    set_error("unknown dtype ab=%d d=%d", d->ab_dtype, d->d_dtype);
+    return CODA_ERR_INVALID_ARG;
+  }
+  if (d->b_layout != CODA_B_KN && d->b_layout != CODA_B_NK) {
+    set_error("unknown B layout %d", d->b_layout);
+    return CODA_ERR_INVALID_ARG;
+  }
+  if (d->n_ops < 0 || d->n_ops > CODA_MAX_OPS) {
+    set_error("n_ops=%d outside 0..%d", d->n_ops, CODA_MAX_OPS);
+    return CODA_ERR_INVALID_ARG;
+  }
+  if (d->flags != 0) {
+    set_error("flags must be 0");
+    return CODA_ERR_INVALID_ARG;
+  }
+  if (d->tile < 0 || d->tile > kNumTileCfgs) {
+    set_error("tile=%d outside 0..%d", d->tile, kNumTileCfgs);
+    return CODA_ERR_INVALID_ARG;
+  }
+  p->ab_dtype = d->ab_dtype;
+  p->d_dtype = d->d_dtype;
+  p->b_layout = d->b_layout;
+  p->M = M;
+  p->N = N;
+  p->K = K;
+  p->lda = d->lda;
+  p->ldb = d->ldb;
+  p->ldd = d->ldd;
+  p->A = A;
+  p->B = B;
+  p->D = d->D;
+  p->workspace = d->workspace;
+  p->workspace_bytes = d->workspace_bytes;
+
+  // ---- op list ----
+  int64_t width = N;
+  int n_red = 0;
+  for (int i = 0; i < d->n_ops; ++i) {
+    const coda_op& o = d->ops[i];
+    if (o.kind < CODA_OP_SCALE || o.kind > CODA_OP_ROW_MEAN) {
+      set_error("op %d: unknown kind %d", i, o.kind);
+      return CODA_ERR_INVALID_ARG;
+    }
+    if (o.reserved0 != 0) {
+      set_error("op %d: reserved0 must be 0", i);
+      return CODA_ERR_INVALID_ARG;
+    }
+    if (o.kind == CODA_OP_RMS_ROWSCALE) {
+      if (i != 0) {
+        set_error("op %d: RMS_ROWSCALE must be the first op", i);
+        return CODA_ERR_INVALID_ARG;
+      }
+      if (K == 0) {
+        set_error("RMS_ROWSCALE needs K > 0");
+        return CODA_ERR_INVALID_ARG;
+      }
+      if (!o.in || o.in_dtype != d->ab_dtype) {
+        set_error("RMS_ROWSCALE needs gamma[K] in the A/B dtype");
+        return CODA_ERR_INVALID_ARG;
+      }
+      if (!(std::isfinite(o.scalar) && o.scalar >= 0.0f)) {
+        set_error("RMS_ROWSCALE eps must be finite and >= 0");
+        return CODA_ERR_INVALID_ARG;
+      }
+      if (!aligned(o.in, 16)) {
+        set_error("gamma must be 16-byte aligned");
+        return CODA_ERR_UNSUPPORTED;
+      }
+      p->has_rms = true;
+      p->gamma = o.in;
+      p->eps = o.scalar;
+      continue;
+    }
+    Op& q = p->ops[p->n_ops];
+    q.kind = o.kind;
+    q.dtype = o.in_dtype;
+    q.in = o.in;
+    q.ld = o.ld;
+    q.scalar = o.scalar;
+    q.out = o.out;
+    q.out_stride = o.out_stride;
+    q.red_slot = -1;
+    q.width = width;
+    if (needs_vector(o.kind) || needs_matrix(o.kind)) {
+      if (!o.in) {
+        set_error("op %d: input is NULL", i);
+        return CODA_ERR_INVALID_ARG;
+      }
+      if (!valid_dtype(o.in_dtype)) {
+        set_error("op %d: unknown input dtype %d", i, o.in_dtype);
+        return CODA_ERR_INVALID_ARG;
+      }
+      if (!aligned(o.in, 16)) {
+        set_error("op %d: input must be 16-byte aligned", i);
+        return CODA_ERR_UNSUPPORTED;
+      }
+    }
+    if (needs_matrix(o.kind)) {
+      if (o.ld < width) {
+        set_error("op %d: ld=%lld < width=%lld", i, (long long)o.ld, (long long)width);
+        return CODA_ERR_INVALID_ARG;
+      }
+      if (o.ld % 8 != 0) {
+        set_error("op %d: ld must be a multiple of 8", i);
+        return CODA_ERR_UNSUPPORTED;
+      }
+    }
+    if ((o.kind == CODA_OP_SCALE || o.kind == CODA_OP_ADD_MAT) && !std::isfinite(o.scalar)) {
+      set_error("op %d: scalar must be finite", i);
+      return CODA_ERR_INVALID_ARG;
+    }
+    if (o.kind == CODA_OP_SWIGLU_PAIR) {
+      if (p->has_swiglu) {
+        set_error("op %d: SWIGLU_PAIR at most once", i);
+        return CODA_ERR_INVALID_ARG;
+      }
+      if (width % 2 != 0) {
+        set_error("op %d: SWIGLU_PAIR needs an even width (N=%lld)", i, (long long)width);
+        return CODA_ERR_INVALID_ARG;
+      }
+      p->has_swiglu = true;
+      width /= 2;
+    }
+    if (is_reduction(o.kind)) {
+      if (n_red >= CODA_MAX_REDUCTIONS) {
+        set_error("more than %d reductions", CODA_MAX_REDUCTIONS);
+        return CODA_ERR_UNSUPPORTED;
+      }
+      if (!o.out || o.out_stride < 1) {
+        set_error("op %d: reduction needs out != NULL and out_stride >= 1", i);
+        return CODA_ERR_INVALID_ARG;
+      }
+      if (!aligned(o.out, 4)) {
+        set_error("op %d: reduction output must be 4-byte aligned", i);
+        return CODA_ERR_UNSUPPORTED;
+      }
+      q.red_slot = n_red++;
+    }
+    p->n_ops++;
+  }
+  p->n_red = n_red;
+  p->out_width = width;
+
+  // ---- shapes, leading dimensions, alignment ----
+  const bool empty = (M == 0 || N == 0);
+  if (empty) {
+    // a no-op: only the descriptor's structure is checked
+    p->grid_m = p->grid_n = 0;
+    p->cfg = d->ab_dtype == CODA_F32 ? kF32Tile : kTileCfgs[0];
+    return CODA_OK;
+  }
+  if (K % 8 != 0) {
+    set_error("K=%lld must be a multiple of 8", (long long)K);
+    return CODA_ERR_UNSUPPORTED;
+  }
+  if (d->b_layout == CODA_B_KN && N % 8 != 0) {
+    set_error("N=%lld must be a multiple of 8 when B is stored [K x N]", (long long)N);
+    return CODA_ERR_UNSUPPORTED;
+  }
+  if (d->lda < K || d->ldb < (d->b_layout == CODA_B_KN ? N : K) || d->ldd < width) {
+    set_error("leading dimension too small (lda=%lld ldb=%lld ldd=%lld)", (long long)d->lda,
+              (long long)d->ldb, (long long)d->ldd);
+    return CODA_ERR_INVALID_ARG;
+  }
+  if (d->lda > kMaxLd || d->ldb > kMaxLd) {
+    set_error("lda/ldb above %lld elements", (long long)kMaxLd);
+    return CODA_ERR_UNSUPPORTED;
+  }
+  if (d->lda % 8 || d->ldb % 8 || d->ldd % 8) {
+    set_error("leading dimensions must be multiples of 8");
+    return CODA_ERR_UNSUPPORTED;
+  }
+  if (check_pointers) {
+    if ((K > 0 && (!A || !B)) || !d->D) {
+      set_error("A, B or D is NULL");
+      return CODA_ERR_INVALID_ARG;
+    }
+    if (!aligned(A, 16) || !aligned(B, 16) || !aligned(d->D, 16)) {
+      set_error("A, B and D must be 16-byte aligned");
+      return CODA_ERR_UNSUPPORTED;
+    }
+  }
+
+  // ---- tile ----
+  if (d->ab_dtype == CODA_F32) {
+    p->tile = 0;
+    p->cfg = kF32Tile;
+  } else {
+    p->tile = d->tile ? d->tile : choose_tile(M, N);
+    p->cfg = kTileCfgs[p->tile - 1];
+  }
+  p->grid_m = (M + p->cfg.bm - 1) / p->cfg.bm;
+  p->grid_n = (N + p->cfg.bn - 1) / p->cfg.bn;
+  if (p->grid_m * p->grid_n > kMaxDim) {
+    set_error("too many tiles");
+    return CODA_ERR_UNSUPPORTED;
+  }
+
+  // ---- overlap ----
+  if (check_pointers) {
+    const size_t abs = dtype_size(d->ab_dtype), ds = dtype_size(d->d_dtype);
+    Extent eD = matrix_extent(d->D, M, width, d->ldd, ds);
+    Extent eA = matrix_extent(A, M, K, d->lda, abs);
+    Extent eB = d->b_layout == CODA_B_KN ? matrix_extent(B, K, N, d->ldb, abs)
+                                         : matrix_extent(B, N, K, d->ldb, abs);
+    if (overlap(eD, eA) || overlap(eD, eB)) {
+      set_error("D overlaps A or B");
+      return CODA_ERR_INVALID_ARG;
+    }
+    if (p->has_rms && overlap(eD, matrix_extent(p->gamma, 1, K, K, abs))) {
+      set_error("D overlaps gamma");
+      return CODA_ERR_INVALID_ARG;
+    }
+    Extent outs[CODA_MAX_REDUCTIONS];
+    int64_t strides[CODA_MAX_REDUCTIONS];
+    int no = 0;
+    for (int i = 0; i < p->n_ops; ++i) {
+      const Op& q = p->ops[i];
+      if (needs_vector(q.kind) || needs_matrix(q.kind)) {
+        const size_t es = dtype_size(q.dtype);
+        Extent e;
+        if (q.kind == CODA_OP_SCALE_ROW || q.kind == CODA_OP_ADD_ROW) e = matrix_extent(q.in, 1, M, M, es);
+        else if (needs_vector(q.kind)) e = matrix_extent(q.in, 1, q.width, q.width, es);
+        else e = matrix_extent(q.in, M, q.width, q.ld, es);
+        bool exact_alias = q.kind == CODA_OP_ADD_MAT && q.in == d->D && q.ld == d->ldd &&
+                           q.dtype == d->d_dtype && q.width == width;
+        if (!exact_alias && overlap(e, eD)) {
+          set_error("op %d input overlaps D (only an exact in-place ADD_MAT is allowed)", i);
+          return CODA_ERR_INVALID_ARG;
+        }
+      }
+      if (is_reduction(q.kind)) {
+        Extent e = matrix_extent(q.out, M, 1, q.out_stride, 4);
+        if (overlap(e, eD) || overlap(e, eA) || overlap(e, eB)) {
+          set_error("reduction output of op %d overlaps D, A or B", i);
+          return CODA_ERR_INVALID_ARG;
+        }
+        for (int j = 0; j < no; ++j) {
+          if (!overlap(e, outs[j])) continue;
+          // interleaved columns of one [M x s] array are fine: same stride, distinct offsets
+          intptr_t diff = intptr_t(e.lo) - intptr_t(outs[j].lo);
+          bool interleaved = strides[j] == q.out_stride &&
+                             (diff % (intptr_t)(4 * q.out_stride)) != 0;
+          if (!interleaved) {
+            set_error("reduction outputs overlap (op %d)", i);
+            return CODA_ERR_INVALID_ARG;
+          }
+        }
+        outs[no] = e;
+        strides[no] = q.out_stride;
+        ++no;
+      }
+    }
+  }
+
+  // ---- workspace ----
+  {
+    size_t need = unfused ? unfused_workspace_bytes(*p) : fused_workspace_bytes(*p);
+    if (need > 0 && check_pointers) {
+      if (!d->workspace || d->workspace_bytes < need) {
+        set_error("workspace of %zu bytes needed, %zu given", need, d->workspace_bytes);
+        return CODA_ERR_WORKSPACE;
+      }
+      if (!aligned(d->workspace, 256)) {
+        set_error("workspace must be 256-byte aligned");
+        return CODA_ERR_UNSUPPORTED;
+      }
+    }
+  }
+  return CODA_OK;
+}
+
+}  // namespace coda
+
+extern "C" {
+
+int coda_validate(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
+                  const coda_epi_desc* desc, int unfused) {
+  coda::Plan p;
+  return coda::build_plan(A, B, M, N, K, desc, unfused, true, &p);
+}
+
+size_t coda_workspace_size(int64_t M, int64_t N, int64_t K, const coda_epi_desc* desc, int unfused) {
+  coda::Plan p;
+  if (coda::build_plan(nullptr, nullptr, M, N, K, desc, unfused, false, &p) != CODA_OK) return 0;
+  if (M == 0 || N == 0) return 0;
+  return unfused ? coda::unfused_workspace_bytes(p) : coda::fused_workspace_bytes(p);
+}
+
+const char* coda_status_string(int status) {
+  switch (status) {
+    case CODA_OK: return "CODA_OK";
+    case CODA_ERR_INVALID_ARG: return "CODA_ERR_INVALID_ARG";
+    case CODA_ERR_UNSUPPORTED: return "CODA_ERR_UNSUPPORTED";
+    case CODA_ERR_WORKSPACE: return "CODA_ERR_WORKSPACE";
+    case CODA_ERR_HIP: return "CODA_ERR_HIP";
+    default: return "CODA_UNKNOWN_STATUS";
+  }
+}
+
+const char* coda_last_error(void) { return coda::last_error(); }
+
+int coda_num_tile_configs(void) { return coda::kNumTileCfgs; }
+
+int coda_tile_config(int index, int* bm, int* bn, int* bk, int* waves) {
+  if (index < 1 || index > coda::kNumTileCfgs) return CODA_ERR_INVALID_ARG;
+  const coda::TileCfg& c = coda::kTileCfgs[index - 1];
+  if (bm) *bm = c.bm;
+  if (bn) *bn = c.bn;
+  if (bk) *bk = c.bk;
+  if (waves) *waves = c.wm * c.wn;
+  return CODA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,84 @@
+// Host-side plan of one call: the validated, normalised form of a coda_epi_desc.
+// Pure C++ (no HIP types) so that validation can be built and tested on the host alone.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "coda.h"
+
+namespace coda {
+
+// bf16 tile configurations: output tile bm x bn (rows of A x columns of B),
+// K step bk, wavefronts arranged wm x wn over the tile.
+struct TileCfg {
+  int bm, bn, bk, wm, wn;
+};
+
+constexpr TileCfg kTileCfgs[] = {
+    {256, 256, 64, 2, 2},   // 1: 4 waves, 128x128 per wave
+    {256, 128, 64, 2, 2},   // 2: 4 waves, 128x64 per wave
+    {128, 128, 64, 2, 2},   // 3: 4 waves, 64x64 per wave
+    {256, 256, 64, 2, 4},   // 4: 8 waves, 128x64 per wave
+};
+constexpr int kNumTileCfgs = sizeof(kTileCfgs) / sizeof(kTileCfgs[0]);
+
+// fp32 operands use one small configuration.
+constexpr TileCfg kF32Tile = {64, 64, 32, 2, 2};
+
+struct Op {
+  int kind;
+  int dtype;
+  const void* in;
+  int64_t ld;
+  float scalar;
+  void* out;
+  int64_t out_stride;
+  int red_slot;      // index among the reductions, -1 otherwise
+  int64_t width;     // width of the running value when the op runs
+};
+
+struct Plan {
+  int ab_dtype, d_dtype, b_layout;
+  int64_t M, N, K, lda, ldb, ldd;
+  int64_t out_width;
+  const void* A;
+  const void* B;
+  void* D;
+  bool has_rms;
+  const void* gamma;
+  float eps;
+  int n_ops;                 // ops after the RMS op
+  Op ops[CODA_MAX_OPS];
+  int n_red;
+  bool has_swiglu;
+  int tile;                  // 1-based bf16 tile config; 0 for the fp32 path
+  TileCfg cfg;
+  int64_t grid_m, grid_n;
+  void* workspace;
+  size_t workspace_bytes;
+};
+
+// Validates and normalises a call.  Returns a coda_status; on error records a
+// message retrievable through coda_last_error().
+int build_plan(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
+               const coda_epi_desc* desc, int unfused, bool check_pointers, Plan* plan);
+
+// Workspace layout of the fused path: fp32 partials [n_red][grid_n][M], then
+// uint32 counters [grid_m], each region 256-byte aligned.
+size_t fused_workspace_bytes(const Plan& p);
+size_t fused_partials_offset(const Plan& p);
+size_t fused_counters_offset(const Plan& p);
+
+// Workspace layout of the unfused path: normalised A (ab dtype, [M x K]) when
+// the list has the RMS op, then two [M x ldi] intermediates in d dtype, with
+// ldi = N rounded up to a multiple of 8.
+size_t unfused_workspace_bytes(const Plan& p);
+int64_t unfused_ld(const Plan& p);
+
+void set_error(const char* fmt, ...);
+void clear_error();
+
+inline size_t dtype_size(int dt) { return dt == CODA_F32 ? 4 : 2; }
+
+}  // namespace coda

@@ -1,0 +1,304 @@
+// The unfused comparison sequence: one kernel per operator, intermediates in
+// global memory (the framework-level execution the agentlenshq.com page
+// describes under "The problem": the GEMM output written out and read straight
+// back by the next operator's kernel).
+//
+//   [rmsnorm pass]  ->  plain GEMM (same main loop as the fused kernel)
+//   ->  one pass per elementwise op  ->  one pass per row reduction
+//
+// Every pass streams its operands with 16-byte vector accesses.
+#include "coda_device.h"
+#include "coda_launch.h"
+
+#include <cstring>
+
+namespace coda {
+namespace dev {
+
+constexpr int kPassThreads = 256;
+
+// ---- RMS normalisation of A's rows: Y = (x * rinv) * gamma, one wave per row ----
+template <bool F32>
+__global__ void __launch_bounds__(kPassThreads) rmsnorm_kernel(const void* X, long long ldx, const void* gamma,
+                                                               float eps, int M, int K, void* Y, long long ldy) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * (kPassThreads / 64) + (threadIdx.x >> 6);
+  if (row >= M) return;
+  constexpr int CE = F32 ? 4 : 8;
+  const int nch = K / CE;
+  const char* xr = static_cast<const char*>(X) + (long long)row * ldx * (F32 ? 4 : 2);
+  char* yr = static_cast<char*>(Y) + (long long)row * ldy * (F32 ? 4 : 2);
+  float ss = 0.0f;
+  for (int c = lane; c < nch; c += 64) {
+    const u32x4_t x = *reinterpret_cast<const u32x4_t*>(xr + c * 16);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      if (F32) {
+        const float v = __uint_as_float(x[w]);
+        ss = fmaf(v, v, ss);
+      } else {
+        const float lo = bf16_lo(x[w]), hi = bf16_hi(x[w]);
+        ss = fmaf(lo, lo, ss);
+        ss = fmaf(hi, hi, ss);
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+  const float rinv = 1.0f / sqrtf(ss / float(K) + eps);
+  const char* gp = static_cast<const char*>(gamma);
+  for (int c = lane; c < nch; c += 64) {
+    const u32x4_t x = *reinterpret_cast<const u32x4_t*>(xr + c * 16);
+    const u32x4_t gv = *reinterpret_cast<const u32x4_t*>(gp + c * 16);
+    u32x4_t y;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      if (F32) {
+        y[w] = __float_as_uint((__uint_as_float(x[w]) * rinv) * __uint_as_float(gv[w]));
+      } else {
+        y[w] = pack_bf16x2((bf16_lo(x[w]) * rinv) * bf16_lo(gv[w]), (bf16_hi(x[w]) * rinv) * bf16_hi(gv[w]));
+      }
+    }
+    *reinterpret_cast<u32x4_t*>(yr + c * 16) = y;
+  }
+}
+
+// ---- one elementwise op per pass; each thread owns 8 consecutive input columns ----
+__device__ __forceinline__ void load8(const void* p, int dtype, long long i, long long limit, float (&v)[8]) {
+  float a[4], b[4];
+  load4(p, dtype, i, limit, a);
+  load4(p, dtype, i + 4, limit, b);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[e] = a[e];
+    v[4 + e] = b[e];
+  }
+}
+
+__device__ __forceinline__ void store_n(void* p, int dtype, long long i, long long limit, const float* v, int n) {
+  if (dtype == CODA_BF16) {
+    uint16_t* d = static_cast<uint16_t*>(p) + i;
+    if (n == 8 && i + 7 < limit) {
+      u32x4_t w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
+      *reinterpret_cast<u32x4_t*>(d) = w;
+    } else if (n == 4 && i + 3 < limit) {
+      u32x2_t w;
+      w[0] = pack_bf16x2(v[0], v[1]);
+      w[1] = pack_bf16x2(v[2], v[3]);
+      *reinterpret_cast<u32x2_t*>(d) = w;
+    } else {
+      for (int e = 0; e < n; ++e)
+        if (i + e < limit) d[e] = f32_to_bf16_bits(v[e]);
+    }
+  } else {
+    float* d = static_cast<float*>(p) + i;
+    if (i + n - 1 < limit) {
+      for (int e = 0; e < n; e += 4) {
+        f32x4_t w;
+        w[0] = v[e]; w[1] = v[e + 1]; w[2] = v[e + 2]; w[3] = v[e + 3];
+        *reinterpret_cast<f32x4_t*>(d + e) = w;
+      }
+    } else {
+      for (int e = 0; e < n; ++e)
+        if (i + e < limit) d[e] = v[e];
+    }
+  }
+}
+
+__global__ void __launch_bounds__(kPassThreads) ew_kernel(const void* in, long long ldi, int width, int M,
+                                                          void* out, long long ldo, int io_dtype, DevOp op) {
+  const long long groups_per_row = (width + 7) / 8;
+  const long long total = groups_per_row * M;
+  for (long long gid = blockIdx.x * (long long)kPassThreads + threadIdx.x; gid < total;
+       gid += (long long)gridDim.x * kPassThreads) {
+    const int row = int(gid / groups_per_row);
+    const long long c = (gid % groups_per_row) * 8;
+    const int esz = io_dtype == CODA_BF16 ? 2 : 4;
+    float v[8];
+    load8(static_cast<const char*>(in) + (long long)row * ldi * esz, io_dtype, c, width, v);
+    int nout = 8;
+    long long oc = c;
+    int out_width = width;
+    switch (op.kind) {
+      case CODA_OP_SCALE:
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] *= op.scalar;
+        break;
+      case CODA_OP_SCALE_ROW:
+      case CODA_OP_ADD_ROW: {
+        const float r = load_elem(op.in, op.dtype, row);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = op.kind == CODA_OP_ADD_ROW ? v[e] + r : v[e] * r;
+        break;
+      }
+      case CODA_OP_SCALE_COL:
+      case CODA_OP_ADD_COL: {
+        float s[8];
+        load8(op.in, op.dtype, c, width, s);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = op.kind == CODA_OP_ADD_COL ? v[e] + s[e] : v[e] * s[e];
+        break;
+      }
+      case CODA_OP_ADD_MAT:
+      case CODA_OP_MUL_DGELU_TANH: {
+        float s[8];
+        const int sz = op.dtype == CODA_BF16 ? 2 : 4;
+        load8(static_cast<const char*>(op.in) + (long long)row * op.ld * sz, op.dtype, c, width, s);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          v[e] = op.kind == CODA_OP_ADD_MAT ? v[e] + op.scalar * s[e] : v[e] * gelu_tanh_grad_f(s[e]);
+        break;
+      }
+      case CODA_OP_GELU_TANH:
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = gelu_tanh_f(v[e]);
+        break;
+      case CODA_OP_SILU:
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = silu_f(v[e]);
+        break;
+      case CODA_OP_SWIGLU_PAIR:
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = silu_f(v[2 * e]) * v[2 * e + 1];
+        nout = 4;
+        oc = c / 2;
+        out_width = width / 2;
+        break;
+      default:
+        break;
+    }
+    store_n(static_cast<char*>(out) + (long long)row * ldo * esz, io_dtype, oc, out_width, v, nout);
+  }
+}
+
+// ---- row reduction pass: one wave per row ----
+__global__ void __launch_bounds__(kPassThreads) rowred_kernel(const void* in, long long ldi, int width, int M,
+                                                              int io_dtype, DevOp op) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * (kPassThreads / 64) + (threadIdx.x >> 6);
+  if (row >= M) return;
+  const int esz = io_dtype == CODA_BF16 ? 2 : 4;
+  const char* r = static_cast<const char*>(in) + (long long)row * ldi * esz;
+  const bool sq = op.kind == CODA_OP_ROW_SUMSQ;
+  float acc = 0.0f;
+  for (long long c = lane * 8LL; c < width; c += 64 * 8) {
+    float v[8];
+    load8(r, io_dtype, c, width, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += sq ? v[e] * v[e] : v[e];
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+  if (lane == 0) {
+    if (op.kind == CODA_OP_ROW_MEAN) acc /= float(width);
+    op.out[(long long)row * op.out_stride] = acc;
+  }
+}
+
+}  // namespace dev
+
+namespace {
+
+bool is_reduction(int kind) {
+  return kind == CODA_OP_ROW_SUM || kind == CODA_OP_ROW_SUMSQ || kind == CODA_OP_ROW_MEAN;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+dev::DevOp to_dev(const Op& q) {
+  dev::DevOp d;
+  std::memset(&d, 0, sizeof(d));
+  d.kind = q.kind;
+  d.dtype = q.dtype;
+  d.in = q.in;
+  d.ld = q.ld;
+  d.scalar = q.scalar;
+  d.width = (int)q.width;
+  d.out = static_cast<float*>(q.out);
+  d.out_stride = q.out_stride;
+  d.red_slot = q.red_slot;
+  return d;
+}
+
+int check_launch() { return hipGetLastError() == hipSuccess ? CODA_OK : CODA_ERR_HIP; }
+
+}  // namespace
+
+int launch_unfused(const Plan& p, hipStream_t stream) {
+  if (p.M == 0 || p.N == 0) return CODA_OK;
+  char* ws = static_cast<char*>(p.workspace);
+  const int M = (int)p.M;
+  const void* gA = p.A;
+  int64_t glda = p.lda;
+  if (p.has_rms) {
+    void* Xn = ws;
+    ws += align256(size_t(p.M) * size_t(p.K) * dtype_size(p.ab_dtype));
+    const unsigned blocks = unsigned((p.M + 3) / 4);
+    if (p.ab_dtype == CODA_F32)
+      hipLaunchKernelGGL(dev::rmsnorm_kernel<true>, dim3(blocks), dim3(dev::kPassThreads), 0, stream, p.A,
+                         (long long)p.lda, p.gamma, p.eps, M, (int)p.K, Xn, (long long)p.K);
+    else
+      hipLaunchKernelGGL(dev::rmsnorm_kernel<false>, dim3(blocks), dim3(dev::kPassThreads), 0, stream, p.A,
+                         (long long)p.lda, p.gamma, p.eps, M, (int)p.K, Xn, (long long)p.K);
+    if (check_launch() != CODA_OK) return CODA_ERR_HIP;
+    gA = Xn;
+    glda = p.K;
+  }
+  const int64_t ldi = unfused_ld(p);
+  void* bufs[2];
+  bufs[0] = ws;
+  bufs[1] = ws + align256(size_t(p.M) * size_t(ldi) * dtype_size(p.d_dtype));
+
+  int last_ew = -1;
+  for (int i = 0; i < p.n_ops; ++i)
+    if (!is_reduction(p.ops[i].kind)) last_ew = i;
+
+  const void* cur;
+  int64_t ldc;
+  int which = 0;
+  if (last_ew < 0) {
+    if (launch_plain_gemm(p, gA, glda, p.D, p.ldd, stream) != CODA_OK) return CODA_ERR_HIP;
+    cur = p.D;
+    ldc = p.ldd;
+  } else {
+    if (launch_plain_gemm(p, gA, glda, bufs[0], ldi, stream) != CODA_OK) return CODA_ERR_HIP;
+    cur = bufs[0];
+    ldc = ldi;
+  }
+  int64_t width = p.N;
+  for (int i = 0; i < p.n_ops; ++i) {
+    const Op& q = p.ops[i];
+    const dev::DevOp d = to_dev(q);
+    if (is_reduction(q.kind)) {
+      const unsigned blocks = unsigned((p.M + 3) / 4);
+      hipLaunchKernelGGL(dev::rowred_kernel, dim3(blocks), dim3(dev::kPassThreads), 0, stream, cur, (long long)ldc,
+                         (int)width, M, p.d_dtype, d);
+      if (check_launch() != CODA_OK) return CODA_ERR_HIP;
+      continue;
+    }
+    void* dst;
+    int64_t ldo;
+    if (i == last_ew) {
+      dst = p.D;
+      ldo = p.ldd;
+    } else {
+      which ^= 1;
+      dst = bufs[which];
+      ldo = ldi;
+    }
+    const int64_t groups = ((width + 7) / 8) * p.M;
+    int64_t blocks = (groups + dev::kPassThreads - 1) / dev::kPassThreads;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(dev::ew_kernel, dim3((unsigned)blocks), dim3(dev::kPassThreads), 0, stream, cur,
+                       (long long)ldc, (int)width, M, dst, (long long)ldo, p.d_dtype, d);
+    if (check_launch() != CODA_OK) return CODA_ERR_HIP;
+    cur = dst;
+    ldc = ldo;
+    if (q.kind == CODA_OP_SWIGLU_PAIR) width /= 2;
+  }
+  return CODA_OK;
+}
+
+}  // namespace coda

@@ -1,0 +1,170 @@
+"""Marshal a workload (device tensors + ordered op list) into a coda_epi_desc.
+
+Argument marshalling only: buffers are torch device tensors, the descriptor
+is filled with their pointers, and the calls go to libcoda.so.  Every step of
+the computation runs in the library's HIP kernels.
+"""
+from __future__ import annotations
+
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+import torch
+
+from . import coda as C
+
+OPCODES = {
+    "scale": C.CODA_OP_SCALE,
+    "scale_row": C.CODA_OP_SCALE_ROW,
+    "scale_col": C.CODA_OP_SCALE_COL,
+    "rms_rowscale": C.CODA_OP_RMS_ROWSCALE,
+    "add_col": C.CODA_OP_ADD_COL,
+    "add_row": C.CODA_OP_ADD_ROW,
+    "add_mat": C.CODA_OP_ADD_MAT,
+    "gelu_tanh": C.CODA_OP_GELU_TANH,
+    "silu": C.CODA_OP_SILU,
+    "swiglu_pair": C.CODA_OP_SWIGLU_PAIR,
+    "mul_dgelu_tanh": C.CODA_OP_MUL_DGELU_TANH,
+    "row_sum": C.CODA_OP_ROW_SUM,
+    "row_sumsq": C.CODA_OP_ROW_SUMSQ,
+    "row_mean": C.CODA_OP_ROW_MEAN,
+}
+
+TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
+CODA_DT = {torch.bfloat16: C.CODA_BF16, torch.float32: C.CODA_F32}
+
+
+def storage_to_tensor(arr: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    """Stored numpy array (bf16 as uint16 bits, or float32) -> device tensor."""
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32))
+    return t.to(device)
+
+
+def tensor_to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def current_stream_ptr() -> int:
+    return int(torch.cuda.current_stream().cuda_stream)
+
+
+class Call:
+    """Descriptor plus the device tensors it points at, for one (A, B, ops) call.
+
+    ``ops`` is a list of (name, args) where array arguments are device tensors:
+    ``gamma``/``vec``/``mat`` inputs, ``out`` a 2-D fp32 tensor with ``col``
+    selecting the column a reduction writes.  Scalars: ``alpha``, ``beta``, ``eps``.
+    """
+
+    def __init__(self, A: torch.Tensor, B: torch.Tensor, ops: Sequence[Tuple[str, Dict]], b_layout: str,
+                 D: Optional[torch.Tensor] = None, d_dtype: Optional[torch.dtype] = None, tile: int = 0,
+                 M: Optional[int] = None, N: Optional[int] = None, K: Optional[int] = None,
+                 lda: Optional[int] = None, ldb: Optional[int] = None):
+        self.A, self.B = A, B
+        self.M = A.shape[0] if M is None else M
+        self.K = A.shape[1] if K is None else K
+        if N is None:
+            N = B.shape[1] if b_layout == "KN" else B.shape[0]
+        self.N = N
+        self.ops = list(ops)
+        self.b_layout = b_layout
+        width = self.N // 2 if any(n == "swiglu_pair" for n, _ in self.ops) else self.N
+        self.out_width = width
+        d_dtype = d_dtype or A.dtype
+        if D is None:
+            # rows padded to a multiple of 8 elements (16-byte aligned row starts)
+            ldd = max((width + 7) // 8 * 8, 8)
+            D = torch.empty((self.M, ldd), dtype=d_dtype, device=A.device)[:, :width]
+        self.D = D
+        self._keep: List[torch.Tensor] = []
+        d = C.coda_epi_desc()
+        d.ab_dtype = CODA_DT[A.dtype]
+        d.d_dtype = CODA_DT[D.dtype]
+        d.b_layout = C.CODA_B_KN if b_layout == "KN" else C.CODA_B_NK
+        if lda is None:
+            lda = A.stride(0) if A.dim() == 2 and A.shape[0] > 0 and A.shape[1] > 0 else max((self.K + 7) // 8 * 8, 8)
+        if ldb is None:
+            inner = self.N if b_layout == "KN" else self.K
+            ldb = B.stride(0) if B.dim() == 2 and B.numel() > 0 else max((inner + 7) // 8 * 8, 8)
+        d.lda = lda
+        d.ldb = ldb
+        d.ldd = D.stride(0) if D.dim() == 2 and D.shape[0] > 0 else max(width, 8)
+        d.D = D.data_ptr() if D.numel() else None
+        if len(self.ops) > C.CODA_MAX_OPS:
+            raise ValueError(f"at most {C.CODA_MAX_OPS} ops")
+        d.n_ops = len(self.ops)
+        for i, (name, args) in enumerate(self.ops):
+            o = d.ops[i]
+            o.kind = OPCODES[name]
+            for key in ("gamma", "vec", "mat"):
+                if key in args:
+                    t = args[key]
+                    self._keep.append(t)
+                    o.in_ = t.data_ptr()
+                    o.in_dtype = CODA_DT[t.dtype]
+                    if key == "mat":
+                        o.ld = t.stride(0)
+            if name == "scale":
+                o.scalar = float(args["alpha"])
+            elif name == "add_mat":
+                o.scalar = float(args.get("beta", 1.0))
+            elif name == "rms_rowscale":
+                o.scalar = float(args["eps"])
+            if name in ("row_sum", "row_sumsq", "row_mean"):
+                out = args["out"]
+                self._keep.append(out)
+                col = int(args.get("col", 0))
+                o.out = out.data_ptr() + 4 * col
+                o.out_stride = out.stride(0)
+        d.tile = tile
+        self.desc = d
+        self.ws = {}
+        for unfused in (0, 1):
+            nbytes = C.coda_workspace_size(self.M, self.N, self.K, d, unfused)
+            self.ws[unfused] = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=A.device) if nbytes else None
+
+    def _set_ws(self, unfused: int):
+        w = self.ws[unfused]
+        self.desc.workspace = None if w is None else w.data_ptr()
+        self.desc.workspace_bytes = 0 if w is None else w.numel()
+
+    def _ptrs(self):
+        a = self.A.data_ptr() if self.A.numel() else None
+        b = self.B.data_ptr() if self.B.numel() else None
+        return a, b
+
+    def fused(self, stream: Optional[int] = None) -> int:
+        self._set_ws(0)
+        a, b = self._ptrs()
+        return C.coda_gemm_epi(a, b, self.M, self.N, self.K, self.desc,
+                               current_stream_ptr() if stream is None else stream)
+
+    def unfused(self, stream: Optional[int] = None) -> int:
+        self._set_ws(1)
+        a, b = self._ptrs()
+        return C.coda_gemm_unfused(a, b, self.M, self.N, self.K, self.desc,
+                                   current_stream_ptr() if stream is None else stream)
+
+
+class WorkloadCall(Call):
+    """A ``workloads`` spec with its seeded inputs uploaded to the device."""
+
+    def __init__(self, spec, inputs: Dict[str, np.ndarray], device="cuda", tile: int = 0):
+        dtypes = {t.name: t.dtype for t in spec.tensors}
+        self.spec = spec
+        self.tensors = {name: storage_to_tensor(arr, dtypes[name], device) for name, arr in inputs.items()}
+        self.outputs = {name: torch.zeros(shape, dtype=torch.float32, device=device) for name, shape in spec.outputs}
+        ops = []
+        for name, args in spec.program:
+            a = dict(args)
+            for key in ("gamma", "vec", "mat"):
+                if key in a:
+                    a[key] = self.tensors[a[key]]
+            if "out" in a:
+                a["out"] = self.outputs[a["out"]]
+            ops.append((name, a))
+        super().__init__(self.tensors[spec.a_name], self.tensors[spec.b_name], ops, spec.b_layout,
+                         d_dtype=TORCH_DT[spec.d_dtype], tile=tile, M=spec.M, N=spec.N, K=spec.K)

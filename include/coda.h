@@ -1,0 +1,204 @@
+/*
+ * coda.h - C ABI of the MI355X (gfx950) fused GEMM + epilogue library.
+ *
+ * The operation is the GEMM-plus-epilogue program of "CODA: Rewriting
+ * Transformer Blocks as GEMM-Epilogue Programs": a dense product C = A * B
+ * (d9bl.com page, section 3.1, where the GEMM is C = alpha*A*B + beta*C_prev
+ * and the epilogue is D = f(C)) whose output tile is transformed by an ordered
+ * list of primitives while it is still on-chip (section 1 and section 3.1 of
+ * the same page; the agentlenshq.com page, "CODA's approach"), before the one
+ * store of D.  The primitives are the four families listed on the
+ * agentlenshq.com page ("How it works"): scaling by a constant or a vector,
+ * reductions over a dimension, pairwise / elementwise transforms, and
+ * accumulation into a residual.  Statements run in list order, each on the
+ * previous value (d9bl.com page, section 3.2, the EPILOGUE example).
+ *
+ * Row-wise RMS normalisation of A is expressed as the CODA_OP_RMS_ROWSCALE op:
+ * the gain gamma is applied to A inside the GEMM main loop, the per-row
+ * sum of squares of A is gathered from the A tiles as they stream through,
+ * and the per-row factor 1/rms is applied to the accumulators in the epilogue.
+ * This is the reparameterisation summarised in the "augment_me" comment on
+ * the zeli.app page (a row-wise norm's per-row scale commutes past the
+ * following projection) and on the agentlenshq.com page ("CODA's approach").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All matrices are row-major.  A is [M x K] with leading dimension lda.
+ *    B is the logical [K x N] operand, stored either row-major [K x N]
+ *    (CODA_B_KN, leading dimension ldb >= N) or row-major [N x K], i.e. the
+ *    transpose of a [K x N] matrix (CODA_B_NK, ldb >= K).  D is
+ *    [M x out_width] with leading dimension ldd, where out_width is N, or N/2
+ *    when the list holds CODA_OP_SWIGLU_PAIR.
+ *  - Every pointer is a device pointer (memory the GPU can read or write),
+ *    except the descriptor itself, which is host memory read only during the
+ *    call and may be reused as soon as the call returns.
+ *  - The caller owns every buffer.  Buffers must stay valid until the work
+ *    enqueued on `stream` has completed.  The library allocates no memory
+ *    and keeps no reference to any pointer after a call returns.
+ *  - `stream` is a hipStream_t passed as an opaque pointer (NULL = the
+ *    default stream).  Work is enqueued asynchronously; device faults surface
+ *    at the caller's next synchronisation, per HIP convention.
+ *  - Validation happens before anything is enqueued: on any error code,
+ *    nothing has been launched and no memory has been touched.
+ *  - Shape rules: M >= 0, N >= 0, K >= 0; K % 8 == 0; N % 8 == 0 when B is
+ *    CODA_B_KN; every matrix leading dimension is a multiple of 8 elements
+ *    and every matrix pointer is 16-byte aligned; vector operands are
+ *    16-byte aligned.  M == 0 or N == 0 is a no-op that returns CODA_OK.
+ *    Sizes beyond the tile (ragged M, N, K) are supported.
+ *  - Aliasing: D may coincide exactly with the matrix of a CODA_OP_ADD_MAT op
+ *    (same pointer, same dtype, same leading dimension: an in-place residual
+ *    update).  Any other overlap between D and an input, or between outputs,
+ *    is CODA_ERR_INVALID_ARG.
+ *  - The library is stateless and reentrant, except for the workspace rule
+ *    of coda_gemm_epi below.
+ */
+#ifndef CODA_H
+#define CODA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CODA_MAX_OPS 16
+#define CODA_MAX_REDUCTIONS 8
+
+typedef enum {
+  CODA_OK = 0,
+  CODA_ERR_INVALID_ARG = -1,  /* a null/ill-formed argument, bad op list, overlap  */
+  CODA_ERR_UNSUPPORTED = -2,  /* well-formed but outside the shape/alignment rules  */
+  CODA_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required         */
+  CODA_ERR_HIP = -4           /* the HIP runtime reported an error at launch        */
+} coda_status;
+
+typedef enum { CODA_BF16 = 0, CODA_F32 = 1 } coda_dtype;
+
+typedef enum {
+  CODA_B_KN = 0,  /* B stored row-major [K x N]                                  */
+  CODA_B_NK = 1   /* B stored row-major [N x K] and used transposed (e.g. W^T)  */
+} coda_b_layout;
+
+/*
+ * Epilogue primitives.  v is the fp32 running value of output element (i, j);
+ * "width" is the current number of columns (N, or N/2 after SWIGLU_PAIR).
+ * `in`, `ld`, `in_dtype`, `scalar`, `out`, `out_stride` are fields of coda_op.
+ */
+typedef enum {
+  /* scaling (agentlenshq.com page, "How it works": scaling) */
+  CODA_OP_SCALE = 0,          /* v *= scalar                                         */
+  CODA_OP_SCALE_ROW = 1,      /* v *= in[i]          in: [M] vector                  */
+  CODA_OP_SCALE_COL = 2,      /* v *= in[j]          in: [width] vector              */
+  CODA_OP_RMS_ROWSCALE = 3,   /* deferred RMSNorm: in = gamma [K], scalar = eps.
+                                 v *= 1/sqrt(mean_k A[i,k]^2 + eps), with A*gamma fed
+                                 to the GEMM.  Must be the first op, at most once,
+                                 and needs K > 0.                                      */
+  /* accumulation (agentlenshq.com page, "How it works": accumulation) */
+  CODA_OP_ADD_COL = 4,        /* v += in[j]          (bias)                          */
+  CODA_OP_ADD_ROW = 5,        /* v += in[i]                                          */
+  CODA_OP_ADD_MAT = 6,        /* v += scalar * in[i*ld + j]   (beta * residual)      */
+  /* pairwise / elementwise transforms (agentlenshq.com page, "How it works") */
+  CODA_OP_GELU_TANH = 7,      /* v = 0.5 v (1 + tanh(sqrt(2/pi)(v + 0.044715 v^3)))  */
+  CODA_OP_SILU = 8,           /* v = v * sigmoid(v)                                  */
+  CODA_OP_SWIGLU_PAIR = 9,    /* out[i,j] = silu(v[i,2j]) * v[i,2j+1]; width halves,
+                                 so width must be even; at most once                  */
+  CODA_OP_MUL_DGELU_TANH = 10,/* v *= d/dp GELU_tanh(p), p = in[i*ld + j]             */
+  /* reductions over the row (agentlenshq.com page, "How it works": reductions).
+     Each writes an fp32 value per row to ((float*)out)[i*out_stride]; the value
+     reduced is the running value at the op's position in the list.  At most
+     CODA_MAX_REDUCTIONS per list. */
+  CODA_OP_ROW_SUM = 11,
+  CODA_OP_ROW_SUMSQ = 12,
+  CODA_OP_ROW_MEAN = 13
+} coda_op_kind;
+
+typedef struct {
+  int32_t kind;         /* coda_op_kind                                              */
+  int32_t in_dtype;     /* coda_dtype of `in` (ignored by ops without an input)      */
+  const void* in;       /* vector / matrix input (device), or NULL                   */
+  int64_t ld;           /* leading dimension of a matrix input                       */
+  float scalar;         /* alpha of SCALE, beta of ADD_MAT, eps of RMS_ROWSCALE      */
+  int32_t reserved0;    /* must be 0                                                 */
+  void* out;            /* reductions: fp32 output (device)                          */
+  int64_t out_stride;   /* reductions: element stride between rows of `out`, >= 1   */
+} coda_op;
+
+typedef struct {
+  int32_t ab_dtype;     /* dtype of A and B: CODA_BF16 (bf16 MFMA) or CODA_F32     */
+  int32_t d_dtype;      /* dtype of D                                               */
+  int32_t b_layout;     /* coda_b_layout                                            */
+  int32_t n_ops;        /* 0..CODA_MAX_OPS                                          */
+  int64_t lda, ldb, ldd;
+  void* D;              /* output (device)                                          */
+  void* workspace;      /* device scratch, see coda_workspace_size                 */
+  size_t workspace_bytes;
+  int32_t tile;         /* 0 = automatic tile choice; k > 0 forces tile config k    */
+  int32_t flags;        /* reserved, must be 0                                      */
+  coda_op ops[CODA_MAX_OPS];
+} coda_epi_desc;
+
+/*
+ * coda_gemm_epi - one fused kernel: D = f(A * B) with f = desc->ops in order.
+ * The GEMM runs on MFMA with fp32 accumulators; every op runs on the fp32
+ * accumulators in registers; D is written once, rounded to d_dtype
+ * (round-to-nearest-even for bf16).  With CODA_OP_RMS_ROWSCALE first, the
+ * GEMM operand is A*gamma rounded to ab_dtype and the row factor is applied
+ * to the accumulators.
+ * Workspace: row reductions whose row spans several output tiles combine
+ * partial sums through the workspace (coda_workspace_size(..., 0) bytes).
+ * Its counter region must be zero before the first call; every call leaves
+ * it zero again.  Two calls that run concurrently must not share a workspace.
+ * Returns a coda_status.
+ */
+int coda_gemm_epi(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
+                  const coda_epi_desc* desc, void* stream);
+
+/*
+ * coda_gemm_unfused - the same computation as the framework-level sequence of
+ * one kernel per operator (agentlenshq.com page, "The problem": each
+ * operator launched as its own kernel, the GEMM output written to global
+ * memory and read straight back): an RMS normalisation pass over A (when the
+ * list starts with CODA_OP_RMS_ROWSCALE), the plain GEMM with the same main
+ * loop as coda_gemm_epi, then one pass per remaining op.  Intermediates are
+ * stored in d_dtype in the workspace (coda_workspace_size(..., 1) bytes).
+ * Meant as the in-run comparison for coda_gemm_epi.  Returns a coda_status.
+ */
+int coda_gemm_unfused(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
+                      const coda_epi_desc* desc, void* stream);
+
+/*
+ * coda_validate - host-only check of a call: returns the status coda_gemm_epi
+ * (unfused == 0) or coda_gemm_unfused (unfused != 0) would return before
+ * launching, without touching the device.
+ */
+int coda_validate(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
+                  const coda_epi_desc* desc, int unfused);
+
+/*
+ * coda_workspace_size - bytes of workspace the call needs (0 when none).
+ * Returns 0 for a descriptor that does not validate.
+ */
+size_t coda_workspace_size(int64_t M, int64_t N, int64_t K, const coda_epi_desc* desc,
+                           int unfused);
+
+/* coda_status_string - static text for a status code. */
+const char* coda_status_string(int status);
+
+/* coda_last_error - detail of the last failing call on this host thread ("" if none). */
+const char* coda_last_error(void);
+
+/*
+ * coda_num_tile_configs / coda_tile_config - the compiled bf16 tile
+ * configurations, numbered 1..n, selectable through coda_epi_desc.tile.
+ * coda_tile_config returns CODA_OK and fills the output tile size (bm x bn),
+ * the K step (bk) and the wavefronts per workgroup, or CODA_ERR_INVALID_ARG.
+ */
+int coda_num_tile_configs(void);
+int coda_tile_config(int index, int* bm, int* bn, int* bk, int* waves);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CODA_H */

@@ -1,0 +1,173 @@
+"""Helpers shared by the GPU parity tests: run a workload through the C ABI
+and compare with the fp64 oracle."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import workloads as w
+from workloads.gen import to_f64
+
+_LIB_CHECKED = False
+
+
+def lib():
+    """The binding; builds libcoda.so first only if nothing is built."""
+    global _LIB_CHECKED
+    import os
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    so = os.path.join(root, "gemm_epilogue_transformer_bf16_amd", "libcoda.so")
+    if not os.path.exists(so):
+        from gemm_epilogue_transformer_bf16_amd import build
+        build.build()
+    from gemm_epilogue_transformer_bf16_amd import coda, runner
+    return coda, runner
+
+
+def announce(msg: str) -> None:
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def tol(ref: np.ndarray) -> np.ndarray:
+    """Per-element bar: |d - ref| <= max(2e-2, 1e-2 |ref|)."""
+    return np.maximum(2e-2, 1e-2 * np.abs(ref))
+
+
+def assert_close(got: np.ndarray, ref: np.ndarray, what: str, extra=None) -> dict:
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    t = tol(ref)
+    if extra is not None:
+        t = t + extra
+    err = np.abs(got - ref)
+    bad = ~(err <= t)           # NaN counts as bad
+    stats = {"max_abs": float(np.nanmax(err)) if err.size else 0.0,
+             "max_rel": float(np.nanmax(err / np.maximum(np.abs(ref), 2.0))) if err.size else 0.0}
+    if bad.any():
+        idx = np.unravel_index(np.argmax(np.where(bad, err - t, -np.inf)), err.shape)
+        raise AssertionError(f"{what}: {int(bad.sum())} of {bad.size} elements outside tolerance; "
+                             f"worst at {idx}: got {got[idx]!r} ref {ref[idx]!r}; {stats}")
+    print(f"  {what}: ok {stats}", flush=True)
+    return stats
+
+
+U_BF16 = 2.0 ** -8   # unit roundoff of bf16 (8 significand bits)
+REDUCTIONS = ("row_sum", "row_sumsq", "row_mean")
+
+
+def unfused_extra(spec, inputs, rows):
+    """Extra error allowance of the unfused sequence, from its bf16 intermediates.
+
+    The unfused path stores the normalised A (in the A/B dtype), the GEMM
+    output and every elementwise op's output except the last (in the D dtype),
+    each a rounding of relative size <= u (2^-8 for bf16, 2^-24 for fp32).  The rounding of the normalised A enters the
+    GEMM as u * (|Y| @ |B|); a stored intermediate v_k contributes u |v_k|,
+    doubled to cover its propagation through the later ops (GELU' and SiLU'
+    stay below 1.13; SwiGLU combines two rounded inputs).  Reductions read a
+    stored tensor, whose elements then carry delta = that allowance + u |v|;
+    the row sum is off by at most sum(delta), the mean by that over the width,
+    the sum of squares by sum(2 |v| delta + delta^2).
+
+    Returns (extra for D, {reduction index: extra per row}).
+    """
+    dtypes = {t.name: t.dtype for t in spec.tensors}
+    u_ab = U_BF16 if spec.ab_dtype == "bf16" else 2.0 ** -24
+    u = U_BF16 if spec.d_dtype == "bf16" else 2.0 ** -24
+    A = to_f64(inputs[spec.a_name], dtypes[spec.a_name])[rows]
+    B = oracle.logical_b(to_f64(inputs[spec.b_name], dtypes[spec.b_name]), spec.b_layout)
+    ops = oracle.resolve_program(spec, inputs, rows)
+    body = ops
+    extra = 0.0
+    if ops and ops[0][0] == "rms_rowscale":
+        Y = oracle.rmsnorm(A, ops[0][1]["gamma"], ops[0][1]["eps"])
+        extra = u_ab * (np.abs(Y) @ np.abs(B))
+        body = ops[1:]
+    ew = [i for i, (n, _) in enumerate(body) if n not in REDUCTIONS]
+    last_ew = ew[-1] if ew else -1
+
+    def value_after(i):   # oracle value after body[:i]
+        v, _ = oracle.forward(A, oracle.logical_b(B, "KN"), ([ops[0]] if body is not ops else []) + body[:i], "KN")
+        return v
+
+    if last_ew >= 0:
+        extra = extra + 2 * u * np.abs(value_after(0))          # stored GEMM output
+    red_extra = {}
+    red_i = 0
+    for i, (name, _) in enumerate(body):
+        if name == "swiglu_pair" and not np.isscalar(extra):
+            # first-order propagation through out = silu(g) * u for errors e_g, e_u
+            v = value_after(i)
+            g, up = v[:, 0::2], v[:, 1::2]
+            sg = oracle.sigmoid(g)
+            dsilu = sg * (1 + g * (1 - sg))
+            extra = 2 * (np.abs(dsilu * up) * extra[:, 0::2] + np.abs(g * sg) * extra[:, 1::2])
+        if name in REDUCTIONS:
+            v = value_after(i)
+            delta = extra + u * np.abs(v)
+            if name == "row_sum":
+                red_extra[red_i] = delta.sum(axis=1)
+            elif name == "row_mean":
+                red_extra[red_i] = delta.sum(axis=1) / v.shape[1]
+            else:
+                red_extra[red_i] = (2 * np.abs(v) * delta + delta * delta).sum(axis=1)
+            red_i += 1
+        elif i != last_ew:
+            extra = extra + 2 * u * np.abs(value_after(i + 1))   # stored intermediate
+    return extra, red_extra
+
+
+def run_and_compare(spec, inputs, mode: str = "fused", tile: int = 0, rows=None, label: str = "",
+                    check_determinism: bool = False):
+    """Run ``spec`` on the GPU through the C ABI and compare with the oracle
+    (on ``rows`` only when given).  Returns the error stats."""
+    coda, runner = lib()
+    announce(f"{label or spec.name} mode={mode} tile={tile} M={spec.M} N={spec.N} K={spec.K}")
+    call = runner.WorkloadCall(spec, inputs, tile=tile)
+    st = call.fused() if mode == "fused" else call.unfused()
+    coda.check(st, f"{spec.name} {mode}")
+    torch.cuda.synchronize()
+    D = runner.tensor_to_f64(call.D if rows is None else call.D[torch.as_tensor(rows, device=call.D.device)])
+    outs = {k: runner.tensor_to_f64(v if rows is None else v[torch.as_tensor(rows, device=v.device)])
+            for k, v in call.outputs.items()}
+    if check_determinism:
+        D1 = call.D.clone()
+        o1 = {k: v.clone() for k, v in call.outputs.items()}
+        st = call.fused() if mode == "fused" else call.unfused()
+        coda.check(st, f"{spec.name} {mode} (repeat)")
+        torch.cuda.synchronize()
+        assert torch.equal(D1.view(torch.int16) if D1.dtype == torch.bfloat16 else D1,
+                           call.D.view(torch.int16) if call.D.dtype == torch.bfloat16 else call.D), "D not bitwise repeatable"
+        for k in o1:
+            assert torch.equal(o1[k], call.outputs[k]), f"{k} not bitwise repeatable"
+    rows_idx = np.arange(spec.M) if rows is None else np.asarray(rows)
+    D_ref, outs_ref = oracle.run_workload(spec, inputs, rows_idx)
+    d_extra, red_extra = (None, {}) if mode == "fused" else unfused_extra(spec, inputs, rows_idx)
+    stats = {"D": assert_close(D, D_ref, f"{spec.name}/{mode}/D", d_extra)}
+    red_i = 0
+    for name, args in spec.program:
+        if name not in ("row_sum", "row_sumsq", "row_mean"):
+            continue
+        o, col = args["out"], args["col"]
+        extra = red_extra.get(red_i) if mode == "unfused" else None
+        stats[f"{o}[{col}]"] = assert_close(outs[o][:, col], outs_ref[o][:, col], f"{spec.name}/{mode}/{o}[:,{col}]",
+                                            extra)
+        red_i += 1
+    del call
+    return stats
+
+
+def sample_rows(M: int, n: int = 48, seed: int = 5) -> np.ndarray:
+    """Seeded sample of rows that always includes the first/last rows and tile edges."""
+    rng = np.random.default_rng(seed)
+    fixed = {0, 1, M - 1, M - 2}
+    for edge in (128, 256):
+        for k in range(edge, M, edge * 7):
+            fixed.update({k - 1, k})
+    fixed = {r for r in fixed if 0 <= r < M}
+    extra = rng.choice(M, size=min(n, M), replace=False)
+    return np.array(sorted(fixed | set(int(x) for x in extra)))

@@ -1,0 +1,180 @@
+// Host-only checks of the call validation (no GPU, no HIP runtime): every
+// invalid descriptor returns its documented status.  Built with
+// -fsanitize=address,undefined by tests/test_abi.py.
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "coda.h"
+#include "coda_plan.h"
+
+static int failures = 0;
+
+#define EXPECT(cond)                                                   \
+  do {                                                                 \
+    if (!(cond)) {                                                     \
+      std::printf("FAIL line %d: %s (%s)\n", __LINE__, #cond, coda_last_error()); \
+      ++failures;                                                      \
+    }                                                                  \
+  } while (0)
+
+// fake, well-aligned, non-overlapping device addresses
+static const void* P(uintptr_t x) { return reinterpret_cast<const void*>(x); }
+static void* Pm(uintptr_t x) { return reinterpret_cast<void*>(x); }
+
+static coda_epi_desc base_desc(int64_t N, int64_t K) {
+  coda_epi_desc d;
+  std::memset(&d, 0, sizeof(d));
+  d.ab_dtype = CODA_BF16;
+  d.d_dtype = CODA_BF16;
+  d.b_layout = CODA_B_KN;
+  d.lda = K;
+  d.ldb = N;
+  d.ldd = N;
+  d.D = Pm(0x30000000);
+  return d;
+}
+
+int main() {
+  const void* A = P(0x10000000);
+  const void* B = P(0x20000000);
+  const int64_t M = 300, N = 520, K = 200;
+
+  coda_epi_desc d = base_desc(N, K);
+  EXPECT(coda_validate(A, B, M, N, K, &d, 0) == CODA_OK);
+  EXPECT(coda_validate(A, B, M, N, K, nullptr, 0) == CODA_ERR_INVALID_ARG);
+  EXPECT(coda_validate(A, B, -1, N, K, &d, 0) == CODA_ERR_INVALID_ARG);
+  EXPECT(coda_validate(A, B, 0, N, K, &d, 0) == CODA_OK);   // empty is fine
+  {  // K must be a multiple of 8
+    coda_epi_desc e = base_desc(N, 204);
+    EXPECT(coda_validate(A, B, M, N, 204, &e, 0) == CODA_ERR_UNSUPPORTED);
+  }
+  {  // N multiple of 8 when B is [K x N]
+    coda_epi_desc e = base_desc(521, K);
+    e.ldb = 528; e.ldd = 528;
+    EXPECT(coda_validate(A, B, M, 521, K, &e, 0) == CODA_ERR_UNSUPPORTED);
+    e.b_layout = CODA_B_NK; e.ldb = K;
+    EXPECT(coda_validate(A, B, M, 521, K, &e, 0) == CODA_OK);
+  }
+  {  // leading dimensions
+    coda_epi_desc e = d; e.lda = K - 8;
+    EXPECT(coda_validate(A, B, M, N, K, &e, 0) == CODA_ERR_INVALID_ARG);
+    e = d; e.ldd = N + 4;
+    EXPECT(coda_validate(A, B, M, N, K, &e, 0) == CODA_ERR_UNSUPPORTED);
+  }
+  {  // misaligned pointers
+    EXPECT(coda_validate(P(0x10000008), B, M, N, K, &d, 0) == CODA_ERR_UNSUPPORTED);
+  }
+  {  // null pointers
+    EXPECT(coda_validate(nullptr, B, M, N, K, &d, 0) == CODA_ERR_INVALID_ARG);
+    coda_epi_desc e = d; e.D = nullptr;
+    EXPECT(coda_validate(A, B, M, N, K, &e, 0) == CODA_ERR_INVALID_ARG);
+  }
+  {  // bad enums, flags, tile
+    coda_epi_desc e = d; e.ab_dtype = 7;
+    EXPECT(coda_validate(A, B, M, N, K, &e, 0) == CODA_ERR_INVALID_ARG);
+    e = d; e.b_layout = 5;
+    EXPECT(coda_validate(A, B, M, N, K, &e, 0) == CODA_ERR_INVALID_ARG);
+    e = d; e.flags = 1;
+    EXPECT(coda_validate(A, B, M, N, K, &e, 0) == CODA_ERR_INVALID_ARG);
+    e = d; e.tile = coda_num_tile_configs() + 1;
+    EXPECT(coda_validate(A, B, M, N, K, &e, 0) == CODA_ERR_INVALID_ARG);
+    e = d; e.n_ops = CODA_MAX_OPS + 1;
+    EXPECT(coda_validate(A, B, M, N, K, &e, 0) == CODA_ERR_INVALID_ARG);
+    e = d; e.n_ops = 1; e.ops[0].kind = 99;
+    EXPECT(coda_validate(A, B, M, N, K, &e, 0) == CODA_ERR_INVALID_ARG);
+  }
+  {  // RMS op: first, once, with gamma in the operand dtype, eps >= 0, K > 0
+    coda_epi_desc e = d; e.n_ops = 1;
+    e.ops[0].kind = CODA_OP_RMS_ROWSCALE; e.ops[0].in = P(0x40000000); e.ops[0].in_dtype = CODA_BF16;
+    e.ops[0].scalar = 1e-6f;
+    EXPECT(coda_validate(A, B, M, N, K, &e, 0) == CODA_OK);
+    coda_epi_desc f = e; f.ops[0].in = nullptr;
+    EXPECT(coda_validate(A, B, M, N, K, &f, 0) == CODA_ERR_INVALID_ARG);
+    f = e; f.ops[0].in_dtype = CODA_F32;
+    EXPECT(coda_validate(A, B, M, N, K, &f, 0) == CODA_ERR_INVALID_ARG);
+    f = e; f.ops[0].scalar = -1.0f;
+    EXPECT(coda_validate(A, B, M, N, K, &f, 0) == CODA_ERR_INVALID_ARG);
+    f = e; f.n_ops = 2; f.ops[1] = f.ops[0]; f.ops[0].kind = CODA_OP_GELU_TANH; f.ops[0].in = nullptr;
+    EXPECT(coda_validate(A, B, M, N, K, &f, 0) == CODA_ERR_INVALID_ARG);   // not first
+    coda_epi_desc g = base_desc(N, 0); g.n_ops = 1; g.ops[0] = e.ops[0];
+    EXPECT(coda_validate(A, B, M, N, 0, &g, 0) == CODA_ERR_INVALID_ARG);   // K == 0
+  }
+  {  // SWIGLU: even width, at most once; D width halves
+    coda_epi_desc e = d; e.n_ops = 1; e.ops[0].kind = CODA_OP_SWIGLU_PAIR; e.ldd = N / 2 + 4;
+    EXPECT(coda_validate(A, B, M, N, K, &e, 0) == CODA_OK);
+    e.n_ops = 2; e.ops[1].kind = CODA_OP_SWIGLU_PAIR;
+    EXPECT(coda_validate(A, B, M, N, K, &e, 0) == CODA_ERR_INVALID_ARG);
+    coda_epi_desc f = base_desc(26, K); f.b_layout = CODA_B_NK; f.ldb = K; f.ldd = 32;
+    f.n_ops = 2; f.ops[0].kind = CODA_OP_SWIGLU_PAIR; f.ops[1].kind = CODA_OP_SWIGLU_PAIR;
+    EXPECT(coda_validate(A, B, M, 26, K, &f, 0) == CODA_ERR_INVALID_ARG);
+    f.n_ops = 1;
+    EXPECT(coda_validate(A, B, M, 26, K, &f, 0) == CODA_OK);   // 26 even; 13 wide after
+    coda_epi_desc h = base_desc(13 * 2 + 1, K); h.b_layout = CODA_B_NK; h.ldb = K; h.ldd = 32;
+    h.n_ops = 1; h.ops[0].kind = CODA_OP_SWIGLU_PAIR;
+    EXPECT(coda_validate(A, B, M, 27, K, &h, 0) == CODA_ERR_INVALID_ARG);   // odd width
+  }
+  {  // side inputs: non-null, aligned, ld rules
+    coda_epi_desc e = d; e.n_ops = 1; e.ops[0].kind = CODA_OP_ADD_COL;
+    EXPECT(coda_validate(A, B, M, N, K, &e, 0) == CODA_ERR_INVALID_ARG);
+    e.ops[0].in = P(0x40000004);
+    EXPECT(coda_validate(A, B, M, N, K, &e, 0) == CODA_ERR_UNSUPPORTED);
+    e.ops[0].in = P(0x40000000);
+    EXPECT(coda_validate(A, B, M, N, K, &e, 0) == CODA_OK);
+    e.ops[0].kind = CODA_OP_ADD_MAT; e.ops[0].ld = N - 8;
+    EXPECT(coda_validate(A, B, M, N, K, &e, 0) == CODA_ERR_INVALID_ARG);
+    e.ops[0].ld = N + 4;
+    EXPECT(coda_validate(A, B, M, N, K, &e, 0) == CODA_ERR_UNSUPPORTED);
+    e.ops[0].ld = N;
+    EXPECT(coda_validate(A, B, M, N, K, &e, 0) == CODA_OK);
+  }
+  {  // aliasing: exact in-place ADD_MAT is allowed, partial overlap is not
+    coda_epi_desc e = d; e.n_ops = 1; e.ops[0].kind = CODA_OP_ADD_MAT; e.ops[0].ld = N;
+    e.ops[0].in = d.D; e.ops[0].in_dtype = CODA_BF16;
+    EXPECT(coda_validate(A, B, M, N, K, &e, 0) == CODA_OK);
+    e.ops[0].in = P(reinterpret_cast<uintptr_t>(d.D) + 16);
+    EXPECT(coda_validate(A, B, M, N, K, &e, 0) == CODA_ERR_INVALID_ARG);
+    e.ops[0].in = d.D; e.ops[0].in_dtype = CODA_F32;
+    EXPECT(coda_validate(A, B, M, N, K, &e, 0) == CODA_ERR_INVALID_ARG);
+    coda_epi_desc f = d; f.D = Pm(reinterpret_cast<uintptr_t>(A) + 256);
+    EXPECT(coda_validate(A, B, M, N, K, &f, 0) == CODA_ERR_INVALID_ARG);   // D overlaps A
+  }
+  {  // reductions: outputs, stride, interleaved columns, workspace
+    coda_epi_desc e = d; e.n_ops = 2;
+    e.ops[0].kind = CODA_OP_ROW_SUM; e.ops[0].out = Pm(0x50000000); e.ops[0].out_stride = 2;
+    e.ops[1].kind = CODA_OP_ROW_SUMSQ; e.ops[1].out = Pm(0x50000004); e.ops[1].out_stride = 2;
+    const size_t ws = coda_workspace_size(M, N, K, &e, 0);
+    EXPECT(ws > 0);   // 520 columns span several tiles
+    EXPECT(coda_validate(A, B, M, N, K, &e, 0) == CODA_ERR_WORKSPACE);
+    e.workspace = Pm(0x60000000); e.workspace_bytes = ws - 1;
+    EXPECT(coda_validate(A, B, M, N, K, &e, 0) == CODA_ERR_WORKSPACE);
+    e.workspace_bytes = ws;
+    EXPECT(coda_validate(A, B, M, N, K, &e, 0) == CODA_OK);
+    coda_epi_desc f = e; f.ops[1].out = Pm(0x50000000);
+    EXPECT(coda_validate(A, B, M, N, K, &f, 0) == CODA_ERR_INVALID_ARG);   // same elements
+    f = e; f.ops[1].out_stride = 0;
+    EXPECT(coda_validate(A, B, M, N, K, &f, 0) == CODA_ERR_INVALID_ARG);
+    f = e; f.ops[1].out = nullptr;
+    EXPECT(coda_validate(A, B, M, N, K, &f, 0) == CODA_ERR_INVALID_ARG);
+    f = e; f.ops[1].out = Pm(0x50000002);
+    EXPECT(coda_validate(A, B, M, N, K, &f, 0) == CODA_ERR_UNSUPPORTED);
+    coda_epi_desc g = d; g.n_ops = CODA_MAX_REDUCTIONS + 1;
+    for (int i = 0; i < g.n_ops; ++i) {
+      g.ops[i].kind = CODA_OP_ROW_SUM; g.ops[i].out = Pm(0x50000000 + 0x100000 * i); g.ops[i].out_stride = 1;
+    }
+    EXPECT(coda_validate(A, B, M, N, K, &g, 0) == CODA_ERR_UNSUPPORTED);
+    // unfused workspace covers normalised A and two intermediates
+    coda_epi_desc u = d; u.n_ops = 1; u.ops[0].kind = CODA_OP_GELU_TANH;
+    EXPECT(coda_workspace_size(M, N, K, &u, 1) >= size_t(2 * M * N * 2));
+    EXPECT(coda_validate(A, B, M, N, K, &u, 1) == CODA_ERR_WORKSPACE);
+  }
+  {  // tile configs
+    int bm = 0, bn = 0, bk = 0, w = 0;
+    EXPECT(coda_num_tile_configs() >= 1);
+    EXPECT(coda_tile_config(1, &bm, &bn, &bk, &w) == CODA_OK && bm > 0 && bn > 0 && bk > 0 && w > 0);
+    EXPECT(coda_tile_config(0, &bm, &bn, &bk, &w) == CODA_ERR_INVALID_ARG);
+  }
+  EXPECT(std::strcmp(coda_status_string(CODA_ERR_WORKSPACE), "CODA_ERR_WORKSPACE") == 0);
+  if (failures == 0) std::printf("ALL OK\n");
+  return failures == 0 ? 0 : 1;
+}
