@@ -1,24 +1,37 @@
 // Fused GEMM + ordered epilogue for gfx950.
 //
-// One workgroup computes one bm x bn output tile.  The main loop streams A and
-// B tiles global -> registers -> LDS (double buffered: the next K step's loads
-// are in flight while MFMA consumes the current one) and accumulates in fp32
-// with v_mfma_f32_32x32x16_bf16 (bf16 operands) or v_mfma_f32_32x32x2f32 (fp32
-// operands).  The tile is computed transposed (MFMA rows = columns of D), so
-// each lane's accumulators hold runs of 4 consecutive output columns of one row:
-// side operands are read and D is written as 8/16-byte vectors.
+// One workgroup computes one bm x bn output tile; its waves form a wm x wn grid
+// over the tile.  The tile is computed transposed (MFMA rows = columns of D):
+// the W fragment is the MFMA A operand and the X fragment the MFMA B operand,
+// so each lane's accumulators hold runs of 4 consecutive output columns.
 //
-// With the deferred RMS op, the A loader multiplies each A element by gamma[k]
-// (rounded to the operand dtype) before it goes to LDS and keeps the raw
-// element's square in an fp32 per-row sum; after the last K step the per-row
-// factor 1/sqrt(sum/K + eps) is applied to the accumulators (the per-row scale
-// of a row-wise norm moved past the projection: the zeli.app "augment_me"
-// comment; the agentlenshq.com page, "CODA's approach").
+// Main loop (bf16 operands), two LDS stages, one barrier per K step of 64:
+//   * operand tiles go global -> LDS with buffer loads that write LDS directly
+//     (16 bytes per lane); out-of-range offsets read as zero, which fills the
+//     M / N / K tails;
+//   * LDS tiles are XOR-swizzled at 16-byte granularity so the MFMA operand
+//     reads (ds_read_b128 for K-contiguous tiles, the transposing
+//     ds_read_b64_tr_b16 for the N-contiguous W tile) are bank-conflict free:
+//     ds_read_b128 serves 16 lanes (256 bytes) per cycle on gfx950, so the
+//     16 rows a K-contiguous read touches must land on distinct 16-byte bank
+//     slots, which the row swizzle swz(r) = (r & 7) ^ ((r >> 3) & 1) provides;
+//   * MFMA fragments for the next k16 step are read while the current step's
+//     v_mfma_f32_32x32x16_bf16 instructions run.
+// With the deferred RMS op, A instead goes through registers: each element is
+// multiplied by gamma[k] and rounded to bf16 on its way into LDS, and its raw
+// square is added to an fp32 per-row sum (the per-row scale of a row-wise norm
+// moved past the projection: the "augment_me" comment on the zeli.app page;
+// the agentlenshq.com page, "CODA's approach").  fp32 operands (a small tile,
+// v_mfma_f32_32x32x2f32) use a register-staged, padded LDS layout.
 //
-// The epilogue walks the op list in order on the accumulators (d9bl.com page,
-// section 3.2), then stores D once.  Row reductions combine lanes, then waves
-// through LDS, then the workgroups of one tile row through a workspace of
-// partial sums finished by the last workgroup to arrive (deterministic order).
+// Epilogue: each wave moves its accumulators, one 32-row block at a time,
+// through a private LDS region into a row-major layout where every lane owns
+// chunks of 8 consecutive columns.  The op list then runs in order on fp32
+// values (d9bl.com page, section 3.2), side operands are read and D is written
+// as whole 16-byte row chunks, and row reductions combine the lanes of a row,
+// then the waves of the tile through LDS, then the workgroups of a tile row
+// through a workspace of partial sums finished by the last workgroup to arrive
+// (a fixed summation order, so results are bitwise repeatable).
 #pragma once
 
 #include "coda_device.h"
@@ -40,7 +53,6 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-
 // Workgroups are dealt to the 8 XCDs round-robin.  Give each XCD a contiguous
 // range of logical tiles, and order the logical tiles in groups of 8 tile rows
 // (column-major inside a group), so concurrently resident tiles on one XCD
@@ -59,79 +71,104 @@ __device__ __forceinline__ void map_tile(int bid, int gm, int gn, int& tm, int& 
   tn = rem / gsz;
 }
 
-template <int BM_, int BN_, int BK_, int WM_, int WN_, bool F32_, bool BKN_, bool RMS_>
-struct Cfg {
-  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
-  static constexpr bool F32 = F32_, BKN = BKN_, RMS = RMS_;
-  static constexpr int NT = 64 * WM * WN;
-  static constexpr int WTM = BM / WM, WTN = BN / WN;
-  static constexpr int MI = WTM / 32, NI = WTN / 32;
-  static constexpr int ES = F32 ? 4 : 2;     // operand element size
-  static constexpr int CE = 16 / ES;         // elements per 16-byte chunk
-  static constexpr int KCH = BK / CE;        // chunks per K row of a K-major tile
-  // LDS row strides (elements).  bf16: 16-byte pad on K-major rows and 32-byte
-  // pad on N-major rows make the MFMA operand reads bank-conflict free.  fp32:
-  // one-element pad on K-major rows (element-wise reads and writes).
-  static constexpr int SA = F32 ? BK + 1 : BK + 8;
-  static constexpr int SB = F32 ? BN + 4 : BN + 16;
-  static constexpr int A_ELEMS = BM * SA;
-  static constexpr int B_ELEMS = BKN ? BK * SB : BN * SA;
-  static constexpr int STAGE = A_ELEMS + B_ELEMS;
-  static constexpr int LDS_BYTES = 2 * STAGE * ES;
-  // loader geometry
-  static constexpr int A_CH = BM * KCH / NT;          // 16-byte chunks of A per thread
-  static constexpr int A_RSTEP = NT / KCH;            // rows between them
-  static constexpr int BKN_CPR = BN / CE;             // chunks per row of an N-major B tile
-  static constexpr int B_CH = BKN ? BK * BKN_CPR / NT : BN * KCH / NT;
-  static constexpr int B_RSTEP = BKN ? NT / BKN_CPR : NT / KCH;
-  static_assert(BM % (32 * WM) == 0 && BN % (32 * WN) == 0, "wave tile must be a multiple of 32");
-  static_assert((BM * KCH) % NT == 0 && A_CH >= 1, "A tile must split evenly over threads");
-  static_assert(B_CH >= 1, "B tile must split evenly over threads");
-  static_assert(NT % KCH == 0 && A_RSTEP % 8 == 0, "loader rows");
-  // epilogue scratch (floats), reusing the main-loop LDS
-  static constexpr int EPI_FLOATS = BM + CODA_MAX_REDUCTIONS * WN * BM + 4;
-  static_assert(EPI_FLOATS * 4 <= LDS_BYTES, "epilogue scratch must fit");
-};
-
-// ---------------------------------------------------------------------------
-// epilogue on the accumulators
-// ---------------------------------------------------------------------------
-
 // The kernel reads its argument block straight from the kernarg segment
 // (constant address space): the op list is indexed with a runtime op number,
 // and indexing a by-value parameter would make the compiler copy the whole
 // block to per-lane scratch memory.
 typedef const __attribute__((address_space(4))) FusedArgs* KArgs;
+typedef const __attribute__((address_space(4))) DevOp& KOp;
+typedef __attribute__((address_space(3))) void* LdsPtr;
+typedef __attribute__((address_space(3))) i16x4_t LdsI16x4;
 
-template <class C>
-struct Geo {
-  int M;
-  int m[C::MI];     // global row of each m-block for this lane
-  int nb;           // global column of (ni = 0, g = 0, e = 0) for this lane
-  int mloc0;        // local row (within the tile) of m-block 0
-  int wn;
-  int lane;
+template <int BM_, int BN_, int WM_, int WN_, bool F32_, bool BKN_, bool RMS_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr bool F32 = F32_, BKN = BKN_, RMS = RMS_;
+  static constexpr int NW = WM * WN;
+  static constexpr int NT = 64 * NW;
+  static constexpr int WTM = BM / WM, WTN = BN / WN;
+  static constexpr int MI = WTM / 32, NI = WTN / 32;
+  static constexpr int BK = F32 ? 32 : 64;
+  static_assert(BM % (32 * WM) == 0 && BN % (32 * WN) == 0, "wave tile must be a multiple of 32");
+
+  // ---- bf16 main loop: swizzled, unpadded stages ----
+  static constexpr int A_BYTES = BM * 128;            // [BM][64] bf16
+  static constexpr int B_BYTES = BN * 128;            // [64][BN] or [BN][64] bf16
+  static constexpr int A_BLK = BM / 8;                // 1 KB blocks of A per stage
+  static constexpr int B_BLK = BN / 8;
+  static_assert(F32 || (A_BLK % NW == 0 && B_BLK % NW == 0), "1 KB blocks must split over the waves");
+  static constexpr int A_BPW = A_BLK / NW, B_BPW = B_BLK / NW;   // blocks per wave
+  static constexpr int KN_CPR = BN / 8;               // 16-byte chunks per row of an N-major W tile
+  static constexpr int KN_RPB = 64 / KN_CPR;          // rows of it per 1 KB block
+
+  // ---- fp32 main loop: register staged, padded ----
+  static constexpr int SA32 = BK + 1, SB32 = BN + 4;
+  static constexpr int A32_CH = BM * (BK / 4) / NT;    // 16-byte chunks per thread
+  static constexpr int B32_CH = BN * (BK / 4) / NT;
+
+  static constexpr int STAGE_BYTES =
+      F32 ? (BM * SA32 + (BKN ? BK * SB32 : BN * SA32)) * 4 : A_BYTES + B_BYTES;
+
+  // ---- epilogue ----
+  static constexpr int CPR = WTN / 8;                 // 8-column chunks per wave-tile row
+  static constexpr int CPL = 32 * CPR / 64;           // chunks per lane per 32-row block
+  static constexpr int RSTEP = 64 / CPR;              // rows between a lane's chunks
+  static constexpr int REGION_BYTES = 32 * WTN * 4;   // per-wave fp32 staging of one block
+  static constexpr int EPI_REGION_OFF = 0;
+  static constexpr int EPI_RED_OFF = NW * REGION_BYTES;
+  static constexpr int EPI_RINV_OFF = EPI_RED_OFF + CODA_MAX_REDUCTIONS * WN * BM * 4;
+  static constexpr int EPI_FLAG_OFF = EPI_RINV_OFF + BM * 4;
+  static constexpr int EPI_BYTES = EPI_FLAG_OFF + 16;
+
+  static constexpr int LDS_BYTES = (2 * STAGE_BYTES > EPI_BYTES) ? 2 * STAGE_BYTES : EPI_BYTES;
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  static_assert(CPR >= 4 && CPR <= 16 && (CPR & (CPR - 1)) == 0, "epilogue lane layout");
 };
 
-template <class C, bool PAIRED>
-__device__ __forceinline__ int col_of(const Geo<C>& g, int ni, int grp) {
-  const int c = g.nb + 32 * ni + 8 * grp;
-  return PAIRED ? (c >> 1) : c;
+// ---------------------------------------------------------------------------
+// epilogue: ops on a lane's row chunks (values v[j][0..7] = columns
+// col[j] .. col[j]+7 of row row[j]; after SWIGLU_PAIR the first 4 hold the
+// 4 output columns col[j]/2 .. col[j]/2 + 3)
+// ---------------------------------------------------------------------------
+
+template <int CPL>
+struct Chunks {
+  float v[CPL][8];
+  int row[CPL];     // global row
+  int mloc[CPL];    // row within the tile
+  int col;          // global first column of the lane's chunk (same for every j)
+};
+
+template <bool PAIRED>
+__device__ __forceinline__ void load_cols(const void* p, int dtype, long long col, long long width, float (&x)[8]) {
+  if (PAIRED) {
+    float t[4];
+    load4(p, dtype, col, width, t);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = t[e];
+#pragma unroll
+    for (int e = 4; e < 8; ++e) x[e] = 0.0f;
+  } else {
+    float t[4], u[4];
+    load4(p, dtype, col, width, t);
+    load4(p, dtype, col + 4, width, u);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[e] = t[e];
+      x[4 + e] = u[e];
+    }
+  }
 }
 
-// Applies ops[o..] to one 32 x 32 accumulator block (m-block mi, n-block ni)
-// until the end of the list or a SWIGLU_PAIR (whose index is returned).  One
-// block at a time keeps the epilogue's live set to the accumulators plus 16
-// side-operand values.  Row reductions add the block's share of each row into
-// the wave's slot of `red` (assigned on the first n-block, accumulated after).
+// Applies ops[o..] until the end of the list or a SWIGLU_PAIR (returned index).
 template <class C, bool PAIRED>
-__device__ __forceinline__ int run_ops(f32x16_t& acc, KArgs a, int o, const Geo<C>& g, int mi, int ni,
-                                       float* red) {
-  constexpr int EPG = PAIRED ? 2 : 4;   // live elements per group of 4 slots
-  const int row = g.m[mi];
-  const bool row_ok = row < g.M;
+__device__ __forceinline__ int run_ops(Chunks<C::CPL>& ch, KArgs a, int o, int M, int lane, int wn, float* red,
+                                       int pf_op, const u32x4_t (&pf)[C::CPL]) {
+  constexpr int CPL = C::CPL;
+  constexpr int EPC = PAIRED ? 4 : 8;   // live values per chunk
+  const int col = PAIRED ? ch.col >> 1 : ch.col;
   for (; o < a->n_ops; ++o) {
-    const __attribute__((address_space(4))) DevOp& op = a->ops[o];
+    KOp op = a->ops[o];
     const int kind = op.kind;
     if (!PAIRED && kind == CODA_OP_SWIGLU_PAIR) return o;
     const int width = op.width;
@@ -139,95 +176,93 @@ __device__ __forceinline__ int run_ops(f32x16_t& acc, KArgs a, int o, const Geo<
       case CODA_OP_SCALE: {
         const float s = op.scalar;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] *= s;
+        for (int j = 0; j < CPL; ++j)
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) ch.v[j][e] *= s;
         break;
       }
       case CODA_OP_SCALE_ROW:
       case CODA_OP_ADD_ROW: {
         const bool add = kind == CODA_OP_ADD_ROW;
-        const float v = row_ok ? load_elem(op.in, op.dtype, row) : 0.0f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] = add ? acc[r] + v : acc[r] * v;
+        for (int j = 0; j < CPL; ++j) {
+          const float x = ch.row[j] < M ? load_elem(op.in, op.dtype, ch.row[j]) : 0.0f;
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) ch.v[j][e] = add ? ch.v[j][e] + x : ch.v[j][e] * x;
+        }
         break;
       }
       case CODA_OP_SCALE_COL:
       case CODA_OP_ADD_COL: {
         const bool add = kind == CODA_OP_ADD_COL;
+        float x[8];
+        load_cols<PAIRED>(op.in, op.dtype, col, width, x);
 #pragma unroll
-        for (int grp = 0; grp < 4; ++grp) {
-          float v[4];
-          if (PAIRED) {
-            float t[2];
-            load2(op.in, op.dtype, col_of<C, PAIRED>(g, ni, grp), width, t);
-            v[0] = t[0]; v[1] = t[1]; v[2] = 0.f; v[3] = 0.f;
-          } else {
-            load4(op.in, op.dtype, col_of<C, PAIRED>(g, ni, grp), width, v);
-          }
+        for (int j = 0; j < CPL; ++j)
 #pragma unroll
-          for (int e = 0; e < EPG; ++e) {
-            const float x = acc[4 * grp + e];
-            acc[4 * grp + e] = add ? x + v[e] : x * v[e];
-          }
-        }
+          for (int e = 0; e < EPC; ++e) ch.v[j][e] = add ? ch.v[j][e] + x[e] : ch.v[j][e] * x[e];
         break;
       }
       case CODA_OP_ADD_MAT:
       case CODA_OP_MUL_DGELU_TANH: {
-        if (!row_ok) break;
         const bool addm = kind == CODA_OP_ADD_MAT;
         const float beta = op.scalar;
-        const char* base = static_cast<const char*>(op.in) + (long long)row * op.ld * (op.dtype == CODA_BF16 ? 2 : 4);
+        const int esz = op.dtype == CODA_BF16 ? 2 : 4;
+        float x[CPL][8];
+        if (!PAIRED && o == pf_op) {
+          // prefetched bf16 row chunks
 #pragma unroll
-        for (int grp = 0; grp < 4; ++grp) {
-          const int c = col_of<C, PAIRED>(g, ni, grp);
-          float v[4];
-          if (PAIRED) {
-            float t[2];
-            load2(base, op.dtype, c, width, t);
-            v[0] = t[0]; v[1] = t[1]; v[2] = 0.f; v[3] = 0.f;
+          for (int j = 0; j < CPL; ++j)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              x[j][2 * w] = bf16_lo(pf[j][w]);
+              x[j][2 * w + 1] = bf16_hi(pf[j][w]);
+            }
+        } else {
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+          if (ch.row[j] < M) {
+            load_cols<PAIRED>(static_cast<const char*>(op.in) + (long long)ch.row[j] * op.ld * esz, op.dtype, col,
+                              width, x[j]);
           } else {
-            load4(base, op.dtype, c, width, v);
-          }
 #pragma unroll
-          for (int e = 0; e < EPG; ++e) {
-            const float x = acc[4 * grp + e];
-            acc[4 * grp + e] = addm ? x + beta * v[e] : x * gelu_tanh_grad_f(v[e]);
+            for (int e = 0; e < 8; ++e) x[j][e] = 0.0f;
           }
         }
+        }
+#pragma unroll
+        for (int j = 0; j < CPL; ++j)
+#pragma unroll
+          for (int e = 0; e < EPC; ++e)
+            ch.v[j][e] = addm ? ch.v[j][e] + beta * x[j][e] : ch.v[j][e] * gelu_tanh_grad_f(x[j][e]);
         break;
       }
       case CODA_OP_GELU_TANH:
       case CODA_OP_SILU: {
         const bool gelu = kind == CODA_OP_GELU_TANH;
 #pragma unroll
-        for (int grp = 0; grp < 4; ++grp)
+        for (int j = 0; j < CPL; ++j)
 #pragma unroll
-          for (int e = 0; e < EPG; ++e) {
-            const float x = acc[4 * grp + e];
-            acc[4 * grp + e] = gelu ? gelu_tanh_f(x) : silu_f(x);
-          }
+          for (int e = 0; e < EPC; ++e) ch.v[j][e] = gelu ? gelu_tanh_f(ch.v[j][e]) : silu_f(ch.v[j][e]);
         break;
       }
       case CODA_OP_ROW_SUM:
       case CODA_OP_ROW_MEAN:
       case CODA_OP_ROW_SUMSQ: {
         const bool sq = kind == CODA_OP_ROW_SUMSQ;
-        float p = 0.0f;
+        float* dst = red + (op.red_slot * C::WN + wn) * C::BM;
 #pragma unroll
-        for (int grp = 0; grp < 4; ++grp) {
-          const int c = col_of<C, PAIRED>(g, ni, grp);
+        for (int j = 0; j < CPL; ++j) {
+          float p = 0.0f;
 #pragma unroll
-          for (int e = 0; e < EPG; ++e) {
-            const float x = acc[4 * grp + e];
-            const float t = sq ? x * x : x;
-            p += (c + e < width) ? t : 0.0f;
+          for (int e = 0; e < EPC; ++e) {
+            const float x = ch.v[j][e];
+            p += (col + e < width) ? (sq ? x * x : x) : 0.0f;
           }
-        }
-        // lanes l and l+32 hold the same row
-        p += __shfl_xor(p, 32);
-        if (g.lane < 32) {
-          float* dst = red + (op.red_slot * C::WN + g.wn) * C::BM + g.mloc0 + 32 * mi + g.lane;
-          *dst = (ni == 0) ? p : *dst + p;
+          // the CPR lanes of a row are consecutive
+#pragma unroll
+          for (int off = 1; off < C::CPR; off <<= 1) p += __shfl_xor(p, off);
+          if ((lane & (C::CPR - 1)) == 0) dst[ch.mloc[j]] = p;
         }
         break;
       }
@@ -238,76 +273,61 @@ __device__ __forceinline__ int run_ops(f32x16_t& acc, KArgs a, int o, const Geo<
   return o;
 }
 
-// out[j] = silu(v[2j]) * v[2j+1] inside each lane's group of 4 columns:
-// slot 4g+0 <- pair (4g+0, 4g+1), slot 4g+1 <- pair (4g+2, 4g+3).
-__device__ __forceinline__ void swiglu_pair_acc(f32x16_t& acc) {
+template <class C>
+__device__ __forceinline__ void swiglu_chunks(Chunks<C::CPL>& ch) {
 #pragma unroll
-  for (int grp = 0; grp < 4; ++grp) {
-    const float g0 = acc[4 * grp + 0], u0 = acc[4 * grp + 1];
-    const float g1 = acc[4 * grp + 2], u1 = acc[4 * grp + 3];
-    acc[4 * grp + 0] = silu_f(g0) * u0;
-    acc[4 * grp + 1] = silu_f(g1) * u1;
-  }
+  for (int j = 0; j < C::CPL; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ch.v[j][e] = silu_f(ch.v[j][2 * e]) * ch.v[j][2 * e + 1];
 }
 
 template <class C, bool PAIRED>
-__device__ __forceinline__ void store_d(const f32x16_t& acc, KArgs a, const Geo<C>& g, int mi, int ni) {
+__device__ __forceinline__ void store_chunks(const Chunks<C::CPL>& ch, KArgs a, int M) {
   const int width = a->out_width;
-  const int row = g.m[mi];
-  if (row >= g.M) return;
-  const long long rowoff = (long long)row * a->ldd;
+  const int col = PAIRED ? ch.col >> 1 : ch.col;
+  constexpr int EPC = PAIRED ? 4 : 8;
 #pragma unroll
-  for (int grp = 0; grp < 4; ++grp) {
-    const int c = col_of<C, PAIRED>(g, ni, grp);
-    const float v0 = acc[4 * grp + 0], v1 = acc[4 * grp + 1];
-    const float v2 = acc[4 * grp + 2], v3 = acc[4 * grp + 3];
+  for (int j = 0; j < C::CPL; ++j) {
+    if (ch.row[j] >= M) continue;
+    const long long off = (long long)ch.row[j] * a->ldd + col;
     if (a->d_dtype == CODA_BF16) {
-      uint16_t* d = static_cast<uint16_t*>(a->D) + rowoff + c;
-      if (PAIRED) {
-        if (c + 1 < width) {
-          *reinterpret_cast<uint32_t*>(d) = pack_bf16x2(v0, v1);
-        } else if (c < width) {
-          d[0] = f32_to_bf16_bits(v0);
-        }
-      } else {
-        if (c + 3 < width) {
+      uint16_t* d = static_cast<uint16_t*>(a->D) + off;
+      if (col + EPC - 1 < width) {
+        if (PAIRED) {
           u32x2_t w;
-          w[0] = pack_bf16x2(v0, v1);
-          w[1] = pack_bf16x2(v2, v3);
+          w[0] = pack_bf16x2(ch.v[j][0], ch.v[j][1]);
+          w[1] = pack_bf16x2(ch.v[j][2], ch.v[j][3]);
           *reinterpret_cast<u32x2_t*>(d) = w;
         } else {
-          const float vv[4] = {v0, v1, v2, v3};
+          u32x4_t w;
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (c + e < width) d[e] = f32_to_bf16_bits(vv[e]);
-        }
-      }
-    } else {
-      float* d = static_cast<float*>(a->D) + rowoff + c;
-      if (PAIRED) {
-        if (c + 1 < width) {
-          d[0] = v0;
-          d[1] = v1;
-        } else if (c < width) {
-          d[0] = v0;
+          for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(ch.v[j][2 * e], ch.v[j][2 * e + 1]);
+          *reinterpret_cast<u32x4_t*>(d) = w;
         }
       } else {
-        if (c + 3 < width) {
-          f32x4_t w;
-          w[0] = v0; w[1] = v1; w[2] = v2; w[3] = v3;
-          *reinterpret_cast<f32x4_t*>(d) = w;
-        } else {
-          const float vv[4] = {v0, v1, v2, v3};
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (c + e < width) d[e] = vv[e];
+        for (int e = 0; e < EPC; ++e)
+          if (col + e < width) d[e] = f32_to_bf16_bits(ch.v[j][e]);
+      }
+    } else {
+      float* d = static_cast<float*>(a->D) + off;
+      if (col + EPC - 1 < width) {
+#pragma unroll
+        for (int e = 0; e < EPC; e += 4) {
+          f32x4_t w;
+          w[0] = ch.v[j][e]; w[1] = ch.v[j][e + 1]; w[2] = ch.v[j][e + 2]; w[3] = ch.v[j][e + 3];
+          *reinterpret_cast<f32x4_t*>(d + e) = w;
         }
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPC; ++e)
+          if (col + e < width) d[e] = ch.v[j][e];
       }
     }
   }
 }
 
-__device__ __forceinline__ void write_reduction(const __attribute__((address_space(4))) DevOp& op, int row, float v) {
+__device__ __forceinline__ void write_reduction(KOp op, int row, float v) {
   if (op.kind == CODA_OP_ROW_MEAN) v = v / float(op.width);
   op.out[(long long)row * op.out_stride] = v;
 }
@@ -321,18 +341,20 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
   (void)args;
   const KArgs a = (KArgs)__builtin_amdgcn_kernarg_segment_ptr();
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, MI = C::MI, NI = C::NI;
-  constexpr int SA = C::SA, SB = C::SB, ES = C::ES, CE = C::CE, KCH = C::KCH;
-  __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave / C::WN, wn = wave % C::WN;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int swz_l = (l32 & 7) ^ ((l32 >> 3) & 1);   // LDS row swizzle; depends on the row mod 16 only
 
   int tile_m, tile_n;
   map_tile(blockIdx.x, a->grid_m, a->grid_n, tile_m, tile_n);
   const int m0 = tile_m * BM, n0 = tile_n * BN;
   const int M = a->M, N = a->N, K = a->K;
+  const long long lda = a->lda, ldb = a->ldb;
 
   f32x16_t acc[MI][NI];
 #pragma unroll
@@ -342,168 +364,249 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
 
-  // ---- loader geometry ----
-  const int a_c = tid % KCH, a_r = tid / KCH;
-  const int b_c = C::BKN ? tid % C::BKN_CPR : tid % KCH;
-  const int b_r = C::BKN ? tid / C::BKN_CPR : tid / KCH;
-  const char* Abase = static_cast<const char*>(a->A) + ((long long)m0 * a->lda) * ES;
-  const char* Bbase = C::BKN ? static_cast<const char*>(a->B) + (long long)n0 * ES
-                             : static_cast<const char*>(a->B) + ((long long)n0 * a->ldb) * ES;
-  const uint32_t a_row_bytes = uint32_t(a->lda * ES);
-  const uint32_t b_row_bytes = uint32_t(a->ldb * ES);
-  const long long a_extent0 = ((long long)(M - 1 - m0) * a->lda + K) * ES;  // bytes from tile base
-  const long long b_extent0 = C::BKN ? ((long long)(K - 1) * a->ldb + (N - n0)) * ES
-                                     : ((long long)(N - 1 - n0) * a->ldb + K) * ES;
-
-  u32x4_t areg[C::A_CH], breg[C::B_CH];
-  u32x4_t greg;           // gamma chunk (RMS)
-  float ss[C::A_CH];      // per-row sum of squares (RMS)
-#pragma unroll
-  for (int i = 0; i < C::A_CH; ++i) ss[i] = 0.0f;
-
   const int KT = (K + BK - 1) / BK;
+  float ss[C::F32 ? C::A32_CH : C::A_BPW];   // per-row sums of squares (RMS)
+#pragma unroll
+  for (int i = 0; i < (C::F32 ? C::A32_CH : C::A_BPW); ++i) ss[i] = 0.0f;
 
-  auto gload = [&](int kt) {
-    const int k0 = kt * BK;
-    const bool kin_a = k0 + a_c * CE < K;
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(Abase + (long long)k0 * ES, a_extent0 - (long long)k0 * ES);
-#pragma unroll
-    for (int i = 0; i < C::A_CH; ++i) {
-      const uint32_t off = uint32_t(a_r + i * C::A_RSTEP) * a_row_bytes + uint32_t(a_c * 16);
-      areg[i] = buffer_load16(ra, kin_a ? off : kOobOffset);
-    }
-    if (C::BKN) {
-      const __amdgpu_buffer_rsrc_t rb =
-          make_rsrc(Bbase + (long long)k0 * a->ldb * ES, b_extent0 - (long long)k0 * a->ldb * ES);
-#pragma unroll
-      for (int i = 0; i < C::B_CH; ++i) {
-        const uint32_t off = uint32_t(b_r + i * C::B_RSTEP) * b_row_bytes + uint32_t(b_c * 16);
-        breg[i] = buffer_load16(rb, off);
-      }
-    } else {
-      const bool kin_b = k0 + b_c * CE < K;
-      const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bbase + (long long)k0 * ES, b_extent0 - (long long)k0 * ES);
-#pragma unroll
-      for (int i = 0; i < C::B_CH; ++i) {
-        const uint32_t off = uint32_t(b_r + i * C::B_RSTEP) * b_row_bytes + uint32_t(b_c * 16);
-        breg[i] = buffer_load16(rb, kin_b ? off : kOobOffset);
-      }
-    }
-    if (C::RMS) {
-      const __amdgpu_buffer_rsrc_t rg = make_rsrc(a->gamma, (long long)K * ES);
-      greg = buffer_load16(rg, uint32_t((k0 + a_c * CE) * ES));
-    }
-  };
+  if constexpr (!C::F32) {
+    // ================= bf16 main loop =================
+    const char* Abase = static_cast<const char*>(a->A) + (long long)m0 * lda * 2;
+    const char* Bbase = C::BKN ? static_cast<const char*>(a->B) + (long long)n0 * 2
+                               : static_cast<const char*>(a->B) + (long long)n0 * ldb * 2;
+    const long long a_ext0 = ((long long)(M - 1 - m0) * lda + K) * 2;
+    const long long b_ext0 = C::BKN ? ((long long)(K - 1) * ldb + (N - n0)) * 2
+                                    : ((long long)(N - 1 - n0) * ldb + K) * 2;
+    // loader lane geometry: a 1 KB block q holds rows 8q .. 8q+7 of a K-major
+    // tile; lane writes physical 16-byte slot (lane & 7) of row 8q + (lane >> 3),
+    // which holds logical chunk (lane & 7) ^ swz(row), swz(r) = (r & 7) ^ ((r >> 3) & 1)
+    // (NW is even, so q & 1 == wave & 1 for every block a wave loads)
+    const int kq_row = lane >> 3;
+    const int kq_chunk = (lane & 7) ^ kq_row ^ (wave & 1);
+    static_assert(C::F32 || C::NW % 2 == 0, "wave count must be even");
+    // N-major W tile: a 1 KB block holds KN_RPB rows of KN_CPR chunks
+    const int kn_row = lane / C::KN_CPR;
+    const int kn_slot = lane % C::KN_CPR;
 
-  auto sstore = [&](int buf) {
-    char* stage = smem + buf * C::STAGE * ES;
-    if constexpr (!C::F32) {
-      uint16_t* As = reinterpret_cast<uint16_t*>(stage);
-      uint16_t* Bs = As + C::A_ELEMS;
-      float gf[8];
-      if (C::RMS) {
+    u32x4_t areg[C::RMS ? C::A_BPW : 1];
+    u32x4_t greg;   // the gamma chunk matching this lane's A chunks
+
+    auto issue_loads = [&](int kt, int stage) {
+      const int k0 = kt * 64;
+      char* As = smem + stage * C::STAGE_BYTES;
+      char* Bs = As + C::A_BYTES;
+      const __amdgpu_buffer_rsrc_t ra = make_rsrc(Abase + (long long)k0 * 2, a_ext0 - (long long)k0 * 2);
+#pragma unroll
+      for (int i = 0; i < C::A_BPW; ++i) {
+        const int q = wave + C::NW * i;
+        const uint32_t off = (k0 + 8 * kq_chunk < K)
+                                 ? uint32_t(8 * q + kq_row) * uint32_t(lda * 2) + uint32_t(kq_chunk * 16)
+                                 : kOobOffset;
+        if constexpr (C::RMS) {
+          areg[i] = buffer_load16(ra, off);
+        } else {
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (LdsPtr)(As + q * 1024), 16, (int)off, 0, 0, 0);
+        }
+      }
+      if constexpr (C::BKN) {
+        const __amdgpu_buffer_rsrc_t rb =
+            make_rsrc(Bbase + (long long)k0 * ldb * 2, b_ext0 - (long long)k0 * ldb * 2);
+#pragma unroll
+        for (int i = 0; i < C::B_BPW; ++i) {
+          const int q = wave + C::NW * i;
+          const int k = q * C::KN_RPB + kn_row;
+          const int c = kn_slot ^ (2 * (k & 3));
+          const uint32_t off = uint32_t(k) * uint32_t(ldb * 2) + uint32_t(c * 16);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (LdsPtr)(Bs + q * 1024), 16, (int)off, 0, 0, 0);
+        }
+      } else {
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bbase + (long long)k0 * 2, b_ext0 - (long long)k0 * 2);
+#pragma unroll
+        for (int i = 0; i < C::B_BPW; ++i) {
+          const int q = wave + C::NW * i;
+          const uint32_t off = (k0 + 8 * kq_chunk < K)
+                                   ? uint32_t(8 * q + kq_row) * uint32_t(ldb * 2) + uint32_t(kq_chunk * 16)
+                                   : kOobOffset;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (LdsPtr)(Bs + q * 1024), 16, (int)off, 0, 0, 0);
+        }
+      }
+      if constexpr (C::RMS) {
+        const __amdgpu_buffer_rsrc_t rg = make_rsrc(a->gamma, (long long)K * 2);
+        greg = buffer_load16(rg, uint32_t((k0 + 8 * kq_chunk) * 2));
+      }
+    };
+
+    // RMS: gain and sum of squares on the A chunks held in registers, then into LDS
+    auto rms_store = [&](int stage) {
+      char* As = smem + stage * C::STAGE_BYTES;
+#pragma unroll
+      for (int i = 0; i < C::A_BPW; ++i) {
+        u32x4_t x = areg[i];
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          gf[2 * w] = bf16_lo(greg[w]);
-          gf[2 * w + 1] = bf16_hi(greg[w]);
+          const float lo = bf16_lo(x[w]), hv = bf16_hi(x[w]);
+          ss[i] = fmaf(lo, lo, ss[i]);
+          ss[i] = fmaf(hv, hv, ss[i]);
+          x[w] = pack_bf16x2(lo * bf16_lo(greg[w]), hv * bf16_hi(greg[w]));
         }
+        *reinterpret_cast<u32x4_t*>(As + (wave + C::NW * i) * 1024 + lane * 16) = x;
       }
+    };
+
+    // MFMA operand read offsets (bytes within a stage)
+    // X fragment (MFMA B operand): row wm*WTM + 32 mi + l32, logical chunk 2kk + hi;
+    // the row base is a multiple of 32, so swz(row) = swz(l32)
+    int xa_off[4];
 #pragma unroll
-      for (int i = 0; i < C::A_CH; ++i) {
-        u32x4_t x = areg[i];
-        if (C::RMS) {
+    for (int kk = 0; kk < 4; ++kk)
+      xa_off[kk] = (wm * C::WTM + l32) * 128 + (((2 * kk + hi) ^ swz_l) * 16);
+    // W fragment (MFMA A operand)
+    int wb_off[C::BKN ? NI : 4];
+    if constexpr (C::BKN) {
+      // transposing read: lane (G, s) supplies row 16kk + 8(G/2) + 4h + s/4 at
+      // column 32ni + 16(G%2) + 4(s%4); lane s of each 16-lane group receives
+      // the 4 K-consecutive values of column 16(G%2) + s
+      const int G = lane >> 4, s = lane & 15;
+      const int r = s >> 2;
 #pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const float lo = bf16_lo(x[w]), hi = bf16_hi(x[w]);
-            ss[i] = fmaf(lo, lo, ss[i]);
-            ss[i] = fmaf(hi, hi, ss[i]);
-            x[w] = pack_bf16x2(lo * gf[2 * w], hi * gf[2 * w + 1]);
-          }
-        }
-        *reinterpret_cast<u32x4_t*>(As + (a_r + i * C::A_RSTEP) * SA + a_c * 8) = x;
-      }
-#pragma unroll
-      for (int i = 0; i < C::B_CH; ++i) {
-        if (C::BKN)
-          *reinterpret_cast<u32x4_t*>(Bs + (b_r + i * C::B_RSTEP) * SB + b_c * 8) = breg[i];
-        else
-          *reinterpret_cast<u32x4_t*>(Bs + (b_r + i * C::B_RSTEP) * SA + b_c * 8) = breg[i];
+      for (int ni = 0; ni < NI; ++ni) {
+        const int krow = 8 * (G >> 1) + r;
+        const int n = wn * C::WTN + 32 * ni + 16 * (G & 1) + 4 * (s & 3);
+        const int phys = (n >> 3) ^ (2 * r);
+        wb_off[ni] = C::A_BYTES + krow * (BN * 2) + phys * 16 + (n & 7) * 2;
       }
     } else {
-      float* As = reinterpret_cast<float*>(stage);
-      float* Bs = As + C::A_ELEMS;
-      float gf[4];
-      if (C::RMS) {
 #pragma unroll
-        for (int w = 0; w < 4; ++w) gf[w] = __uint_as_float(greg[w]);
+      for (int kk = 0; kk < 4; ++kk)
+        wb_off[kk] = C::A_BYTES + (wn * C::WTN + l32) * 128 + (((2 * kk + hi) ^ swz_l) * 16);
+    }
+
+    auto read_frags = [&](const char* stage, int kk, bf16x8_t (&xf)[MI], bf16x8_t (&wf)[NI]) {
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+        xf[mi] = *reinterpret_cast<const bf16x8_t*>(stage + xa_off[kk] + mi * 32 * 128);
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        if constexpr (C::BKN) {
+          const char* p = stage + wb_off[ni] + kk * 16 * (BN * 2);
+          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LdsI16x4*)(p));
+          const i16x4_t hv = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LdsI16x4*)(p + 4 * (BN * 2)));
+          wf[ni] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hv, 0, 1, 2, 3, 4, 5, 6, 7));
+        } else {
+          wf[ni] = *reinterpret_cast<const bf16x8_t*>(stage + wb_off[kk] + ni * 32 * 128);
+        }
       }
+    };
+
+    auto compute = [&](int stage_idx) {
+      const char* stage = smem + stage_idx * C::STAGE_BYTES;
+      bf16x8_t xf[2][MI], wf[2][NI];
+      read_frags(stage, 0, xf[0], wf[0]);
+      static_for<0, 4>([&](auto kkc) {
+        constexpr int kk = decltype(kkc)::value;
+        if constexpr (kk < 3) read_frags(stage, kk + 1, xf[(kk + 1) & 1], wf[(kk + 1) & 1]);
 #pragma unroll
-      for (int i = 0; i < C::A_CH; ++i) {
-        float* dst = As + (a_r + i * C::A_RSTEP) * SA + a_c * 4;
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < NI; ++ni)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[kk & 1][ni], xf[kk & 1][mi], acc[mi][ni], 0, 0, 0);
+      });
+    };
+
+    if (KT > 0) {
+      issue_loads(0, 0);
+      if constexpr (C::RMS) rms_store(0);
+      for (int kt = 0; kt < KT; ++kt) {
+        // tile kt is in LDS stage kt&1; every wave is done with stage (kt+1)&1
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        const bool more = kt + 1 < KT;
+        if (more) issue_loads(kt + 1, (kt + 1) & 1);
+        compute(kt & 1);
+        if constexpr (C::RMS) {
+          if (more) rms_store((kt + 1) & 1);
+        }
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __syncthreads();
+  } else {
+    // ================= fp32 main loop (small tile, register staged) =================
+    constexpr int SA = C::SA32, SB = C::SB32;
+    constexpr int KCH = BK / 4;   // 16-byte chunks per K row
+    const int a_c = tid % KCH, a_r = tid / KCH;
+    const int bkn_cpr = BN / 4;
+    const int b_c = C::BKN ? tid % bkn_cpr : tid % KCH;
+    const int b_r = C::BKN ? tid / bkn_cpr : tid / KCH;
+    constexpr int A_RSTEP = C::NT / KCH;
+    const int B_RSTEP = C::BKN ? C::NT / bkn_cpr : C::NT / KCH;
+    const char* Abase = static_cast<const char*>(a->A) + (long long)m0 * lda * 4;
+    const char* Bbase = C::BKN ? static_cast<const char*>(a->B) + (long long)n0 * 4
+                               : static_cast<const char*>(a->B) + (long long)n0 * ldb * 4;
+    const long long a_ext0 = ((long long)(M - 1 - m0) * lda + K) * 4;
+    const long long b_ext0 = C::BKN ? ((long long)(K - 1) * ldb + (N - n0)) * 4
+                                    : ((long long)(N - 1 - n0) * ldb + K) * 4;
+    u32x4_t areg[C::A32_CH], breg[C::B32_CH], greg;
+
+    auto gload = [&](int kt) {
+      const int k0 = kt * BK;
+      const bool kin_a = k0 + a_c * 4 < K;
+      const __amdgpu_buffer_rsrc_t ra = make_rsrc(Abase + (long long)k0 * 4, a_ext0 - (long long)k0 * 4);
+#pragma unroll
+      for (int i = 0; i < C::A32_CH; ++i) {
+        const uint32_t off = uint32_t(a_r + i * A_RSTEP) * uint32_t(lda * 4) + uint32_t(a_c * 16);
+        areg[i] = buffer_load16(ra, kin_a ? off : kOobOffset);
+      }
+      if (C::BKN) {
+        const __amdgpu_buffer_rsrc_t rb =
+            make_rsrc(Bbase + (long long)k0 * ldb * 4, b_ext0 - (long long)k0 * ldb * 4);
+#pragma unroll
+        for (int i = 0; i < C::B32_CH; ++i)
+          breg[i] = buffer_load16(rb, uint32_t(b_r + i * B_RSTEP) * uint32_t(ldb * 4) + uint32_t(b_c * 16));
+      } else {
+        const bool kin_b = k0 + b_c * 4 < K;
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bbase + (long long)k0 * 4, b_ext0 - (long long)k0 * 4);
+#pragma unroll
+        for (int i = 0; i < C::B32_CH; ++i) {
+          const uint32_t off = uint32_t(b_r + i * B_RSTEP) * uint32_t(ldb * 4) + uint32_t(b_c * 16);
+          breg[i] = buffer_load16(rb, kin_b ? off : kOobOffset);
+        }
+      }
+      if (C::RMS) {
+        const __amdgpu_buffer_rsrc_t rg = make_rsrc(a->gamma, (long long)K * 4);
+        greg = buffer_load16(rg, uint32_t((k0 + a_c * 4) * 4));
+      }
+    };
+    auto sstore = [&](int buf) {
+      float* As = reinterpret_cast<float*>(smem + buf * C::STAGE_BYTES);
+      float* Bs = As + BM * SA;
+#pragma unroll
+      for (int i = 0; i < C::A32_CH; ++i) {
+        float* dst = As + (a_r + i * A_RSTEP) * SA + a_c * 4;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           float x = __uint_as_float(areg[i][w]);
           if (C::RMS) {
             ss[i] = fmaf(x, x, ss[i]);
-            x = x * gf[w];
+            x = x * __uint_as_float(greg[w]);
           }
           dst[w] = x;
         }
       }
 #pragma unroll
-      for (int i = 0; i < C::B_CH; ++i) {
+      for (int i = 0; i < C::B32_CH; ++i) {
         if (C::BKN) {
-          *reinterpret_cast<u32x4_t*>(Bs + (b_r + i * C::B_RSTEP) * SB + b_c * 4) = breg[i];
+          *reinterpret_cast<u32x4_t*>(Bs + (b_r + i * B_RSTEP) * SB + b_c * 4) = breg[i];
         } else {
-          float* dst = Bs + (b_r + i * C::B_RSTEP) * SA + b_c * 4;
+          float* dst = Bs + (b_r + i * B_RSTEP) * SA + b_c * 4;
 #pragma unroll
           for (int w = 0; w < 4; ++w) dst[w] = __uint_as_float(breg[i][w]);
         }
       }
-    }
-  };
-
-  auto compute = [&](int buf) {
-    const char* stage = smem + buf * C::STAGE * ES;
-    if constexpr (!C::F32) {
-      const uint16_t* As = reinterpret_cast<const uint16_t*>(stage);
-      const uint16_t* Bs = As + C::A_ELEMS;
-      const int l32 = lane & 31, hi = lane >> 5;
-      const int G = lane >> 4, s = lane & 15;
-#pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
-        bf16x8_t xf[MI], wf[NI];
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-          xf[mi] = *reinterpret_cast<const bf16x8_t*>(As + (wm * C::WTM + 32 * mi + l32) * SA + 16 * kk + 8 * hi);
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) {
-          if (C::BKN) {
-            // transposing LDS read: lane (G, s) supplies row 16kk + 8(G/2) + 4h + s/4 at
-            // column 32ni + 16(G%2) + 4(s%4); lane s of each 16-lane group receives the
-            // 4 K-consecutive values of column 16(G%2) + s.
-            const int krow = 16 * kk + 8 * (G >> 1) + (s >> 2);
-            const int ncol = wn * C::WTN + 32 * ni + 16 * (G & 1) + 4 * (s & 3);
-            typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
-            const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4*)(Bs + krow * SB + ncol));
-            const i16x4_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4*)(Bs + (krow + 4) * SB + ncol));
-            wf[ni] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
-          } else {
-            wf[ni] = *reinterpret_cast<const bf16x8_t*>(Bs + (wn * C::WTN + 32 * ni + l32) * SA + 16 * kk + 8 * hi);
-          }
-        }
-#pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-          for (int ni = 0; ni < NI; ++ni)
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[ni], xf[mi], acc[mi][ni], 0, 0, 0);
-      }
-    } else {
-      const float* As = reinterpret_cast<const float*>(stage);
-      const float* Bs = As + C::A_ELEMS;
-      const int l32 = lane & 31, hi = lane >> 5;
+    };
+    auto compute = [&](int buf) {
+      const float* As = reinterpret_cast<const float*>(smem + buf * C::STAGE_BYTES);
+      const float* Bs = As + BM * SA;
 #pragma unroll
       for (int kk = 0; kk < BK / 2; ++kk) {
         float xf[MI], wf[NI];
@@ -519,69 +622,128 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
           for (int ni = 0; ni < NI; ++ni)
             acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x2f32(wf[ni], xf[mi], acc[mi][ni], 0, 0, 0);
       }
+    };
+    if (KT > 0) {
+      gload(0);
+      sstore(0);
+      __syncthreads();
+      for (int kt = 0; kt < KT; ++kt) {
+        const int cur = kt & 1;
+        const bool more = kt + 1 < KT;
+        if (more) gload(kt + 1);
+        compute(cur);
+        if (more) sstore(cur ^ 1);
+        __syncthreads();
+      }
+    }
+  }
+
+  // ================= epilogue =================
+  char* region = smem + C::EPI_REGION_OFF + wave * C::REGION_BYTES;
+  float* red = reinterpret_cast<float*>(smem + C::EPI_RED_OFF);
+  float* rinv = reinterpret_cast<float*>(smem + C::EPI_RINV_OFF);
+  int* flag = reinterpret_cast<int*>(smem + C::EPI_FLAG_OFF);
+
+  if constexpr (C::RMS) {
+    if constexpr (!C::F32) {
+      // rows 8q + (lane >> 3): the 8 lanes of a row are consecutive
+#pragma unroll
+      for (int i = 0; i < C::A_BPW; ++i) {
+        float v = ss[i];
+        v += __shfl_xor(v, 1);
+        v += __shfl_xor(v, 2);
+        v += __shfl_xor(v, 4);
+        if ((lane & 7) == 0) rinv[8 * (wave + C::NW * i) + (lane >> 3)] = 1.0f / sqrtf(v / float(K) + a->eps);
+      }
+    } else {
+      constexpr int KCH = BK / 4;
+#pragma unroll
+      for (int i = 0; i < C::A32_CH; ++i) {
+        float v = ss[i];
+#pragma unroll
+        for (int off = 1; off < KCH; off <<= 1) v += __shfl_xor(v, off);
+        if (tid % KCH == 0) rinv[tid / KCH + i * (C::NT / KCH)] = 1.0f / sqrtf(v / float(K) + a->eps);
+      }
+    }
+    __syncthreads();
+  }
+
+  // The first bf16 side matrix of the list (before any SWIGLU_PAIR) is read one
+  // 32-row block ahead, so its load latency overlaps the previous block's work.
+  int pf_op = -1;
+  for (int q = 0; q < a->n_ops; ++q) {
+    const int k = a->ops[q].kind;
+    if (k == CODA_OP_SWIGLU_PAIR) break;
+    if ((k == CODA_OP_ADD_MAT || k == CODA_OP_MUL_DGELU_TANH) && a->ops[q].dtype == CODA_BF16) {
+      pf_op = q;
+      break;
+    }
+  }
+  u32x4_t pf_buf[2][C::CPL];
+  auto prefetch = [&](int mi_next, u32x4_t (&dst)[C::CPL]) {
+    KOp op = a->ops[pf_op];
+    // rows from m0 on; reads past the matrix (rows >= M) return zero
+    const char* base = static_cast<const char*>(op.in) + (long long)m0 * op.ld * 2;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, ((long long)(M - 1 - m0) * op.ld + op.width) * 2);
+    const int colb = wn * C::WTN + 8 * (lane % C::CPR) + n0;
+#pragma unroll
+    for (int j = 0; j < C::CPL; ++j) {
+      const int mloc = wm * C::WTM + 32 * mi_next + lane / C::CPR + C::RSTEP * j;
+      dst[j] = buffer_load16(rs, uint32_t(mloc) * uint32_t(op.ld * 2) + uint32_t(colb * 2));
     }
   };
+  if (pf_op >= 0) prefetch(0, pf_buf[0]);
 
-  // ---- main loop: one barrier per K step ----
-  if (KT > 0) {
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-      const int cur = kt & 1;
-      const bool more = kt + 1 < KT;
-      if (more) gload(kt + 1);
-      compute(cur);
-      if (more) sstore(cur ^ 1);
-      __syncthreads();
+  static_for<0, MI>([&](auto mic) {
+    constexpr int mi = decltype(mic)::value;
+    if constexpr (mi + 1 < MI) {
+      if (pf_op >= 0) prefetch(mi + 1, pf_buf[(mi + 1) & 1]);
     }
-  }
-
-  // ---- epilogue ----
-  float* epi = reinterpret_cast<float*>(smem);
-  float* rinv = epi;                 // [BM]
-  float* red = epi + BM;             // [MAX_RED][WN][BM]
-  int* flag = reinterpret_cast<int*>(epi + BM + CODA_MAX_REDUCTIONS * C::WN * BM);
-
-  Geo<C> g;
-  g.M = M;
-  g.lane = lane;
-  g.wn = wn;
-  g.mloc0 = wm * C::WTM;
+    // accumulators of block mi -> the wave's region, row-major [32][WTN] fp32,
+    // 16-byte slot s of row r stored at slot s ^ swz(r)
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi) g.m[mi] = m0 + wm * C::WTM + 32 * mi + (lane & 31);
-  g.nb = n0 + wn * C::WTN + 4 * (lane >> 5);
-
-  if (C::RMS) {
-    // rows a_r + i*A_RSTEP are shared by the KCH consecutive lanes with equal a_r
+    for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
-    for (int i = 0; i < C::A_CH; ++i) {
-      float v = ss[i];
+      for (int g = 0; g < 4; ++g) {
+        const int slot = 8 * ni + 2 * g + hi;
+        f32x4_t w;
+        w[0] = acc[mi][ni][4 * g + 0];
+        w[1] = acc[mi][ni][4 * g + 1];
+        w[2] = acc[mi][ni][4 * g + 2];
+        w[3] = acc[mi][ni][4 * g + 3];
+        *reinterpret_cast<f32x4_t*>(region + l32 * (C::WTN * 4) + ((slot ^ swz_l) * 16)) = w;
+      }
+    __builtin_amdgcn_wave_barrier();
+    Chunks<C::CPL> ch;
+    const int c = lane % C::CPR;
+    ch.col = n0 + wn * C::WTN + 8 * c;
 #pragma unroll
-      for (int off = 1; off < KCH; off <<= 1) v += __shfl_xor(v, off);
-      if (a_c == 0) rinv[a_r + i * C::A_RSTEP] = 1.0f / sqrtf(v / float(K) + a->eps);
+    for (int j = 0; j < C::CPL; ++j) {
+      const int r = lane / C::CPR + C::RSTEP * j;
+      ch.mloc[j] = wm * C::WTM + 32 * mi + r;
+      ch.row[j] = m0 + ch.mloc[j];
+      const int sw = (r & 7) ^ ((r >> 3) & 1);
+      const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(region + r * (C::WTN * 4) + (((2 * c) ^ sw) * 16));
+      const f32x4_t hv = *reinterpret_cast<const f32x4_t*>(region + r * (C::WTN * 4) + (((2 * c + 1) ^ sw) * 16));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ch.v[j][e] = lo[e];
+        ch.v[j][4 + e] = hv[e];
+      }
+      if constexpr (C::RMS) {
+        const float s = rinv[ch.mloc[j]];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ch.v[j][e] *= s;
+      }
     }
-    __syncthreads();
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi) {
-      const float r = rinv[wm * C::WTM + 32 * mi + (lane & 31)];
-#pragma unroll
-      for (int ni = 0; ni < NI; ++ni)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) acc[mi][ni][q] *= r;
-    }
-  }
-
-  static_for<0, MI * NI>([&](auto blk) {
-    constexpr int mi = decltype(blk)::value / NI;
-    constexpr int ni = decltype(blk)::value % NI;
-    const int o = run_ops<C, false>(acc[mi][ni], a, 0, g, mi, ni, red);
+    __builtin_amdgcn_wave_barrier();
+    const int o = run_ops<C, false>(ch, a, 0, M, lane, wn, red, pf_op, pf_buf[mi & 1]);
     if (o < a->n_ops) {   // SWIGLU_PAIR
-      swiglu_pair_acc(acc[mi][ni]);
-      run_ops<C, true>(acc[mi][ni], a, o + 1, g, mi, ni, red);
-      store_d<C, true>(acc[mi][ni], a, g, mi, ni);
+      swiglu_chunks<C>(ch);
+      run_ops<C, true>(ch, a, o + 1, M, lane, wn, red, -1, pf_buf[mi & 1]);
+      store_chunks<C, true>(ch, a, M);
     } else {
-      store_d<C, false>(acc[mi][ni], a, g, mi, ni);
+      store_chunks<C, false>(ch, a, M);
     }
   });
 
@@ -589,7 +751,7 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
     __syncthreads();
     const bool multi = a->grid_n > 1;
     for (int q = 0; q < a->n_ops; ++q) {
-      const __attribute__((address_space(4))) DevOp& op = a->ops[q];
+      KOp op = a->ops[q];
       if (op.kind < CODA_OP_ROW_SUM) continue;
       const int s = op.red_slot;
       for (int t = tid; t < BM; t += C::NT) {
@@ -608,17 +770,21 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
       }
     }
     if (multi) {
-      __threadfence();
+      // The partial sums went out as agent-scope atomic stores, which are
+      // coherent across the XCDs' L2s.  Waiting for their completion before the
+      // counter increment publishes them without a device-wide L2 write-back.
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       if (tid == 0) {
-        const unsigned old = atomicAdd(a->counters + tile_m, 1u);
+        const unsigned old =
+            __hip_atomic_fetch_add(a->counters + tile_m, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         *flag = (old == unsigned(a->grid_n - 1)) ? 1 : 0;
       }
       __syncthreads();
       if (*flag) {
-        __threadfence();
+        // last workgroup of the tile row: sum the partials in tile order
         for (int q = 0; q < a->n_ops; ++q) {
-          const __attribute__((address_space(4))) DevOp& op = a->ops[q];
+          KOp op = a->ops[q];
           if (op.kind < CODA_OP_ROW_SUM) continue;
           const int s = op.red_slot;
           for (int t = tid; t < BM; t += C::NT) {
@@ -631,7 +797,8 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
             write_reduction(op, row, v);
           }
         }
-        if (tid == 0) atomicExch(a->counters + tile_m, 0u);
+        // leave the counter at zero for the next call
+        if (tid == 0) __hip_atomic_store(a->counters + tile_m, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
@@ -647,14 +814,14 @@ int launch_cfg(const FusedArgs& args, int64_t nwg, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? CODA_OK : CODA_ERR_HIP;
 }
 
-template <int BM, int BN, int BK, int WM, int WN, bool F32>
+template <int BM, int BN, int WM, int WN, bool F32>
 int launch_variants(const FusedArgs& args, int64_t nwg, bool bkn, bool rms, hipStream_t s) {
   if (bkn) {
-    return rms ? launch_cfg<Cfg<BM, BN, BK, WM, WN, F32, true, true>>(args, nwg, s)
-               : launch_cfg<Cfg<BM, BN, BK, WM, WN, F32, true, false>>(args, nwg, s);
+    return rms ? launch_cfg<Cfg<BM, BN, WM, WN, F32, true, true>>(args, nwg, s)
+               : launch_cfg<Cfg<BM, BN, WM, WN, F32, true, false>>(args, nwg, s);
   }
-  return rms ? launch_cfg<Cfg<BM, BN, BK, WM, WN, F32, false, true>>(args, nwg, s)
-             : launch_cfg<Cfg<BM, BN, BK, WM, WN, F32, false, false>>(args, nwg, s);
+  return rms ? launch_cfg<Cfg<BM, BN, WM, WN, F32, false, true>>(args, nwg, s)
+             : launch_cfg<Cfg<BM, BN, WM, WN, F32, false, false>>(args, nwg, s);
 }
 
 // one function per compiled tile configuration (defined in coda_fused_t*.hip)

@@ -48,23 +48,13 @@ bool overlap(const Extent& a, const Extent& b) {
   return a.lo < b.hi && b.lo < a.hi;
 }
 
-// Tile count cost model for the automatic choice: waves of 256 workgroups
-// times the per-tile work, weighted by how well each shape keeps MFMA fed.
+// Automatic tile choice, from measurements on MI355X: the 8-wave 256 x 256
+// tile (config 4) is fastest once the grid fills the 256 CUs about twice;
+// smaller grids do better with 128 x 128 tiles (config 3), which give four
+// times as many workgroups.
 int choose_tile(int64_t M, int64_t N) {
-  static const double kEff[kNumTileCfgs] = {1.0, 0.93, 0.80, 0.97};
-  int best = 1;
-  double best_cost = 0;
-  for (int i = 0; i < kNumTileCfgs; ++i) {
-    const TileCfg& c = kTileCfgs[i];
-    int64_t tiles = ((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
-    int64_t waves = (tiles + 255) / 256;
-    double cost = double(waves) * c.bm * c.bn / kEff[i];
-    if (i == 0 || cost < best_cost) {
-      best = i + 1;
-      best_cost = cost;
-    }
-  }
-  return best;
+  const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
+  return big >= 480 ? 4 : 3;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
