@@ -31,6 +31,7 @@ PEAK_BF16_TFLOPS = 2500.0        # MI355X published dense bf16 MFMA peak
 PEAK_HBM_GBPS = 8000.0
 WORKLOAD_INDEX = 4               # LLaMA-7B SwiGLU gate/up
 FLUSH_BYTES = 512 << 20          # larger than L2 (8 x 4 MB) plus the 256 MB Infinity Cache
+COPY_BYTES = 256 << 20           # plain copy used to calibrate the HBM traffic counters
 
 
 def kernel_source_hash() -> str:
@@ -105,6 +106,8 @@ def main():
     ap.add_argument("--no-flush", action="store_true", help="do not evict L2 / Infinity Cache between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unfused", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain 256 MiB device copy three times (reference for traffic counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -126,6 +129,14 @@ def main():
     call = runner.WorkloadCall(spec, inputs, tile=args.tile)
     flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
+    if args.copy_calibration:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    tile_used = coda.coda_selected_tile(spec.M, spec.N, spec.K, call.desc)
 
     def step(fn):
         if not args.no_flush:
@@ -170,7 +181,6 @@ def main():
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         cpu = cpu_baseline(spec, inputs)
 
-    tile = call.desc.tile or 0
     line = {
         "metric": "fused GEMM+epilogue TFLOP/s, % bf16 MFMA peak; speedup vs unfused HIP",
         "value": round(tflops, 2),
@@ -189,7 +199,7 @@ def main():
                         "N=2x11008 column-interleaved, bf16 in/out, fp32 accumulate",
             "M": spec.M, "N": spec.N, "K": spec.K,
             "cache_flush_between_steps": not args.no_flush,
-            "tile": args.tile,
+            "tile": tile_used,
         },
         "pct_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
         "unfused_ms_per_step": None if unfused_ms is None else round(unfused_ms, 4),

@@ -46,6 +46,7 @@ CODA_OP_ROW_MEAN = 13
 EXPORTED = (
     "coda_gemm_epi", "coda_gemm_unfused", "coda_validate", "coda_workspace_size",
     "coda_status_string", "coda_last_error", "coda_num_tile_configs", "coda_tile_config",
+    "coda_selected_tile",
 )
 
 
@@ -111,6 +112,8 @@ def _load():
     lib.coda_num_tile_configs.restype = ctypes.c_int
     lib.coda_tile_config.argtypes = [ctypes.c_int] + [ctypes.POINTER(ctypes.c_int)] * 4
     lib.coda_tile_config.restype = ctypes.c_int
+    lib.coda_selected_tile.argtypes = [I64, I64, I64, DESC]
+    lib.coda_selected_tile.restype = ctypes.c_int
     return lib
 
 
@@ -157,6 +160,10 @@ def coda_tile_config(index: int):
     if st != CODA_OK:
         raise CodaError(st, "coda_tile_config")
     return tuple(v.value for v in vals)   # (bm, bn, bk, waves)
+
+
+def coda_selected_tile(M: int, N: int, K: int, desc: coda_epi_desc) -> int:
+    return lib.coda_selected_tile(M, N, K, _desc_ptr(desc))
 
 
 def check(status: int, where: str) -> None:

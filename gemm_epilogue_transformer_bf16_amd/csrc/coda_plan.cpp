@@ -52,10 +52,14 @@ bool overlap(const Extent& a, const Extent& b) {
 // tile (config 4) is fastest once the grid fills the 256 CUs about twice;
 // smaller grids do better with 128 x 128 tiles (config 3), which give four
 // times as many workgroups.
+}  // namespace
+
 int choose_tile(int64_t M, int64_t N) {
   const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
   return big >= 480 ? 4 : 3;
 }
+
+namespace {
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -413,6 +417,14 @@ const char* coda_status_string(int status) {
 const char* coda_last_error(void) { return coda::last_error(); }
 
 int coda_num_tile_configs(void) { return coda::kNumTileCfgs; }
+
+int coda_selected_tile(int64_t M, int64_t N, int64_t K, const coda_epi_desc* desc) {
+  coda::Plan p;
+  const int st = coda::build_plan(nullptr, nullptr, M, N, K, desc, 0, false, &p);
+  if (st != CODA_OK) return st;
+  if (desc->ab_dtype == CODA_F32) return 0;
+  return desc->tile ? desc->tile : coda::choose_tile(M, N);
+}
 
 int coda_tile_config(int index, int* bm, int* bn, int* bk, int* waves) {
   if (index < 1 || index > coda::kNumTileCfgs) return CODA_ERR_INVALID_ARG;

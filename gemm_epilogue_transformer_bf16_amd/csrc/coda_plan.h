@@ -76,6 +76,9 @@ size_t fused_counters_offset(const Plan& p);
 size_t unfused_workspace_bytes(const Plan& p);
 int64_t unfused_ld(const Plan& p);
 
+// Automatic bf16 tile configuration (1-based) for an M x N output.
+int choose_tile(int64_t M, int64_t N);
+
 void set_error(const char* fmt, ...);
 void clear_error();
 

@@ -1,0 +1,95 @@
+"""Summarise a rocprofv3 results database (rocpd SQLite) as text.
+
+  python -m gemm_epilogue_transformer_bf16_amd.prof_summary trace <results.db>
+      per-kernel calls, total and average duration (us)
+  python -m gemm_epilogue_transformer_bf16_amd.prof_summary pmc <results.db> [<results.db> ...]
+      per-kernel average of each collected counter (summed over the hardware
+      instances of one dispatch), plus the average dispatch duration
+  python -m gemm_epilogue_transformer_bf16_amd.prof_summary traffic <fetch.db> <write.db> <kernel-substring> <copy-bytes>
+      HBM bytes per launch of the kernel from FETCH_SIZE / WRITE_SIZE (KiB per
+      dispatch), each scaled by bytes / counter of the plain device copy
+      (__amd_rocclr_copyBuffer) of <copy-bytes> bytes in the same run; JSON
+"""
+from __future__ import annotations
+
+import collections
+import sqlite3
+import sys
+
+
+def short(name: str, width: int = 110) -> str:
+    return name if len(name) <= width else name[: width - 3] + "..."
+
+
+def trace(db: str) -> str:
+    c = sqlite3.connect(db)
+    rows = c.execute("select name, total_calls, total_duration, average, percentage from top_kernels").fetchall()
+    # top_kernels reports durations in microseconds
+    out = [f"{'calls':>6} {'total_us':>12} {'avg_us':>10} {'pct':>6}  kernel"]
+    for name, calls, total, avg, pct in rows:
+        out.append(f"{calls:>6} {total:>12.1f} {avg:>10.2f} {pct:>6.2f}  {short(name)}")
+    return "\n".join(out)
+
+
+def pmc(dbs) -> str:
+    per_kernel = collections.defaultdict(lambda: collections.defaultdict(list))
+    durations = collections.defaultdict(dict)
+    for db in dbs:
+        c = sqlite3.connect(db)
+        q = ("select dispatch_id, kernel_name, counter_name, sum(value), avg(duration) "
+             "from counters_collection group by dispatch_id, counter_name")
+        for disp, kname, cname, val, dur in c.execute(q):
+            per_kernel[kname][cname].append(val)
+            durations[kname][(db, disp)] = dur
+    out = []
+    for kname, counters in per_kernel.items():
+        d = list(durations[kname].values())
+        out.append(f"{short(kname)}")
+        out.append(f"    dispatches={len(d)}  avg_duration_us={sum(d) / len(d) / 1000.0:.2f}")
+        for cname, vals in sorted(counters.items()):
+            out.append(f"    {cname:32s} avg={sum(vals) / len(vals):.6g}  (n={len(vals)})")
+    return "\n".join(out)
+
+
+def _counter_per_dispatch(db: str, counter: str):
+    c = sqlite3.connect(db)
+    q = ("select dispatch_id, kernel_name, sum(value) from counters_collection "
+         "where counter_name = ? group by dispatch_id")
+    return [(k, v) for _, k, v in c.execute(q, (counter,))]
+
+
+def traffic(fetch_db: str, write_db: str, kernel: str, copy_bytes: int) -> dict:
+    out = {}
+    for counter, db in (("FETCH_SIZE", fetch_db), ("WRITE_SIZE", write_db)):
+        rows = _counter_per_dispatch(db, counter)
+        copies = sorted(v for k, v in rows if "copyBuffer" in k)
+        if not copies:
+            raise SystemExit(f"no copy kernel in {db}")
+        ref_kib = copies[-1]                       # the large calibration copy
+        scale = copy_bytes / (ref_kib * 1024.0)
+        vals = [v for k, v in rows if kernel in k]
+        if not vals:
+            raise SystemExit(f"no dispatch of {kernel!r} in {db}")
+        avg_kib = sum(vals) / len(vals)
+        out[counter] = {"copy_counter_kib": ref_kib, "scale": scale, "kernel_avg_kib": avg_kib,
+                        "kernel_bytes": avg_kib * 1024.0 * scale, "dispatches": len(vals)}
+    out["hbm_bytes_per_launch"] = out["FETCH_SIZE"]["kernel_bytes"] + out["WRITE_SIZE"]["kernel_bytes"]
+    return out
+
+
+def main(argv):
+    if len(argv) < 3 or argv[1] not in ("trace", "pmc", "traffic"):
+        print(__doc__)
+        return 2
+    if argv[1] == "trace":
+        print(trace(argv[2]))
+    elif argv[1] == "pmc":
+        print(pmc(argv[2:]))
+    else:
+        import json
+        print(json.dumps(traffic(argv[2], argv[3], argv[4], int(argv[5])), indent=1))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv))

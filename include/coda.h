@@ -40,11 +40,12 @@
  *    at the caller's next synchronisation, per HIP convention.
  *  - Validation happens before anything is enqueued: on any error code,
  *    nothing has been launched and no memory has been touched.
- *  - Shape rules: M >= 0, N >= 0, K >= 0; K % 8 == 0; N % 8 == 0 when B is
- *    CODA_B_KN; every matrix leading dimension is a multiple of 8 elements
- *    and every matrix pointer is 16-byte aligned; vector operands are
- *    16-byte aligned.  M == 0 or N == 0 is a no-op that returns CODA_OK.
- *    Sizes beyond the tile (ragged M, N, K) are supported.
+ *  - Shape rules: 0 <= M, N, K < 2^31; K % 8 == 0; N % 8 == 0 when B is
+ *    CODA_B_KN; every matrix leading dimension is a multiple of 8 elements,
+ *    and lda, ldb are at most 2^21 elements; every matrix pointer is 16-byte
+ *    aligned; vector operands are 16-byte aligned.  Outside these rules a call
+ *    returns CODA_ERR_UNSUPPORTED.  M == 0 or N == 0 is a no-op that returns
+ *    CODA_OK.  Sizes that are not tile multiples (ragged M, N, K) are supported.
  *  - Aliasing: D may coincide exactly with the matrix of a CODA_OP_ADD_MAT op
  *    (same pointer, same dtype, same leading dimension: an in-place residual
  *    update).  Any other overlap between D and an input, or between outputs,
@@ -196,6 +197,14 @@ const char* coda_last_error(void);
  */
 int coda_num_tile_configs(void);
 int coda_tile_config(int index, int* bm, int* bn, int* bk, int* waves);
+
+/*
+ * coda_selected_tile - the tile configuration coda_gemm_epi would use for this
+ * call: desc->tile when it is nonzero, else the automatic choice.  Returns the
+ * 1-based bf16 configuration, 0 for fp32 operands (one fixed 64 x 64 tile), or
+ * a negative coda_status when the descriptor does not validate.  Host-only.
+ */
+int coda_selected_tile(int64_t M, int64_t N, int64_t K, const coda_epi_desc* desc);
 
 #ifdef __cplusplus
 }

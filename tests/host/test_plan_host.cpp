@@ -174,6 +174,16 @@ int main() {
     EXPECT(coda_tile_config(1, &bm, &bn, &bk, &w) == CODA_OK && bm > 0 && bn > 0 && bk > 0 && w > 0);
     EXPECT(coda_tile_config(0, &bm, &bn, &bk, &w) == CODA_ERR_INVALID_ARG);
   }
+  {  // selected tile: explicit, automatic (large grid -> 256 x 256 / 8 waves), fp32
+    coda_epi_desc e = base_desc(22016, 4096);
+    EXPECT(coda_selected_tile(4096, 22016, 4096, &e) == 4);
+    EXPECT(coda_selected_tile(300, 520, 200, &d) == 3);
+    e.tile = 2;
+    EXPECT(coda_selected_tile(4096, 22016, 4096, &e) == 2);
+    e.ab_dtype = CODA_F32; e.tile = 0;
+    EXPECT(coda_selected_tile(4096, 22016, 4096, &e) == 0);
+    EXPECT(coda_selected_tile(4096, 22016, 4100, &e) == CODA_ERR_UNSUPPORTED);
+  }
   EXPECT(std::strcmp(coda_status_string(CODA_ERR_WORKSPACE), "CODA_ERR_WORKSPACE") == 0);
   if (failures == 0) std::printf("ALL OK\n");
   return failures == 0 ? 0 : 1;
