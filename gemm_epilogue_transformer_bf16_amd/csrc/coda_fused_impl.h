@@ -114,14 +114,19 @@ struct Cfg {
   static constexpr int CPL = 32 * CPR / 64;           // chunks per lane per 32-row block
   static constexpr int RSTEP = 64 / CPR;              // rows between a lane's chunks
   static constexpr int REGION_BYTES = 32 * WTN * 4;   // per-wave fp32 staging of one block
-  static constexpr int EPI_REGION_OFF = 0;
-  static constexpr int EPI_RED_OFF = NW * REGION_BYTES;
+  // LDS is two arrays, one per main-loop stage (distinct objects, so the
+  // compiler does not make reads of one stage wait for direct-to-LDS loads
+  // into the other); the epilogue reuses array 0 for the per-wave regions and
+  // array 1 for the reduction partials, 1/rms and a flag.
+  static constexpr int EPI_RED_OFF = 0;                // in array 1
   static constexpr int EPI_RINV_OFF = EPI_RED_OFF + CODA_MAX_REDUCTIONS * WN * BM * 4;
   static constexpr int EPI_FLAG_OFF = EPI_RINV_OFF + BM * 4;
-  static constexpr int EPI_BYTES = EPI_FLAG_OFF + 16;
-
-  static constexpr int LDS_BYTES = (2 * STAGE_BYTES > EPI_BYTES) ? 2 * STAGE_BYTES : EPI_BYTES;
-  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+  static constexpr int ARR0_BYTES = STAGE_BYTES > NW * REGION_BYTES ? STAGE_BYTES : NW * REGION_BYTES;
+  static constexpr int ARR1_BYTES = STAGE_BYTES > EPI_FLAG_OFF + 16 ? STAGE_BYTES : EPI_FLAG_OFF + 16;
+  // RMS: raw A of the next K step lands in a third array by direct loads and is
+  // converted (gain, bf16 rounding, sum of squares) from there into the stage
+  static constexpr int RAW_BYTES = (RMS && !F32) ? A_BYTES : 16;
+  static_assert(ARR0_BYTES + ARR1_BYTES + RAW_BYTES <= 160 * 1024, "LDS budget");
   static_assert(CPR >= 4 && CPR <= 16 && (CPR & (CPR - 1)) == 0, "epilogue lane layout");
 };
 
@@ -341,7 +346,9 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
   (void)args;
   const KArgs a = (KArgs)__builtin_amdgcn_kernarg_segment_ptr();
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, MI = C::MI, NI = C::NI;
-  __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem0[C::ARR0_BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem1[C::ARR1_BYTES];
+  __shared__ __attribute__((aligned(1024))) char smem_raw[C::RAW_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -388,13 +395,12 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
     const int kn_row = lane / C::KN_CPR;
     const int kn_slot = lane % C::KN_CPR;
 
-    u32x4_t areg[C::RMS ? C::A_BPW : 1];
-    u32x4_t greg;   // the gamma chunk matching this lane's A chunks
+    u32x4_t greg;   // RMS: the gamma chunk matching this lane's A chunks
 
-    auto issue_loads = [&](int kt, int stage) {
+    // A (raw, into smem_raw, with RMS) or A (into the stage) plus B, all
+    // straight to LDS; the swizzled block layout is the same for both A targets
+    auto load_a = [&](int kt, char* dst) {
       const int k0 = kt * 64;
-      char* As = smem + stage * C::STAGE_BYTES;
-      char* Bs = As + C::A_BYTES;
       const __amdgpu_buffer_rsrc_t ra = make_rsrc(Abase + (long long)k0 * 2, a_ext0 - (long long)k0 * 2);
 #pragma unroll
       for (int i = 0; i < C::A_BPW; ++i) {
@@ -402,12 +408,16 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
         const uint32_t off = (k0 + 8 * kq_chunk < K)
                                  ? uint32_t(8 * q + kq_row) * uint32_t(lda * 2) + uint32_t(kq_chunk * 16)
                                  : kOobOffset;
-        if constexpr (C::RMS) {
-          areg[i] = buffer_load16(ra, off);
-        } else {
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (LdsPtr)(As + q * 1024), 16, (int)off, 0, 0, 0);
-        }
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (LdsPtr)(dst + q * 1024), 16, (int)off, 0, 0, 0);
       }
+      if constexpr (C::RMS) {
+        const __amdgpu_buffer_rsrc_t rg = make_rsrc(a->gamma, (long long)K * 2);
+        greg = buffer_load16(rg, uint32_t((k0 + 8 * kq_chunk) * 2));
+      }
+    };
+    auto load_b = [&](int kt, char* As) {
+      const int k0 = kt * 64;
+      char* Bs = As + C::A_BYTES;
       if constexpr (C::BKN) {
         const __amdgpu_buffer_rsrc_t rb =
             make_rsrc(Bbase + (long long)k0 * ldb * 2, b_ext0 - (long long)k0 * ldb * 2);
@@ -430,26 +440,26 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (LdsPtr)(Bs + q * 1024), 16, (int)off, 0, 0, 0);
         }
       }
-      if constexpr (C::RMS) {
-        const __amdgpu_buffer_rsrc_t rg = make_rsrc(a->gamma, (long long)K * 2);
-        greg = buffer_load16(rg, uint32_t((k0 + 8 * kq_chunk) * 2));
-      }
     };
 
-    // RMS: gain and sum of squares on the A chunks held in registers, then into LDS
-    auto rms_store = [&](int stage) {
-      char* As = smem + stage * C::STAGE_BYTES;
+    // RMS: convert this wave's raw A blocks into the stage `As`: fp32 sum of
+    // squares of the raw values (scaled by `live`, 0 when there is nothing to
+    // convert), then bf16(x * gamma).  Each wave reads only the blocks its own
+    // direct loads wrote, so no barrier is needed between load and conversion.
+    auto convert_a = [&](char* As, float live) {
 #pragma unroll
       for (int i = 0; i < C::A_BPW; ++i) {
-        u32x4_t x = areg[i];
+        const int q = wave + C::NW * i;
+        u32x4_t x = *reinterpret_cast<const u32x4_t*>(smem_raw + q * 1024 + lane * 16);
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           const float lo = bf16_lo(x[w]), hv = bf16_hi(x[w]);
-          ss[i] = fmaf(lo, lo, ss[i]);
-          ss[i] = fmaf(hv, hv, ss[i]);
+          const float lo_l = lo * live, hv_l = hv * live;
+          ss[i] = fmaf(lo_l, lo, ss[i]);
+          ss[i] = fmaf(hv_l, hv, ss[i]);
           x[w] = pack_bf16x2(lo * bf16_lo(greg[w]), hv * bf16_hi(greg[w]));
         }
-        *reinterpret_cast<u32x4_t*>(As + (wave + C::NW * i) * 1024 + lane * 16) = x;
+        *reinterpret_cast<u32x4_t*>(As + q * 1024 + lane * 16) = x;
       }
     };
 
@@ -498,34 +508,93 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
       }
     };
 
-    auto compute = [&](int stage_idx) {
-      const char* stage = smem + stage_idx * C::STAGE_BYTES;
+    // MFMAs of one K step.  With the RMS op, the next step's A chunks (already in
+    // registers) are scaled and written to `rms_dst` between the MFMAs of the
+    // last k16 step, so that VALU work overlaps the matrix pipe.
+    auto compute = [&](const char* stage) {
       bf16x8_t xf[2][MI], wf[2][NI];
       read_frags(stage, 0, xf[0], wf[0]);
       static_for<0, 4>([&](auto kkc) {
         constexpr int kk = decltype(kkc)::value;
+        // the next step's fragment reads are issued before this step's MFMAs
+        // (scheduling barriers keep them there), so their latency is covered
         if constexpr (kk < 3) read_frags(stage, kk + 1, xf[(kk + 1) & 1], wf[(kk + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
           for (int ni = 0; ni < NI; ++ni)
             acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[kk & 1][ni], xf[kk & 1][mi], acc[mi][ni], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       });
     };
 
-    if (KT > 0) {
-      issue_loads(0, 0);
-      if constexpr (C::RMS) rms_store(0);
-      for (int kt = 0; kt < KT; ++kt) {
-        // tile kt is in LDS stage kt&1; every wave is done with stage (kt+1)&1
+    // Direct loads complete in issue order, so a wait for a given load is
+    // "at most `later` loads outstanding", `later` being those issued after it.
+    auto wait_vm = [&](auto later_c) {
+      constexpr int later = decltype(later_c)::value;
+      constexpr int enc = (later & 0xF) | (0x7 << 4) | (0xF << 8) | (((later >> 4) & 3) << 14);
+      __builtin_amdgcn_s_waitcnt(enc);
+    };
+    constexpr std::integral_constant<int, C::A_BPW + 1> kAfterB{};   // raw A + gamma of the next step
+    constexpr std::integral_constant<int, C::B_BPW> kAfterA{};       // B of the next step
+
+    // RMS: the waves of a workgroup are spread round-robin over the 4 SIMDs, so
+    // waves w and w + NW/2 share a SIMD.  The upper half converts A(kt+1) before
+    // its MFMAs and the lower half after them: on every SIMD one wave's VALU
+    // conversion overlaps the other wave's matrix work.
+    const bool convert_first = wave >= C::NW / 2;
+    auto convert_phase = [&](int kt, char* nxt) {
+      wait_vm(kAfterA);                     // raw A(kt+1) and its gamma have landed
+      convert_a(nxt, 1.0f);
+      if (kt + 2 < KT) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // raw reads done before reuse
+        load_a(kt + 2, smem_raw);
+      }
+    };
+
+    // One K step: tile kt is in `cur`; every wave is done reading `nxt`.
+    // RMS order of a wave's direct loads: B(kt) at the top of step kt-1, then
+    // raw A(kt+1) and gamma after that wave's conversion in step kt-1; so at the
+    // top of step kt only the latter may still be in flight.
+    auto step = [&](int kt, char* cur, char* nxt) {
+      if constexpr (C::RMS) {
+        if (kt + 1 < KT) wait_vm(kAfterB);
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      } else {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        const bool more = kt + 1 < KT;
-        if (more) issue_loads(kt + 1, (kt + 1) & 1);
-        compute(kt & 1);
-        if constexpr (C::RMS) {
-          if (more) rms_store((kt + 1) & 1);
+      }
+      __syncthreads();
+      const bool more = kt + 1 < KT;
+      if (more) {
+        if constexpr (!C::RMS) load_a(kt + 1, nxt);
+        load_b(kt + 1, nxt);
+      }
+      if constexpr (C::RMS) {
+        if (more && convert_first) convert_phase(kt, nxt);
+      }
+      compute(cur);
+      if constexpr (C::RMS) {
+        if (more && !convert_first) convert_phase(kt, nxt);
+      }
+    };
+    if (KT > 0) {
+      if constexpr (C::RMS) {
+        load_a(0, smem_raw);
+        load_b(0, smem0);
+        wait_vm(kAfterA);
+        convert_a(smem0, 1.0f);
+        if (KT > 1) {
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          load_a(1, smem_raw);
         }
+      } else {
+        load_a(0, smem0);
+        load_b(0, smem0);
+      }
+      for (int kt = 0; kt < KT; kt += 2) {   // two steps per trip keep each stage a fixed array
+        step(kt, smem0, smem1);
+        if (kt + 1 < KT) step(kt + 1, smem1, smem0);
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
@@ -578,7 +647,7 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
       }
     };
     auto sstore = [&](int buf) {
-      float* As = reinterpret_cast<float*>(smem + buf * C::STAGE_BYTES);
+      float* As = reinterpret_cast<float*>(buf ? smem1 : smem0);
       float* Bs = As + BM * SA;
 #pragma unroll
       for (int i = 0; i < C::A32_CH; ++i) {
@@ -605,7 +674,7 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
       }
     };
     auto compute = [&](int buf) {
-      const float* As = reinterpret_cast<const float*>(smem + buf * C::STAGE_BYTES);
+      const float* As = reinterpret_cast<const float*>(buf ? smem1 : smem0);
       const float* Bs = As + BM * SA;
 #pragma unroll
       for (int kk = 0; kk < BK / 2; ++kk) {
@@ -639,10 +708,10 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
   }
 
   // ================= epilogue =================
-  char* region = smem + C::EPI_REGION_OFF + wave * C::REGION_BYTES;
-  float* red = reinterpret_cast<float*>(smem + C::EPI_RED_OFF);
-  float* rinv = reinterpret_cast<float*>(smem + C::EPI_RINV_OFF);
-  int* flag = reinterpret_cast<int*>(smem + C::EPI_FLAG_OFF);
+  char* region = smem0 + wave * C::REGION_BYTES;
+  float* red = reinterpret_cast<float*>(smem1 + C::EPI_RED_OFF);
+  float* rinv = reinterpret_cast<float*>(smem1 + C::EPI_RINV_OFF);
+  int* flag = reinterpret_cast<int*>(smem1 + C::EPI_FLAG_OFF);
 
   if constexpr (C::RMS) {
     if constexpr (!C::F32) {
