@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libcoda.so")
 # ---- constants (mirror coda.h) ----
 CODA_MAX_OPS = 16
 CODA_MAX_REDUCTIONS = 8
+CODA_FLAG_NO_SPLIT_K = 1
 
 CODA_OK = 0
 CODA_ERR_INVALID_ARG = -1

@@ -115,6 +115,14 @@ struct FusedArgs {
   int n_red;
   int grid_m, grid_n;
   float eps;
+  // split of the last round over K (split_s == 1: none)
+  int full_tiles;       // workgroups [0, full_tiles) compute whole tiles
+  int split_s;          // then split_s workgroups per split tile
+  int k_steps;          // K steps of the whole tile
+  int pad_;
+  float* split_acc;     // [split tiles][split_s][NT][acc registers]
+  float* split_ss;      // [split tiles][split_s][BM] (RMS)
+  unsigned* split_cnt;  // [split tiles]
   DevOp ops[CODA_MAX_OPS];
 };
 

@@ -41,16 +41,24 @@ dev::FusedArgs make_args(const Plan& p) {
     d.out_stride = q.out_stride;
     d.red_slot = q.red_slot;
   }
+  char* ws = static_cast<char*>(p.workspace);
   if (p.n_red > 0 && p.grid_n > 1) {
-    char* ws = static_cast<char*>(p.workspace);
     a.partials = reinterpret_cast<float*>(ws + fused_partials_offset(p));
     a.counters = reinterpret_cast<unsigned*>(ws + fused_counters_offset(p));
+  }
+  a.full_tiles = (int)p.full_tiles;
+  a.split_s = p.split_s;
+  a.k_steps = (int)p.k_steps;
+  if (p.split_s > 1) {
+    a.split_acc = reinterpret_cast<float*>(ws + fused_split_acc_offset(p));
+    a.split_ss = reinterpret_cast<float*>(ws + fused_split_ss_offset(p));
+    a.split_cnt = reinterpret_cast<unsigned*>(ws + fused_split_counters_offset(p));
   }
   return a;
 }
 
 int launch_args(const Plan& p, const dev::FusedArgs& a, hipStream_t stream) {
-  const int64_t nwg = p.grid_m * p.grid_n;
+  const int64_t nwg = p.full_tiles + p.split_tiles * p.split_s;
   const bool bkn = p.b_layout == CODA_B_KN;
   const bool rms = p.has_rms;
   if (p.ab_dtype == CODA_F32) {
@@ -88,6 +96,10 @@ int launch_plain_gemm(const Plan& p, const void* A, int64_t lda, void* out, int6
   q.n_red = 0;
   q.has_swiglu = false;
   q.out_width = p.N;
+  // no workspace here: the tiles are computed whole
+  q.full_tiles = q.grid_m * q.grid_n;
+  q.split_tiles = 0;
+  q.split_s = 1;
   dev::FusedArgs a = make_args(q);
   return launch_args(q, a, stream);
 }

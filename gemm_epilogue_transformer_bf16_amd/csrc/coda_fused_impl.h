@@ -54,14 +54,16 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 // Workgroups are dealt to the 8 XCDs round-robin.  Give each XCD a contiguous
-// range of logical tiles, and order the logical tiles in groups of 8 tile rows
-// (column-major inside a group), so concurrently resident tiles on one XCD
-// share A row panels and B column panels in that XCD's L2.
-__device__ __forceinline__ void map_tile(int bid, int gm, int gn, int& tm, int& tn) {
-  const int nwg = gm * gn;
+// range of logical tiles (of the first nwg), and order the logical tiles in
+// groups of 8 tile rows (column-major inside a group), so concurrently
+// resident tiles on one XCD share A row panels and B column panels in that
+// XCD's L2.
+__device__ __forceinline__ int xcd_logical(int bid, int nwg) {
   const int xcd = bid & 7, idx = bid >> 3;
   const int q = nwg >> 3, r = nwg & 7;
-  const int L = (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+  return (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+}
+__device__ __forceinline__ void tile_of(int L, int gm, int gn, int& tm, int& tn) {
   constexpr int G = 8;
   const int group = L / (G * gn);
   const int first = group * G;
@@ -357,8 +359,28 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
   const int l32 = lane & 31, hi = lane >> 5;
   const int swz_l = (l32 & 7) ^ ((l32 >> 3) & 1);   // LDS row swizzle; depends on the row mod 16 only
 
+  // work item: a whole tile, or one part (over K) of a tile of the last round
   int tile_m, tile_n;
-  map_tile(blockIdx.x, a->grid_m, a->grid_n, tile_m, tile_n);
+  int kt_lo = 0;      // first K step of this workgroup
+  int split = -1;     // index of the split tile, -1 for a whole tile
+  int part = 0;       // part of the split tile
+  const int KT_all = a->k_steps;
+  int KT = KT_all;    // K steps of this workgroup
+  {
+    const int bid = blockIdx.x;
+    int L;
+    if (bid < a->full_tiles) {
+      L = xcd_logical(bid, a->full_tiles);
+    } else {
+      const int u = bid - a->full_tiles;
+      split = u / a->split_s;
+      part = u % a->split_s;
+      L = a->full_tiles + split;
+      kt_lo = (KT_all * part) / a->split_s;
+      KT = (KT_all * (part + 1)) / a->split_s - kt_lo;
+    }
+    tile_of(L, a->grid_m, a->grid_n, tile_m, tile_n);
+  }
   const int m0 = tile_m * BM, n0 = tile_n * BN;
   const int M = a->M, N = a->N, K = a->K;
   const long long lda = a->lda, ldb = a->ldb;
@@ -371,7 +393,6 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
 
-  const int KT = (K + BK - 1) / BK;
   float ss[C::F32 ? C::A32_CH : C::A_BPW];   // per-row sums of squares (RMS)
 #pragma unroll
   for (int i = 0; i < (C::F32 ? C::A32_CH : C::A_BPW); ++i) ss[i] = 0.0f;
@@ -400,7 +421,7 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
     // A (raw, into smem_raw, with RMS) or A (into the stage) plus B, all
     // straight to LDS; the swizzled block layout is the same for both A targets
     auto load_a = [&](int kt, char* dst) {
-      const int k0 = kt * 64;
+      const int k0 = (kt_lo + kt) * 64;
       const __amdgpu_buffer_rsrc_t ra = make_rsrc(Abase + (long long)k0 * 2, a_ext0 - (long long)k0 * 2);
 #pragma unroll
       for (int i = 0; i < C::A_BPW; ++i) {
@@ -416,7 +437,7 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
       }
     };
     auto load_b = [&](int kt, char* As) {
-      const int k0 = kt * 64;
+      const int k0 = (kt_lo + kt) * 64;
       char* Bs = As + C::A_BYTES;
       if constexpr (C::BKN) {
         const __amdgpu_buffer_rsrc_t rb =
@@ -704,6 +725,92 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
         if (more) sstore(cur ^ 1);
         __syncthreads();
       }
+    }
+  }
+
+  // ================= parts of a split tile =================
+  // Each part stores its fp32 accumulators (and, with RMS, its per-row sums of
+  // squares) to the workspace and counts itself in; the part that arrives last
+  // adds all parts in part order, so the sum does not depend on the arrival
+  // order, and goes on to the epilogue.  The others are done.  The partials go
+  // out and come back as agent-scope atomic accesses, which are coherent across
+  // the XCDs' L2 caches; waiting for the stores to complete before the count
+  // publishes them without writing back or invalidating a whole L2.
+  if constexpr (!C::F32) {
+    if (split >= 0) {
+      const int S = a->split_s;
+      constexpr int NG = MI * NI * 8;   // pairs of accumulator registers per thread
+      const size_t slot0 = size_t(split) * size_t(S);
+      // [slot][pair][thread], 8 bytes per entry: each store or load instruction
+      // covers 512 contiguous bytes
+      unsigned long long* accp = reinterpret_cast<unsigned long long*>(a->split_acc) + tid;
+      static_for<0, NG>([&](auto gc) {
+        constexpr int gi = decltype(gc)::value;
+        constexpr int mi = gi / (NI * 8), ni = (gi / 8) % NI, g = gi % 8;
+        const unsigned long long bits = (unsigned long long)__float_as_uint(acc[mi][ni][2 * g]) |
+                                        ((unsigned long long)__float_as_uint(acc[mi][ni][2 * g + 1]) << 32);
+        __hip_atomic_store(accp + ((slot0 + part) * NG + gi) * C::NT, bits, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      });
+      if constexpr (C::RMS) {
+        // rows 8q + (lane >> 3): the 8 lanes of a row are consecutive
+#pragma unroll
+        for (int i = 0; i < C::A_BPW; ++i) {
+          float v = ss[i];
+          v += __shfl_xor(v, 1);
+          v += __shfl_xor(v, 2);
+          v += __shfl_xor(v, 4);
+          if ((lane & 7) == 0)
+            __hip_atomic_store(a->split_ss + (slot0 + part) * BM + 8 * (wave + C::NW * i) + (lane >> 3), v,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      int* last = reinterpret_cast<int*>(smem1 + C::EPI_FLAG_OFF);
+      if (tid == 0) {
+        const unsigned old =
+            __hip_atomic_fetch_add(a->split_cnt + split, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *last = (old == unsigned(S - 1)) ? 1 : 0;
+      }
+      __syncthreads();
+      if (*last == 0) return;
+      // the parts in part order (this part's own values from its registers)
+      static_for<0, NG>([&](auto gc) {
+        constexpr int gi = decltype(gc)::value;
+        constexpr int mi = gi / (NI * 8), ni = (gi / 8) % NI, g = gi % 8;
+        float s0 = 0.0f, s1 = 0.0f;
+        for (int pp = 0; pp < S; ++pp) {
+          float v0 = acc[mi][ni][2 * g], v1 = acc[mi][ni][2 * g + 1];
+          if (pp != part) {
+            const unsigned long long bits = __hip_atomic_load(accp + ((slot0 + pp) * NG + gi) * C::NT,
+                                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            v0 = __uint_as_float(uint32_t(bits));
+            v1 = __uint_as_float(uint32_t(bits >> 32));
+          }
+          s0 = pp == 0 ? v0 : s0 + v0;
+          s1 = pp == 0 ? v1 : s1 + v1;
+        }
+        acc[mi][ni][2 * g] = s0;
+        acc[mi][ni][2 * g + 1] = s1;
+      });
+      if constexpr (C::RMS) {
+        // whole-row sums in part order, on the first lane of each row (the row
+        // sum below adds the zeros of the other lanes)
+#pragma unroll
+        for (int i = 0; i < C::A_BPW; ++i) {
+          const int row = 8 * (wave + C::NW * i) + (lane >> 3);
+          float t = 0.0f;
+          for (int pp = 0; pp < S; ++pp) {
+            const float v =
+                __hip_atomic_load(a->split_ss + (slot0 + pp) * BM + row, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            t = pp == 0 ? v : t + v;
+          }
+          ss[i] = (lane & 7) == 0 ? t : 0.0f;
+        }
+      }
+      // leave the counter at zero for the next call
+      if (tid == 0) __hip_atomic_store(a->split_cnt + split, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 

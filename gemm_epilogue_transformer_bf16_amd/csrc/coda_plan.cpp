@@ -78,13 +78,55 @@ const char* last_error() { return g_err; }
 
 size_t fused_partials_offset(const Plan&) { return 0; }
 
+namespace {
+bool has_row_partials(const Plan& p) { return p.n_red > 0 && p.grid_n > 1; }
+}  // namespace
+
 size_t fused_counters_offset(const Plan& p) {
-  return align256(size_t(p.n_red) * size_t(p.grid_n) * size_t(p.M) * sizeof(float));
+  return has_row_partials(p) ? align256(size_t(p.n_red) * size_t(p.grid_n) * size_t(p.M) * sizeof(float)) : 0;
+}
+
+size_t fused_split_acc_offset(const Plan& p) {
+  return fused_counters_offset(p) + (has_row_partials(p) ? align256(size_t(p.grid_m) * sizeof(uint32_t)) : 0);
+}
+
+size_t fused_split_ss_offset(const Plan& p) {
+  return fused_split_acc_offset(p) +
+         align256(size_t(p.split_tiles) * size_t(p.split_s) * size_t(p.cfg.bm) * size_t(p.cfg.bn) * sizeof(float));
+}
+
+size_t fused_split_counters_offset(const Plan& p) {
+  const size_t ss = p.has_rms ? size_t(p.split_tiles) * size_t(p.split_s) * size_t(p.cfg.bm) * sizeof(float) : 0;
+  return fused_split_ss_offset(p) + align256(ss);
 }
 
 size_t fused_workspace_bytes(const Plan& p) {
-  if (p.n_red == 0 || p.grid_n <= 1 || p.M == 0 || p.N == 0) return 0;
-  return fused_counters_offset(p) + align256(size_t(p.grid_m) * sizeof(uint32_t));
+  if (p.M == 0 || p.N == 0) return 0;
+  if (p.split_s <= 1) return has_row_partials(p) ? fused_split_acc_offset(p) : 0;
+  return fused_split_counters_offset(p) + align256(size_t(p.split_tiles) * sizeof(uint32_t));
+}
+
+// Split of the last round (bf16 configurations): with T tiles and `slots`
+// workgroups resident at once, the grid runs T / slots full rounds and a last
+// round of r = T % slots tiles.  Splitting each of those r tiles over K into s
+// parts (s <= slots / r, each part at least kMinSplitSteps K steps) lets the
+// last round take about 1/s of a round.
+void plan_split(Plan* p, bool allow) {
+  p->full_tiles = p->grid_m * p->grid_n;
+  p->split_tiles = 0;
+  p->split_s = 1;
+  if (!allow || p->ab_dtype != CODA_BF16 || p->K == 0) return;
+  const int64_t tiles = p->grid_m * p->grid_n;
+  const int64_t slots = int64_t(kNumCUs) * p->cfg.wg_per_cu;
+  const int64_t r = tiles % slots;
+  if (r == 0) return;
+  int64_t s = slots / r;
+  if (s > kMaxSplit) s = kMaxSplit;
+  if (s > p->k_steps / kMinSplitSteps) s = p->k_steps / kMinSplitSteps;
+  if (s < 2) return;
+  p->split_tiles = r;
+  p->split_s = int(s);
+  p->full_tiles = tiles - r;
 }
 
 int64_t unfused_ld(const Plan& p) { return (p.N + 7) / 8 * 8; }
@@ -125,8 +167,8 @@ int build_plan(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
     set_error("n_ops=%d outside 0..%d", d->n_ops, CODA_MAX_OPS);
     return CODA_ERR_INVALID_ARG;
   }
-  if (d->flags != 0) {
-    set_error("flags must be 0");
+  if ((d->flags & ~CODA_FLAG_NO_SPLIT_K) != 0) {
+    set_error("unknown flags 0x%x", d->flags);
     return CODA_ERR_INVALID_ARG;
   }
   if (d->tile < 0 || d->tile > kNumTileCfgs) {
@@ -263,6 +305,7 @@ int build_plan(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
     // a no-op: only the descriptor's structure is checked
     p->grid_m = p->grid_n = 0;
     p->cfg = d->ab_dtype == CODA_F32 ? kF32Tile : kTileCfgs[0];
+    p->split_s = 1;
     return CODA_OK;
   }
   if (K % 8 != 0) {
@@ -307,10 +350,12 @@ int build_plan(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
   }
   p->grid_m = (M + p->cfg.bm - 1) / p->cfg.bm;
   p->grid_n = (N + p->cfg.bn - 1) / p->cfg.bn;
-  if (p->grid_m * p->grid_n > kMaxDim) {
+  if (p->grid_m * p->grid_n * kMaxSplit > kMaxDim) {
     set_error("too many tiles");
     return CODA_ERR_UNSUPPORTED;
   }
+  p->k_steps = (K + p->cfg.bk - 1) / p->cfg.bk;
+  plan_split(p, !unfused && !(d->flags & CODA_FLAG_NO_SPLIT_K));
 
   // ---- overlap ----
   if (check_pointers) {

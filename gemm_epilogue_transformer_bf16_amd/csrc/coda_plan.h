@@ -11,20 +11,30 @@ namespace coda {
 
 // bf16 tile configurations: output tile bm x bn (rows of A x columns of B),
 // K step bk, wavefronts arranged wm x wn over the tile.
+// wg_per_cu: workgroups of the configuration that fit on one CU at once (LDS
+// bound), used to size the split of the last, partial round of tiles.
 struct TileCfg {
-  int bm, bn, bk, wm, wn;
+  int bm, bn, bk, wm, wn, wg_per_cu;
 };
 
 constexpr TileCfg kTileCfgs[] = {
-    {256, 256, 64, 2, 2},   // 1: 4 waves, 128x128 per wave
-    {256, 128, 64, 2, 2},   // 2: 4 waves, 128x64 per wave
-    {128, 128, 64, 2, 2},   // 3: 4 waves, 64x64 per wave
-    {256, 256, 64, 2, 4},   // 4: 8 waves, 128x64 per wave
+    {256, 256, 64, 2, 2, 1},   // 1: 4 waves, 128x128 per wave
+    {256, 128, 64, 2, 2, 1},   // 2: 4 waves, 128x64 per wave
+    {128, 128, 64, 2, 2, 2},   // 3: 4 waves, 64x64 per wave
+    {256, 256, 64, 2, 4, 1},   // 4: 8 waves, 128x64 per wave
 };
 constexpr int kNumTileCfgs = sizeof(kTileCfgs) / sizeof(kTileCfgs[0]);
 
 // fp32 operands use one small configuration.
-constexpr TileCfg kF32Tile = {64, 64, 32, 2, 2};
+constexpr TileCfg kF32Tile = {64, 64, 32, 2, 2, 4};
+
+// Compute units of an MI355X; the split below balances the grid for this count
+// (on another device the result is the same, only the balance differs).
+constexpr int kNumCUs = 256;
+constexpr int kMaxSplit = 4;
+// Fewest K steps per part: the parts exchange fp32 partial tiles through
+// memory, which costs about as much as 8 - 16 K steps of the main loop.
+constexpr int kMinSplitSteps = 16;
 
 struct Op {
   int kind;
@@ -55,6 +65,14 @@ struct Plan {
   int tile;                  // 1-based bf16 tile config; 0 for the fp32 path
   TileCfg cfg;
   int64_t grid_m, grid_n;
+  // Split of the last round: when the tiles do not fill a whole number of
+  // rounds of the GPU, the last `split_tiles` tiles (in launch order) are each
+  // computed by `split_s` workgroups over consecutive parts of K; the last of
+  // them to finish adds the partial accumulators and runs the epilogue.
+  int64_t k_steps;           // K steps of the tile configuration
+  int64_t full_tiles;        // tiles computed whole
+  int64_t split_tiles;       // tiles split over K
+  int split_s;               // parts per split tile (1: no split)
   void* workspace;
   size_t workspace_bytes;
 };
@@ -64,11 +82,17 @@ struct Plan {
 int build_plan(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
                const coda_epi_desc* desc, int unfused, bool check_pointers, Plan* plan);
 
-// Workspace layout of the fused path: fp32 partials [n_red][grid_n][M], then
-// uint32 counters [grid_m], each region 256-byte aligned.
+// Workspace layout of the fused path, each region 256-byte aligned: fp32 row
+// reduction partials [n_red][grid_n][M], uint32 counters [grid_m]; then for
+// split tiles fp32 partial accumulators [split_tiles][split_s][bm * bn], fp32
+// partial row sums of squares [split_tiles][split_s][bm] (RMS op only) and
+// uint32 counters [split_tiles].
 size_t fused_workspace_bytes(const Plan& p);
 size_t fused_partials_offset(const Plan& p);
 size_t fused_counters_offset(const Plan& p);
+size_t fused_split_acc_offset(const Plan& p);
+size_t fused_split_ss_offset(const Plan& p);
+size_t fused_split_counters_offset(const Plan& p);
 
 // Workspace layout of the unfused path: normalised A (ab dtype, [M x K]) when
 // the list has the RMS op, then two [M x ldi] intermediates in d dtype, with

@@ -62,7 +62,7 @@ class Call:
     def __init__(self, A: torch.Tensor, B: torch.Tensor, ops: Sequence[Tuple[str, Dict]], b_layout: str,
                  D: Optional[torch.Tensor] = None, d_dtype: Optional[torch.dtype] = None, tile: int = 0,
                  M: Optional[int] = None, N: Optional[int] = None, K: Optional[int] = None,
-                 lda: Optional[int] = None, ldb: Optional[int] = None):
+                 lda: Optional[int] = None, ldb: Optional[int] = None, flags: int = 0):
         self.A, self.B = A, B
         self.M = A.shape[0] if M is None else M
         self.K = A.shape[1] if K is None else K
@@ -120,6 +120,7 @@ class Call:
                 o.out = out.data_ptr() + 4 * col
                 o.out_stride = out.stride(0)
         d.tile = tile
+        d.flags = flags
         self.desc = d
         self.ws = {}
         for unfused in (0, 1):
@@ -152,7 +153,7 @@ class Call:
 class WorkloadCall(Call):
     """A ``workloads`` spec with its seeded inputs uploaded to the device."""
 
-    def __init__(self, spec, inputs: Dict[str, np.ndarray], device="cuda", tile: int = 0):
+    def __init__(self, spec, inputs: Dict[str, np.ndarray], device="cuda", tile: int = 0, flags: int = 0):
         dtypes = {t.name: t.dtype for t in spec.tensors}
         self.spec = spec
         self.tensors = {name: storage_to_tensor(arr, dtypes[name], device) for name, arr in inputs.items()}
@@ -167,4 +168,4 @@ class WorkloadCall(Call):
                 a["out"] = self.outputs[a["out"]]
             ops.append((name, a))
         super().__init__(self.tensors[spec.a_name], self.tensors[spec.b_name], ops, spec.b_layout,
-                         d_dtype=TORCH_DT[spec.d_dtype], tile=tile, M=spec.M, N=spec.N, K=spec.K)
+                         d_dtype=TORCH_DT[spec.d_dtype], tile=tile, M=spec.M, N=spec.N, K=spec.K, flags=flags)

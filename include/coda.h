@@ -66,6 +66,10 @@ extern "C" {
 #define CODA_MAX_OPS 16
 #define CODA_MAX_REDUCTIONS 8
 
+/* coda_epi_desc.flags */
+#define CODA_FLAG_NO_SPLIT_K 1   /* coda_gemm_epi: never split the last round of
+                                    tiles over K (see coda_gemm_epi)            */
+
 typedef enum {
   CODA_OK = 0,
   CODA_ERR_INVALID_ARG = -1,  /* a null/ill-formed argument, bad op list, overlap  */
@@ -135,7 +139,7 @@ typedef struct {
   void* workspace;      /* device scratch, see coda_workspace_size                 */
   size_t workspace_bytes;
   int32_t tile;         /* 0 = automatic tile choice; k > 0 forces tile config k    */
-  int32_t flags;        /* reserved, must be 0                                      */
+  int32_t flags;        /* 0, or CODA_FLAG_NO_SPLIT_K; other bits must be 0         */
   coda_op ops[CODA_MAX_OPS];
 } coda_epi_desc;
 
@@ -146,10 +150,18 @@ typedef struct {
  * (round-to-nearest-even for bf16).  With CODA_OP_RMS_ROWSCALE first, the
  * GEMM operand is A*gamma rounded to ab_dtype and the row factor is applied
  * to the accumulators.
+ * Load balance: when the output tiles do not fill a whole number of rounds
+ * of the GPU's compute units, each tile of the last, partial round is split
+ * over K between up to 4 workgroups (bf16 operands only, unless flags holds
+ * CODA_FLAG_NO_SPLIT_K); the last of them to finish adds the fp32 partial
+ * accumulators in a fixed order and runs the epilogue, so results do not
+ * depend on timing.
  * Workspace: row reductions whose row spans several output tiles combine
- * partial sums through the workspace (coda_workspace_size(..., 0) bytes).
- * Its counter region must be zero before the first call; every call leaves
- * it zero again.  Two calls that run concurrently must not share a workspace.
+ * partial sums through the workspace, and so do the parts of a split tile
+ * (coda_workspace_size(..., 0) bytes, 0 when neither happens).  Its counter
+ * regions must be zero before the first call (a zero-filled workspace will
+ * do); every call leaves them zero again.  Two calls that run concurrently
+ * must not share a workspace.
  * Returns a coda_status.
  */
 int coda_gemm_epi(const void* A, const void* B, int64_t M, int64_t N, int64_t K,

@@ -122,12 +122,12 @@ def unfused_extra(spec, inputs, rows):
 
 
 def run_and_compare(spec, inputs, mode: str = "fused", tile: int = 0, rows=None, label: str = "",
-                    check_determinism: bool = False):
+                    check_determinism: bool = False, flags: int = 0, return_call: bool = False):
     """Run ``spec`` on the GPU through the C ABI and compare with the oracle
-    (on ``rows`` only when given).  Returns the error stats."""
+    (on ``rows`` only when given).  Returns the error stats (and the call)."""
     coda, runner = lib()
-    announce(f"{label or spec.name} mode={mode} tile={tile} M={spec.M} N={spec.N} K={spec.K}")
-    call = runner.WorkloadCall(spec, inputs, tile=tile)
+    announce(f"{label or spec.name} mode={mode} tile={tile} flags={flags} M={spec.M} N={spec.N} K={spec.K}")
+    call = runner.WorkloadCall(spec, inputs, tile=tile, flags=flags)
     st = call.fused() if mode == "fused" else call.unfused()
     coda.check(st, f"{spec.name} {mode}")
     torch.cuda.synchronize()
@@ -157,6 +157,8 @@ def run_and_compare(spec, inputs, mode: str = "fused", tile: int = 0, rows=None,
         stats[f"{o}[{col}]"] = assert_close(outs[o][:, col], outs_ref[o][:, col], f"{spec.name}/{mode}/{o}[:,{col}]",
                                             extra)
         red_i += 1
+    if return_call:
+        return stats, call
     del call
     return stats
 

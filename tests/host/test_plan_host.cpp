@@ -32,7 +32,17 @@ static coda_epi_desc base_desc(int64_t N, int64_t K) {
   d.ldb = N;
   d.ldd = N;
   d.D = Pm(0x30000000);
+  // most checks below are about validation, not load balance: keep every tile
+  // whole so that no workspace is needed (the split is tested on its own)
+  d.flags = CODA_FLAG_NO_SPLIT_K;
   return d;
+}
+
+static coda::Plan plan_of(int64_t M, int64_t N, int64_t K, const coda_epi_desc& d, int unfused = 0) {
+  coda::Plan p;
+  const int st = coda::build_plan(nullptr, nullptr, M, N, K, &d, unfused, false, &p);
+  if (st != CODA_OK) std::printf("build_plan failed: %s\n", coda_last_error());
+  return p;
 }
 
 int main() {
@@ -75,7 +85,7 @@ int main() {
     EXPECT(coda_validate(A, B, M, N, K, &e, 0) == CODA_ERR_INVALID_ARG);
     e = d; e.b_layout = 5;
     EXPECT(coda_validate(A, B, M, N, K, &e, 0) == CODA_ERR_INVALID_ARG);
-    e = d; e.flags = 1;
+    e = d; e.flags = 2;
     EXPECT(coda_validate(A, B, M, N, K, &e, 0) == CODA_ERR_INVALID_ARG);
     e = d; e.tile = coda_num_tile_configs() + 1;
     EXPECT(coda_validate(A, B, M, N, K, &e, 0) == CODA_ERR_INVALID_ARG);
@@ -183,6 +193,45 @@ int main() {
     e.ab_dtype = CODA_F32; e.tile = 0;
     EXPECT(coda_selected_tile(4096, 22016, 4096, &e) == 0);
     EXPECT(coda_selected_tile(4096, 22016, 4100, &e) == CODA_ERR_UNSUPPORTED);
+  }
+  {  // split of the last round over K
+    coda_epi_desc e = base_desc(22016, 4096); e.flags = 0; e.ldd = 11008;
+    e.n_ops = 1; e.ops[0].kind = CODA_OP_SWIGLU_PAIR;
+    // 16 x 86 = 1376 tiles of 256 x 256 = 5 rounds of 256 CUs + 96: split in 2
+    coda::Plan p = plan_of(4096, 22016, 4096, e);
+    EXPECT(p.tile == 4 && p.full_tiles == 1280 && p.split_tiles == 96 && p.split_s == 2 && p.k_steps == 64);
+    const size_t ws = coda_workspace_size(4096, 22016, 4096, &e, 0);
+    EXPECT(ws >= size_t(96) * 2 * 256 * 256 * 4 + 96 * 4);
+    EXPECT(coda_validate(A, B, 4096, 22016, 4096, &e, 0) == CODA_ERR_WORKSPACE);
+    e.workspace = Pm(0x60000000); e.workspace_bytes = ws;
+    EXPECT(coda_validate(A, B, 4096, 22016, 4096, &e, 0) == CODA_OK);
+    // with the RMS op the partial row sums of squares need room too
+    coda_epi_desc r = e; r.n_ops = 2; r.ops[1] = r.ops[0];
+    r.ops[0].kind = CODA_OP_RMS_ROWSCALE; r.ops[0].in = P(0x40000000); r.ops[0].in_dtype = CODA_BF16;
+    EXPECT(coda_workspace_size(4096, 22016, 4096, &r, 0) >= ws + size_t(96) * 2 * 256 * 4);
+    // the unfused sequence and CODA_FLAG_NO_SPLIT_K never split
+    coda::Plan u = plan_of(4096, 22016, 4096, e, 1);
+    EXPECT(u.split_s == 1 && u.split_tiles == 0 && u.full_tiles == 1376);
+    coda_epi_desc n = e; n.flags = CODA_FLAG_NO_SPLIT_K;
+    EXPECT(coda_workspace_size(4096, 22016, 4096, &n, 0) == 0);
+    // whole rounds: 32 x 16 = 512 tiles
+    coda_epi_desc w = base_desc(4096, 1024); w.flags = 0;
+    coda::Plan q = plan_of(8192, 4096, 1024, w);
+    EXPECT(q.split_s == 1 && q.full_tiles == 512 && coda_workspace_size(8192, 4096, 1024, &w, 0) == 0);
+    // a small grid (15 tiles of 128 x 128, two per CU) takes up to 4 parts of
+    // at least 16 K steps each
+    coda_epi_desc sm = base_desc(N, 4096); sm.flags = 0;
+    coda::Plan t = plan_of(M, N, 4096, sm);
+    EXPECT(t.tile == 3 && t.full_tiles == 0 && t.split_tiles == 15 && t.split_s == 4 && t.k_steps == 64);
+    coda_epi_desc k1 = base_desc(N, 2040); k1.flags = 0;   // 32 K steps: 2 parts
+    EXPECT(plan_of(M, N, 2040, k1).split_s == 2);
+    coda_epi_desc k2 = base_desc(N, 1984); k2.flags = 0;   // 31 K steps: too few to split
+    EXPECT(plan_of(M, N, 1984, k2).split_s == 1 && coda_workspace_size(M, N, 1984, &k2, 0) == 0);
+    coda_epi_desc k3 = d; k3.flags = 0;                   // K = 200
+    EXPECT(plan_of(M, N, K, k3).split_s == 1);
+    // fp32 operands are not split
+    coda_epi_desc f = sm; f.ab_dtype = CODA_F32; f.d_dtype = CODA_F32; f.lda = 4096;
+    EXPECT(plan_of(M, N, 4096, f).split_s == 1);
   }
   EXPECT(std::strcmp(coda_status_string(CODA_ERR_WORKSPACE), "CODA_ERR_WORKSPACE") == 0);
   if (failures == 0) std::printf("ALL OK\n");
