@@ -101,7 +101,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=40,
+                    help="untimed steps first; the clock needs a few tens of steps to settle under this load")
     ap.add_argument("--tile", type=int, default=0, help="force a tile configuration (0 = automatic)")
     ap.add_argument("--no-flush", action="store_true", help="do not evict L2 / Infinity Cache between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -31,6 +31,19 @@ def trace(db: str) -> str:
     return "\n".join(out)
 
 
+def last_dispatches(db: str, kernel_substring: str, n: int) -> str:
+    """Average duration (us) of the last n dispatches of the kernel: the timed
+    steps of a run that starts with untimed warm-up steps."""
+    c = sqlite3.connect(db)
+    rows = c.execute("select name, duration from kernels order by start").fetchall()
+    d = [dur for name, dur in rows if kernel_substring in name]
+    if not d:
+        return f"no dispatch of {kernel_substring!r}"
+    tail = d[-n:]
+    return (f"{len(tail)} last dispatches of {kernel_substring!r} (of {len(d)}): "
+            f"avg {sum(tail) / len(tail) / 1000.0:.2f} us, min {min(tail) / 1000.0:.2f}, max {max(tail) / 1000.0:.2f}")
+
+
 def pmc(dbs) -> str:
     per_kernel = collections.defaultdict(lambda: collections.defaultdict(list))
     durations = collections.defaultdict(dict)
@@ -77,7 +90,50 @@ def traffic(fetch_db: str, write_db: str, kernel: str, copy_bytes: int) -> dict:
     return out
 
 
+def bench_profiles(out_dir: str, kt_db: str, fetch_db: str, write_db: str, command: str) -> None:
+    """The two summaries kept for the LLaMA-7B gate/up bench: the kernel trace
+    with a header naming the command and kernel sources, and the calibrated
+    HBM traffic of the fused kernel."""
+    import json
+    import os
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    sys.path.insert(0, root)
+    import bench
+    khash = bench.kernel_source_hash()
+    header = [
+        "# rocprofv3 kernel trace of bench.py (LLaMA-7B SwiGLU gate/up: M=4096, N=22016, K=4096)",
+        f"# command: {command}",
+        "#   (runs: rocprofv3 --kernel-trace --stats -- python3 bench.py --steps 10 --warmup 20 --no-cpu-baseline)",
+        "# fused kernel: Cfg<256,256,2,4,bf16,B[KxN],RMS>; the <...,false> kernel is the plain GEMM of the unfused",
+        "# sequence, ew_kernel / rmsnorm_kernel its other passes; FillFunctor<float> is the 512 MiB cache flush",
+        "# between steps; averages include the warm-up steps.",
+        f"# kernel source hash: {khash}",
+    ]
+    timed = "# timed steps: " + last_dispatches(kt_db, "true, true>", 10)
+    with open(os.path.join(out_dir, "fused_llama7b_gate_up_kernel_trace.txt"), "w") as f:
+        f.write("\n".join(header) + "\n" + trace(kt_db) + "\n" + timed + "\n")
+    t = traffic(fetch_db, write_db, "true, true>", 256 << 20)   # the <..., B[KxN], RMS> fused kernel
+    spec_bytes = 2 * (4096 * 4096 + 4096 * 22016 + 4096 + 4096 * 11008)
+    rec = {
+        "kernel": "fused_kernel<Cfg<256, 256, 2, 4, bf16, B row-major [K x N], deferred RMS>> on "
+                  "llama7b_swiglu_gate_up (M=4096, N=22016, K=4096)",
+        "kernel_source_hash": khash,
+        "command": command,
+        "counters": "rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE (KiB per dispatch), each scaled by "
+                    "256 MiB / (counter of a plain 256 MiB device copy in the same run)",
+        "fetch": t["FETCH_SIZE"],
+        "write": t["WRITE_SIZE"],
+        "hbm_bytes_per_launch": int(round(t["hbm_bytes_per_launch"])),
+        "algorithmic_bytes_per_launch": spec_bytes,
+    }
+    with open(os.path.join(out_dir, "fused_llama7b_gate_up_traffic.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+
+
 def main(argv):
+    if len(argv) >= 2 and argv[1] == "bench-profiles":
+        bench_profiles(*argv[2:7])
+        return 0
     if len(argv) < 3 or argv[1] not in ("trace", "pmc", "traffic"):
         print(__doc__)
         return 2

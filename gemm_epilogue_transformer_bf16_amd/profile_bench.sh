@@ -10,7 +10,7 @@ R=$(cd "$(dirname "$0")/.." && pwd)
 mkdir -p "$OUT"
 cd /tmp && export TMPDIR=/tmp
 timeout -k 10 300 rocprofv3 --kernel-trace --stats -d "$OUT/kt" -o bench -- \
-  python3 "$R/bench.py" --steps 5 --warmup 2 --no-cpu-baseline > "$OUT/bench_kt.log" 2>&1 || exit 1
+  python3 "$R/bench.py" --steps 10 --warmup 20 --no-cpu-baseline > "$OUT/bench_kt.log" 2>&1 || exit 1
 echo "kernel trace done"
 timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE -d "$OUT/fetch" -o p -- \
   python3 "$R/bench.py" --steps 3 --warmup 1 --no-cpu-baseline --no-unfused --copy-calibration > "$OUT/fetch.log" 2>&1 || exit 1
@@ -20,5 +20,7 @@ timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE -d "$OUT/write" -o p -- \
 echo "write pass done"
 cd "$R"
 python3 -m gemm_epilogue_transformer_bf16_amd.prof_summary trace "$OUT"/kt/*.db > "$OUT/trace.txt"
-python3 -m gemm_epilogue_transformer_bf16_amd.prof_summary traffic "$OUT"/fetch/*.db "$OUT"/write/*.db fused_kernel 268435456 > "$OUT/traffic.json"
+python3 -m gemm_epilogue_transformer_bf16_amd.prof_summary traffic "$OUT"/fetch/*.db "$OUT"/write/*.db "true, true>" 268435456 > "$OUT/traffic.json"
+python3 -m gemm_epilogue_transformer_bf16_amd.prof_summary bench-profiles "$OUT" "$(ls "$OUT"/kt/*.db)" \
+  "$(ls "$OUT"/fetch/*.db)" "$(ls "$OUT"/write/*.db)" "bash gemm_epilogue_transformer_bf16_amd/profile_bench.sh <out-dir>"
 echo "summaries done"
