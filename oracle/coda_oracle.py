@@ -31,6 +31,9 @@ Readings of points the pages leave open (each also listed in the design notes):
     eps inside the square root.
   * The RMS row scale precedes every other epilogue op (it is a property of A's
     rows and only commutes past the matmul, not past a nonlinearity).
+  * LayerNorm (ln_rowscale) is the mean-centred norm: mu and the 1/K variance
+    of the row's deviations, eps inside the root, gain gamma and shift beta
+    per feature (beta optional, zero when absent).
   * A reduction observes the running value at its position in the list, over
     the current width (half the GEMM width after swiglu_pair).
 """
@@ -122,6 +125,52 @@ def deferred_rmsnorm_gemm(X: np.ndarray, gamma: np.ndarray, B: np.ndarray, eps: 
     return C / rms(X, eps)[:, None]
 
 
+# --- mean-centred row norm (LayerNorm; zeli.app comment, d9bl.com Fig. 4) ---
+
+def layernorm(X: np.ndarray, gamma: np.ndarray, eps: float, beta=None) -> np.ndarray:
+    """Normalise-first form: Y[i,k] = (X[i,k] - mu_i) / sqrt(var_i + eps) * gamma[k] + beta[k].
+
+    mu_i is the mean of row i over its K features and var_i the mean of the
+    squared deviations from it (the 1/K variance), eps inside the root; beta
+    defaults to zero.
+    """
+    X = np.asarray(X, dtype=np.float64)
+    K = X.shape[1]
+    if K == 0:
+        raise ValueError("layernorm of an empty row is undefined")
+    mu = np.sum(X, axis=1) / K
+    Xc = X - mu[:, None]
+    var = np.sum(Xc * Xc, axis=1) / K
+    Y = Xc / np.sqrt(var + eps)[:, None] * np.asarray(gamma, dtype=np.float64)[None, :]
+    if beta is not None:
+        Y = Y + np.asarray(beta, dtype=np.float64)[None, :]
+    return Y
+
+
+def ln_fold(B: np.ndarray, gamma: np.ndarray, beta: np.ndarray):
+    """The two constant rows of the deferred form: u = gamma^T B and c = beta^T B."""
+    B = np.asarray(B, dtype=np.float64)
+    return (np.asarray(gamma, dtype=np.float64) @ B, np.asarray(beta, dtype=np.float64) @ B)
+
+
+def deferred_layernorm_gemm(X: np.ndarray, gamma: np.ndarray, beta: np.ndarray, B: np.ndarray,
+                            eps: float) -> np.ndarray:
+    """The rewritten form: rstd_i * ((X * gamma) @ B - mu_i * u) + c.
+
+    Both per-row factors of the norm move past the projection: the scale
+    rstd_i as for RMSNorm, and the shift mu_i as the rank-one term mu_i * u_j
+    with u = gamma^T B; beta becomes c = beta^T B.  Used only to check the
+    normalise-first form against the identity.
+    """
+    X = np.asarray(X, dtype=np.float64)
+    K = X.shape[1]
+    mu = np.sum(X, axis=1) / K
+    var = np.sum((X - mu[:, None]) ** 2, axis=1) / K
+    u, c = ln_fold(B, gamma, beta)
+    P = (X * np.asarray(gamma, dtype=np.float64)[None, :]) @ np.asarray(B, dtype=np.float64)
+    return (P - mu[:, None] * u[None, :]) / np.sqrt(var + eps)[:, None] + c[None, :]
+
+
 # --- the GEMM (d9bl.com section 3.1) ---
 
 def logical_b(B_stored: np.ndarray, b_layout: str) -> np.ndarray:
@@ -179,8 +228,8 @@ def apply_epilogue(C: np.ndarray, ops: Sequence[Tuple[str, Dict]]) -> Tuple[np.n
             if width == 0:
                 raise ValueError("row_mean over an empty row is undefined")
             reductions.append((name, args, np.sum(v, axis=1) / width))
-        elif name == "rms_rowscale":
-            raise ValueError("rms_rowscale is applied to A by forward(); it must come first")
+        elif name in ("rms_rowscale", "ln_rowscale"):
+            raise ValueError(f"{name} is applied to A by forward(); it must come first")
         else:
             raise ValueError(f"unknown op {name}")
     return v, reductions
@@ -188,7 +237,7 @@ def apply_epilogue(C: np.ndarray, ops: Sequence[Tuple[str, Dict]]) -> Tuple[np.n
 
 def forward(A: np.ndarray, B_stored: np.ndarray, ops: Sequence[Tuple[str, Dict]],
             b_layout: str = "KN", alpha: float = 1.0):
-    """Normalise (if the list starts with rms_rowscale) -> GEMM -> ordered epilogue.
+    """Normalise (if the list starts with rms_rowscale or ln_rowscale) -> GEMM -> ordered epilogue.
 
     ``ops`` items are (name, args) with array-valued args already resolved.
     Returns (D fp64, list of (name, args, fp64 per-row result)).
@@ -196,12 +245,15 @@ def forward(A: np.ndarray, B_stored: np.ndarray, ops: Sequence[Tuple[str, Dict]]
     A = np.asarray(A, dtype=np.float64)
     ops = list(ops)
     Y = A
-    if ops and ops[0][0] == "rms_rowscale":
-        args = ops[0][1]
-        Y = rmsnorm(A, args["gamma"], float(args["eps"]))
+    if ops and ops[0][0] in ("rms_rowscale", "ln_rowscale"):
+        name, args = ops[0]
+        if name == "rms_rowscale":
+            Y = rmsnorm(A, args["gamma"], float(args["eps"]))
+        else:
+            Y = layernorm(A, args["gamma"], float(args["eps"]), args.get("beta"))
         ops = ops[1:]
     for name, _ in ops:
-        if name == "rms_rowscale":
-            raise ValueError("rms_rowscale must be the first op")
+        if name in ("rms_rowscale", "ln_rowscale"):
+            raise ValueError(f"{name} must be the first op")
     C = gemm(Y, logical_b(B_stored, b_layout), alpha)
     return apply_epilogue(C, ops)

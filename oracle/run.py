@@ -33,7 +33,7 @@ def resolve_program(spec, inputs: Dict[str, np.ndarray], rows: Optional[np.ndarr
     ops = []
     for name, args in spec.program:
         r = dict(args)
-        for key in ("gamma", "vec", "mat"):
+        for key in ("gamma", "beta", "vec", "mat"):
             if key in r:
                 r[key] = arr(r[key])
         ops.append((name, r))

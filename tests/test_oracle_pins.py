@@ -42,6 +42,21 @@ def brute_force(A, B_logical, ops):
             for k in range(K):
                 Y[i][k] = A[i][k] / r * g[k]
         ops = ops[1:]
+    elif ops and ops[0][0] == "ln_rowscale":
+        g, eps = ops[0][1]["gamma"], ops[0][1]["eps"]
+        bt = ops[0][1].get("beta", [0.0] * K)
+        for i in range(M):
+            mu = 0.0
+            for k in range(K):
+                mu += A[i][k]
+            mu /= K
+            var = 0.0
+            for k in range(K):
+                var += (A[i][k] - mu) * (A[i][k] - mu)
+            var /= K
+            for k in range(K):
+                Y[i][k] = (A[i][k] - mu) / math.sqrt(var + eps) * g[k] + bt[k]
+        ops = ops[1:]
     V = [[0.0] * N for _ in range(M)]
     for i in range(M):
         for j in range(N):
@@ -132,6 +147,9 @@ PROGRAMS = {
     "cfg4": lambda r, M, N, K: [("rms_rowscale", {"gamma": 1 + 0.1 * r.standard_normal(K), "eps": 1e-6}),
                                 ("swiglu_pair", {}), ("row_mean", {})],
     "cfg5": lambda r, M, N, K: [("mul_dgelu_tanh", {"mat": r.standard_normal((M, N))}), ("row_sum", {})],
+    "ln": lambda r, M, N, K: [("ln_rowscale", {"gamma": 1 + 0.1 * r.standard_normal(K),
+                                               "beta": 0.1 * r.standard_normal(K), "eps": 1e-5}),
+                              ("add_col", {"vec": r.standard_normal(N)}), ("gelu_tanh", {}), ("row_sum", {})],
     "scales": lambda r, M, N, K: [("scale", {"alpha": -1.5}), ("scale_row", {"vec": r.standard_normal(M)}),
                                   ("scale_col", {"vec": r.standard_normal(N)}), ("add_row", {"vec": r.standard_normal(M)}),
                                   ("silu", {}), ("row_sum", {})],
@@ -217,6 +235,91 @@ def test_rms_gamma_scales_feature_not_row():
     g = np.array([1.0, 2.0, 3.0, 4.0])
     D, _ = oracle.forward(X, np.eye(K), [("rms_rowscale", {"gamma": g, "eps": 0.0})])
     assert np.allclose(D[0], g)
+
+
+# ----------------------------------------------------------------------------
+# the mean-centred norm (LayerNorm) and its deferred form
+# ----------------------------------------------------------------------------
+
+def test_layernorm_zero_mean_rows_reduce_to_rmsnorm():
+    # with every row's mean exactly zero, centring does nothing and the
+    # variance is the mean square: LayerNorm is RMSNorm (pinned separately)
+    rng = np.random.default_rng(11)
+    K = 16
+    H = rng.standard_normal((6, K // 2))
+    X = np.concatenate([H, -H], axis=1)       # exact zero row sums
+    g = 1 + 0.2 * rng.standard_normal(K)
+    assert np.allclose(oracle.layernorm(X, g, 1e-3), oracle.rmsnorm(X, g, 1e-3), rtol=1e-14, atol=0)
+
+
+def test_layernorm_moments_pin_centring_biased_variance_and_eps_inside_root():
+    rng = np.random.default_rng(12)
+    K, eps = 20, 0.5
+    X = 3.0 + 2.0 * rng.standard_normal((7, K))     # far from zero mean
+    Y = oracle.layernorm(X, np.ones(K), eps)
+    var = X.var(axis=1)                              # numpy's default: 1/K
+    assert np.allclose(Y.mean(axis=1), 0.0, atol=1e-14)
+    assert np.allclose((Y * Y).mean(axis=1), var / (var + eps), rtol=1e-13)
+
+
+def test_layernorm_invariant_to_row_shift_and_positive_row_scale():
+    rng = np.random.default_rng(13)
+    K = 12
+    X = rng.standard_normal((4, K))
+    g = rng.standard_normal(K)
+    shift = rng.standard_normal((4, 1)) * 10
+    Y0 = oracle.layernorm(X, g, 0.0)
+    assert np.allclose(oracle.layernorm(X + shift, g, 0.0), Y0, rtol=1e-11, atol=1e-11)
+    assert np.allclose(oracle.layernorm(X * 7.5, g, 0.0), Y0, rtol=1e-12, atol=1e-12)
+
+
+def test_ln_fold_brute_force():
+    rng = np.random.default_rng(14)
+    K, N = 5, 3
+    B = rng.standard_normal((K, N))
+    g, b = rng.standard_normal(K), rng.standard_normal(K)
+    u, c = oracle.ln_fold(B, g, b)
+    for j in range(N):
+        su = sc = 0.0
+        for k in range(K):
+            su += g[k] * B[k][j]
+            sc += b[k] * B[k][j]
+        assert u[j] == pytest.approx(su, rel=1e-13, abs=1e-13)
+        assert c[j] == pytest.approx(sc, rel=1e-13, abs=1e-13)
+
+
+@pytest.mark.parametrize("idx", [2, 3])
+def test_deferred_layernorm_equals_normalise_first_at_config_shapes(idx):
+    spec = w.get_config(idx)
+    M = 256
+    rng = np.random.default_rng(spec.seed + 1)
+    X = rng.normal(0.5, 1.0, size=(M, spec.K)) + rng.normal(0, 1, size=(M, 1))
+    g = 1 + 0.1 * rng.standard_normal(spec.K)
+    b = 0.1 * rng.standard_normal(spec.K)
+    W = rng.standard_normal((spec.K, spec.N)) / math.sqrt(spec.K)
+    eps = 1e-5
+    u, c = oracle.ln_fold(W, g, b)
+    D_first, _ = oracle.forward(X, W, [("ln_rowscale", {"gamma": g, "eps": eps}), ("add_col", {"vec": c})])
+    D_def = oracle.deferred_layernorm_gemm(X, g, b, W, eps)
+    assert np.abs(D_first - D_def).max() <= 1e-11 * np.abs(D_first).max()
+    # and beta folded after the projection is beta applied before it
+    D_beta, _ = oracle.forward(X, W, [("ln_rowscale", {"gamma": g, "beta": b, "eps": eps})])
+    assert np.abs(D_beta - D_first).max() <= 1e-11 * np.abs(D_first).max()
+
+
+def test_hand_worked_layernorm_golden_case():
+    import os
+    g = _read_golden(os.path.join(os.path.dirname(__file__), "golden", "hand_layernorm_gemm.txt"))
+    u, c = oracle.ln_fold(g["B"], g["gamma"], g["beta"])
+    assert np.array_equal(u, g["u"]) and np.array_equal(c, g["c"])
+    D, _ = oracle.forward(g["A"], g["B"], [("ln_rowscale", {"gamma": g["gamma"], "eps": 0.0}),
+                                           ("add_col", {"vec": c})], "KN")
+    assert np.allclose(D[0], g["D0"], rtol=1e-14) and np.allclose(D[1], g["D1"], rtol=1e-14)
+    D, _ = oracle.forward(g["A"], g["B"], [("ln_rowscale", {"gamma": g["gamma"], "beta": g["beta"],
+                                                            "eps": 0.0})], "KN")
+    assert np.allclose(D[0], g["D0"], rtol=1e-14) and np.allclose(D[1], g["D1"], rtol=1e-14)
+    D_def = oracle.deferred_layernorm_gemm(g["A"], g["gamma"], g["beta"], g["B"], 0.0)
+    assert np.allclose(D_def, np.stack([g["D0"], g["D1"]]), rtol=1e-14)
 
 
 def test_activation_closed_forms():
@@ -341,6 +444,43 @@ def test_planted_dropped_derivative_term_is_caught(monkeypatch):
     _plant(monkeypatch, "gelu_tanh_grad", bad_grad)
     with pytest.raises(AssertionError):
         test_gelu_grad_matches_central_difference()
+
+
+def test_planted_uncentred_layernorm_is_caught(monkeypatch):
+    def bad_ln(X, gamma, eps, beta=None):      # forgets the centring: an RMSNorm
+        Y = co.rmsnorm(X, gamma, eps)
+        return Y if beta is None else Y + np.asarray(beta)[None, :]
+    _plant(monkeypatch, "layernorm", bad_ln)
+    with pytest.raises(AssertionError):
+        test_layernorm_moments_pin_centring_biased_variance_and_eps_inside_root()
+    with pytest.raises(AssertionError):
+        test_hand_worked_layernorm_golden_case()
+
+
+def test_planted_unbiased_variance_is_caught(monkeypatch):
+    def bad_ln(X, gamma, eps, beta=None):      # 1/(K-1) variance
+        X = np.asarray(X, dtype=np.float64)
+        Xc = X - X.mean(axis=1, keepdims=True)
+        var = (Xc * Xc).sum(axis=1) / (X.shape[1] - 1)
+        Y = Xc / np.sqrt(var + eps)[:, None] * np.asarray(gamma)[None, :]
+        return Y if beta is None else Y + np.asarray(beta)[None, :]
+    _plant(monkeypatch, "layernorm", bad_ln)
+    with pytest.raises(AssertionError):
+        test_hand_worked_layernorm_golden_case()
+
+
+def test_planted_wrong_sign_of_mean_term_is_caught(monkeypatch):
+    def bad_def(X, gamma, beta, B, eps):
+        X = np.asarray(X, dtype=np.float64)
+        K = X.shape[1]
+        mu = X.sum(axis=1) / K
+        var = ((X - mu[:, None]) ** 2).sum(axis=1) / K
+        u, c = co.ln_fold(B, gamma, beta)
+        P = (X * gamma[None, :]) @ B
+        return (P + mu[:, None] * u[None, :]) / np.sqrt(var + eps)[:, None] + c[None, :]
+    _plant(monkeypatch, "deferred_layernorm_gemm", bad_def)
+    with pytest.raises(AssertionError):
+        test_deferred_layernorm_equals_normalise_first_at_config_shapes(2)
 
 
 def _read_golden(path):

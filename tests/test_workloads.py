@@ -46,7 +46,7 @@ def test_bf16_roundtrip_is_exact():
     assert np.array_equal(w.bf16_bits_from_f64(w.bf16_bits_to_f64(neg)), neg)
 
 
-@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("idx", [1, 2, 3, 4, 5, 6])
 def test_generator_deterministic_and_shaped(idx):
     spec = w.scaled_config(idx, 64, 96, 48) if idx != 1 else w.get_config(1)
     a = w.make_inputs(spec)
@@ -72,11 +72,16 @@ def test_distributions_match_recipe():
     s2 = w.scaled_config(2, 256, 512, 4096)
     g = w.bf16_bits_to_f64(w.make_inputs(s2)["gamma"])
     assert abs(g.mean() - 1.0) < 0.01 and abs(g.std() - 0.1) < 0.01
+    s6 = w.scaled_config(6, 4096, 64, 256)
+    X = w.bf16_bits_to_f64(w.make_inputs(s6)["X"])
+    mu = X.mean(axis=1)                                     # one N(0, 1) offset per row
+    assert abs(mu.std() - 1.0) < 0.05 and abs((X - mu[:, None]).std() - 1.0) < 0.02
 
 
 def test_full_config_table():
     shapes = {i: (w.CONFIGS[i].M, w.CONFIGS[i].N, w.CONFIGS[i].K, w.CONFIGS[i].out_width) for i in w.CONFIGS}
     assert shapes == {1: (256, 256, 256, 256), 2: (8192, 3072, 768, 3072), 3: (8192, 1024, 4096, 1024),
-                      4: (4096, 22016, 4096, 11008), 5: (8192, 4096, 1024, 4096)}
+                      4: (4096, 22016, 4096, 11008), 5: (8192, 4096, 1024, 4096),
+                      6: (8192, 3072, 768, 3072)}
     assert w.CONFIGS[5].b_layout == "NK" and w.CONFIGS[1].ab_dtype == "f32"
     assert [op for op, _ in w.CONFIGS[4].program] == ["rms_rowscale", "swiglu_pair"]

@@ -1,6 +1,6 @@
 """Seeded synthetic workloads for the fused GEMM + epilogue path.
 
-This module only describes the five transformer-layer workloads (shapes,
+This module only describes the transformer-layer workloads (shapes,
 storage dtypes, value distributions, the ordered epilogue program as plain
 data) and draws seeded inputs for them.  It holds none of the method's
 arithmetic: the HIP path and the CPU oracle each turn the symbolic program

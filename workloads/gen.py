@@ -61,6 +61,10 @@ def draw_tensor(rng: np.random.Generator, t: TensorSpec) -> np.ndarray:
         v = np.abs(z * std)
     elif t.dist == "one_plus_normal":
         v = 1.0 + z * std
+    elif t.dist == "row_shift_normal":
+        # N(0, var) plus one N(0, 1) offset per row (drawn after the values):
+        # rows whose means are of the order of their spread
+        v = z * std + rng.standard_normal((t.shape[0], 1))
     else:
         raise ValueError(t.dist)
     if t.dtype == "bf16":

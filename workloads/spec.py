@@ -1,4 +1,4 @@
-"""Declarative description of the five workloads.
+"""Declarative description of the workloads.
 
 Each workload is: GEMM shape (M, N, K) where N is the width the contraction
 computes, the storage layout of B, storage dtypes, the tensors to draw (in the
@@ -9,6 +9,8 @@ order they are drawn), and the ordered epilogue program as a list of
   scale_row(vec)            v[i,j] *= vec[i]
   scale_col(vec)            v[i,j] *= vec[j]
   rms_rowscale(gamma, eps)  deferred RMSNorm row scale (must come first)
+  ln_rowscale(gamma, beta, eps)  deferred LayerNorm of A's rows with gain gamma
+                            and shift beta (must come first)
   add_col(vec)              v[i,j] += vec[j]
   add_row(vec)              v[i,j] += vec[i]
   add_mat(mat, beta)        v[i,j] += beta * mat[i,j]
@@ -29,7 +31,7 @@ from typing import Dict, List, Optional, Tuple
 class TensorSpec:
     name: str
     shape: Tuple[int, ...]
-    dist: str            # "normal", "abs_normal", "one_plus_normal"
+    dist: str            # "normal", "abs_normal", "one_plus_normal", "row_shift_normal"
     var: float           # variance of the underlying normal
     dtype: str           # "bf16" | "f32"
 
@@ -68,7 +70,7 @@ def _normal(name, shape, var, dtype):
 
 
 def _build(index: int, M: int, N: int, K: int) -> WorkloadSpec:
-    """Build workload ``index`` (1..5) at the given GEMM shape."""
+    """Build workload ``index`` (1..6) at the given GEMM shape."""
     if index == 1:
         dt = "f32"
         tensors = (
@@ -146,16 +148,35 @@ def _build(index: int, M: int, N: int, K: int) -> WorkloadSpec:
         )
         return WorkloadSpec(5, "gpt2m_mlp_bwd_act", M, N, K, "NK", dt, dt, "dY", "W2",
                             tensors, program, (("rowsum", (M, 1)),))
+    if index == 6:
+        dt = "bf16"
+        # the GPT-2-small MLP up-projection with the LayerNorm GPT-2 actually
+        # uses in front of it; rows of X carry a mean of the order of their spread
+        tensors = (
+            TensorSpec("X", (M, K), "row_shift_normal", 1.0, dt),
+            _normal("W", (K, N), 1.0 / K, dt),
+            TensorSpec("gamma", (K,), "one_plus_normal", 0.01, dt),
+            _normal("beta", (K,), 0.01, dt),
+            _normal("bias", (N,), 0.02, dt),
+        )
+        program = (
+            ("ln_rowscale", {"gamma": "gamma", "beta": "beta", "eps": 1e-5}),
+            ("add_col", {"vec": "bias"}),
+            ("gelu_tanh", {}),
+        )
+        return WorkloadSpec(6, "gpt2s_mlp_up_layernorm", M, N, K, "KN", dt, dt, "X", "W",
+                            tensors, program, ())
     raise ValueError(f"unknown workload index {index}")
 
 
-# Full-size shapes of the five workloads (M, GEMM N, K).
+# Full-size shapes of the workloads (M, GEMM N, K).
 FULL_SHAPES = {
     1: (256, 256, 256),
     2: (8192, 3072, 768),
     3: (8192, 1024, 4096),
     4: (4096, 22016, 4096),
     5: (8192, 4096, 1024),
+    6: (8192, 3072, 768),
 }
 
 CONFIGS: Dict[int, WorkloadSpec] = {i: _build(i, *FULL_SHAPES[i]) for i in FULL_SHAPES}
