@@ -34,7 +34,8 @@ def resolve_program(spec, inputs: Dict[str, np.ndarray], rows: Optional[np.ndarr
     for name, args in spec.program:
         r = dict(args)
         for key in ("gamma", "beta", "vec", "mat"):
-            if key in r:
+            # tensor arguments are names; add_mat's beta is a number
+            if isinstance(r.get(key), str):
                 r[key] = arr(r[key])
         ops.append((name, r))
     return ops

@@ -506,3 +506,38 @@ def test_hand_worked_golden_case():
     D, reds = oracle.forward(g["A"], g["B"], ops, "KN")
     assert np.allclose(D[0], g["D0"], rtol=1e-14) and np.allclose(D[1], g["D1"], rtol=1e-14)
     assert np.allclose(reds[0][2], g["sum"], rtol=1e-14) and np.allclose(reds[1][2], g["sumsq"], rtol=1e-14)
+
+
+# ----------------------------------------------------------------------------
+# the seeded-workload driver: every workload's symbolic program resolves to
+# arrays (tensor names) and numbers (scalars) and agrees with the brute force,
+# on all rows and on a row subset
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("idx", sorted(w.CONFIGS))
+def test_run_workload_matches_brute_force_on_every_program(idx):
+    from oracle.run import resolve_program
+    from workloads.gen import to_f64
+    M, N, K = 5, 8, 6
+    spec = w.scaled_config(idx, M, N, K)
+    inputs = w.make_inputs(spec)
+    dtypes = {t.name: t.dtype for t in spec.tensors}
+    A = to_f64(inputs[spec.a_name], dtypes[spec.a_name])
+    B = oracle.logical_b(to_f64(inputs[spec.b_name], dtypes[spec.b_name]), spec.b_layout)
+    ops = resolve_program(spec, inputs)
+    for name, args in ops:
+        for key, val in args.items():
+            assert key == "out" or not isinstance(val, str), (name, key)
+    bf_ops = [(n, {k: (_lists(v) if isinstance(v, np.ndarray) and v.ndim == 2 else
+                       (list(map(float, v)) if isinstance(v, np.ndarray) else v)) for k, v in a.items()})
+              for n, a in ops]
+    V, _ = brute_force(_lists(A), _lists(B), bf_ops)
+    D, outs = oracle.run_workload(spec, inputs)
+    tol = 1e-8 if idx == 5 else 1e-12
+    assert np.allclose(D, np.array(V), rtol=tol, atol=tol)
+    rows = [4, 0, 2]
+    D_sub, outs_sub = oracle.run_workload(spec, inputs, rows)
+    assert np.array_equal(D_sub, D[rows])
+    for name in outs:
+        assert np.array_equal(outs_sub[name], outs[name][rows])
+        assert np.all(np.isfinite(outs[name]))
