@@ -68,7 +68,6 @@ int launch_args(const Plan& p, const dev::FusedArgs& a, hipStream_t stream) {
     case 1: return dev::launch_tile1(a, nwg, bkn, rms, stream);
     case 2: return dev::launch_tile2(a, nwg, bkn, rms, stream);
     case 3: return dev::launch_tile3(a, nwg, bkn, rms, stream);
-    case 4: return dev::launch_tile4(a, nwg, bkn, rms, stream);
     default:
       set_error("no kernel for tile config %d", p.tile);
       return CODA_ERR_UNSUPPORTED;

@@ -1046,7 +1046,6 @@ int launch_variants(const FusedArgs& args, int64_t nwg, bool bkn, bool rms, hipS
 int launch_tile1(const FusedArgs& a, int64_t nwg, bool bkn, bool rms, hipStream_t s);
 int launch_tile2(const FusedArgs& a, int64_t nwg, bool bkn, bool rms, hipStream_t s);
 int launch_tile3(const FusedArgs& a, int64_t nwg, bool bkn, bool rms, hipStream_t s);
-int launch_tile4(const FusedArgs& a, int64_t nwg, bool bkn, bool rms, hipStream_t s);
 int launch_tile_f32(const FusedArgs& a, int64_t nwg, bool bkn, bool rms, hipStream_t s);
 
 }  // namespace dev

@@ -49,14 +49,14 @@ bool overlap(const Extent& a, const Extent& b) {
 }
 
 // Automatic tile choice, from measurements on MI355X: the 8-wave 256 x 256
-// tile (config 4) is fastest once its grid fills the 256 CUs at least once;
-// smaller grids do better with 128 x 128 tiles (config 3), which give four
+// tile (config 3) is fastest once its grid fills the 256 CUs at least once;
+// smaller grids do better with 128 x 128 tiles (config 2), which give four
 // times as many workgroups (two resident per CU).
 }  // namespace
 
 int choose_tile(int64_t M, int64_t N) {
   const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
-  return big >= kNumCUs ? 4 : 3;
+  return big >= kNumCUs ? 3 : 2;
 }
 
 namespace {

@@ -18,10 +18,9 @@ struct TileCfg {
 };
 
 constexpr TileCfg kTileCfgs[] = {
-    {256, 256, 64, 2, 2, 1},   // 1: 4 waves, 128x128 per wave
-    {256, 128, 64, 2, 2, 1},   // 2: 4 waves, 128x64 per wave
-    {128, 128, 64, 2, 2, 2},   // 3: 4 waves, 64x64 per wave
-    {256, 256, 64, 2, 4, 1},   // 4: 8 waves, 128x64 per wave
+    {256, 128, 64, 2, 2, 1},   // 1: 4 waves, 128x64 per wave
+    {128, 128, 64, 2, 2, 2},   // 2: 4 waves, 64x64 per wave
+    {256, 256, 64, 2, 4, 1},   // 3: 8 waves, 128x64 per wave
 };
 constexpr int kNumTileCfgs = sizeof(kTileCfgs) / sizeof(kTileCfgs[0]);
 

@@ -186,8 +186,8 @@ int main() {
   }
   {  // selected tile: explicit, automatic (large grid -> 256 x 256 / 8 waves), fp32
     coda_epi_desc e = base_desc(22016, 4096);
-    EXPECT(coda_selected_tile(4096, 22016, 4096, &e) == 4);
-    EXPECT(coda_selected_tile(300, 520, 200, &d) == 3);
+    EXPECT(coda_selected_tile(4096, 22016, 4096, &e) == 3);
+    EXPECT(coda_selected_tile(300, 520, 200, &d) == 2);
     e.tile = 2;
     EXPECT(coda_selected_tile(4096, 22016, 4096, &e) == 2);
     e.ab_dtype = CODA_F32; e.tile = 0;
@@ -199,7 +199,7 @@ int main() {
     e.n_ops = 1; e.ops[0].kind = CODA_OP_SWIGLU_PAIR;
     // 16 x 86 = 1376 tiles of 256 x 256 = 5 rounds of 256 CUs + 96: split in 2
     coda::Plan p = plan_of(4096, 22016, 4096, e);
-    EXPECT(p.tile == 4 && p.full_tiles == 1280 && p.split_tiles == 96 && p.split_s == 2 && p.k_steps == 64);
+    EXPECT(p.tile == 3 && p.full_tiles == 1280 && p.split_tiles == 96 && p.split_s == 2 && p.k_steps == 64);
     const size_t ws = coda_workspace_size(4096, 22016, 4096, &e, 0);
     EXPECT(ws >= size_t(96) * 2 * 256 * 256 * 4 + 96 * 4);
     EXPECT(coda_validate(A, B, 4096, 22016, 4096, &e, 0) == CODA_ERR_WORKSPACE);
@@ -222,7 +222,7 @@ int main() {
     // at least 16 K steps each
     coda_epi_desc sm = base_desc(N, 4096); sm.flags = 0;
     coda::Plan t = plan_of(M, N, 4096, sm);
-    EXPECT(t.tile == 3 && t.full_tiles == 0 && t.split_tiles == 15 && t.split_s == 4 && t.k_steps == 64);
+    EXPECT(t.tile == 2 && t.full_tiles == 0 && t.split_tiles == 15 && t.split_s == 4 && t.k_steps == 64);
     coda_epi_desc k1 = base_desc(N, 2040); k1.flags = 0;   // 32 K steps: 2 parts
     EXPECT(plan_of(M, N, 2040, k1).split_s == 2);
     coda_epi_desc k2 = base_desc(N, 1984); k2.flags = 0;   // 31 K steps: too few to split

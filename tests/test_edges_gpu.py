@@ -94,7 +94,7 @@ def test_tiny_and_ragged_plain_gemm(CR, shape, layout):
     b = rng.standard_normal((K, N)) / np.sqrt(K)
     A = bf16(a)
     B = bf16(b if layout == "KN" else np.ascontiguousarray(b.T))
-    for tile in (1, 3):
+    for tile in (1, 2):
         call = run(CR, A, B, [], layout, tile=tile)
         ref, _ = oracle.forward(f64(A), f64(B), [], layout)
         assert_close(f64(call.D), ref, f"plain {shape} {layout} tile{tile}")
@@ -150,7 +150,7 @@ def every_op_program(M, N, K, rng, use_rms=True):
 
 
 @pytest.mark.parametrize("layout", ["KN", "NK"])
-@pytest.mark.parametrize("tile", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("tile", [0, 1, 2, 3])
 def test_every_op_fused(CR, layout, tile):
     announce(f"every op fused {layout} tile{tile}")
     rng = np.random.default_rng(21)
@@ -227,7 +227,7 @@ def test_workspace_counters_left_zero(CR):
     coda, runner = CR
     spec = w.scaled_config(3, 512, 1024, 64)
     inputs = w.make_inputs(spec)
-    call = runner.WorkloadCall(spec, inputs, tile=3)
+    call = runner.WorkloadCall(spec, inputs, tile=2)
     assert call.ws[0] is not None
     for _ in range(3):
         coda.check(call.fused(), "fused")
