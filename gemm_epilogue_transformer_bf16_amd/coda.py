@@ -43,11 +43,12 @@ CODA_OP_MUL_DGELU_TANH = 10
 CODA_OP_ROW_SUM = 11
 CODA_OP_ROW_SUMSQ = 12
 CODA_OP_ROW_MEAN = 13
+CODA_OP_LN_ROWSCALE = 14
 
 EXPORTED = (
     "coda_gemm_epi", "coda_gemm_unfused", "coda_validate", "coda_workspace_size",
     "coda_status_string", "coda_last_error", "coda_num_tile_configs", "coda_tile_config",
-    "coda_selected_tile",
+    "coda_selected_tile", "coda_ln_fold",
 )
 
 
@@ -61,6 +62,7 @@ class coda_op(ctypes.Structure):
         ("reserved0", ctypes.c_int32),
         ("out", ctypes.c_void_p),
         ("out_stride", ctypes.c_int64),
+        ("in2", ctypes.c_void_p),
     ]
 
 
@@ -115,6 +117,8 @@ def _load():
     lib.coda_tile_config.restype = ctypes.c_int
     lib.coda_selected_tile.argtypes = [I64, I64, I64, DESC]
     lib.coda_selected_tile.restype = ctypes.c_int
+    lib.coda_ln_fold.argtypes = [P, I64, I64, I64, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P]
+    lib.coda_ln_fold.restype = ctypes.c_int
     return lib
 
 
@@ -165,6 +169,11 @@ def coda_tile_config(index: int):
 
 def coda_selected_tile(M: int, N: int, K: int, desc: coda_epi_desc) -> int:
     return lib.coda_selected_tile(M, N, K, _desc_ptr(desc))
+
+
+def coda_ln_fold(B: int, K: int, N: int, ldb: int, b_layout: int, dtype: int, gamma: int, beta,
+                 u: int, c, stream: int = 0) -> int:
+    return lib.coda_ln_fold(B, K, N, ldb, b_layout, dtype, gamma, beta, u, c, stream)
 
 
 def check(status: int, where: str) -> None:

@@ -105,6 +105,7 @@ struct FusedArgs {
   const void* B;
   void* D;
   const void* gamma;
+  const float* ln_u;    // LayerNorm: u = gamma^T B [N]
   float* partials;      // [n_red][grid_n][M]
   unsigned* counters;   // [grid_m]
   long long lda, ldb, ldd;

@@ -15,6 +15,7 @@ dev::FusedArgs make_args(const Plan& p) {
   a.B = p.B;
   a.D = p.D;
   a.gamma = p.gamma;
+  a.ln_u = p.ln_u;
   a.lda = p.lda;
   a.ldb = p.ldb;
   a.ldd = p.ldd;
@@ -60,14 +61,14 @@ dev::FusedArgs make_args(const Plan& p) {
 int launch_args(const Plan& p, const dev::FusedArgs& a, hipStream_t stream) {
   const int64_t nwg = p.full_tiles + p.split_tiles * p.split_s;
   const bool bkn = p.b_layout == CODA_B_KN;
-  const bool rms = p.has_rms;
+  const int norm = p.has_ln ? dev::kNormLn : p.has_norm ? dev::kNormRms : dev::kNormNone;
   if (p.ab_dtype == CODA_F32) {
-    return dev::launch_tile_f32(a, nwg, bkn, rms, stream);
+    return dev::launch_tile_f32(a, nwg, bkn, norm, stream);
   }
   switch (p.tile) {
-    case 1: return dev::launch_tile1(a, nwg, bkn, rms, stream);
-    case 2: return dev::launch_tile2(a, nwg, bkn, rms, stream);
-    case 3: return dev::launch_tile3(a, nwg, bkn, rms, stream);
+    case 1: return dev::launch_tile1(a, nwg, bkn, norm, stream);
+    case 2: return dev::launch_tile2(a, nwg, bkn, norm, stream);
+    case 3: return dev::launch_tile3(a, nwg, bkn, norm, stream);
     default:
       set_error("no kernel for tile config %d", p.tile);
       return CODA_ERR_UNSUPPORTED;
@@ -89,8 +90,10 @@ int launch_plain_gemm(const Plan& p, const void* A, int64_t lda, void* out, int6
   q.lda = lda;
   q.D = out;
   q.ldd = ldo;
-  q.has_rms = false;
+  q.has_norm = false;
+  q.has_ln = false;
   q.gamma = nullptr;
+  q.ln_u = nullptr;
   q.n_ops = 0;
   q.n_red = 0;
   q.has_swiglu = false;

@@ -82,10 +82,16 @@ typedef const __attribute__((address_space(4))) DevOp& KOp;
 typedef __attribute__((address_space(3))) void* LdsPtr;
 typedef __attribute__((address_space(3))) i16x4_t LdsI16x4;
 
-template <int BM_, int BN_, int WM_, int WN_, bool F32_, bool BKN_, bool RMS_>
+// deferred row norm in front of the GEMM: none, RMSNorm, LayerNorm
+constexpr int kNormNone = 0, kNormRms = 1, kNormLn = 2;
+
+template <int BM_, int BN_, int WM_, int WN_, bool F32_, bool BKN_, int NORM_>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
-  static constexpr bool F32 = F32_, BKN = BKN_, RMS = RMS_;
+  static constexpr bool F32 = F32_, BKN = BKN_;
+  // RMS: gain in the main loop, sums of squares, a row scale in the epilogue;
+  // LN: additionally row sums and the mean term of the deferred LayerNorm
+  static constexpr bool RMS = NORM_ != kNormNone, LN = NORM_ == kNormLn;
   static constexpr int NW = WM * WN;
   static constexpr int NT = 64 * NW;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -122,7 +128,8 @@ struct Cfg {
   // array 1 for the reduction partials, 1/rms and a flag.
   static constexpr int EPI_RED_OFF = 0;                // in array 1
   static constexpr int EPI_RINV_OFF = EPI_RED_OFF + CODA_MAX_REDUCTIONS * WN * BM * 4;
-  static constexpr int EPI_FLAG_OFF = EPI_RINV_OFF + BM * 4;
+  static constexpr int EPI_RMU_OFF = EPI_RINV_OFF + BM * 4;   // LN: mean * rstd per row
+  static constexpr int EPI_FLAG_OFF = EPI_RMU_OFF + BM * 4;
   static constexpr int ARR0_BYTES = STAGE_BYTES > NW * REGION_BYTES ? STAGE_BYTES : NW * REGION_BYTES;
   static constexpr int ARR1_BYTES = STAGE_BYTES > EPI_FLAG_OFF + 16 ? STAGE_BYTES : EPI_FLAG_OFF + 16;
   // RMS: raw A of the next K step lands in a third array by direct loads and is
@@ -394,9 +401,12 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
 
-  float ss[C::F32 ? C::A32_CH : C::A_BPW];   // per-row sums of squares (RMS)
+  // per-row sums of squares (RMS, LN) and sums (LN) of the A values this lane
+  // converts; with bf16 operands LN shifts each row by its first element first
+  constexpr int NSS = C::F32 ? C::A32_CH : C::A_BPW;
+  float ss[NSS], sx[NSS], sh[NSS];
 #pragma unroll
-  for (int i = 0; i < (C::F32 ? C::A32_CH : C::A_BPW); ++i) ss[i] = 0.0f;
+  for (int i = 0; i < NSS; ++i) ss[i] = sx[i] = sh[i] = 0.0f;
 
   if constexpr (!C::F32) {
     // ================= bf16 main loop =================
@@ -508,18 +518,45 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
     // squares of the raw values (scaled by `live`, 0 when there is nothing to
     // convert), then bf16(x * gamma).  Each wave reads only the blocks its own
     // direct loads wrote, so no barrier is needed between load and conversion.
-    auto convert_a = [&](char* As, float live) {
+    // LN: the values converted are x - s, s the mean of the row's first 64 values
+    // (taken at the first conversion over the 8 lanes that hold the row; any
+    // per-row constant leaves the norm unchanged, and one close to the row mean
+    // keeps x - s, and so the bf16 rounding of the operand, small); chunks past K
+    // (zeros) use s = 0 so that they add nothing to the sums.
+    auto convert_a = [&](char* As, float live, int k0, bool first) {
+      const bool kin = k0 + 8 * kq_chunk < K;
 #pragma unroll
       for (int i = 0; i < C::A_BPW; ++i) {
         const int q = wave + C::NW * i;
         u32x4_t x = *reinterpret_cast<const u32x4_t*>(smem_raw + q * 1024 + lane * 16);
+        if constexpr (C::LN) {
+          if (first) {
+            float t = 0.0f;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float lo = bf16_lo(x[w]), hv = bf16_hi(x[w]);
-          const float lo_l = lo * live, hv_l = hv * live;
-          ss[i] = fmaf(lo_l, lo, ss[i]);
-          ss[i] = fmaf(hv_l, hv, ss[i]);
-          x[w] = pack_bf16x2(lo * bf16_lo(greg[w]), hv * bf16_hi(greg[w]));
+            for (int w = 0; w < 4; ++w) t += bf16_lo(x[w]) + bf16_hi(x[w]);
+            t += __shfl_xor(t, 1);
+            t += __shfl_xor(t, 2);
+            t += __shfl_xor(t, 4);
+            sh[i] = t * (1.0f / 64.0f);
+          }
+          const float s0 = kin ? sh[i] : 0.0f;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const float lo = bf16_lo(x[w]) - s0, hv = bf16_hi(x[w]) - s0;
+            ss[i] = fmaf(lo * live, lo, ss[i]);
+            ss[i] = fmaf(hv * live, hv, ss[i]);
+            sx[i] += (lo + hv) * live;
+            x[w] = pack_bf16x2(lo * bf16_lo(greg[w]), hv * bf16_hi(greg[w]));
+          }
+        } else {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const float lo = bf16_lo(x[w]), hv = bf16_hi(x[w]);
+            const float lo_l = lo * live, hv_l = hv * live;
+            ss[i] = fmaf(lo_l, lo, ss[i]);
+            ss[i] = fmaf(hv_l, hv, ss[i]);
+            x[w] = pack_bf16x2(lo * bf16_lo(greg[w]), hv * bf16_hi(greg[w]));
+          }
         }
         *reinterpret_cast<u32x4_t*>(As + q * 1024 + lane * 16) = x;
       }
@@ -608,7 +645,7 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
     const bool convert_first = wave >= C::NW / 2;
     auto convert_phase = [&](int kt, char* nxt) {
       wait_vm(kAfterA);                     // raw A(kt+1) and its gamma have landed
-      convert_a(nxt, 1.0f);
+      convert_a(nxt, 1.0f, (kt_lo + kt + 1) * 64, false);
       if (kt + 2 < KT) {
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // raw reads done before reuse
         load_a(kt + 2, smem_raw);
@@ -646,7 +683,7 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
         load_a(0, smem_raw);
         load_b(0, smem0);
         wait_vm(kAfterA);
-        convert_a(smem0, 1.0f);
+        convert_a(smem0, 1.0f, kt_lo * 64, true);
         if (KT > 1) {
           asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
           load_a(1, smem_raw);
@@ -709,17 +746,30 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
         greg = buffer_load16(rg, uint32_t((k0 + a_c * 4) * 4));
       }
     };
-    auto sstore = [&](int buf) {
+    // LN: as in the bf16 loop, A - s with s the mean of the row's first BK
+    // values (the KCH threads of a row are consecutive lanes)
+    auto sstore = [&](int buf, int k0) {
       float* As = reinterpret_cast<float*>(buf ? smem1 : smem0);
       float* Bs = As + BM * SA;
+      const bool kin = k0 + a_c * 4 < K;
 #pragma unroll
       for (int i = 0; i < C::A32_CH; ++i) {
         float* dst = As + (a_r + i * A_RSTEP) * SA + a_c * 4;
+        if (C::LN && k0 == 0) {
+          float t = 0.0f;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) t += __uint_as_float(areg[i][w]);
+#pragma unroll
+          for (int off = 1; off < KCH; off <<= 1) t += __shfl_xor(t, off);
+          sh[i] = t * (1.0f / float(BK));
+        }
+        const float s0 = (C::LN && kin) ? sh[i] : 0.0f;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          float x = __uint_as_float(areg[i][w]);
+          float x = __uint_as_float(areg[i][w]) - s0;
           if (C::RMS) {
             ss[i] = fmaf(x, x, ss[i]);
+            if (C::LN) sx[i] += x;
             x = x * __uint_as_float(greg[w]);
           }
           dst[w] = x;
@@ -757,14 +807,14 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
     };
     if (KT > 0) {
       gload(0);
-      sstore(0);
+      sstore(0, 0);
       __syncthreads();
       for (int kt = 0; kt < KT; ++kt) {
         const int cur = kt & 1;
         const bool more = kt + 1 < KT;
         if (more) gload(kt + 1);
         compute(cur);
-        if (more) sstore(cur ^ 1);
+        if (more) sstore(cur ^ 1, (kt + 1) * BK);
         __syncthreads();
       }
     }
@@ -778,7 +828,7 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
   // out and come back as agent-scope atomic accesses, which are coherent across
   // the XCDs' L2 caches; waiting for the stores to complete before the count
   // publishes them without writing back or invalidating a whole L2.
-  if constexpr (!C::F32) {
+  if constexpr (!C::F32 && !C::LN) {   // LN tiles are never split
     if (split >= 0) {
       const int S = a->split_s;
       constexpr int NG = MI * NI * 8;   // pairs of accumulator registers per thread
@@ -860,6 +910,20 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
   char* region = smem0 + wave * C::REGION_BYTES;
   float* red = reinterpret_cast<float*>(smem1 + C::EPI_RED_OFF);
   float* rinv = reinterpret_cast<float*>(smem1 + C::EPI_RINV_OFF);
+  float* rmu = reinterpret_cast<float*>(smem1 + C::EPI_RMU_OFF);
+  // row factors from the sums: RMS 1/sqrt(ss/K + eps); LN rstd = 1/sqrt(var + eps)
+  // with mean m = sx/K and var = ss/K - m^2 (of the shifted values), and m * rstd
+  auto row_factors = [&](int row, float v, float s) {
+    if constexpr (C::LN) {
+      const float m = s / float(K);
+      const float var = fmaxf(v / float(K) - m * m, 0.0f);
+      const float r = 1.0f / sqrtf(var + a->eps);
+      rinv[row] = r;
+      rmu[row] = m * r;
+    } else {
+      rinv[row] = 1.0f / sqrtf(v / float(K) + a->eps);
+    }
+  };
   int* flag = reinterpret_cast<int*>(smem1 + C::EPI_FLAG_OFF);
 
   if constexpr (C::RMS) {
@@ -867,20 +931,28 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
       // rows 8q + (lane >> 3): the 8 lanes of a row are consecutive
 #pragma unroll
       for (int i = 0; i < C::A_BPW; ++i) {
-        float v = ss[i];
+        float v = ss[i], s = sx[i];
         v += __shfl_xor(v, 1);
         v += __shfl_xor(v, 2);
         v += __shfl_xor(v, 4);
-        if ((lane & 7) == 0) rinv[8 * (wave + C::NW * i) + (lane >> 3)] = 1.0f / sqrtf(v / float(K) + a->eps);
+        if constexpr (C::LN) {
+          s += __shfl_xor(s, 1);
+          s += __shfl_xor(s, 2);
+          s += __shfl_xor(s, 4);
+        }
+        if ((lane & 7) == 0) row_factors(8 * (wave + C::NW * i) + (lane >> 3), v, s);
       }
     } else {
       constexpr int KCH = BK / 4;
 #pragma unroll
       for (int i = 0; i < C::A32_CH; ++i) {
-        float v = ss[i];
+        float v = ss[i], s = sx[i];
 #pragma unroll
-        for (int off = 1; off < KCH; off <<= 1) v += __shfl_xor(v, off);
-        if (tid % KCH == 0) rinv[tid / KCH + i * (C::NT / KCH)] = 1.0f / sqrtf(v / float(K) + a->eps);
+        for (int off = 1; off < KCH; off <<= 1) {
+          v += __shfl_xor(v, off);
+          if constexpr (C::LN) s += __shfl_xor(s, off);
+        }
+        if (tid % KCH == 0) row_factors(tid / KCH + i * (C::NT / KCH), v, s);
       }
     }
     __syncthreads();
@@ -911,6 +983,9 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
     }
   };
   if (pf_op >= 0) prefetch(0, pf_buf[0]);
+  // LN: u[j] for the lane's 8 columns (the same in every block)
+  float uv[8];
+  if constexpr (C::LN) load_cols<false>(a->ln_u, CODA_F32, n0 + wn * C::WTN + 8 * (lane % C::CPR), N, uv);
 
   static_for<0, MI>([&](auto mic) {
     constexpr int mi = decltype(mic)::value;
@@ -948,7 +1023,11 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
         ch.v[j][e] = lo[e];
         ch.v[j][4 + e] = hv[e];
       }
-      if constexpr (C::RMS) {
+      if constexpr (C::LN) {
+        const float s = rinv[ch.mloc[j]], mr = rmu[ch.mloc[j]];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ch.v[j][e] = fmaf(ch.v[j][e], s, -mr * uv[e]);
+      } else if constexpr (C::RMS) {
         const float s = rinv[ch.mloc[j]];
 #pragma unroll
         for (int e = 0; e < 8; ++e) ch.v[j][e] *= s;
@@ -1032,21 +1111,26 @@ int launch_cfg(const FusedArgs& args, int64_t nwg, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? CODA_OK : CODA_ERR_HIP;
 }
 
-template <int BM, int BN, int WM, int WN, bool F32>
-int launch_variants(const FusedArgs& args, int64_t nwg, bool bkn, bool rms, hipStream_t s) {
-  if (bkn) {
-    return rms ? launch_cfg<Cfg<BM, BN, WM, WN, F32, true, true>>(args, nwg, s)
-               : launch_cfg<Cfg<BM, BN, WM, WN, F32, true, false>>(args, nwg, s);
+template <int BM, int BN, int WM, int WN, bool F32, bool BKN>
+int launch_norms(const FusedArgs& args, int64_t nwg, int norm, hipStream_t s) {
+  switch (norm) {
+    case kNormRms: return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormRms>>(args, nwg, s);
+    case kNormLn: return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormLn>>(args, nwg, s);
+    default: return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormNone>>(args, nwg, s);
   }
-  return rms ? launch_cfg<Cfg<BM, BN, WM, WN, F32, false, true>>(args, nwg, s)
-             : launch_cfg<Cfg<BM, BN, WM, WN, F32, false, false>>(args, nwg, s);
+}
+
+template <int BM, int BN, int WM, int WN, bool F32>
+int launch_variants(const FusedArgs& args, int64_t nwg, bool bkn, int norm, hipStream_t s) {
+  return bkn ? launch_norms<BM, BN, WM, WN, F32, true>(args, nwg, norm, s)
+             : launch_norms<BM, BN, WM, WN, F32, false>(args, nwg, norm, s);
 }
 
 // one function per compiled tile configuration (defined in coda_fused_t*.hip)
-int launch_tile1(const FusedArgs& a, int64_t nwg, bool bkn, bool rms, hipStream_t s);
-int launch_tile2(const FusedArgs& a, int64_t nwg, bool bkn, bool rms, hipStream_t s);
-int launch_tile3(const FusedArgs& a, int64_t nwg, bool bkn, bool rms, hipStream_t s);
-int launch_tile_f32(const FusedArgs& a, int64_t nwg, bool bkn, bool rms, hipStream_t s);
+int launch_tile1(const FusedArgs& a, int64_t nwg, bool bkn, int norm, hipStream_t s);
+int launch_tile2(const FusedArgs& a, int64_t nwg, bool bkn, int norm, hipStream_t s);
+int launch_tile3(const FusedArgs& a, int64_t nwg, bool bkn, int norm, hipStream_t s);
+int launch_tile_f32(const FusedArgs& a, int64_t nwg, bool bkn, int norm, hipStream_t s);
 
 }  // namespace dev
 }  // namespace coda

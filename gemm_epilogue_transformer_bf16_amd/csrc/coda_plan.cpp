@@ -96,7 +96,7 @@ size_t fused_split_ss_offset(const Plan& p) {
 }
 
 size_t fused_split_counters_offset(const Plan& p) {
-  const size_t ss = p.has_rms ? size_t(p.split_tiles) * size_t(p.split_s) * size_t(p.cfg.bm) * sizeof(float) : 0;
+  const size_t ss = p.has_norm ? size_t(p.split_tiles) * size_t(p.split_s) * size_t(p.cfg.bm) * sizeof(float) : 0;
   return fused_split_ss_offset(p) + align256(ss);
 }
 
@@ -115,7 +115,7 @@ void plan_split(Plan* p, bool allow) {
   p->full_tiles = p->grid_m * p->grid_n;
   p->split_tiles = 0;
   p->split_s = 1;
-  if (!allow || p->ab_dtype != CODA_BF16 || p->K == 0) return;
+  if (!allow || p->ab_dtype != CODA_BF16 || p->K == 0 || p->has_ln) return;
   const int64_t tiles = p->grid_m * p->grid_n;
   const int64_t slots = int64_t(kNumCUs) * p->cfg.wg_per_cu;
   const int64_t r = tiles % slots;
@@ -134,7 +134,7 @@ int64_t unfused_ld(const Plan& p) { return (p.N + 7) / 8 * 8; }
 size_t unfused_workspace_bytes(const Plan& p) {
   if (p.M == 0 || p.N == 0) return 0;
   size_t bytes = 0;
-  if (p.has_rms) bytes += align256(size_t(p.M) * size_t(p.K) * dtype_size(p.ab_dtype));
+  if (p.has_norm) bytes += align256(size_t(p.M) * size_t(p.K) * dtype_size(p.ab_dtype));
   bytes += 2 * align256(size_t(p.M) * size_t(unfused_ld(p)) * dtype_size(p.d_dtype));
   return bytes;
 }
@@ -195,7 +195,7 @@ int build_plan(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
   int n_red = 0;
   for (int i = 0; i < d->n_ops; ++i) {
     const coda_op& o = d->ops[i];
-    if (o.kind < CODA_OP_SCALE || o.kind > CODA_OP_ROW_MEAN) {
+    if (o.kind < CODA_OP_SCALE || o.kind > CODA_OP_LN_ROWSCALE) {
       set_error("op %d: unknown kind %d", i, o.kind);
       return CODA_ERR_INVALID_ARG;
     }
@@ -203,29 +203,47 @@ int build_plan(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
       set_error("op %d: reserved0 must be 0", i);
       return CODA_ERR_INVALID_ARG;
     }
-    if (o.kind == CODA_OP_RMS_ROWSCALE) {
+    const bool ln = o.kind == CODA_OP_LN_ROWSCALE;
+    if (!ln && o.in2) {
+      set_error("op %d: in2 must be NULL", i);
+      return CODA_ERR_INVALID_ARG;
+    }
+    if (o.kind == CODA_OP_RMS_ROWSCALE || ln) {
+      const char* name = ln ? "LN_ROWSCALE" : "RMS_ROWSCALE";
       if (i != 0) {
-        set_error("op %d: RMS_ROWSCALE must be the first op", i);
+        set_error("op %d: %s must be the first op", i, name);
         return CODA_ERR_INVALID_ARG;
       }
       if (K == 0) {
-        set_error("RMS_ROWSCALE needs K > 0");
+        set_error("%s needs K > 0", name);
         return CODA_ERR_INVALID_ARG;
       }
       if (!o.in || o.in_dtype != d->ab_dtype) {
-        set_error("RMS_ROWSCALE needs gamma[K] in the A/B dtype");
+        set_error("%s needs gamma[K] in the A/B dtype", name);
         return CODA_ERR_INVALID_ARG;
       }
       if (!(std::isfinite(o.scalar) && o.scalar >= 0.0f)) {
-        set_error("RMS_ROWSCALE eps must be finite and >= 0");
+        set_error("%s eps must be finite and >= 0", name);
         return CODA_ERR_INVALID_ARG;
       }
       if (!aligned(o.in, 16)) {
         set_error("gamma must be 16-byte aligned");
         return CODA_ERR_UNSUPPORTED;
       }
-      p->has_rms = true;
+      if (ln) {
+        if (!o.in2) {
+          set_error("LN_ROWSCALE needs u = gamma^T B [N] in in2");
+          return CODA_ERR_INVALID_ARG;
+        }
+        if (!aligned(o.in2, 16)) {
+          set_error("LN_ROWSCALE u must be 16-byte aligned");
+          return CODA_ERR_UNSUPPORTED;
+        }
+      }
+      p->has_norm = true;
+      p->has_ln = ln;
       p->gamma = o.in;
+      p->ln_u = static_cast<const float*>(o.in2);
       p->eps = o.scalar;
       continue;
     }
@@ -368,8 +386,12 @@ int build_plan(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
       set_error("D overlaps A or B");
       return CODA_ERR_INVALID_ARG;
     }
-    if (p->has_rms && overlap(eD, matrix_extent(p->gamma, 1, K, K, abs))) {
+    if (p->has_norm && overlap(eD, matrix_extent(p->gamma, 1, K, K, abs))) {
       set_error("D overlaps gamma");
+      return CODA_ERR_INVALID_ARG;
+    }
+    if (p->has_ln && overlap(eD, matrix_extent(p->ln_u, 1, N, N, 4))) {
+      set_error("D overlaps LN_ROWSCALE's u");
       return CODA_ERR_INVALID_ARG;
     }
     Extent outs[CODA_MAX_REDUCTIONS];
@@ -427,6 +449,57 @@ int build_plan(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
         return CODA_ERR_UNSUPPORTED;
       }
     }
+  }
+  return CODA_OK;
+}
+
+int validate_ln_fold(const void* B, int64_t K, int64_t N, int64_t ldb, int32_t b_layout, int32_t dtype,
+                     const void* gamma, const void* beta, const float* u, const float* c) {
+  clear_error();
+  if (K < 0 || N < 0) {
+    set_error("negative size K=%lld N=%lld", (long long)K, (long long)N);
+    return CODA_ERR_INVALID_ARG;
+  }
+  if (K > kMaxDim || N > kMaxDim) {
+    set_error("size above 2^31-1");
+    return CODA_ERR_UNSUPPORTED;
+  }
+  if (!valid_dtype(dtype) || (b_layout != CODA_B_KN && b_layout != CODA_B_NK)) {
+    set_error("unknown dtype %d or B layout %d", dtype, b_layout);
+    return CODA_ERR_INVALID_ARG;
+  }
+  if ((beta == nullptr) != (c == nullptr)) {
+    set_error("beta and c must be both NULL or both set");
+    return CODA_ERR_INVALID_ARG;
+  }
+  if (N == 0) return CODA_OK;
+  if (!u || (K > 0 && (!B || !gamma))) {
+    set_error("B, gamma or u is NULL");
+    return CODA_ERR_INVALID_ARG;
+  }
+  if (ldb < (b_layout == CODA_B_KN ? N : K)) {
+    set_error("ldb=%lld too small", (long long)ldb);
+    return CODA_ERR_INVALID_ARG;
+  }
+  if (K % 8 || ldb % 8 || (b_layout == CODA_B_KN && N % 8)) {
+    set_error("K, ldb (and N for B stored [K x N]) must be multiples of 8 (K=%lld N=%lld ldb=%lld)",
+              (long long)K, (long long)N, (long long)ldb);
+    return CODA_ERR_UNSUPPORTED;
+  }
+  if (!aligned(B, 16) || !aligned(gamma, 16) || !aligned(beta, 16) || !aligned(u, 16) || !aligned(c, 16)) {
+    set_error("B, gamma, beta, u and c must be 16-byte aligned");
+    return CODA_ERR_UNSUPPORTED;
+  }
+  const size_t es = dtype_size(dtype);
+  // a NULL c / beta has no extent
+  auto vec = [](const void* q, int64_t n, size_t e) { return q ? matrix_extent(q, 1, n, n, e) : Extent{0, 0}; };
+  const Extent eu = vec(u, N, 4), ec = vec(c, N, 4);
+  const Extent eB = b_layout == CODA_B_KN ? matrix_extent(B, K, N, ldb, es) : matrix_extent(B, N, K, ldb, es);
+  const Extent eg = vec(gamma, K, es), eb = vec(beta, K, es);
+  if (overlap(eu, ec) || overlap(eu, eB) || overlap(ec, eB) || overlap(eu, eg) || overlap(ec, eg) ||
+      overlap(eu, eb) || overlap(ec, eb)) {
+    set_error("u or c overlaps an input or each other");
+    return CODA_ERR_INVALID_ARG;
   }
   return CODA_OK;
 }

@@ -54,10 +54,12 @@ struct Plan {
   const void* A;
   const void* B;
   void* D;
-  bool has_rms;
+  bool has_norm;             // a deferred row norm (RMS_ROWSCALE or LN_ROWSCALE) is op 0
+  bool has_ln;               // ... and it is LN_ROWSCALE
   const void* gamma;
+  const float* ln_u;         // LN_ROWSCALE: u = gamma^T B [N]
   float eps;
-  int n_ops;                 // ops after the RMS op
+  int n_ops;                 // ops after the norm op
   Op ops[CODA_MAX_OPS];
   int n_red;
   bool has_swiglu;
@@ -98,6 +100,10 @@ size_t fused_split_counters_offset(const Plan& p);
 // ldi = N rounded up to a multiple of 8.
 size_t unfused_workspace_bytes(const Plan& p);
 int64_t unfused_ld(const Plan& p);
+
+// Validates a coda_ln_fold call.  Returns a coda_status.
+int validate_ln_fold(const void* B, int64_t K, int64_t N, int64_t ldb, int32_t b_layout, int32_t dtype,
+                     const void* gamma, const void* beta, const float* u, const float* c);
 
 // Automatic bf16 tile configuration (1-based) for an M x N output.
 int choose_tile(int64_t M, int64_t N);

@@ -3,7 +3,7 @@
 // describes under "The problem": the GEMM output written out and read straight
 // back by the next operator's kernel).
 //
-//   [rmsnorm pass]  ->  plain GEMM (same main loop as the fused kernel)
+//   [row norm pass]  ->  plain GEMM (same main loop as the fused kernel)
 //   ->  one pass per elementwise op  ->  one pass per row reduction
 //
 // Every pass streams its operands with 16-byte vector accesses.
@@ -17,9 +17,41 @@ namespace dev {
 
 constexpr int kPassThreads = 256;
 
-// ---- RMS normalisation of A's rows: Y = (x * rinv) * gamma, one wave per row ----
+// ---- row normalisation of A, one wave per row ----
+// RMS: Y = (x * rinv) * gamma with rinv = 1/sqrt(mean(x^2) + eps).
+// LN:  Y = ((x - mu) * rstd) * gamma with mu the row mean and rstd = 1/sqrt(var +
+//      eps), var the mean squared deviation (a second pass over the row, which
+//      is in cache).  The shift beta is left to the epilogue's column term.
 template <bool F32>
-__global__ void __launch_bounds__(kPassThreads) rmsnorm_kernel(const void* X, long long ldx, const void* gamma,
+__device__ __forceinline__ float row_pass(const char* xr, int nch, int lane, float mu, bool sq) {
+  float acc = 0.0f;
+  for (int c = lane; c < nch; c += 64) {
+    const u32x4_t x = *reinterpret_cast<const u32x4_t*>(xr + c * 16);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      float v[2];
+      if (F32) {
+        v[0] = __uint_as_float(x[w]) - mu;
+        v[1] = 0.0f;
+      } else {
+        v[0] = bf16_lo(x[w]) - mu;
+        v[1] = bf16_hi(x[w]) - mu;
+      }
+      if (sq) {
+        acc = fmaf(v[0], v[0], acc);
+        acc = fmaf(v[1], v[1], acc);
+      } else {
+        acc += v[0] + v[1];
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+  return acc;
+}
+
+template <bool F32, bool LN>
+__global__ void __launch_bounds__(kPassThreads) rownorm_kernel(const void* X, long long ldx, const void* gamma,
                                                                float eps, int M, int K, void* Y, long long ldy) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * (kPassThreads / 64) + (threadIdx.x >> 6);
@@ -28,23 +60,8 @@ __global__ void __launch_bounds__(kPassThreads) rmsnorm_kernel(const void* X, lo
   const int nch = K / CE;
   const char* xr = static_cast<const char*>(X) + (long long)row * ldx * (F32 ? 4 : 2);
   char* yr = static_cast<char*>(Y) + (long long)row * ldy * (F32 ? 4 : 2);
-  float ss = 0.0f;
-  for (int c = lane; c < nch; c += 64) {
-    const u32x4_t x = *reinterpret_cast<const u32x4_t*>(xr + c * 16);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      if (F32) {
-        const float v = __uint_as_float(x[w]);
-        ss = fmaf(v, v, ss);
-      } else {
-        const float lo = bf16_lo(x[w]), hi = bf16_hi(x[w]);
-        ss = fmaf(lo, lo, ss);
-        ss = fmaf(hi, hi, ss);
-      }
-    }
-  }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+  const float mu = LN ? row_pass<F32>(xr, nch, lane, 0.0f, false) / float(K) : 0.0f;
+  const float ss = row_pass<F32>(xr, nch, lane, mu, true);
   const float rinv = 1.0f / sqrtf(ss / float(K) + eps);
   const char* gp = static_cast<const char*>(gamma);
   for (int c = lane; c < nch; c += 64) {
@@ -54,9 +71,10 @@ __global__ void __launch_bounds__(kPassThreads) rmsnorm_kernel(const void* X, lo
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       if (F32) {
-        y[w] = __float_as_uint((__uint_as_float(x[w]) * rinv) * __uint_as_float(gv[w]));
+        y[w] = __float_as_uint(((__uint_as_float(x[w]) - mu) * rinv) * __uint_as_float(gv[w]));
       } else {
-        y[w] = pack_bf16x2((bf16_lo(x[w]) * rinv) * bf16_lo(gv[w]), (bf16_hi(x[w]) * rinv) * bf16_hi(gv[w]));
+        y[w] = pack_bf16x2(((bf16_lo(x[w]) - mu) * rinv) * bf16_lo(gv[w]),
+                           ((bf16_hi(x[w]) - mu) * rinv) * bf16_hi(gv[w]));
       }
     }
     *reinterpret_cast<u32x4_t*>(yr + c * 16) = y;
@@ -232,16 +250,14 @@ int launch_unfused(const Plan& p, hipStream_t stream) {
   const int M = (int)p.M;
   const void* gA = p.A;
   int64_t glda = p.lda;
-  if (p.has_rms) {
+  if (p.has_norm) {
     void* Xn = ws;
     ws += align256(size_t(p.M) * size_t(p.K) * dtype_size(p.ab_dtype));
     const unsigned blocks = unsigned((p.M + 3) / 4);
-    if (p.ab_dtype == CODA_F32)
-      hipLaunchKernelGGL(dev::rmsnorm_kernel<true>, dim3(blocks), dim3(dev::kPassThreads), 0, stream, p.A,
-                         (long long)p.lda, p.gamma, p.eps, M, (int)p.K, Xn, (long long)p.K);
-    else
-      hipLaunchKernelGGL(dev::rmsnorm_kernel<false>, dim3(blocks), dim3(dev::kPassThreads), 0, stream, p.A,
-                         (long long)p.lda, p.gamma, p.eps, M, (int)p.K, Xn, (long long)p.K);
+    auto* kern = p.ab_dtype == CODA_F32 ? (p.has_ln ? dev::rownorm_kernel<true, true> : dev::rownorm_kernel<true, false>)
+                                        : (p.has_ln ? dev::rownorm_kernel<false, true> : dev::rownorm_kernel<false, false>);
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(dev::kPassThreads), 0, stream, p.A, (long long)p.lda, p.gamma,
+                       p.eps, M, (int)p.K, Xn, (long long)p.K);
     if (check_launch() != CODA_OK) return CODA_ERR_HIP;
     gA = Xn;
     glda = p.K;

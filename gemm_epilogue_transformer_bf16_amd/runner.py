@@ -28,6 +28,7 @@ OPCODES = {
     "row_sum": C.CODA_OP_ROW_SUM,
     "row_sumsq": C.CODA_OP_ROW_SUMSQ,
     "row_mean": C.CODA_OP_ROW_MEAN,
+    "ln_rowscale": C.CODA_OP_LN_ROWSCALE,
 }
 
 TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
@@ -57,6 +58,9 @@ class Call:
     ``ops`` is a list of (name, args) where array arguments are device tensors:
     ``gamma``/``vec``/``mat`` inputs, ``out`` a 2-D fp32 tensor with ``col``
     selecting the column a reduction writes.  Scalars: ``alpha``, ``beta``, ``eps``.
+    ``ln_rowscale`` takes ``gamma``, ``eps`` and an optional shift ``beta``
+    tensor: the call computes u = gamma^T B and c = beta^T B once with
+    coda_ln_fold and passes LN_ROWSCALE(gamma, u) followed by ADD_COL(c).
     """
 
     def __init__(self, A: torch.Tensor, B: torch.Tensor, ops: Sequence[Tuple[str, Dict]], b_layout: str,
@@ -69,8 +73,14 @@ class Call:
         if N is None:
             N = B.shape[1] if b_layout == "KN" else B.shape[0]
         self.N = N
-        self.ops = list(ops)
         self.b_layout = b_layout
+        self._keep: List[torch.Tensor] = []
+        if lda is None:
+            lda = A.stride(0) if A.dim() == 2 and A.shape[0] > 0 and A.shape[1] > 0 else max((self.K + 7) // 8 * 8, 8)
+        if ldb is None:
+            inner = self.N if b_layout == "KN" else self.K
+            ldb = B.stride(0) if B.dim() == 2 and B.numel() > 0 else max((inner + 7) // 8 * 8, 8)
+        self.ops = self._expand_layernorm(list(ops), B, ldb)
         width = self.N // 2 if any(n == "swiglu_pair" for n, _ in self.ops) else self.N
         self.out_width = width
         d_dtype = d_dtype or A.dtype
@@ -79,16 +89,10 @@ class Call:
             ldd = max((width + 7) // 8 * 8, 8)
             D = torch.empty((self.M, ldd), dtype=d_dtype, device=A.device)[:, :width]
         self.D = D
-        self._keep: List[torch.Tensor] = []
         d = C.coda_epi_desc()
         d.ab_dtype = CODA_DT[A.dtype]
         d.d_dtype = CODA_DT[D.dtype]
         d.b_layout = C.CODA_B_KN if b_layout == "KN" else C.CODA_B_NK
-        if lda is None:
-            lda = A.stride(0) if A.dim() == 2 and A.shape[0] > 0 and A.shape[1] > 0 else max((self.K + 7) // 8 * 8, 8)
-        if ldb is None:
-            inner = self.N if b_layout == "KN" else self.K
-            ldb = B.stride(0) if B.dim() == 2 and B.numel() > 0 else max((inner + 7) // 8 * 8, 8)
         d.lda = lda
         d.ldb = ldb
         d.ldd = D.stride(0) if D.dim() == 2 and D.shape[0] > 0 else max(width, 8)
@@ -111,8 +115,10 @@ class Call:
                 o.scalar = float(args["alpha"])
             elif name == "add_mat":
                 o.scalar = float(args.get("beta", 1.0))
-            elif name == "rms_rowscale":
+            elif name in ("rms_rowscale", "ln_rowscale"):
                 o.scalar = float(args["eps"])
+            if name == "ln_rowscale":
+                o.in2 = args["u"].data_ptr()
             if name in ("row_sum", "row_sumsq", "row_mean"):
                 out = args["out"]
                 self._keep.append(out)
@@ -126,6 +132,29 @@ class Call:
         for unfused in (0, 1):
             nbytes = C.coda_workspace_size(self.M, self.N, self.K, d, unfused)
             self.ws[unfused] = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=A.device) if nbytes else None
+
+    def _expand_layernorm(self, ops, B: torch.Tensor, ldb: int):
+        """ln_rowscale(gamma, beta, eps) -> LN_ROWSCALE(gamma, u) [+ ADD_COL(c)],
+        with u, c from coda_ln_fold on the current stream."""
+        if not ops or ops[0][0] != "ln_rowscale" or "u" in ops[0][1]:
+            return ops
+        args = dict(ops[0][1])
+        gamma, beta = args["gamma"], args.pop("beta", None)
+        n = max(self.N, 1)
+        u = torch.empty(n, dtype=torch.float32, device=B.device)
+        c = torch.empty(n, dtype=torch.float32, device=B.device) if beta is not None else None
+        self._keep += [t for t in (gamma, beta, u, c) if t is not None]
+        st = C.coda_ln_fold(B.data_ptr() if B.numel() else None, self.K, self.N, ldb,
+                            C.CODA_B_KN if self.b_layout == "KN" else C.CODA_B_NK, CODA_DT[B.dtype],
+                            gamma.data_ptr() if gamma.numel() else None,
+                            None if beta is None else beta.data_ptr(), u.data_ptr(),
+                            None if c is None else c.data_ptr(), current_stream_ptr())
+        C.check(st, "coda_ln_fold")
+        args["u"] = u
+        out = [("ln_rowscale", args)]
+        if c is not None:
+            out.append(("add_col", {"vec": c}))
+        return out + list(ops[1:])
 
     def _set_ws(self, unfused: int):
         w = self.ws[unfused]
@@ -161,8 +190,8 @@ class WorkloadCall(Call):
         ops = []
         for name, args in spec.program:
             a = dict(args)
-            for key in ("gamma", "vec", "mat"):
-                if key in a:
+            for key in ("gamma", "beta", "vec", "mat"):
+                if isinstance(a.get(key), str):   # tensor names (add_mat's beta is a number)
                     a[key] = self.tensors[a[key]]
             if "out" in a:
                 a["out"] = self.outputs[a["out"]]

@@ -115,7 +115,19 @@ typedef enum {
      CODA_MAX_REDUCTIONS per list. */
   CODA_OP_ROW_SUM = 11,
   CODA_OP_ROW_SUMSQ = 12,
-  CODA_OP_ROW_MEAN = 13
+  CODA_OP_ROW_MEAN = 13,
+  /* deferred LayerNorm (the mean-centred row norm of the Transformer operators
+     in the d9bl.com page's Fig. 4, moved past the projection as the zeli.app
+     page's "augment_me" comment moves a row-wise norm's per-row factors):
+     in = gamma [K] in the A/B dtype, in2 = u [N] fp32 with u[j] = sum_k
+     gamma[k] B[k,j] (coda_ln_fold computes it), scalar = eps.
+     v = (sum_k (A[i,k] - mu_i) gamma[k] B[k,j]) / sqrt(var_i + eps), with mu_i
+     the mean of row i of A over K and var_i the mean squared deviation from it:
+     the GEMM of the normalised, gained A.  The shift beta is not part of the
+     op: its term beta^T B is a column vector (coda_ln_fold's c) that a later
+     CODA_OP_ADD_COL adds.  Must be the first op and needs K > 0; at most one
+     of RMS_ROWSCALE / LN_ROWSCALE. */
+  CODA_OP_LN_ROWSCALE = 14
 } coda_op_kind;
 
 typedef struct {
@@ -127,6 +139,7 @@ typedef struct {
   int32_t reserved0;    /* must be 0                                                 */
   void* out;            /* reductions: fp32 output (device)                          */
   int64_t out_stride;   /* reductions: element stride between rows of `out`, >= 1   */
+  const void* in2;      /* LN_ROWSCALE: fp32 u [N] (device); NULL for every other op */
 } coda_op;
 
 typedef struct {
@@ -149,7 +162,12 @@ typedef struct {
  * accumulators in registers; D is written once, rounded to d_dtype
  * (round-to-nearest-even for bf16).  With CODA_OP_RMS_ROWSCALE first, the
  * GEMM operand is A*gamma rounded to ab_dtype and the row factor is applied
- * to the accumulators.
+ * to the accumulators.  With CODA_OP_LN_ROWSCALE first and bf16 operands, the
+ * GEMM operand is (A - s_i)*gamma rounded to bf16, s_i being the row's first
+ * element (a shift that leaves the norm unchanged and keeps rows whose spread
+ * is small against their mean accurate); the row mean and variance come from
+ * sums of A - s_i gathered in the main loop.  LN_ROWSCALE tiles are never
+ * split over K.
  * Load balance: when the output tiles do not fill a whole number of rounds
  * of the GPU's compute units, each tile of the last, partial round is split
  * over K between up to 4 workgroups (bf16 operands only, unless flags holds
@@ -171,8 +189,9 @@ int coda_gemm_epi(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
  * coda_gemm_unfused - the same computation as the framework-level sequence of
  * one kernel per operator (agentlenshq.com page, "The problem": each
  * operator launched as its own kernel, the GEMM output written to global
- * memory and read straight back): an RMS normalisation pass over A (when the
- * list starts with CODA_OP_RMS_ROWSCALE), the plain GEMM with the same main
+ * memory and read straight back): an RMS or LayerNorm normalisation pass over
+ * A (when the list starts with CODA_OP_RMS_ROWSCALE or CODA_OP_LN_ROWSCALE;
+ * the latter writes (A - mu) / sqrt(var + eps) * gamma), the plain GEMM with the same main
  * loop as coda_gemm_epi, then one pass per remaining op.  Intermediates are
  * stored in d_dtype in the workspace (coda_workspace_size(..., 1) bytes).
  * Meant as the in-run comparison for coda_gemm_epi.  Returns a coda_status.
@@ -194,6 +213,21 @@ int coda_validate(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
  */
 size_t coda_workspace_size(int64_t M, int64_t N, int64_t K, const coda_epi_desc* desc,
                            int unfused);
+
+/*
+ * coda_ln_fold - the two constant rows of the deferred LayerNorm:
+ * u[j] = sum_k gamma[k] B[k,j] and, when beta is not NULL, c[j] = sum_k
+ * beta[k] B[k,j], for j < N, in fp32 from exact products.  B is the logical
+ * [K x N] operand in `b_layout` (ldb as for coda_gemm_epi); B, gamma and beta
+ * are in `dtype` (CODA_BF16 or CODA_F32); u and c are fp32 [N] device arrays,
+ * c may be NULL only together with beta.  Depends on the weights alone, so a
+ * caller computes it once per weight set.  Shape rules as for coda_gemm_epi
+ * (K % 8 == 0, ldb % 8 == 0, 16-byte aligned B, gamma, beta, u, c); u and c
+ * must not overlap the inputs or each other.  Enqueued on `stream`; nothing is
+ * launched on error.  Returns a coda_status.
+ */
+int coda_ln_fold(const void* B, int64_t K, int64_t N, int64_t ldb, int32_t b_layout, int32_t dtype,
+                 const void* gamma, const void* beta, float* u, float* c, void* stream);
 
 /* coda_status_string - static text for a status code. */
 const char* coda_status_string(int status);

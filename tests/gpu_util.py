@@ -87,6 +87,14 @@ def unfused_extra(spec, inputs, rows):
         Y = oracle.rmsnorm(A, ops[0][1]["gamma"], ops[0][1]["eps"])
         extra = u_ab * (np.abs(Y) @ np.abs(B))
         body = ops[1:]
+    elif ops and ops[0][0] == "ln_rowscale":
+        # the unfused pass stores the beta-free normalised A; beta's term beta^T B
+        # is its own column pass, so the GEMM output without it is stored too
+        Y = oracle.layernorm(A, ops[0][1]["gamma"], ops[0][1]["eps"])
+        extra = u_ab * (np.abs(Y) @ np.abs(B))
+        if ops[0][1].get("beta") is not None:
+            extra = extra + 2 * u * np.abs(Y @ B)
+        body = ops[1:]
     ew = [i for i, (n, _) in enumerate(body) if n not in REDUCTIONS]
     last_ew = ew[-1] if ew else -1
 

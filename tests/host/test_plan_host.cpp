@@ -233,6 +233,50 @@ int main() {
     coda_epi_desc f = sm; f.ab_dtype = CODA_F32; f.d_dtype = CODA_F32; f.lda = 4096;
     EXPECT(plan_of(M, N, 4096, f).split_s == 1);
   }
+  {  // deferred LayerNorm: first op, gamma in the A/B dtype, u in in2, never split
+    coda_epi_desc e = base_desc(22016, 4096); e.flags = 0;
+    e.n_ops = 2;
+    e.ops[0].kind = CODA_OP_LN_ROWSCALE; e.ops[0].in = P(0x40000000); e.ops[0].in_dtype = CODA_BF16;
+    e.ops[0].scalar = 1e-5f; e.ops[0].in2 = P(0x50000000);
+    e.ops[1].kind = CODA_OP_GELU_TANH;
+    EXPECT(coda_validate(A, B, 4096, 22016, 4096, &e, 0) == CODA_OK);
+    coda::Plan p = plan_of(4096, 22016, 4096, e);
+    EXPECT(p.has_norm && p.has_ln && p.n_ops == 1 && p.split_s == 1 && p.ln_u == P(0x50000000));
+    EXPECT(coda_workspace_size(4096, 22016, 4096, &e, 0) == 0);
+    coda_epi_desc f = e; f.ops[0].in2 = nullptr;
+    EXPECT(coda_validate(A, B, 4096, 22016, 4096, &f, 0) == CODA_ERR_INVALID_ARG);
+    f = e; f.ops[0].in2 = P(0x50000004);
+    EXPECT(coda_validate(A, B, 4096, 22016, 4096, &f, 0) == CODA_ERR_UNSUPPORTED);
+    f = e; f.ops[1].in2 = P(0x50000000);   // in2 only on LN_ROWSCALE
+    EXPECT(coda_validate(A, B, 4096, 22016, 4096, &f, 0) == CODA_ERR_INVALID_ARG);
+    f = e; f.ops[1] = e.ops[0]; f.ops[0].kind = CODA_OP_GELU_TANH; f.ops[0].in = nullptr; f.ops[0].in2 = nullptr;
+    EXPECT(coda_validate(A, B, 4096, 22016, 4096, &f, 0) == CODA_ERR_INVALID_ARG);   // not first
+    f = e; f.ops[0].in_dtype = CODA_F32;
+    EXPECT(coda_validate(A, B, 4096, 22016, 4096, &f, 0) == CODA_ERR_INVALID_ARG);
+    EXPECT(coda_validate(A, B, 4096, 22016, 0, &e, 0) == CODA_ERR_INVALID_ARG);      // K = 0
+    f = e; f.D = Pm(0x50000000);                                                     // D over u
+    EXPECT(coda_validate(A, B, 4096, 22016, 4096, &f, 0) == CODA_ERR_INVALID_ARG);
+    EXPECT(coda_workspace_size(4096, 22016, 4096, &e, 1) >= size_t(4096) * 4096 * 2);   // unfused: normalised A
+  }
+  {  // coda_ln_fold validation
+    float* u = static_cast<float*>(Pm(0x60000000));
+    float* c = static_cast<float*>(Pm(0x61000000));
+    const void* g = P(0x40000000);
+    const void* bt = P(0x41000000);
+    EXPECT(coda::validate_ln_fold(B, 768, 3072, 3072, CODA_B_KN, CODA_BF16, g, bt, u, c) == CODA_OK);
+    EXPECT(coda::validate_ln_fold(B, 768, 3072, 768, CODA_B_NK, CODA_BF16, g, nullptr, u, nullptr) == CODA_OK);
+    EXPECT(coda::validate_ln_fold(B, 768, 3072, 3072, CODA_B_KN, CODA_BF16, g, bt, u, nullptr) ==
+           CODA_ERR_INVALID_ARG);
+    EXPECT(coda::validate_ln_fold(B, 768, 3076, 3080, CODA_B_KN, CODA_BF16, g, nullptr, u, nullptr) ==
+           CODA_ERR_UNSUPPORTED);
+    EXPECT(coda::validate_ln_fold(B, 768, 3072, 3000, CODA_B_KN, CODA_BF16, g, nullptr, u, nullptr) ==
+           CODA_ERR_INVALID_ARG);
+    EXPECT(coda::validate_ln_fold(B, 768, 3072, 3072, CODA_B_KN, CODA_BF16, g, bt, u,
+                                  static_cast<float*>(Pm(0x60000100))) == CODA_ERR_INVALID_ARG);   // u, c overlap
+    EXPECT(coda::validate_ln_fold(B, 768, 3072, 3072, CODA_B_KN, CODA_BF16, g, nullptr,
+                                  static_cast<float*>(Pm(0x20000010)), nullptr) == CODA_ERR_INVALID_ARG);   // u in B
+    EXPECT(coda::validate_ln_fold(B, 768, 0, 8, CODA_B_KN, CODA_BF16, g, nullptr, nullptr, nullptr) == CODA_OK);
+  }
   EXPECT(std::strcmp(coda_status_string(CODA_ERR_WORKSPACE), "CODA_ERR_WORKSPACE") == 0);
   if (failures == 0) std::printf("ALL OK\n");
   return failures == 0 ? 0 : 1;
