@@ -6,6 +6,8 @@ SwiGLU gate/up layer: M = 4096 tokens, K = 4096, [W_gate | W_up] column
 interleaved, N = 2 x 11008, deferred RMSNorm row scale then SiLU(gate) * up,
 bf16 storage and fp32 accumulation.  Inputs are seeded synthetic tensors with
 the layer's shapes and value distributions, resident in HBM before timing.
+``--workload`` times another of the synthetic transformer layers instead (the
+default line is the LLaMA layer's).
 
 Prints one JSON line: fused TFLOP/s (2 M N K / kernel time), the share of the
 bf16 dense MFMA peak, the speedup over the in-run unfused HIP sequence (same
@@ -28,8 +30,27 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0        # MI355X published dense bf16 MFMA peak
+PEAK_F32_TFLOPS = 157.3          # MI355X published fp32 matrix peak
 PEAK_HBM_GBPS = 8000.0
 WORKLOAD_INDEX = 4               # LLaMA-7B SwiGLU gate/up
+WORKLOAD_TEXT = {
+    1: "tiny forward layer, fp32: deferred RMSNorm + bias + GELU_tanh + residual, M=N=K=256",
+    2: "gpt2s_mlp_up: deferred RMSNorm + bias + GELU_tanh, M=8192 tokens, K=768, N=3072, bf16 in/out",
+    3: "bertl_mlp_down: bias + residual + row sum and sum of squares, M=8192, K=4096, N=1024, bf16 in/out",
+    4: "llama7b_swiglu_gate_up: deferred RMSNorm + SwiGLU(gate,up), M=4096 tokens, K=4096, "
+       "N=2x11008 column-interleaved, bf16 in/out, fp32 accumulate",
+    5: "gpt2m_mlp_bwd_act: dH = dY W2^T times GELU_tanh'(P) + row sum, M=8192, K=1024, N=4096, bf16 in/out",
+    6: "gpt2s_mlp_up_layernorm: deferred LayerNorm + bias + GELU_tanh, M=8192 tokens, K=768, N=3072, bf16 in/out",
+}
+
+
+def algorithmic_bytes(spec) -> float:
+    """One read of every input tensor, one write of D and of the reduction outputs."""
+    size = {"bf16": 2, "f32": 4}
+    b = sum(float(np.prod(t.shape)) * size[t.dtype] for t in spec.tensors)
+    b += float(spec.M) * spec.out_width * size[spec.d_dtype]
+    b += sum(float(np.prod(shape)) * 4 for _, shape in spec.outputs)
+    return b
 FLUSH_BYTES = 512 << 20          # larger than L2 (8 x 4 MB) plus the 256 MB Infinity Cache
 COPY_BYTES = 256 << 20           # plain copy used to calibrate the HBM traffic counters
 
@@ -92,8 +113,8 @@ def cpu_baseline(spec, inputs, budget_s: float = 10.0):
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"{rows_done} of {spec.M} rows of the same layer (fp64 numpy: RMS normalise, matmul, SwiGLU), "
-                  f"{elapsed:.1f} s",
+        "sample": f"{rows_done} of {spec.M} rows of the same layer (fp64 numpy: "
+                  f"{', '.join(op for op, _ in spec.program)} around the matmul), {elapsed:.1f} s",
     }
 
 
@@ -104,6 +125,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=40,
                     help="untimed steps first; the clock needs a few tens of steps to settle under this load")
     ap.add_argument("--tile", type=int, default=0, help="force a tile configuration (0 = automatic)")
+    ap.add_argument("--workload", type=int, default=WORKLOAD_INDEX, choices=sorted(WORKLOAD_TEXT),
+                    help="synthetic layer to time (default: the LLaMA-7B gate/up layer)")
     ap.add_argument("--no-flush", action="store_true", help="do not evict L2 / Infinity Cache between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unfused", action="store_true")
@@ -124,7 +147,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
 
-    spec = w.get_config(WORKLOAD_INDEX)
+    spec = w.get_config(args.workload)
     print(f"[bench] generating {spec.name} inputs", file=sys.stderr, flush=True)
     inputs = w.make_inputs(spec)
     call = runner.WorkloadCall(spec, inputs, tile=args.tile)
@@ -172,10 +195,11 @@ def main():
 
     flops = float(spec.flops)
     tflops = flops / (ms * 1e-3) / 1e12
-    # fused algorithmic bytes: read X, W, gamma once, write D once
-    alg_bytes = 2.0 * (spec.M * spec.K + spec.K * spec.N + spec.K + spec.M * spec.out_width)
+    peak = PEAK_F32_TFLOPS if spec.ab_dtype == "f32" else PEAK_BF16_TFLOPS
+    alg_bytes = algorithmic_bytes(spec)
     khash = kernel_source_hash()
-    traffic = load_traffic(khash)
+    # the committed counter runs cover the LLaMA layer's kernel
+    traffic = load_traffic(khash) if args.workload == WORKLOAD_INDEX else None
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -193,16 +217,15 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "f32" if spec.ab_dtype == "f32" else "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "llama7b_swiglu_gate_up: deferred RMSNorm + SwiGLU(gate,up), M=4096 tokens, K=4096, "
-                        "N=2x11008 column-interleaved, bf16 in/out, fp32 accumulate",
+            "workload": WORKLOAD_TEXT[args.workload],
             "M": spec.M, "N": spec.N, "K": spec.K,
             "cache_flush_between_steps": not args.no_flush,
             "tile": tile_used,
         },
-        "pct_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "pct_peak": round(100.0 * tflops / peak, 2),
         "unfused_ms_per_step": None if unfused_ms is None else round(unfused_ms, 4),
         "speedup_vs_unfused": None if unfused_ms is None else round(unfused_ms / ms, 3),
         "effective_GBps": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
@@ -212,9 +235,9 @@ def main():
         "roofline": {
             "bound": "mfma",
             "achieved": round(tflops, 2),
-            "peak": PEAK_BF16_TFLOPS,
+            "peak": peak,
             "unit": "TFLOP/s",
-            "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "frac": round(tflops / peak, 4),
             "traffic": traffic,
         },
         "cpu_baseline": cpu,
