@@ -128,6 +128,8 @@ def main():
     ap.add_argument("--workload", type=int, default=WORKLOAD_INDEX, choices=sorted(WORKLOAD_TEXT),
                     help="synthetic layer to time (default: the LLaMA-7B gate/up layer)")
     ap.add_argument("--no-flush", action="store_true", help="do not evict L2 / Infinity Cache between steps")
+    ap.add_argument("--fold-gain", action="store_true",
+                    help="fold the RMSNorm gain into a copy of the weights once (coda_fold_gain) before timing")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unfused", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -150,7 +152,7 @@ def main():
     spec = w.get_config(args.workload)
     print(f"[bench] generating {spec.name} inputs", file=sys.stderr, flush=True)
     inputs = w.make_inputs(spec)
-    call = runner.WorkloadCall(spec, inputs, tile=args.tile)
+    call = runner.WorkloadCall(spec, inputs, tile=args.tile, fold_gain=args.fold_gain)
     flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
     if args.copy_calibration:
@@ -223,6 +225,7 @@ def main():
             "workload": WORKLOAD_TEXT[args.workload],
             "M": spec.M, "N": spec.N, "K": spec.K,
             "cache_flush_between_steps": not args.no_flush,
+            "gain_folded_into_weights": bool(args.fold_gain),
             "tile": tile_used,
         },
         "pct_peak": round(100.0 * tflops / peak, 2),

@@ -48,7 +48,7 @@ CODA_OP_LN_ROWSCALE = 14
 EXPORTED = (
     "coda_gemm_epi", "coda_gemm_unfused", "coda_validate", "coda_workspace_size",
     "coda_status_string", "coda_last_error", "coda_num_tile_configs", "coda_tile_config",
-    "coda_selected_tile", "coda_ln_fold",
+    "coda_selected_tile", "coda_ln_fold", "coda_fold_gain",
 )
 
 
@@ -119,6 +119,8 @@ def _load():
     lib.coda_selected_tile.restype = ctypes.c_int
     lib.coda_ln_fold.argtypes = [P, I64, I64, I64, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P]
     lib.coda_ln_fold.restype = ctypes.c_int
+    lib.coda_fold_gain.argtypes = [P, I64, I64, I64, ctypes.c_int32, ctypes.c_int32, P, P, I64, P]
+    lib.coda_fold_gain.restype = ctypes.c_int
     return lib
 
 
@@ -174,6 +176,11 @@ def coda_selected_tile(M: int, N: int, K: int, desc: coda_epi_desc) -> int:
 def coda_ln_fold(B: int, K: int, N: int, ldb: int, b_layout: int, dtype: int, gamma: int, beta,
                  u: int, c, stream: int = 0) -> int:
     return lib.coda_ln_fold(B, K, N, ldb, b_layout, dtype, gamma, beta, u, c, stream)
+
+
+def coda_fold_gain(B: int, K: int, N: int, ldb: int, b_layout: int, dtype: int, gamma: int, B_out: int,
+                   ldo: int, stream: int = 0) -> int:
+    return lib.coda_fold_gain(B, K, N, ldb, b_layout, dtype, gamma, B_out, ldo, stream)
 
 
 def check(status: int, where: str) -> None:

@@ -1,4 +1,12 @@
-// The constant rows of the deferred LayerNorm: u = gamma^T B and c = beta^T B.
+// Weight-side preparation of the deferred row norms.
+//
+// coda_fold_gain: B' = diag(gamma) B, the per-feature gain of a row norm moved
+// into the rows of the following projection ((x * gamma) W = x (gamma W), the
+// reparameterisation of the zeli.app page's "augment_me" comment), rounded
+// once to B's dtype; the fused kernel then feeds A to the MFMAs unchanged.
+//
+// coda_ln_fold: the constant rows of the deferred LayerNorm, u = gamma^T B
+// and c = beta^T B.
 //
 // Moving a LayerNorm past the projection (the zeli.app page's "augment_me"
 // comment moves a row-wise norm's per-row factors past the matmul; the norm is
@@ -111,8 +119,69 @@ __global__ void __launch_bounds__(kFoldThreads) fold_nk_kernel(const void* B, lo
   }
 }
 
+// B' = diag(gamma) B, 8 consecutive elements of a storage row per thread
+// (the storage rows are K rows of B for [K x N] storage, N rows for [N x K]).
+template <bool F32>
+__global__ void __launch_bounds__(kFoldThreads) fold_gain_kernel(const void* B, long long ldb, const void* gamma,
+                                                                 void* Bo, long long ldo, long long rows, int inner,
+                                                                 bool kn) {
+  const int cpr = inner / 8;
+  const long long t = (long long)blockIdx.x * kFoldThreads + threadIdx.x;
+  if (t >= rows * cpr) return;
+  const long long r = t / cpr;
+  const int c0 = int(t % cpr) * 8;
+  float b[8], g[8];
+  load8f(B, F32 ? CODA_F32 : CODA_BF16, r * ldb + c0, b);
+  if (kn) {
+    const float gk = load_elem(gamma, F32 ? CODA_F32 : CODA_BF16, r);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) g[e] = gk;
+  } else {
+    load8f(gamma, F32 ? CODA_F32 : CODA_BF16, c0, g);
+  }
+  if (F32) {
+    f32x4_t lo, hv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      lo[e] = b[e] * g[e];
+      hv[e] = b[4 + e] * g[4 + e];
+    }
+    float* o = static_cast<float*>(Bo) + r * ldo + c0;
+    *reinterpret_cast<f32x4_t*>(o) = lo;
+    *reinterpret_cast<f32x4_t*>(o + 4) = hv;
+  } else {
+    u32x4_t w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(b[2 * e] * g[2 * e], b[2 * e + 1] * g[2 * e + 1]);
+    *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(Bo) + r * ldo + c0) = w;
+  }
+}
+
 }  // namespace dev
 }  // namespace coda
+
+extern "C" int coda_fold_gain(const void* B, int64_t K, int64_t N, int64_t ldb, int32_t b_layout, int32_t dtype,
+                              const void* gamma, void* B_out, int64_t ldo, void* stream) {
+  const int st = coda::validate_fold_gain(B, K, N, ldb, b_layout, dtype, gamma, B_out, ldo);
+  if (st != CODA_OK || K == 0 || N == 0) return st;
+  const bool kn = b_layout == CODA_B_KN;
+  const long long rows = kn ? K : N;
+  const int inner = int(kn ? N : K);
+  const long long threads = rows * (inner / 8);
+  const unsigned blocks = unsigned((threads + coda::dev::kFoldThreads - 1) / coda::dev::kFoldThreads);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == CODA_F32)
+    hipLaunchKernelGGL(coda::dev::fold_gain_kernel<true>, dim3(blocks), dim3(coda::dev::kFoldThreads), 0, s, B,
+                       (long long)ldb, gamma, B_out, (long long)ldo, rows, inner, kn);
+  else
+    hipLaunchKernelGGL(coda::dev::fold_gain_kernel<false>, dim3(blocks), dim3(coda::dev::kFoldThreads), 0, s, B,
+                       (long long)ldb, gamma, B_out, (long long)ldo, rows, inner, kn);
+  if (hipGetLastError() != hipSuccess) {
+    coda::set_error("HIP launch failed (coda_fold_gain)");
+    return CODA_ERR_HIP;
+  }
+  return CODA_OK;
+}
 
 extern "C" int coda_ln_fold(const void* B, int64_t K, int64_t N, int64_t ldb, int32_t b_layout, int32_t dtype,
                             const void* gamma, const void* beta, float* u, float* c, void* stream) {

@@ -61,7 +61,10 @@ dev::FusedArgs make_args(const Plan& p) {
 int launch_args(const Plan& p, const dev::FusedArgs& a, hipStream_t stream) {
   const int64_t nwg = p.full_tiles + p.split_tiles * p.split_s;
   const bool bkn = p.b_layout == CODA_B_KN;
-  const int norm = p.has_ln ? dev::kNormLn : p.has_norm ? dev::kNormRms : dev::kNormNone;
+  const int norm = p.has_ln      ? dev::kNormLn
+                   : p.gain_in_b ? dev::kNormRmsB
+                   : p.has_norm  ? dev::kNormRms
+                                 : dev::kNormNone;
   if (p.ab_dtype == CODA_F32) {
     return dev::launch_tile_f32(a, nwg, bkn, norm, stream);
   }
@@ -92,6 +95,7 @@ int launch_plain_gemm(const Plan& p, const void* A, int64_t lda, void* out, int6
   q.ldd = ldo;
   q.has_norm = false;
   q.has_ln = false;
+  q.gain_in_b = false;
   q.gamma = nullptr;
   q.ln_u = nullptr;
   q.n_ops = 0;

@@ -82,16 +82,20 @@ typedef const __attribute__((address_space(4))) DevOp& KOp;
 typedef __attribute__((address_space(3))) void* LdsPtr;
 typedef __attribute__((address_space(3))) i16x4_t LdsI16x4;
 
-// deferred row norm in front of the GEMM: none, RMSNorm, LayerNorm
-constexpr int kNormNone = 0, kNormRms = 1, kNormLn = 2;
+// deferred row norm in front of the GEMM: none, RMSNorm (gain applied to A in
+// the main loop), LayerNorm, RMSNorm with the gain already folded into B's rows
+constexpr int kNormNone = 0, kNormRms = 1, kNormLn = 2, kNormRmsB = 3;
 
 template <int BM_, int BN_, int WM_, int WN_, bool F32_, bool BKN_, int NORM_>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
   static constexpr bool F32 = F32_, BKN = BKN_;
-  // RMS: gain in the main loop, sums of squares, a row scale in the epilogue;
-  // LN: additionally row sums and the mean term of the deferred LayerNorm
-  static constexpr bool RMS = NORM_ != kNormNone, LN = NORM_ == kNormLn;
+  // RMS: gain applied to A in the main loop, sums of squares, a row scale in
+  // the epilogue; LN: additionally row sums and the mean term of the deferred
+  // LayerNorm; SSF: A goes to the MFMAs unchanged (the gain is in B) and the
+  // sums of squares come from the X fragments the MFMAs read
+  static constexpr bool RMS = NORM_ == kNormRms || NORM_ == kNormLn, LN = NORM_ == kNormLn;
+  static constexpr bool SSF = NORM_ == kNormRmsB;
   static constexpr int NW = WM * WN;
   static constexpr int NT = 64 * NW;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -135,7 +139,13 @@ struct Cfg {
   // RMS: raw A of the next K step lands in a third array by direct loads and is
   // converted (gain, bf16 rounding, sum of squares) from there into the stage
   static constexpr int RAW_BYTES = (RMS && !F32) ? A_BYTES : 16;
-  static_assert(ARR0_BYTES + ARR1_BYTES + RAW_BYTES <= 160 * 1024, "LDS budget");
+  // SSF: per-row partial sums of squares, one row of BM per wave column
+  static constexpr int SS_BYTES = (SSF && !F32) ? WN * BM * 4 : 16;
+  // (arrays a variant never touches are dropped by the compiler: the raw A array
+  // without RMS, the sums array without SSF, the 256-byte warm-up word with RMS)
+  static_assert(ARR0_BYTES + ARR1_BYTES + (RMS ? RAW_BYTES : 0) + (SSF ? SS_BYTES : 0) + (RMS ? 0 : 256) <=
+                    160 * 1024,
+                "LDS budget");
   static_assert(CPR >= 4 && CPR <= 16 && (CPR & (CPR - 1)) == 0, "epilogue lane layout");
 };
 
@@ -358,6 +368,7 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
   __shared__ __attribute__((aligned(1024))) char smem0[C::ARR0_BYTES];
   __shared__ __attribute__((aligned(1024))) char smem1[C::ARR1_BYTES];
   __shared__ __attribute__((aligned(1024))) char smem_raw[C::RAW_BYTES];
+  __shared__ __attribute__((aligned(16))) float smem_ss[C::SS_BYTES / 4];
   __shared__ __attribute__((aligned(256))) char smem_warm[256];
 
   const int tid = threadIdx.x;
@@ -403,7 +414,8 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
 
   // per-row sums of squares (RMS, LN) and sums (LN) of the A values this lane
   // converts; with bf16 operands LN shifts each row by its first element first
-  constexpr int NSS = C::F32 ? C::A32_CH : C::A_BPW;
+  // SSF: one sum per k16 slice and per row block the wave takes at that slice
+  constexpr int NSS = C::F32 ? C::A32_CH : (C::SSF ? 4 * (MI / C::WN) : C::A_BPW);
   float ss[NSS], sx[NSS], sh[NSS];
 #pragma unroll
   for (int i = 0; i < NSS; ++i) ss[i] = sx[i] = sh[i] = 0.0f;
@@ -610,6 +622,42 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
     // MFMAs of one K step.  With the RMS op, the next step's A chunks (already in
     // registers) are scaled and written to `rms_dst` between the MFMAs of the
     // last k16 step, so that VALU work overlaps the matrix pipe.
+    // SSF: squares of the X fragments (rows wm*WTM + 32 mi + l32, K indices
+    // 16 kk + 8 (lane >> 5) + 0..7).  The WN waves that share those rows split
+    // the (row block, slice) pairs: at slice kk wave wn takes the blocks
+    // mi = ((wn - kk) mod WN) + WN t, picked with wave-uniform selects so that
+    // the work has no branch and can sit between the slice's MFMAs; the sum
+    // goes to ss[kk * (MI / WN) + t].
+    static_assert(C::F32 || !C::SSF || MI % C::WN == 0, "row blocks must split over the wave columns");
+    const int wn_s = __builtin_amdgcn_readfirstlane(wn);
+    auto sumsq_frags = [&](auto kkc, const bf16x8_t (&xf)[MI]) {
+      constexpr int kk = decltype(kkc)::value;
+      constexpr int TPW = MI / C::WN;
+      const int sel = (wn_s - kk + 4 * C::WN) % C::WN;   // wave-uniform
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        u32x4_t v = __builtin_bit_cast(u32x4_t, xf[C::WN * t]);
+#pragma unroll
+        for (int c = 1; c < C::WN; ++c) {
+          // a bitwise select on a wave-uniform mask (indexing the fragment
+          // array with `sel` would move it to scratch memory)
+          const uint32_t m = sel == c ? 0xffffffffu : 0u;
+          const u32x4_t o = __builtin_bit_cast(u32x4_t, xf[C::WN * t + c]);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) v[w] = (o[w] & m) | (v[w] & ~m);
+        }
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float lo = bf16_lo(v[w]), hv = bf16_hi(v[w]);
+          ss[kk * TPW + t] = fmaf(lo, lo, ss[kk * TPW + t]);
+          ss[kk * TPW + t] = fmaf(hv, hv, ss[kk * TPW + t]);
+        }
+        // keeps the sum computed inside this slice's scheduling region (the
+        // arithmetic would otherwise be sunk past the MFMAs of the whole step)
+        asm volatile("" ::"v"(ss[kk * TPW + t]));
+      }
+    };
+
     auto compute = [&](const char* stage) {
       bf16x8_t xf[2][MI], wf[2][NI];
       read_frags(stage, 0, xf[0], wf[0]);
@@ -624,6 +672,15 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
 #pragma unroll
           for (int ni = 0; ni < NI; ++ni)
             acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[kk & 1][ni], xf[kk & 1][mi], acc[mi][ni], 0, 0, 0);
+        if constexpr (C::SSF) {
+          // the slice's squares between its MFMAs: one MFMA, then up to 4 VALU
+          sumsq_frags(kkc, xf[kk & 1]);
+#pragma unroll
+          for (int q = 0; q < MI * NI; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+          }
+        }
         __builtin_amdgcn_sched_barrier(0);
       });
     };
@@ -698,6 +755,25 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
+    if constexpr (C::SSF) {
+      // the two lane halves of a row, then this wave column's LDS row: the pair
+      // (block mi, slice kk) was taken by wave column (mi + kk) mod WN only, so
+      // the WN rows add up to the whole sum
+      constexpr int TPW = MI / C::WN;
+      float* col = smem_ss + wn * BM + wm * C::WTM + l32;
+      if (hi == 0) {
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) col[32 * mi] = 0.0f;
+      }
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+          const float v = ss[kk * TPW + t] + __shfl_xor(ss[kk * TPW + t], 32);
+          const int mi = (wn - kk + 4 * C::WN) % C::WN + C::WN * t;
+          if (hi == 0) col[32 * mi] += v;
+        }
+    }
     __syncthreads();
   } else {
     // ================= fp32 main loop (small tile, register staged) =================
@@ -767,10 +843,10 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           float x = __uint_as_float(areg[i][w]) - s0;
-          if (C::RMS) {
+          if (C::RMS || C::SSF) {
             ss[i] = fmaf(x, x, ss[i]);
             if (C::LN) sx[i] += x;
-            x = x * __uint_as_float(greg[w]);
+            if (C::RMS) x = x * __uint_as_float(greg[w]);
           }
           dst[w] = x;
         }
@@ -856,6 +932,14 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
             __hip_atomic_store(a->split_ss + (slot0 + part) * BM + 8 * (wave + C::NW * i) + (lane >> 3), v,
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
+      } else if constexpr (C::SSF) {
+        // this part's row sums of squares (its wave columns in order)
+        for (int t = tid; t < BM; t += C::NT) {
+          float v = smem_ss[t];
+#pragma unroll
+          for (int w = 1; w < C::WN; ++w) v += smem_ss[w * BM + t];
+          __hip_atomic_store(a->split_ss + (slot0 + part) * BM + t, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
@@ -900,6 +984,19 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
           }
           ss[i] = (lane & 7) == 0 ? t : 0.0f;
         }
+      } else if constexpr (C::SSF) {
+        // whole-row sums in part order, left in the first wave column's LDS row
+        for (int t = tid; t < BM; t += C::NT) {
+          float v = 0.0f;
+          for (int pp = 0; pp < S; ++pp) {
+            const float x =
+                __hip_atomic_load(a->split_ss + (slot0 + pp) * BM + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            v = pp == 0 ? x : v + x;
+          }
+          smem_ss[t] = v;
+#pragma unroll
+          for (int w = 1; w < C::WN; ++w) smem_ss[w * BM + t] = 0.0f;
+        }
       }
       // leave the counter at zero for the next call
       if (tid == 0) __hip_atomic_store(a->split_cnt + split, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -926,7 +1023,15 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
   };
   int* flag = reinterpret_cast<int*>(smem1 + C::EPI_FLAG_OFF);
 
-  if constexpr (C::RMS) {
+  if constexpr (C::SSF && !C::F32) {
+    for (int t = tid; t < BM; t += C::NT) {
+      float v = smem_ss[t];
+#pragma unroll
+      for (int w = 1; w < C::WN; ++w) v += smem_ss[w * BM + t];
+      row_factors(t, v, 0.0f);
+    }
+    __syncthreads();
+  } else if constexpr (C::RMS || C::SSF) {
     if constexpr (!C::F32) {
       // rows 8q + (lane >> 3): the 8 lanes of a row are consecutive
 #pragma unroll
@@ -1027,7 +1132,7 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
         const float s = rinv[ch.mloc[j]], mr = rmu[ch.mloc[j]];
 #pragma unroll
         for (int e = 0; e < 8; ++e) ch.v[j][e] = fmaf(ch.v[j][e], s, -mr * uv[e]);
-      } else if constexpr (C::RMS) {
+      } else if constexpr (C::RMS || C::SSF) {
         const float s = rinv[ch.mloc[j]];
 #pragma unroll
         for (int e = 0; e < 8; ++e) ch.v[j][e] *= s;
@@ -1116,6 +1221,7 @@ int launch_norms(const FusedArgs& args, int64_t nwg, int norm, hipStream_t s) {
   switch (norm) {
     case kNormRms: return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormRms>>(args, nwg, s);
     case kNormLn: return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormLn>>(args, nwg, s);
+    case kNormRmsB: return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormRmsB>>(args, nwg, s);
     default: return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormNone>>(args, nwg, s);
   }
 }

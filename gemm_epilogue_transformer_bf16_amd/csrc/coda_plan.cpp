@@ -218,7 +218,9 @@ int build_plan(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
         set_error("%s needs K > 0", name);
         return CODA_ERR_INVALID_ARG;
       }
-      if (!o.in || o.in_dtype != d->ab_dtype) {
+      // RMS_ROWSCALE may leave gamma NULL: the gain is then already in B's rows
+      const bool folded = !ln && !o.in;
+      if (!folded && (!o.in || o.in_dtype != d->ab_dtype)) {
         set_error("%s needs gamma[K] in the A/B dtype", name);
         return CODA_ERR_INVALID_ARG;
       }
@@ -242,6 +244,7 @@ int build_plan(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
       }
       p->has_norm = true;
       p->has_ln = ln;
+      p->gain_in_b = folded;
       p->gamma = o.in;
       p->ln_u = static_cast<const float*>(o.in2);
       p->eps = o.scalar;
@@ -386,7 +389,7 @@ int build_plan(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
       set_error("D overlaps A or B");
       return CODA_ERR_INVALID_ARG;
     }
-    if (p->has_norm && overlap(eD, matrix_extent(p->gamma, 1, K, K, abs))) {
+    if (p->gamma && overlap(eD, matrix_extent(p->gamma, 1, K, K, abs))) {
       set_error("D overlaps gamma");
       return CODA_ERR_INVALID_ARG;
     }
@@ -449,6 +452,51 @@ int build_plan(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
         return CODA_ERR_UNSUPPORTED;
       }
     }
+  }
+  return CODA_OK;
+}
+
+int validate_fold_gain(const void* B, int64_t K, int64_t N, int64_t ldb, int32_t b_layout, int32_t dtype,
+                       const void* gamma, const void* B_out, int64_t ldo) {
+  clear_error();
+  if (K < 0 || N < 0) {
+    set_error("negative size K=%lld N=%lld", (long long)K, (long long)N);
+    return CODA_ERR_INVALID_ARG;
+  }
+  if (K > kMaxDim || N > kMaxDim) {
+    set_error("size above 2^31-1");
+    return CODA_ERR_UNSUPPORTED;
+  }
+  if (!valid_dtype(dtype) || (b_layout != CODA_B_KN && b_layout != CODA_B_NK)) {
+    set_error("unknown dtype %d or B layout %d", dtype, b_layout);
+    return CODA_ERR_INVALID_ARG;
+  }
+  if (K == 0 || N == 0) return CODA_OK;
+  if (!B || !gamma || !B_out) {
+    set_error("B, gamma or B_out is NULL");
+    return CODA_ERR_INVALID_ARG;
+  }
+  const int64_t inner = b_layout == CODA_B_KN ? N : K;
+  if (ldb < inner || ldo < inner) {
+    set_error("ldb=%lld or ldo=%lld below %lld", (long long)ldb, (long long)ldo, (long long)inner);
+    return CODA_ERR_INVALID_ARG;
+  }
+  if (inner % 8 || ldb % 8 || ldo % 8) {
+    set_error("the contiguous dimension and ldb, ldo must be multiples of 8");
+    return CODA_ERR_UNSUPPORTED;
+  }
+  if (!aligned(B, 16) || !aligned(gamma, 16) || !aligned(B_out, 16)) {
+    set_error("B, gamma and B_out must be 16-byte aligned");
+    return CODA_ERR_UNSUPPORTED;
+  }
+  const size_t es = dtype_size(dtype);
+  const int64_t rows = b_layout == CODA_B_KN ? K : N;
+  const Extent eB = matrix_extent(B, rows, inner, ldb, es), eO = matrix_extent(B_out, rows, inner, ldo, es);
+  const Extent eg = matrix_extent(gamma, 1, K, K, es);
+  const bool in_place = B == B_out && ldb == ldo;
+  if ((!in_place && overlap(eB, eO)) || overlap(eO, eg)) {
+    set_error("B_out overlaps B (other than exactly in place) or gamma");
+    return CODA_ERR_INVALID_ARG;
   }
   return CODA_OK;
 }

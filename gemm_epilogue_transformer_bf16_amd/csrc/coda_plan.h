@@ -56,6 +56,7 @@ struct Plan {
   void* D;
   bool has_norm;             // a deferred row norm (RMS_ROWSCALE or LN_ROWSCALE) is op 0
   bool has_ln;               // ... and it is LN_ROWSCALE
+  bool gain_in_b;            // RMS_ROWSCALE with gamma NULL: the gain is folded into B
   const void* gamma;
   const float* ln_u;         // LN_ROWSCALE: u = gamma^T B [N]
   float eps;
@@ -104,6 +105,10 @@ int64_t unfused_ld(const Plan& p);
 // Validates a coda_ln_fold call.  Returns a coda_status.
 int validate_ln_fold(const void* B, int64_t K, int64_t N, int64_t ldb, int32_t b_layout, int32_t dtype,
                      const void* gamma, const void* beta, const float* u, const float* c);
+
+// Validates a coda_fold_gain call.  Returns a coda_status.
+int validate_fold_gain(const void* B, int64_t K, int64_t N, int64_t ldb, int32_t b_layout, int32_t dtype,
+                       const void* gamma, const void* B_out, int64_t ldo);
 
 // Automatic bf16 tile configuration (1-based) for an M x N output.
 int choose_tile(int64_t M, int64_t N);

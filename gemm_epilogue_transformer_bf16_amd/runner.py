@@ -61,12 +61,15 @@ class Call:
     ``ln_rowscale`` takes ``gamma``, ``eps`` and an optional shift ``beta``
     tensor: the call computes u = gamma^T B and c = beta^T B once with
     coda_ln_fold and passes LN_ROWSCALE(gamma, u) followed by ADD_COL(c).
+    With ``fold_gain``, an ``rms_rowscale`` gain is folded into a copy of B once
+    (coda_fold_gain) and the op is passed with gamma NULL.
     """
 
     def __init__(self, A: torch.Tensor, B: torch.Tensor, ops: Sequence[Tuple[str, Dict]], b_layout: str,
                  D: Optional[torch.Tensor] = None, d_dtype: Optional[torch.dtype] = None, tile: int = 0,
                  M: Optional[int] = None, N: Optional[int] = None, K: Optional[int] = None,
-                 lda: Optional[int] = None, ldb: Optional[int] = None, flags: int = 0):
+                 lda: Optional[int] = None, ldb: Optional[int] = None, flags: int = 0,
+                 fold_gain: bool = False):
         self.A, self.B = A, B
         self.M = A.shape[0] if M is None else M
         self.K = A.shape[1] if K is None else K
@@ -81,6 +84,9 @@ class Call:
             inner = self.N if b_layout == "KN" else self.K
             ldb = B.stride(0) if B.dim() == 2 and B.numel() > 0 else max((inner + 7) // 8 * 8, 8)
         self.ops = self._expand_layernorm(list(ops), B, ldb)
+        if fold_gain:
+            B, ldb = self._fold_gain(B, ldb)
+            self.B = B
         width = self.N // 2 if any(n == "swiglu_pair" for n, _ in self.ops) else self.N
         self.out_width = width
         d_dtype = d_dtype or A.dtype
@@ -104,7 +110,7 @@ class Call:
             o = d.ops[i]
             o.kind = OPCODES[name]
             for key in ("gamma", "vec", "mat"):
-                if key in args:
+                if args.get(key) is not None:
                     t = args[key]
                     self._keep.append(t)
                     o.in_ = t.data_ptr()
@@ -156,6 +162,23 @@ class Call:
             out.append(("add_col", {"vec": c}))
         return out + list(ops[1:])
 
+    def _fold_gain(self, B: torch.Tensor, ldb: int):
+        """rms_rowscale(gamma) on B -> rms_rowscale(NULL) on diag(gamma) B."""
+        if not self.ops or self.ops[0][0] != "rms_rowscale" or self.ops[0][1].get("gamma") is None:
+            return B, ldb
+        args = dict(self.ops[0][1])
+        gamma = args["gamma"]
+        Bf = torch.empty_like(B)
+        self._keep += [gamma, B]
+        st = C.coda_fold_gain(B.data_ptr() if B.numel() else None, self.K, self.N, ldb,
+                              C.CODA_B_KN if self.b_layout == "KN" else C.CODA_B_NK, CODA_DT[B.dtype],
+                              gamma.data_ptr() if gamma.numel() else None, Bf.data_ptr() if Bf.numel() else None,
+                              Bf.stride(0) if Bf.dim() == 2 and Bf.numel() else ldb, current_stream_ptr())
+        C.check(st, "coda_fold_gain")
+        args["gamma"] = None
+        self.ops = [("rms_rowscale", args)] + self.ops[1:]
+        return Bf, (Bf.stride(0) if Bf.dim() == 2 and Bf.numel() else ldb)
+
     def _set_ws(self, unfused: int):
         w = self.ws[unfused]
         self.desc.workspace = None if w is None else w.data_ptr()
@@ -182,7 +205,8 @@ class Call:
 class WorkloadCall(Call):
     """A ``workloads`` spec with its seeded inputs uploaded to the device."""
 
-    def __init__(self, spec, inputs: Dict[str, np.ndarray], device="cuda", tile: int = 0, flags: int = 0):
+    def __init__(self, spec, inputs: Dict[str, np.ndarray], device="cuda", tile: int = 0, flags: int = 0,
+                 fold_gain: bool = False):
         dtypes = {t.name: t.dtype for t in spec.tensors}
         self.spec = spec
         self.tensors = {name: storage_to_tensor(arr, dtypes[name], device) for name, arr in inputs.items()}
@@ -197,4 +221,5 @@ class WorkloadCall(Call):
                 a["out"] = self.outputs[a["out"]]
             ops.append((name, a))
         super().__init__(self.tensors[spec.a_name], self.tensors[spec.b_name], ops, spec.b_layout,
-                         d_dtype=TORCH_DT[spec.d_dtype], tile=tile, M=spec.M, N=spec.N, K=spec.K, flags=flags)
+                         d_dtype=TORCH_DT[spec.d_dtype], tile=tile, M=spec.M, N=spec.N, K=spec.K, flags=flags,
+                         fold_gain=fold_gain)

@@ -97,8 +97,11 @@ typedef enum {
   CODA_OP_SCALE_COL = 2,      /* v *= in[j]          in: [width] vector              */
   CODA_OP_RMS_ROWSCALE = 3,   /* deferred RMSNorm: in = gamma [K], scalar = eps.
                                  v *= 1/sqrt(mean_k A[i,k]^2 + eps), with A*gamma fed
-                                 to the GEMM.  Must be the first op, at most once,
-                                 and needs K > 0.                                      */
+                                 to the GEMM.  in = NULL: the gain is already in the
+                                 rows of B (B = diag(gamma) W, see coda_fold_gain), A
+                                 is fed unchanged and the row sums of squares come from
+                                 the A fragments the matrix cores read.  Must be the
+                                 first op, at most once, and needs K > 0.             */
   /* accumulation (agentlenshq.com page, "How it works": accumulation) */
   CODA_OP_ADD_COL = 4,        /* v += in[j]          (bias)                          */
   CODA_OP_ADD_ROW = 5,        /* v += in[i]                                          */
@@ -213,6 +216,23 @@ int coda_validate(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
  */
 size_t coda_workspace_size(int64_t M, int64_t N, int64_t K, const coda_epi_desc* desc,
                            int unfused);
+
+/*
+ * coda_fold_gain - B_out = diag(gamma) B: row k of the logical [K x N] operand
+ * B scaled by gamma[k] and rounded to `dtype` (round-to-nearest-even for bf16),
+ * the per-feature gain of a row norm moved into the following projection's
+ * weights ((x * gamma) W = x (gamma W), the reparameterisation in the zeli.app
+ * page's "augment_me" comment).  A fused call with CODA_OP_RMS_ROWSCALE and
+ * in = NULL on B_out then computes what the call with in = gamma computes on
+ * B.  B and B_out have the same layout (`b_layout`) with leading dimensions ldb
+ * and ldo; B_out may be B itself (ldo == ldb: in place), otherwise they must
+ * not overlap.  Depends on the weights alone, so a caller folds once per weight
+ * set.  Shape rules: the contiguous dimension (N for CODA_B_KN, K for
+ * CODA_B_NK), ldb and ldo multiples of 8; 16-byte aligned pointers.  Enqueued
+ * on `stream`; nothing is launched on error.  Returns a coda_status.
+ */
+int coda_fold_gain(const void* B, int64_t K, int64_t N, int64_t ldb, int32_t b_layout, int32_t dtype,
+                   const void* gamma, void* B_out, int64_t ldo, void* stream);
 
 /*
  * coda_ln_fold - the two constant rows of the deferred LayerNorm:

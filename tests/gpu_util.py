@@ -60,7 +60,7 @@ U_BF16 = 2.0 ** -8   # unit roundoff of bf16 (8 significand bits)
 REDUCTIONS = ("row_sum", "row_sumsq", "row_mean")
 
 
-def unfused_extra(spec, inputs, rows):
+def unfused_extra(spec, inputs, rows, fold_gain: bool = False):
     """Extra error allowance of the unfused sequence, from its bf16 intermediates.
 
     The unfused path stores the normalised A (in the A/B dtype), the GEMM
@@ -72,6 +72,10 @@ def unfused_extra(spec, inputs, rows):
     stored tensor, whose elements then carry delta = that allowance + u |v|;
     the row sum is off by at most sum(delta), the mean by that over the width,
     the sum of squares by sum(2 |v| delta + delta^2).
+
+    With ``fold_gain`` the gain sits in a bf16 copy of B (diag(gamma) B, rounded
+    once) and the stored normalised A carries none, so the GEMM sees two
+    roundings of relative size u per product: twice the first term.
 
     Returns (extra for D, {reduction index: extra per row}).
     """
@@ -85,7 +89,7 @@ def unfused_extra(spec, inputs, rows):
     extra = 0.0
     if ops and ops[0][0] == "rms_rowscale":
         Y = oracle.rmsnorm(A, ops[0][1]["gamma"], ops[0][1]["eps"])
-        extra = u_ab * (np.abs(Y) @ np.abs(B))
+        extra = (2 if fold_gain else 1) * u_ab * (np.abs(Y) @ np.abs(B))
         body = ops[1:]
     elif ops and ops[0][0] == "ln_rowscale":
         # the unfused pass stores the beta-free normalised A; beta's term beta^T B
@@ -130,12 +134,14 @@ def unfused_extra(spec, inputs, rows):
 
 
 def run_and_compare(spec, inputs, mode: str = "fused", tile: int = 0, rows=None, label: str = "",
-                    check_determinism: bool = False, flags: int = 0, return_call: bool = False):
+                    check_determinism: bool = False, flags: int = 0, return_call: bool = False,
+                    fold_gain: bool = False):
     """Run ``spec`` on the GPU through the C ABI and compare with the oracle
     (on ``rows`` only when given).  Returns the error stats (and the call)."""
     coda, runner = lib()
-    announce(f"{label or spec.name} mode={mode} tile={tile} flags={flags} M={spec.M} N={spec.N} K={spec.K}")
-    call = runner.WorkloadCall(spec, inputs, tile=tile, flags=flags)
+    announce(f"{label or spec.name} mode={mode} tile={tile} flags={flags} fold_gain={fold_gain} "
+             f"M={spec.M} N={spec.N} K={spec.K}")
+    call = runner.WorkloadCall(spec, inputs, tile=tile, flags=flags, fold_gain=fold_gain)
     st = call.fused() if mode == "fused" else call.unfused()
     coda.check(st, f"{spec.name} {mode}")
     torch.cuda.synchronize()
@@ -154,7 +160,7 @@ def run_and_compare(spec, inputs, mode: str = "fused", tile: int = 0, rows=None,
             assert torch.equal(o1[k], call.outputs[k]), f"{k} not bitwise repeatable"
     rows_idx = np.arange(spec.M) if rows is None else np.asarray(rows)
     D_ref, outs_ref = oracle.run_workload(spec, inputs, rows_idx)
-    d_extra, red_extra = (None, {}) if mode == "fused" else unfused_extra(spec, inputs, rows_idx)
+    d_extra, red_extra = (None, {}) if mode == "fused" else unfused_extra(spec, inputs, rows_idx, fold_gain)
     stats = {"D": assert_close(D, D_ref, f"{spec.name}/{mode}/D", d_extra)}
     red_i = 0
     for name, args in spec.program:

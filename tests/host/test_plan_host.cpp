@@ -99,8 +99,14 @@ int main() {
     e.ops[0].kind = CODA_OP_RMS_ROWSCALE; e.ops[0].in = P(0x40000000); e.ops[0].in_dtype = CODA_BF16;
     e.ops[0].scalar = 1e-6f;
     EXPECT(coda_validate(A, B, M, N, K, &e, 0) == CODA_OK);
-    coda_epi_desc f = e; f.ops[0].in = nullptr;
-    EXPECT(coda_validate(A, B, M, N, K, &f, 0) == CODA_ERR_INVALID_ARG);
+    coda_epi_desc f = e; f.ops[0].in = nullptr;   // gamma NULL: the gain is folded into B
+    EXPECT(coda_validate(A, B, M, N, K, &f, 0) == CODA_OK);
+    {
+      coda::Plan q = plan_of(M, N, K, f);
+      EXPECT(q.has_norm && q.gain_in_b && !q.has_ln && q.gamma == nullptr && q.n_ops == 0);
+      coda::Plan r = plan_of(M, N, K, e);
+      EXPECT(r.has_norm && !r.gain_in_b);
+    }
     f = e; f.ops[0].in_dtype = CODA_F32;
     EXPECT(coda_validate(A, B, M, N, K, &f, 0) == CODA_ERR_INVALID_ARG);
     f = e; f.ops[0].scalar = -1.0f;
@@ -257,6 +263,24 @@ int main() {
     f = e; f.D = Pm(0x50000000);                                                     // D over u
     EXPECT(coda_validate(A, B, 4096, 22016, 4096, &f, 0) == CODA_ERR_INVALID_ARG);
     EXPECT(coda_workspace_size(4096, 22016, 4096, &e, 1) >= size_t(4096) * 4096 * 2);   // unfused: normalised A
+  }
+  {  // coda_fold_gain validation
+    const void* g = P(0x40000000);
+    EXPECT(coda::validate_fold_gain(B, 768, 3072, 3072, CODA_B_KN, CODA_BF16, g, Pm(0x70000000), 3072) == CODA_OK);
+    EXPECT(coda::validate_fold_gain(B, 768, 3072, 768, CODA_B_NK, CODA_BF16, g, Pm(0x70000000), 768) == CODA_OK);
+    EXPECT(coda::validate_fold_gain(B, 768, 3072, 3072, CODA_B_KN, CODA_BF16, g, Pm(0x20000000), 3072) ==
+           CODA_OK);   // exactly in place
+    EXPECT(coda::validate_fold_gain(B, 768, 3072, 3072, CODA_B_KN, CODA_BF16, g, Pm(0x20000010), 3072) ==
+           CODA_ERR_INVALID_ARG);   // overlapping, not in place
+    EXPECT(coda::validate_fold_gain(B, 768, 3072, 3072, CODA_B_KN, CODA_BF16, nullptr, Pm(0x70000000), 3072) ==
+           CODA_ERR_INVALID_ARG);
+    EXPECT(coda::validate_fold_gain(B, 768, 3076, 3080, CODA_B_KN, CODA_BF16, g, Pm(0x70000000), 3080) ==
+           CODA_ERR_UNSUPPORTED);   // contiguous dimension not a multiple of 8
+    EXPECT(coda::validate_fold_gain(B, 768, 3072, 3072, CODA_B_KN, CODA_BF16, g, Pm(0x70000000), 3000) ==
+           CODA_ERR_INVALID_ARG);   // ldo too small
+    EXPECT(coda::validate_fold_gain(B, 768, 3072, 3072, CODA_B_KN, 7, g, Pm(0x70000000), 3072) ==
+           CODA_ERR_INVALID_ARG);
+    EXPECT(coda::validate_fold_gain(B, 0, 3072, 3072, CODA_B_KN, CODA_BF16, nullptr, nullptr, 3072) == CODA_OK);
   }
   {  // coda_ln_fold validation
     float* u = static_cast<float*>(Pm(0x60000000));
