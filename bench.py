@@ -128,8 +128,9 @@ def main():
     ap.add_argument("--workload", type=int, default=WORKLOAD_INDEX, choices=sorted(WORKLOAD_TEXT),
                     help="synthetic layer to time (default: the LLaMA-7B gate/up layer)")
     ap.add_argument("--no-flush", action="store_true", help="do not evict L2 / Infinity Cache between steps")
-    ap.add_argument("--fold-gain", action="store_true",
-                    help="fold the RMSNorm gain into a copy of the weights once (coda_fold_gain) before timing")
+    ap.add_argument("--in-loop-gain", action="store_true",
+                    help="time the RMSNorm gain applied to A in the main loop instead of folded into a copy of the "
+                         "weights once (coda_fold_gain, outside the timed region; the default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unfused", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -152,7 +153,9 @@ def main():
     spec = w.get_config(args.workload)
     print(f"[bench] generating {spec.name} inputs", file=sys.stderr, flush=True)
     inputs = w.make_inputs(spec)
-    call = runner.WorkloadCall(spec, inputs, tile=args.tile, fold_gain=args.fold_gain)
+    has_rms = any(op == "rms_rowscale" for op, _ in spec.program)
+    fold = has_rms and not args.in_loop_gain
+    call = runner.WorkloadCall(spec, inputs, tile=args.tile, fold_gain=fold)
     flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
     if args.copy_calibration:
@@ -195,6 +198,19 @@ def main():
         torch.cuda.synchronize()
         unfused_ms = float(np.mean([s.elapsed_time(e) for s, e in uevs]))
 
+    # the other placement of the RMSNorm gain, for comparison (not the headline)
+    other_ms = None
+    if has_rms and not args.no_unfused:
+        print("[bench] fused, other gain placement", file=sys.stderr, flush=True)
+        other = runner.WorkloadCall(spec, inputs, tile=args.tile, fold_gain=not fold)
+        for _ in range(max(2, args.warmup // 2)):
+            step(other.fused)
+        torch.cuda.synchronize()
+        oevs = [step(other.fused) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        other_ms = float(np.mean([s.elapsed_time(e) for s, e in oevs]))
+        del other
+
     flops = float(spec.flops)
     tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_F32_TFLOPS if spec.ab_dtype == "f32" else PEAK_BF16_TFLOPS
@@ -225,13 +241,15 @@ def main():
             "workload": WORKLOAD_TEXT[args.workload],
             "M": spec.M, "N": spec.N, "K": spec.K,
             "cache_flush_between_steps": not args.no_flush,
-            "gain_folded_into_weights": bool(args.fold_gain),
+            "gain_folded_into_weights": bool(fold),
             "tile": tile_used,
         },
         "pct_peak": round(100.0 * tflops / peak, 2),
         "unfused_ms_per_step": None if unfused_ms is None else round(unfused_ms, 4),
         "speedup_vs_unfused": None if unfused_ms is None else round(unfused_ms / ms, 3),
         "effective_GBps": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
+        ("fused_in_loop_gain_ms_per_step" if fold else "fused_folded_gain_ms_per_step"):
+            None if other_ms is None else round(other_ms, 4),
         "fused_ms_p10_p90": [round(float(np.percentile(fused_ms, 10)), 4),
                              round(float(np.percentile(fused_ms, 90)), 4)],
         "wall_s_timed_region": round(wall, 4),
