@@ -51,6 +51,9 @@ GELU_CUBIC = 0.044715
 ELEMENTWISE_OPS = ("scale", "scale_row", "scale_col", "add_col", "add_row", "add_mat",
                    "gelu_tanh", "silu", "swiglu_pair", "mul_dgelu_tanh")
 REDUCTION_OPS = ("row_sum", "row_sumsq", "row_mean")
+# reductions over the rows of the output, one value per column (the bias
+# gradient of a backward layer is the column sum of its output gradient)
+COLUMN_REDUCTION_OPS = ("col_sum", "col_sumsq")
 
 
 # --- pairwise / elementwise transforms (agentlenshq.com, "How it works": pairwise) ---
@@ -193,7 +196,8 @@ def apply_epilogue(C: np.ndarray, ops: Sequence[Tuple[str, Dict]]) -> Tuple[np.n
     """Apply ``ops`` in order to the running value v = C.
 
     Returns the final value and, for each reduction op in list order, a tuple
-    (op name, its args, the fp64 per-row result).  ``rms_rowscale`` is not an
+    (op name, its args, the fp64 result): one value per row for row_*, one per
+    column (over all rows given) for col_*.  ``rms_rowscale`` is not an
     epilogue op here: the oracle applies it to A before the GEMM.
     """
     v = np.array(C, dtype=np.float64, copy=True)
@@ -228,6 +232,10 @@ def apply_epilogue(C: np.ndarray, ops: Sequence[Tuple[str, Dict]]) -> Tuple[np.n
             if width == 0:
                 raise ValueError("row_mean over an empty row is undefined")
             reductions.append((name, args, np.sum(v, axis=1) / width))
+        elif name == "col_sum":
+            reductions.append((name, args, np.sum(v, axis=0)))
+        elif name == "col_sumsq":
+            reductions.append((name, args, np.sum(v * v, axis=0)))
         elif name in ("rms_rowscale", "ln_rowscale"):
             raise ValueError(f"{name} is applied to A by forward(); it must come first")
         else:

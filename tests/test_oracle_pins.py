@@ -98,6 +98,10 @@ def brute_force(A, B_logical, ops):
             reds.append([sum(x * x for x in row) for row in V])
         elif name == "row_mean":
             reds.append([sum(row) / len(row) for row in V])
+        elif name == "col_sum":
+            reds.append([sum(V[i][j] for i in range(len(V))) for j in range(width)])
+        elif name == "col_sumsq":
+            reds.append([sum(V[i][j] * V[i][j] for i in range(len(V))) for j in range(width)])
     return V, reds
 
 
@@ -147,6 +151,9 @@ PROGRAMS = {
     "cfg4": lambda r, M, N, K: [("rms_rowscale", {"gamma": 1 + 0.1 * r.standard_normal(K), "eps": 1e-6}),
                                 ("swiglu_pair", {}), ("row_mean", {})],
     "cfg5": lambda r, M, N, K: [("mul_dgelu_tanh", {"mat": r.standard_normal((M, N))}), ("row_sum", {})],
+    "colred": lambda r, M, N, K: [("mul_dgelu_tanh", {"mat": r.standard_normal((M, N))}), ("col_sum", {}),
+                                  ("add_col", {"vec": r.standard_normal(N)}), ("col_sumsq", {}),
+                                  ("swiglu_pair", {}), ("col_sum", {}), ("row_sum", {})],
     "ln": lambda r, M, N, K: [("ln_rowscale", {"gamma": 1 + 0.1 * r.standard_normal(K),
                                                "beta": 0.1 * r.standard_normal(K), "eps": 1e-5}),
                               ("add_col", {"vec": r.standard_normal(N)}), ("gelu_tanh", {}), ("row_sum", {})],
@@ -168,7 +175,7 @@ def test_oracle_matches_brute_force(prog):
     D, reds = oracle.forward(A, B, ops, "KN")
     V, bred = brute_force(_lists(A), _lists(B), bf_ops)
     # mul_dgelu_tanh's brute force uses a finite difference (error ~1e-10)
-    tol = 1e-8 if prog == "cfg5" else 1e-12
+    tol = 1e-8 if prog in ("cfg5", "colred") else 1e-12
     assert np.allclose(D, np.array(V), rtol=tol, atol=tol)
     assert len(reds) == len(bred)
     for (_, _, r1), r2 in zip(reds, bred):
@@ -374,6 +381,51 @@ def test_reductions_constant_rows():
     C = np.full((3, N), c)
     _, reds = oracle.apply_epilogue(C, [("row_sum", {}), ("row_sumsq", {}), ("row_mean", {})])
     assert np.allclose(reds[0][2], N * c) and np.allclose(reds[1][2], N * c * c) and np.allclose(reds[2][2], c)
+
+
+def test_column_reductions_closed_forms_and_axis():
+    # a constant M x N matrix: every column sums to M c, its squares to M c^2
+    c, M, N = -1.25, 7, 4
+    _, reds = oracle.apply_epilogue(np.full((M, N), c), [("col_sum", {}), ("col_sumsq", {})])
+    assert reds[0][2].shape == (N,) and np.allclose(reds[0][2], M * c)
+    assert np.allclose(reds[1][2], M * c * c)
+    # rows 0..M-1 holding i + 10 j: column j sums to M(M-1)/2 + 10 j M (pins the axis)
+    V = np.arange(M)[:, None] + 10.0 * np.arange(N)[None, :]
+    _, reds = oracle.apply_epilogue(V, [("col_sum", {}), ("row_sum", {})])
+    assert np.array_equal(reds[0][2], M * (M - 1) / 2 + 10.0 * np.arange(N) * M)
+    # the total is the same whichever way it is reduced
+    assert np.isclose(reds[0][2].sum(), reds[1][2].sum())
+
+
+def test_column_reduction_of_a_backward_layer_is_the_bias_gradient():
+    # y = h W2 + b2 upstream of dY: the gradient of a bias b1 added before the
+    # activation is sum over tokens of dY W2^T * GELU'(P), the column sum of dH
+    rng = np.random.default_rng(12)
+    T, H, O = 6, 5, 3
+    dY, W2, P = rng.standard_normal((T, O)), rng.standard_normal((H, O)), rng.standard_normal((T, H))
+    _, reds = oracle.forward(dY, W2, [("mul_dgelu_tanh", {"mat": P}), ("col_sum", {})], "NK")
+    # finite-difference gradient of L(b1) = sum(dY * (gelu_tanh(P + b1) W2)) at b1 = 0
+    h = 1e-6
+    def L(b1):
+        return float(np.sum(dY * (oracle.gelu_tanh(P + b1[None, :]) @ W2)))
+    fd = np.array([(L(h * e) - L(-h * e)) / (2 * h) for e in np.eye(H)])
+    assert np.allclose(reds[0][2], fd, rtol=1e-6, atol=1e-8)
+
+
+def test_planted_column_sum_over_the_wrong_axis_is_caught(monkeypatch):
+    real = oracle.apply_epilogue
+
+    def wrong(C, ops):
+        v, reds = real(C, ops)
+        return v, [(n, a, (np.sum(v, axis=1) if n == "col_sum" else r)) for n, a, r in reds]
+    rng = np.random.default_rng(13)
+    M, N, K = 3, 6, 5
+    A, B = _tiny_case(rng, M, N, K)
+    ops = [("col_sum", {})]
+    _, bred = brute_force(_lists(A), _lists(B), ops)
+    monkeypatch.setattr(oracle, "apply_epilogue", wrong)
+    _, reds = oracle.apply_epilogue(oracle.gemm(A, B), ops)
+    assert reds[0][2].shape != np.array(bred[0]).shape or not np.allclose(reds[0][2], bred[0])
 
 
 def test_reduction_sees_value_at_its_position():
