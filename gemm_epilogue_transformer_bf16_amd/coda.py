@@ -15,6 +15,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libcoda.so")
 # ---- constants (mirror coda.h) ----
 CODA_MAX_OPS = 16
 CODA_MAX_REDUCTIONS = 8
+CODA_MAX_COL_REDUCTIONS = 2
 CODA_FLAG_NO_SPLIT_K = 1
 
 CODA_OK = 0
@@ -44,6 +45,8 @@ CODA_OP_ROW_SUM = 11
 CODA_OP_ROW_SUMSQ = 12
 CODA_OP_ROW_MEAN = 13
 CODA_OP_LN_ROWSCALE = 14
+CODA_OP_COL_SUM = 15
+CODA_OP_COL_SUMSQ = 16
 
 EXPORTED = (
     "coda_gemm_epi", "coda_gemm_unfused", "coda_validate", "coda_workspace_size",

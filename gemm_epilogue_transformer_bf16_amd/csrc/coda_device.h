@@ -114,6 +114,7 @@ struct FusedArgs {
   int out_width;
   int n_ops;
   int n_red;
+  int n_colred;         // column reductions
   int grid_m, grid_n;
   float eps;
   // split of the last round over K (split_s == 1: none)
@@ -124,6 +125,8 @@ struct FusedArgs {
   float* split_acc;     // [split tiles][split_s][NT][acc registers]
   float* split_ss;      // [split tiles][split_s][BM] (RMS)
   unsigned* split_cnt;  // [split tiles]
+  float* col_partials;  // [n_colred][grid_m][N]
+  unsigned* col_counters;   // [grid_n]
   DevOp ops[CODA_MAX_OPS];
 };
 

@@ -26,6 +26,7 @@ dev::FusedArgs make_args(const Plan& p) {
   a.out_width = (int)p.out_width;
   a.n_ops = p.n_ops;
   a.n_red = p.n_red;
+  a.n_colred = p.n_colred;
   a.grid_m = (int)p.grid_m;
   a.grid_n = (int)p.grid_n;
   a.eps = p.eps;
@@ -46,6 +47,10 @@ dev::FusedArgs make_args(const Plan& p) {
   if (p.n_red > 0 && p.grid_n > 1) {
     a.partials = reinterpret_cast<float*>(ws + fused_partials_offset(p));
     a.counters = reinterpret_cast<unsigned*>(ws + fused_counters_offset(p));
+  }
+  if (p.n_colred > 0 && p.grid_m > 1) {
+    a.col_partials = reinterpret_cast<float*>(ws + fused_col_partials_offset(p));
+    a.col_counters = reinterpret_cast<unsigned*>(ws + fused_col_counters_offset(p));
   }
   a.full_tiles = (int)p.full_tiles;
   a.split_s = p.split_s;
@@ -100,6 +105,7 @@ int launch_plain_gemm(const Plan& p, const void* A, int64_t lda, void* out, int6
   q.ln_u = nullptr;
   q.n_ops = 0;
   q.n_red = 0;
+  q.n_colred = 0;
   q.has_swiglu = false;
   q.out_width = p.N;
   // no workspace here: the tiles are computed whole

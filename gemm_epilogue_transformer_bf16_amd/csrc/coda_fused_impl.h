@@ -134,8 +134,11 @@ struct Cfg {
   static constexpr int EPI_RINV_OFF = EPI_RED_OFF + CODA_MAX_REDUCTIONS * WN * BM * 4;
   static constexpr int EPI_RMU_OFF = EPI_RINV_OFF + BM * 4;   // LN: mean * rstd per row
   static constexpr int EPI_FLAG_OFF = EPI_RMU_OFF + BM * 4;
+  // column reductions: per-block column partials [slot][wm][mi][BN]
+  static constexpr int EPI_COL_OFF = EPI_FLAG_OFF + 16;
+  static constexpr int EPI_END = EPI_COL_OFF + CODA_MAX_COL_REDUCTIONS * WM * MI * BN * 4;
   static constexpr int ARR0_BYTES = STAGE_BYTES > NW * REGION_BYTES ? STAGE_BYTES : NW * REGION_BYTES;
-  static constexpr int ARR1_BYTES = STAGE_BYTES > EPI_FLAG_OFF + 16 ? STAGE_BYTES : EPI_FLAG_OFF + 16;
+  static constexpr int ARR1_BYTES = STAGE_BYTES > EPI_END ? STAGE_BYTES : EPI_END;
   // RMS: raw A of the next K step lands in a third array by direct loads and is
   // converted (gain, bf16 rounding, sum of squares) from there into the stage
   static constexpr int RAW_BYTES = (RMS && !F32) ? A_BYTES : 16;
@@ -187,7 +190,7 @@ __device__ __forceinline__ void load_cols(const void* p, int dtype, long long co
 // Applies ops[o..] until the end of the list or a SWIGLU_PAIR (returned index).
 template <class C, bool PAIRED>
 __device__ __forceinline__ int run_ops(Chunks<C::CPL>& ch, KArgs a, int o, int M, int lane, int wn, float* red,
-                                       int pf_op, const u32x4_t (&pf)[C::CPL]) {
+                                       int pf_op, const u32x4_t (&pf)[C::CPL], float* colp, int wm, int mi) {
   constexpr int CPL = C::CPL;
   constexpr int EPC = PAIRED ? 4 : 8;   // live values per chunk
   const int col = PAIRED ? ch.col >> 1 : ch.col;
@@ -287,6 +290,32 @@ __device__ __forceinline__ int run_ops(Chunks<C::CPL>& ch, KArgs a, int o, int M
 #pragma unroll
           for (int off = 1; off < C::CPR; off <<= 1) p += __shfl_xor(p, off);
           if ((lane & (C::CPR - 1)) == 0) dst[ch.mloc[j]] = p;
+        }
+        break;
+      }
+      case CODA_OP_COL_SUM:
+      case CODA_OP_COL_SUMSQ: {
+        // the lane's rows, then the lanes that hold the same columns (lane %
+        // CPR): the wave's partial for its 32-row block, kept per block in LDS
+        const bool sq = kind == CODA_OP_COL_SUMSQ;
+        float p[EPC];
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) p[e] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j)
+          if (ch.row[j] < M) {
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) p[e] += sq ? ch.v[j][e] * ch.v[j][e] : ch.v[j][e];
+          }
+#pragma unroll
+        for (int off = C::CPR; off < 64; off <<= 1)
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) p[e] += __shfl_xor(p[e], off);
+        if (lane < C::CPR) {
+          const int tcol = wn * C::WTN + 8 * lane;   // tile-local first column of the chunk
+          float* dst = colp + ((op.red_slot * C::WM + wm) * C::MI + mi) * C::BN + (PAIRED ? tcol / 2 : tcol);
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) dst[e] = p[e];
         }
         break;
       }
@@ -1008,6 +1037,7 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
   float* red = reinterpret_cast<float*>(smem1 + C::EPI_RED_OFF);
   float* rinv = reinterpret_cast<float*>(smem1 + C::EPI_RINV_OFF);
   float* rmu = reinterpret_cast<float*>(smem1 + C::EPI_RMU_OFF);
+  float* colp = reinterpret_cast<float*>(smem1 + C::EPI_COL_OFF);
   // row factors from the sums: RMS 1/sqrt(ss/K + eps); LN rstd = 1/sqrt(var + eps)
   // with mean m = sx/K and var = ss/K - m^2 (of the shifted values), and m * rstd
   auto row_factors = [&](int row, float v, float s) {
@@ -1139,10 +1169,10 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
       }
     }
     __builtin_amdgcn_wave_barrier();
-    const int o = run_ops<C, false>(ch, a, 0, M, lane, wn, red, pf_op, pf_buf[mi & 1]);
+    const int o = run_ops<C, false>(ch, a, 0, M, lane, wn, red, pf_op, pf_buf[mi & 1], colp, wm, mi);
     if (o < a->n_ops) {   // SWIGLU_PAIR
       swiglu_chunks<C>(ch);
-      run_ops<C, true>(ch, a, o + 1, M, lane, wn, red, -1, pf_buf[mi & 1]);
+      run_ops<C, true>(ch, a, o + 1, M, lane, wn, red, -1, pf_buf[mi & 1], colp, wm, mi);
       store_chunks<C, true>(ch, a, M);
     } else {
       store_chunks<C, false>(ch, a, M);
@@ -1154,7 +1184,7 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
     const bool multi = a->grid_n > 1;
     for (int q = 0; q < a->n_ops; ++q) {
       KOp op = a->ops[q];
-      if (op.kind < CODA_OP_ROW_SUM) continue;
+      if (op.kind < CODA_OP_ROW_SUM || op.kind > CODA_OP_ROW_MEAN) continue;
       const int s = op.red_slot;
       for (int t = tid; t < BM; t += C::NT) {
         float v = 0.0f;
@@ -1187,7 +1217,7 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
         // last workgroup of the tile row: sum the partials in tile order
         for (int q = 0; q < a->n_ops; ++q) {
           KOp op = a->ops[q];
-          if (op.kind < CODA_OP_ROW_SUM) continue;
+          if (op.kind < CODA_OP_ROW_SUM || op.kind > CODA_OP_ROW_MEAN) continue;
           const int s = op.red_slot;
           for (int t = tid; t < BM; t += C::NT) {
             const int row = m0 + t;
@@ -1201,6 +1231,71 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
         }
         // leave the counter at zero for the next call
         if (tid == 0) __hip_atomic_store(a->counters + tile_m, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+
+  // Column reductions: the tile's partial per column (its row blocks in a
+  // fixed order), then across the tile rows of the grid through the workspace,
+  // finished in tile order by the last workgroup of the tile column, as for
+  // the row reductions.
+  if (a->n_colred > 0) {
+    __syncthreads();
+    const bool multi = a->grid_m > 1;
+    for (int q = 0; q < a->n_ops; ++q) {
+      KOp op = a->ops[q];
+      if (op.kind != CODA_OP_COL_SUM && op.kind != CODA_OP_COL_SUMSQ) continue;
+      const int s = op.red_slot;
+      const bool paired = op.width != N;   // after SWIGLU_PAIR: half the columns
+      const int cols = paired ? BN / 2 : BN;
+      const int c0 = paired ? n0 / 2 : n0;
+      for (int t = tid; t < cols; t += C::NT) {
+        const int col = c0 + t;
+        if (col >= op.width) continue;
+        float v = 0.0f;
+#pragma unroll
+        for (int w = 0; w < C::WM; ++w)
+#pragma unroll
+          for (int mi = 0; mi < MI; ++mi) v += colp[((s * C::WM + w) * MI + mi) * BN + t];
+        if (!multi) {
+          op.out[(long long)col * op.out_stride] = v;
+        } else {
+          __hip_atomic_store(a->col_partials + ((long long)s * a->grid_m + tile_m) * N + col, v, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+    if (multi) {
+      // publish the partials (agent-scope atomic stores, coherent across the
+      // XCDs' L2s) before the count, as for the row reductions
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (tid == 0) {
+        const unsigned old =
+            __hip_atomic_fetch_add(a->col_counters + tile_n, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *flag = (old == unsigned(a->grid_m - 1)) ? 1 : 0;
+      }
+      __syncthreads();
+      if (*flag) {
+        for (int q = 0; q < a->n_ops; ++q) {
+          KOp op = a->ops[q];
+          if (op.kind != CODA_OP_COL_SUM && op.kind != CODA_OP_COL_SUMSQ) continue;
+          const int s = op.red_slot;
+          const bool paired = op.width != N;
+          const int cols = paired ? BN / 2 : BN;
+          const int c0 = paired ? n0 / 2 : n0;
+          for (int t = tid; t < cols; t += C::NT) {
+            const int col = c0 + t;
+            if (col >= op.width) continue;
+            float v = 0.0f;
+            for (int tm = 0; tm < a->grid_m; ++tm)
+              v += __hip_atomic_load(a->col_partials + ((long long)s * a->grid_m + tm) * N + col, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+            op.out[(long long)col * op.out_stride] = v;
+          }
+        }
+        // leave the counter at zero for the next call
+        if (tid == 0) __hip_atomic_store(a->col_counters + tile_n, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }

@@ -21,6 +21,8 @@ bool is_reduction(int kind) {
   return kind == CODA_OP_ROW_SUM || kind == CODA_OP_ROW_SUMSQ || kind == CODA_OP_ROW_MEAN;
 }
 
+bool is_col_reduction(int kind) { return kind == CODA_OP_COL_SUM || kind == CODA_OP_COL_SUMSQ; }
+
 bool needs_vector(int kind) {
   return kind == CODA_OP_SCALE_ROW || kind == CODA_OP_SCALE_COL || kind == CODA_OP_ADD_COL ||
          kind == CODA_OP_ADD_ROW;
@@ -100,10 +102,25 @@ size_t fused_split_counters_offset(const Plan& p) {
   return fused_split_ss_offset(p) + align256(ss);
 }
 
-size_t fused_workspace_bytes(const Plan& p) {
-  if (p.M == 0 || p.N == 0) return 0;
+namespace {
+bool has_col_partials(const Plan& p) { return p.n_colred > 0 && p.grid_m > 1; }
+size_t fused_row_and_split_bytes(const Plan& p) {
   if (p.split_s <= 1) return has_row_partials(p) ? fused_split_acc_offset(p) : 0;
   return fused_split_counters_offset(p) + align256(size_t(p.split_tiles) * sizeof(uint32_t));
+}
+}  // namespace
+
+size_t fused_col_partials_offset(const Plan& p) { return fused_row_and_split_bytes(p); }
+
+size_t fused_col_counters_offset(const Plan& p) {
+  return fused_col_partials_offset(p) +
+         (has_col_partials(p) ? align256(size_t(p.n_colred) * size_t(p.grid_m) * size_t(p.N) * sizeof(float)) : 0);
+}
+
+size_t fused_workspace_bytes(const Plan& p) {
+  if (p.M == 0 || p.N == 0) return 0;
+  if (!has_col_partials(p)) return fused_row_and_split_bytes(p);
+  return fused_col_counters_offset(p) + align256(size_t(p.grid_n) * sizeof(uint32_t));
 }
 
 // Split of the last round (bf16 configurations): with T tiles and `slots`
@@ -131,11 +148,18 @@ void plan_split(Plan* p, bool allow) {
 
 int64_t unfused_ld(const Plan& p) { return (p.N + 7) / 8 * 8; }
 
-size_t unfused_workspace_bytes(const Plan& p) {
-  if (p.M == 0 || p.N == 0) return 0;
+size_t unfused_col_partials_offset(const Plan& p) {
   size_t bytes = 0;
   if (p.has_norm) bytes += align256(size_t(p.M) * size_t(p.K) * dtype_size(p.ab_dtype));
   bytes += 2 * align256(size_t(p.M) * size_t(unfused_ld(p)) * dtype_size(p.d_dtype));
+  return bytes;
+}
+
+size_t unfused_workspace_bytes(const Plan& p) {
+  if (p.M == 0 || p.N == 0) return 0;
+  size_t bytes = unfused_col_partials_offset(p);
+  if (p.n_colred > 0)
+    bytes += align256(size_t((p.M + kColChunk - 1) / kColChunk) * size_t(unfused_ld(p)) * sizeof(float));
   return bytes;
 }
 
@@ -192,10 +216,10 @@ int build_plan(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
 
   // ---- op list ----
   int64_t width = N;
-  int n_red = 0;
+  int n_red = 0, n_col = 0;
   for (int i = 0; i < d->n_ops; ++i) {
     const coda_op& o = d->ops[i];
-    if (o.kind < CODA_OP_SCALE || o.kind > CODA_OP_LN_ROWSCALE) {
+    if (o.kind < CODA_OP_SCALE || o.kind > CODA_OP_COL_SUMSQ) {
       set_error("op %d: unknown kind %d", i, o.kind);
       return CODA_ERR_INVALID_ARG;
     }
@@ -315,9 +339,25 @@ int build_plan(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
       }
       q.red_slot = n_red++;
     }
+    if (is_col_reduction(o.kind)) {
+      if (n_col >= CODA_MAX_COL_REDUCTIONS) {
+        set_error("more than %d column reductions", CODA_MAX_COL_REDUCTIONS);
+        return CODA_ERR_UNSUPPORTED;
+      }
+      if (!o.out || o.out_stride < 1) {
+        set_error("op %d: reduction needs out != NULL and out_stride >= 1", i);
+        return CODA_ERR_INVALID_ARG;
+      }
+      if (!aligned(o.out, 4)) {
+        set_error("op %d: reduction output must be 4-byte aligned", i);
+        return CODA_ERR_UNSUPPORTED;
+      }
+      q.red_slot = n_col++;
+    }
     p->n_ops++;
   }
   p->n_red = n_red;
+  p->n_colred = n_col;
   p->out_width = width;
 
   // ---- shapes, leading dimensions, alignment ----
@@ -397,8 +437,8 @@ int build_plan(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
       set_error("D overlaps LN_ROWSCALE's u");
       return CODA_ERR_INVALID_ARG;
     }
-    Extent outs[CODA_MAX_REDUCTIONS];
-    int64_t strides[CODA_MAX_REDUCTIONS];
+    Extent outs[CODA_MAX_REDUCTIONS + CODA_MAX_COL_REDUCTIONS];
+    int64_t strides[CODA_MAX_REDUCTIONS + CODA_MAX_COL_REDUCTIONS];
     int no = 0;
     for (int i = 0; i < p->n_ops; ++i) {
       const Op& q = p->ops[i];
@@ -415,8 +455,9 @@ int build_plan(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
           return CODA_ERR_INVALID_ARG;
         }
       }
-      if (is_reduction(q.kind)) {
-        Extent e = matrix_extent(q.out, M, 1, q.out_stride, 4);
+      if (is_reduction(q.kind) || is_col_reduction(q.kind)) {
+        Extent e = is_col_reduction(q.kind) ? matrix_extent(q.out, q.width, 1, q.out_stride, 4)
+                                            : matrix_extent(q.out, M, 1, q.out_stride, 4);
         if (overlap(e, eD) || overlap(e, eA) || overlap(e, eB)) {
           set_error("reduction output of op %d overlaps D, A or B", i);
           return CODA_ERR_INVALID_ARG;
@@ -437,6 +478,11 @@ int build_plan(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
         ++no;
       }
     }
+  }
+
+  if (unfused && p->n_colred > 0 && (M + kColChunk - 1) / kColChunk > 65535) {
+    set_error("unfused column reductions support at most %lld rows", (long long)kColChunk * 65535);
+    return CODA_ERR_UNSUPPORTED;
   }
 
   // ---- workspace ----

@@ -43,7 +43,7 @@ struct Op {
   float scalar;
   void* out;
   int64_t out_stride;
-  int red_slot;      // index among the reductions, -1 otherwise
+  int red_slot;      // index among the row (or, for COL_*, the column) reductions, -1 otherwise
   int64_t width;     // width of the running value when the op runs
 };
 
@@ -63,6 +63,7 @@ struct Plan {
   int n_ops;                 // ops after the norm op
   Op ops[CODA_MAX_OPS];
   int n_red;
+  int n_colred;              // column reductions
   bool has_swiglu;
   int tile;                  // 1-based bf16 tile config; 0 for the fp32 path
   TileCfg cfg;
@@ -95,12 +96,19 @@ size_t fused_counters_offset(const Plan& p);
 size_t fused_split_acc_offset(const Plan& p);
 size_t fused_split_ss_offset(const Plan& p);
 size_t fused_split_counters_offset(const Plan& p);
+// then, with column reductions over several tile rows: fp32 column partials
+// [n_colred][grid_m][N] and uint32 counters [grid_n]
+size_t fused_col_partials_offset(const Plan& p);
+size_t fused_col_counters_offset(const Plan& p);
 
 // Workspace layout of the unfused path: normalised A (ab dtype, [M x K]) when
 // the list has the RMS op, then two [M x ldi] intermediates in d dtype, with
-// ldi = N rounded up to a multiple of 8.
+// ldi = N rounded up to a multiple of 8, then (column reductions) fp32 column
+// partials [ceil(M / kColChunk)][ldi].
+constexpr int kColChunk = 128;
 size_t unfused_workspace_bytes(const Plan& p);
 int64_t unfused_ld(const Plan& p);
+size_t unfused_col_partials_offset(const Plan& p);
 
 // Validates a coda_ln_fold call.  Returns a coda_status.
 int validate_ln_fold(const void* B, int64_t K, int64_t N, int64_t ldb, int32_t b_layout, int32_t dtype,

@@ -218,13 +218,49 @@ __global__ void __launch_bounds__(kPassThreads) rowred_kernel(const void* in, lo
   }
 }
 
+// ---- column reductions over a stored tensor: partial sums over chunks of
+// kColChunk rows (8 columns per thread), then the chunks in order per column ----
+__global__ void __launch_bounds__(kPassThreads) colred_partial_kernel(const void* in, long long ldi, int width, int M,
+                                                                      int io_dtype, DevOp op, float* part,
+                                                                      long long ldp) {
+  const long long c = ((long long)blockIdx.x * kPassThreads + threadIdx.x) * 8;
+  if (c >= width) return;
+  const int r0 = blockIdx.y * kColChunk;
+  const int r1 = min(M, r0 + kColChunk);
+  const int esz = io_dtype == CODA_BF16 ? 2 : 4;
+  const bool sq = op.kind == CODA_OP_COL_SUMSQ;
+  float acc[8] = {};
+  for (int r = r0; r < r1; ++r) {
+    float v[8];
+    load8(static_cast<const char*>(in) + (long long)r * ldi * esz, io_dtype, c, width, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += sq ? v[e] * v[e] : v[e];
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    if (c + e < width) part[(long long)blockIdx.y * ldp + c + e] = acc[e];
+}
+
+__global__ void __launch_bounds__(kPassThreads) colred_final_kernel(const float* part, long long ldp, int chunks,
+                                                                    int width, DevOp op) {
+  const long long c = (long long)blockIdx.x * kPassThreads + threadIdx.x;
+  if (c >= width) return;
+  float v = 0.0f;
+  for (int k = 0; k < chunks; ++k) v += part[(long long)k * ldp + c];
+  op.out[c * op.out_stride] = v;
+}
+
 }  // namespace dev
 
 namespace {
 
-bool is_reduction(int kind) {
+bool is_row_reduction(int kind) {
   return kind == CODA_OP_ROW_SUM || kind == CODA_OP_ROW_SUMSQ || kind == CODA_OP_ROW_MEAN;
 }
+
+bool is_col_reduction(int kind) { return kind == CODA_OP_COL_SUM || kind == CODA_OP_COL_SUMSQ; }
+
+bool is_reduction(int kind) { return is_row_reduction(kind) || is_col_reduction(kind); }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -290,10 +326,23 @@ int launch_unfused(const Plan& p, hipStream_t stream) {
   for (int i = 0; i < p.n_ops; ++i) {
     const Op& q = p.ops[i];
     const dev::DevOp d = to_dev(q);
-    if (is_reduction(q.kind)) {
+    if (is_row_reduction(q.kind)) {
       const unsigned blocks = unsigned((p.M + 3) / 4);
       hipLaunchKernelGGL(dev::rowred_kernel, dim3(blocks), dim3(dev::kPassThreads), 0, stream, cur, (long long)ldc,
                          (int)width, M, p.d_dtype, d);
+      if (check_launch() != CODA_OK) return CODA_ERR_HIP;
+      continue;
+    }
+    if (is_col_reduction(q.kind)) {
+      float* part = reinterpret_cast<float*>(static_cast<char*>(p.workspace) + unfused_col_partials_offset(p));
+      const int chunks = int((p.M + kColChunk - 1) / kColChunk);
+      const unsigned gx = unsigned(((width + 7) / 8 + dev::kPassThreads - 1) / dev::kPassThreads);
+      hipLaunchKernelGGL(dev::colred_partial_kernel, dim3(gx, (unsigned)chunks), dim3(dev::kPassThreads), 0, stream,
+                         cur, (long long)ldc, (int)width, M, p.d_dtype, d, part, (long long)ldi);
+      if (check_launch() != CODA_OK) return CODA_ERR_HIP;
+      const unsigned gf = unsigned((width + dev::kPassThreads - 1) / dev::kPassThreads);
+      hipLaunchKernelGGL(dev::colred_final_kernel, dim3(gf), dim3(dev::kPassThreads), 0, stream, part,
+                         (long long)ldi, chunks, (int)width, d);
       if (check_launch() != CODA_OK) return CODA_ERR_HIP;
       continue;
     }

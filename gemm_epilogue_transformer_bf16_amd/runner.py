@@ -29,6 +29,8 @@ OPCODES = {
     "row_sumsq": C.CODA_OP_ROW_SUMSQ,
     "row_mean": C.CODA_OP_ROW_MEAN,
     "ln_rowscale": C.CODA_OP_LN_ROWSCALE,
+    "col_sum": C.CODA_OP_COL_SUM,
+    "col_sumsq": C.CODA_OP_COL_SUMSQ,
 }
 
 TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
@@ -57,7 +59,8 @@ class Call:
 
     ``ops`` is a list of (name, args) where array arguments are device tensors:
     ``gamma``/``vec``/``mat`` inputs, ``out`` a 2-D fp32 tensor with ``col``
-    selecting the column a reduction writes.  Scalars: ``alpha``, ``beta``, ``eps``.
+    selecting the column a reduction writes (its rows index the output's rows
+    for row_* reductions and the output's columns for col_* reductions).  Scalars: ``alpha``, ``beta``, ``eps``.
     ``ln_rowscale`` takes ``gamma``, ``eps`` and an optional shift ``beta``
     tensor: the call computes u = gamma^T B and c = beta^T B once with
     coda_ln_fold and passes LN_ROWSCALE(gamma, u) followed by ADD_COL(c).
@@ -125,7 +128,7 @@ class Call:
                 o.scalar = float(args["eps"])
             if name == "ln_rowscale":
                 o.in2 = args["u"].data_ptr()
-            if name in ("row_sum", "row_sumsq", "row_mean"):
+            if name in ("row_sum", "row_sumsq", "row_mean", "col_sum", "col_sumsq"):
                 out = args["out"]
                 self._keep.append(out)
                 col = int(args.get("col", 0))

@@ -65,6 +65,7 @@ extern "C" {
 
 #define CODA_MAX_OPS 16
 #define CODA_MAX_REDUCTIONS 8
+#define CODA_MAX_COL_REDUCTIONS 2
 
 /* coda_epi_desc.flags */
 #define CODA_FLAG_NO_SPLIT_K 1   /* coda_gemm_epi: never split the last round of
@@ -130,7 +131,14 @@ typedef enum {
      op: its term beta^T B is a column vector (coda_ln_fold's c) that a later
      CODA_OP_ADD_COL adds.  Must be the first op and needs K > 0; at most one
      of RMS_ROWSCALE / LN_ROWSCALE. */
-  CODA_OP_LN_ROWSCALE = 14
+  CODA_OP_LN_ROWSCALE = 14,
+  /* reductions over the rows (the survey's backward set: the bias gradient of a
+     layer is the column sum of its output gradient).  Each writes an fp32 value
+     per column j < width to ((float*)out)[j*out_stride]: the sum over all M
+     rows of the running value (COL_SUM) or of its square (COL_SUMSQ) at the
+     op's position.  At most CODA_MAX_COL_REDUCTIONS per list. */
+  CODA_OP_COL_SUM = 15,
+  CODA_OP_COL_SUMSQ = 16
 } coda_op_kind;
 
 typedef struct {
@@ -178,7 +186,8 @@ typedef struct {
  * accumulators in a fixed order and runs the epilogue, so results do not
  * depend on timing.
  * Workspace: row reductions whose row spans several output tiles combine
- * partial sums through the workspace, and so do the parts of a split tile
+ * partial sums through the workspace, column reductions whose column spans
+ * several tiles likewise, and so do the parts of a split tile
  * (coda_workspace_size(..., 0) bytes, 0 when neither happens).  Its counter
  * regions must be zero before the first call (a zero-filled workspace will
  * do); every call leaves them zero again.  Two calls that run concurrently

@@ -264,6 +264,35 @@ int main() {
     EXPECT(coda_validate(A, B, 4096, 22016, 4096, &f, 0) == CODA_ERR_INVALID_ARG);
     EXPECT(coda_workspace_size(4096, 22016, 4096, &e, 1) >= size_t(4096) * 4096 * 2);   // unfused: normalised A
   }
+  {  // column reductions: at most CODA_MAX_COL_REDUCTIONS, an output, workspace over several tile rows
+    coda_epi_desc e = base_desc(N, K);
+    e.n_ops = 2;
+    e.ops[0].kind = CODA_OP_COL_SUM; e.ops[0].out = Pm(0x50000000); e.ops[0].out_stride = 2;
+    e.ops[1].kind = CODA_OP_COL_SUMSQ; e.ops[1].out = Pm(0x50000004); e.ops[1].out_stride = 2;
+    coda::Plan q = plan_of(M, N, K, e);
+    EXPECT(q.n_colred == 2 && q.n_red == 0 && q.ops[0].red_slot == 0 && q.ops[1].red_slot == 1);
+    // 300 rows span two or three tile rows: partials and counters are needed
+    const size_t ws = coda_workspace_size(M, N, K, &e, 0);
+    EXPECT(ws >= size_t(2) * size_t(q.grid_m) * size_t(N) * 4 + size_t(q.grid_n) * 4);
+    EXPECT(coda_validate(A, B, M, N, K, &e, 0) == CODA_ERR_WORKSPACE);
+    // overlapping outputs (same stride, same start) are rejected
+    coda_epi_desc f = e; f.ops[1].out = Pm(0x50000000); f.ops[1].out_stride = 1;
+    f.workspace = Pm(0x70000000); f.workspace_bytes = ws;
+    EXPECT(coda_validate(A, B, M, N, K, &f, 0) == CODA_ERR_INVALID_ARG);
+    f = e; f.n_ops = 3; f.ops[2] = f.ops[0]; f.ops[2].out = Pm(0x51000000);
+    EXPECT(coda_validate(A, B, M, N, K, &f, 0) == CODA_ERR_UNSUPPORTED);   // a third column reduction
+    f = e; f.ops[0].out = nullptr;
+    EXPECT(coda_validate(A, B, M, N, K, &f, 0) == CODA_ERR_INVALID_ARG);
+    f = e; f.ops[0].out_stride = 0;
+    EXPECT(coda_validate(A, B, M, N, K, &f, 0) == CODA_ERR_INVALID_ARG);
+    f = e; f.ops[0].out = Pm(0x30000000);                                   // over D
+    f.workspace = Pm(0x70000000); f.workspace_bytes = ws;
+    EXPECT(coda_validate(A, B, M, N, K, &f, 0) == CODA_ERR_INVALID_ARG);
+    // one tile row: no workspace
+    EXPECT(coda_workspace_size(100, N, K, &e, 0) == 0);
+    // the unfused sequence keeps column partials per chunk of rows
+    EXPECT(coda_workspace_size(M, N, K, &e, 1) > coda_workspace_size(M, N, K, &d, 1));
+  }
   {  // coda_fold_gain validation
     const void* g = P(0x40000000);
     EXPECT(coda::validate_fold_gain(B, 768, 3072, 3072, CODA_B_KN, CODA_BF16, g, Pm(0x70000000), 3072) == CODA_OK);
