@@ -128,6 +128,9 @@ def main():
     ap.add_argument("--workload", type=int, default=WORKLOAD_INDEX, choices=sorted(WORKLOAD_TEXT),
                     help="synthetic layer to time (default: the LLaMA-7B gate/up layer)")
     ap.add_argument("--no-flush", action="store_true", help="do not evict L2 / Infinity Cache between steps")
+    ap.add_argument("--bias-grad", action="store_true",
+                    help="GPT-2-medium backward layer (workload 5) with the bias gradient: a column sum of dH "
+                         "appended to its epilogue")
     ap.add_argument("--in-loop-gain", action="store_true",
                     help="time the RMSNorm gain applied to A in the main loop instead of folded into a copy of the "
                          "weights once (coda_fold_gain, outside the timed region; the default)")
@@ -151,6 +154,13 @@ def main():
         sys.exit(1)
 
     spec = w.get_config(args.workload)
+    if args.bias_grad:
+        import dataclasses
+        if args.workload != 5:
+            print("--bias-grad applies to the backward layer (--workload 5)", file=sys.stderr)
+            sys.exit(2)
+        spec = dataclasses.replace(spec, program=spec.program + (("col_sum", {"out": "db", "col": 0}),),
+                                   outputs=spec.outputs + (("db", (spec.out_width, 1)),))
     print(f"[bench] generating {spec.name} inputs", file=sys.stderr, flush=True)
     inputs = w.make_inputs(spec)
     has_rms = any(op == "rms_rowscale" for op, _ in spec.program)
@@ -238,7 +248,8 @@ def main():
         "dtype": "f32" if spec.ab_dtype == "f32" else "bf16",
         "data": "synthetic",
         "config": {
-            "workload": WORKLOAD_TEXT[args.workload],
+            "workload": WORKLOAD_TEXT[args.workload] + (" + bias gradient (column sum of dH)"
+                                                        if args.bias_grad else ""),
             "M": spec.M, "N": spec.N, "K": spec.K,
             "cache_flush_between_steps": not args.no_flush,
             "gain_folded_into_weights": bool(fold),

@@ -55,9 +55,12 @@ def run_workload(spec, inputs: Dict[str, np.ndarray], rows: Optional[Sequence[in
     B = to_f64(inputs[spec.b_name], dtypes[spec.b_name])
     ops = resolve_program(spec, inputs, rows_arr)
     D, reds = forward(A, B, ops, spec.b_layout)
+    # outputs of column reductions are indexed by column (over the rows given);
+    # all others by row
+    col_outs = {args["out"] for name, args in spec.program if name in ("col_sum", "col_sumsq")}
     outs = {}
     for oname, shape in spec.outputs:
-        outs[oname] = np.full((A.shape[0], shape[1]), np.nan)
+        outs[oname] = np.full((shape[0] if oname in col_outs else A.shape[0], shape[1]), np.nan)
     for name, args, val in reds:
         outs[args["out"]][:, args["col"]] = val
     return D, outs
