@@ -27,6 +27,9 @@ CODA_ERR_HIP = -4
 CODA_BF16 = 0
 CODA_F32 = 1
 
+CODA_A_MK = 0
+CODA_A_KM = 1
+
 CODA_B_KN = 0
 CODA_B_NK = 1
 
@@ -83,6 +86,8 @@ class coda_epi_desc(ctypes.Structure):
         ("workspace_bytes", ctypes.c_size_t),
         ("tile", ctypes.c_int32),
         ("flags", ctypes.c_int32),
+        ("a_layout", ctypes.c_int32),
+        ("reserved1", ctypes.c_int32),
         ("ops", coda_op * CODA_MAX_OPS),
     ]
 

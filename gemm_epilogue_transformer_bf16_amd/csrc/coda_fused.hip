@@ -66,17 +66,18 @@ dev::FusedArgs make_args(const Plan& p) {
 int launch_args(const Plan& p, const dev::FusedArgs& a, hipStream_t stream) {
   const int64_t nwg = p.full_tiles + p.split_tiles * p.split_s;
   const bool bkn = p.b_layout == CODA_B_KN;
+  const bool akm = p.a_layout == CODA_A_KM;
   const int norm = p.has_ln      ? dev::kNormLn
                    : p.gain_in_b ? dev::kNormRmsB
                    : p.has_norm  ? dev::kNormRms
                                  : dev::kNormNone;
   if (p.ab_dtype == CODA_F32) {
-    return dev::launch_tile_f32(a, nwg, bkn, norm, stream);
+    return dev::launch_tile_f32(a, nwg, bkn, norm, akm, stream);
   }
   switch (p.tile) {
-    case 1: return dev::launch_tile1(a, nwg, bkn, norm, stream);
-    case 2: return dev::launch_tile2(a, nwg, bkn, norm, stream);
-    case 3: return dev::launch_tile3(a, nwg, bkn, norm, stream);
+    case 1: return dev::launch_tile1(a, nwg, bkn, norm, akm, stream);
+    case 2: return dev::launch_tile2(a, nwg, bkn, norm, akm, stream);
+    case 3: return dev::launch_tile3(a, nwg, bkn, norm, akm, stream);
     default:
       set_error("no kernel for tile config %d", p.tile);
       return CODA_ERR_UNSUPPORTED;

@@ -86,10 +86,16 @@ typedef __attribute__((address_space(3))) i16x4_t LdsI16x4;
 // the main loop), LayerNorm, RMSNorm with the gain already folded into B's rows
 constexpr int kNormNone = 0, kNormRms = 1, kNormLn = 2, kNormRmsB = 3;
 
-template <int BM_, int BN_, int WM_, int WN_, bool F32_, bool BKN_, int NORM_>
+template <int BM_, int BN_, int WM_, int WN_, bool F32_, bool BKN_, int NORM_, bool AKM_ = false>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
   static constexpr bool F32 = F32_, BKN = BKN_;
+  // AKM: A stored [K x M] (M contiguous) and used transposed, as X^T in the
+  // weight gradient X^T dY; its tile is staged and read like an N-major W tile
+  static constexpr bool AKM = AKM_;
+  static_assert(!AKM || (!F32 && NORM_ == kNormNone), "A stored [K x M]: bf16 operands, no row norm");
+  static constexpr int KM_CPR = BM / 8;               // 16-byte chunks per row of an M-major A tile
+  static constexpr int KM_RPB = 64 / KM_CPR;          // rows of it per 1 KB block
   // RMS: gain applied to A in the main loop, sums of squares, a row scale in
   // the epilogue; LN: additionally row sums and the mean term of the deferred
   // LayerNorm; SSF: A goes to the MFMAs unchanged (the gain is in B) and the
@@ -451,10 +457,12 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
 
   if constexpr (!C::F32) {
     // ================= bf16 main loop =================
-    const char* Abase = static_cast<const char*>(a->A) + (long long)m0 * lda * 2;
+    const char* Abase = C::AKM ? static_cast<const char*>(a->A) + (long long)m0 * 2
+                               : static_cast<const char*>(a->A) + (long long)m0 * lda * 2;
     const char* Bbase = C::BKN ? static_cast<const char*>(a->B) + (long long)n0 * 2
                                : static_cast<const char*>(a->B) + (long long)n0 * ldb * 2;
-    const long long a_ext0 = ((long long)(M - 1 - m0) * lda + K) * 2;
+    const long long a_ext0 = C::AKM ? ((long long)(K - 1) * lda + (M - m0)) * 2
+                                    : ((long long)(M - 1 - m0) * lda + K) * 2;
     const long long b_ext0 = C::BKN ? ((long long)(K - 1) * ldb + (N - n0)) * 2
                                     : ((long long)(N - 1 - n0) * ldb + K) * 2;
     // loader lane geometry: a 1 KB block q holds rows 8q .. 8q+7 of a K-major
@@ -474,6 +482,23 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
     // straight to LDS; the swizzled block layout is the same for both A targets
     auto load_a = [&](int kt, char* dst) {
       const int k0 = (kt_lo + kt) * 64;
+      if constexpr (C::AKM) {
+        // K rows of BM contiguous M values, 16-byte chunk c of row k at slot
+        // c ^ 2(k & 3) (rows past K read as zero); the same layout as an
+        // N-major W tile
+        const int km_row = lane / C::KM_CPR, km_slot = lane % C::KM_CPR;
+        const __amdgpu_buffer_rsrc_t ra =
+            make_rsrc(Abase + (long long)k0 * lda * 2, a_ext0 - (long long)k0 * lda * 2);
+#pragma unroll
+        for (int i = 0; i < C::A_BPW; ++i) {
+          const int q = wave + C::NW * i;
+          const int k = q * C::KM_RPB + km_row;
+          const int c = km_slot ^ (2 * (k & 3));
+          const uint32_t off = uint32_t(k) * uint32_t(lda * 2) + uint32_t(c * 16);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (LdsPtr)(dst + q * 1024), 16, (int)off, 0, 0, 0);
+        }
+        return;
+      }
       const __amdgpu_buffer_rsrc_t ra = make_rsrc(Abase + (long long)k0 * 2, a_ext0 - (long long)k0 * 2);
 #pragma unroll
       for (int i = 0; i < C::A_BPW; ++i) {
@@ -606,10 +631,24 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
     // MFMA operand read offsets (bytes within a stage)
     // X fragment (MFMA B operand): row wm*WTM + 32 mi + l32, logical chunk 2kk + hi;
     // the row base is a multiple of 32, so swz(row) = swz(l32)
-    int xa_off[4];
+    int xa_off[C::AKM ? MI : 4];
+    if constexpr (C::AKM) {
+      // M-major A tile: the transposing read of the W fragments below, with
+      // rows m of the tile in place of columns n
+      const int G = lane >> 4, s = lane & 15;
+      const int r = s >> 2;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-      xa_off[kk] = (wm * C::WTM + l32) * 128 + (((2 * kk + hi) ^ swz_l) * 16);
+      for (int mi = 0; mi < MI; ++mi) {
+        const int krow = 8 * (G >> 1) + r;
+        const int m = wm * C::WTM + 32 * mi + 16 * (G & 1) + 4 * (s & 3);
+        const int phys = (m >> 3) ^ (2 * r);
+        xa_off[mi] = krow * (BM * 2) + phys * 16 + (m & 7) * 2;
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        xa_off[kk] = (wm * C::WTM + l32) * 128 + (((2 * kk + hi) ^ swz_l) * 16);
+    }
     // W fragment (MFMA A operand)
     int wb_off[C::BKN ? NI : 4];
     if constexpr (C::BKN) {
@@ -633,8 +672,16 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
 
     auto read_frags = [&](const char* stage, int kk, bf16x8_t (&xf)[MI], bf16x8_t (&wf)[NI]) {
 #pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-        xf[mi] = *reinterpret_cast<const bf16x8_t*>(stage + xa_off[kk] + mi * 32 * 128);
+      for (int mi = 0; mi < MI; ++mi) {
+        if constexpr (C::AKM) {
+          const char* p = stage + xa_off[mi] + kk * 16 * (BM * 2);
+          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LdsI16x4*)(p));
+          const i16x4_t hv = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LdsI16x4*)(p + 4 * (BM * 2)));
+          xf[mi] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hv, 0, 1, 2, 3, 4, 5, 6, 7));
+        } else {
+          xf[mi] = *reinterpret_cast<const bf16x8_t*>(stage + xa_off[kk] + mi * 32 * 128);
+        }
+      }
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) {
         if constexpr (C::BKN) {
@@ -1322,16 +1369,22 @@ int launch_norms(const FusedArgs& args, int64_t nwg, int norm, hipStream_t s) {
 }
 
 template <int BM, int BN, int WM, int WN, bool F32>
-int launch_variants(const FusedArgs& args, int64_t nwg, bool bkn, int norm, hipStream_t s) {
+int launch_variants(const FusedArgs& args, int64_t nwg, bool bkn, int norm, bool akm, hipStream_t s) {
+  if constexpr (!F32) {
+    if (akm) {   // A stored [K x M]: no row norm (validated on the host)
+      return bkn ? launch_cfg<Cfg<BM, BN, WM, WN, F32, true, kNormNone, true>>(args, nwg, s)
+                 : launch_cfg<Cfg<BM, BN, WM, WN, F32, false, kNormNone, true>>(args, nwg, s);
+    }
+  }
   return bkn ? launch_norms<BM, BN, WM, WN, F32, true>(args, nwg, norm, s)
              : launch_norms<BM, BN, WM, WN, F32, false>(args, nwg, norm, s);
 }
 
 // one function per compiled tile configuration (defined in coda_fused_t*.hip)
-int launch_tile1(const FusedArgs& a, int64_t nwg, bool bkn, int norm, hipStream_t s);
-int launch_tile2(const FusedArgs& a, int64_t nwg, bool bkn, int norm, hipStream_t s);
-int launch_tile3(const FusedArgs& a, int64_t nwg, bool bkn, int norm, hipStream_t s);
-int launch_tile_f32(const FusedArgs& a, int64_t nwg, bool bkn, int norm, hipStream_t s);
+int launch_tile1(const FusedArgs& a, int64_t nwg, bool bkn, int norm, bool akm, hipStream_t s);
+int launch_tile2(const FusedArgs& a, int64_t nwg, bool bkn, int norm, bool akm, hipStream_t s);
+int launch_tile3(const FusedArgs& a, int64_t nwg, bool bkn, int norm, bool akm, hipStream_t s);
+int launch_tile_f32(const FusedArgs& a, int64_t nwg, bool bkn, int norm, bool akm, hipStream_t s);
 
 }  // namespace dev
 }  // namespace coda

@@ -187,6 +187,10 @@ int build_plan(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
     set_error("unknown B layout %d", d->b_layout);
     return CODA_ERR_INVALID_ARG;
   }
+  if ((d->a_layout != CODA_A_MK && d->a_layout != CODA_A_KM) || d->reserved1 != 0) {
+    set_error("unknown A layout %d (or reserved1 != 0)", d->a_layout);
+    return CODA_ERR_INVALID_ARG;
+  }
   if (d->n_ops < 0 || d->n_ops > CODA_MAX_OPS) {
     set_error("n_ops=%d outside 0..%d", d->n_ops, CODA_MAX_OPS);
     return CODA_ERR_INVALID_ARG;
@@ -202,6 +206,7 @@ int build_plan(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
   p->ab_dtype = d->ab_dtype;
   p->d_dtype = d->d_dtype;
   p->b_layout = d->b_layout;
+  p->a_layout = d->a_layout;
   p->M = M;
   p->N = N;
   p->K = K;
@@ -377,7 +382,12 @@ int build_plan(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
     set_error("N=%lld must be a multiple of 8 when B is stored [K x N]", (long long)N);
     return CODA_ERR_UNSUPPORTED;
   }
-  if (d->lda < K || d->ldb < (d->b_layout == CODA_B_KN ? N : K) || d->ldd < width) {
+  const bool akm = d->a_layout == CODA_A_KM;
+  if (akm && (M % 8 != 0 || d->ab_dtype != CODA_BF16 || p->has_norm)) {
+    set_error("A stored [K x M] needs M %% 8 == 0, bf16 operands and no RMS/LN_ROWSCALE");
+    return CODA_ERR_UNSUPPORTED;
+  }
+  if (d->lda < (akm ? M : K) || d->ldb < (d->b_layout == CODA_B_KN ? N : K) || d->ldd < width) {
     set_error("leading dimension too small (lda=%lld ldb=%lld ldd=%lld)", (long long)d->lda,
               (long long)d->ldb, (long long)d->ldd);
     return CODA_ERR_INVALID_ARG;
@@ -422,7 +432,7 @@ int build_plan(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
   if (check_pointers) {
     const size_t abs = dtype_size(d->ab_dtype), ds = dtype_size(d->d_dtype);
     Extent eD = matrix_extent(d->D, M, width, d->ldd, ds);
-    Extent eA = matrix_extent(A, M, K, d->lda, abs);
+    Extent eA = akm ? matrix_extent(A, K, M, d->lda, abs) : matrix_extent(A, M, K, d->lda, abs);
     Extent eB = d->b_layout == CODA_B_KN ? matrix_extent(B, K, N, d->ldb, abs)
                                          : matrix_extent(B, N, K, d->ldb, abs);
     if (overlap(eD, eA) || overlap(eD, eB)) {

@@ -48,7 +48,7 @@ struct Op {
 };
 
 struct Plan {
-  int ab_dtype, d_dtype, b_layout;
+  int ab_dtype, d_dtype, b_layout, a_layout;
   int64_t M, N, K, lda, ldb, ldd;
   int64_t out_width;
   const void* A;

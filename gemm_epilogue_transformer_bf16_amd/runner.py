@@ -72,17 +72,20 @@ class Call:
                  D: Optional[torch.Tensor] = None, d_dtype: Optional[torch.dtype] = None, tile: int = 0,
                  M: Optional[int] = None, N: Optional[int] = None, K: Optional[int] = None,
                  lda: Optional[int] = None, ldb: Optional[int] = None, flags: int = 0,
-                 fold_gain: bool = False):
+                 fold_gain: bool = False, a_layout: str = "MK"):
         self.A, self.B = A, B
-        self.M = A.shape[0] if M is None else M
-        self.K = A.shape[1] if K is None else K
+        # a_layout "KM": A is given as its [K x M] storage (the X of X^T dY)
+        akm = a_layout == "KM"
+        self.M = (A.shape[1] if akm else A.shape[0]) if M is None else M
+        self.K = (A.shape[0] if akm else A.shape[1]) if K is None else K
         if N is None:
             N = B.shape[1] if b_layout == "KN" else B.shape[0]
         self.N = N
         self.b_layout = b_layout
         self._keep: List[torch.Tensor] = []
         if lda is None:
-            lda = A.stride(0) if A.dim() == 2 and A.shape[0] > 0 and A.shape[1] > 0 else max((self.K + 7) // 8 * 8, 8)
+            inner_a = self.M if akm else self.K
+            lda = A.stride(0) if A.dim() == 2 and A.shape[0] > 0 and A.shape[1] > 0 else max((inner_a + 7) // 8 * 8, 8)
         if ldb is None:
             inner = self.N if b_layout == "KN" else self.K
             ldb = B.stride(0) if B.dim() == 2 and B.numel() > 0 else max((inner + 7) // 8 * 8, 8)
@@ -103,6 +106,7 @@ class Call:
         d.d_dtype = CODA_DT[D.dtype]
         d.b_layout = C.CODA_B_KN if b_layout == "KN" else C.CODA_B_NK
         d.lda = lda
+        d.a_layout = C.CODA_A_KM if akm else C.CODA_A_MK
         d.ldb = ldb
         d.ldd = D.stride(0) if D.dim() == 2 and D.shape[0] > 0 else max(width, 8)
         d.D = D.data_ptr() if D.numel() else None

@@ -23,7 +23,8 @@
  *
  * Conventions shared by every entry point
  * ---------------------------------------
- *  - All matrices are row-major.  A is [M x K] with leading dimension lda.
+ *  - All matrices are row-major.  A is [M x K] with leading dimension lda
+ *    (lda >= K), or, with a_layout CODA_A_KM, stored [K x M] (lda >= M).
  *    B is the logical [K x N] operand, stored either row-major [K x N]
  *    (CODA_B_KN, leading dimension ldb >= N) or row-major [N x K], i.e. the
  *    transpose of a [K x N] matrix (CODA_B_NK, ldb >= K).  D is
@@ -80,6 +81,14 @@ typedef enum {
 } coda_status;
 
 typedef enum { CODA_BF16 = 0, CODA_F32 = 1 } coda_dtype;
+
+typedef enum {
+  CODA_A_MK = 0,  /* A stored row-major [M x K] (the default)                    */
+  CODA_A_KM = 1   /* A stored row-major [K x M] and used transposed: the X^T of a
+                     weight gradient dW = X^T dY, X being [tokens x features] and
+                     tokens the contraction; bf16 only, no RMS/LN_ROWSCALE, and
+                     M % 8 == 0 (the survey's backward set)                      */
+} coda_a_layout;
 
 typedef enum {
   CODA_B_KN = 0,  /* B stored row-major [K x N]                                  */
@@ -164,6 +173,8 @@ typedef struct {
   size_t workspace_bytes;
   int32_t tile;         /* 0 = automatic tile choice; k > 0 forces tile config k    */
   int32_t flags;        /* 0, or CODA_FLAG_NO_SPLIT_K; other bits must be 0         */
+  int32_t a_layout;     /* coda_a_layout (0 = CODA_A_MK)                            */
+  int32_t reserved1;    /* must be 0                                                 */
   coda_op ops[CODA_MAX_OPS];
 } coda_epi_desc;
 

@@ -293,6 +293,24 @@ int main() {
     // the unfused sequence keeps column partials per chunk of rows
     EXPECT(coda_workspace_size(M, N, K, &e, 1) > coda_workspace_size(M, N, K, &d, 1));
   }
+  {  // A stored [K x M] (weight gradient): M % 8, lda >= M, bf16, no row norm
+    coda_epi_desc e = base_desc(N, K); e.a_layout = CODA_A_KM; e.lda = 304;
+    EXPECT(coda_validate(A, B, 304, N, K, &e, 0) == CODA_OK);
+    EXPECT(coda_validate(A, B, 300, N, K, &e, 0) == CODA_ERR_UNSUPPORTED);   // M % 8
+    coda_epi_desc f = e; f.lda = 296;
+    EXPECT(coda_validate(A, B, 304, N, K, &f, 0) == CODA_ERR_INVALID_ARG);   // lda < M
+    f = e; f.ab_dtype = CODA_F32; f.d_dtype = CODA_F32;
+    EXPECT(coda_validate(A, B, 304, N, K, &f, 0) == CODA_ERR_UNSUPPORTED);
+    f = e; f.n_ops = 1; f.ops[0].kind = CODA_OP_RMS_ROWSCALE; f.ops[0].in = P(0x40000000);
+    f.ops[0].in_dtype = CODA_BF16;
+    EXPECT(coda_validate(A, B, 304, N, K, &f, 0) == CODA_ERR_UNSUPPORTED);
+    f = e; f.a_layout = 2;
+    EXPECT(coda_validate(A, B, 304, N, K, &f, 0) == CODA_ERR_INVALID_ARG);
+    f = e; f.reserved1 = 1;
+    EXPECT(coda_validate(A, B, 304, N, K, &f, 0) == CODA_ERR_INVALID_ARG);
+    f = e; f.D = Pm(0x10000000 + 2 * 304 * 8);                               // D inside A's [K x M] extent
+    EXPECT(coda_validate(A, B, 304, N, K, &f, 0) == CODA_ERR_INVALID_ARG);
+  }
   {  // coda_fold_gain validation
     const void* g = P(0x40000000);
     EXPECT(coda::validate_fold_gain(B, 768, 3072, 3072, CODA_B_KN, CODA_BF16, g, Pm(0x70000000), 3072) == CODA_OK);

@@ -412,6 +412,24 @@ def test_column_reduction_of_a_backward_layer_is_the_bias_gradient():
     assert np.allclose(reds[0][2], fd, rtol=1e-6, atol=1e-8)
 
 
+def test_weight_gradient_is_the_transposed_product():
+    # y = x W: dL/dW for L = sum(dy * y) is x^T dy; the oracle's GEMM of the
+    # transposed storage against finite differences (pins which operand is
+    # transposed and that the contraction runs over the tokens)
+    rng = np.random.default_rng(14)
+    T, Fi, Fo = 7, 4, 3
+    x, dy, W = rng.standard_normal((T, Fi)), rng.standard_normal((T, Fo)), rng.standard_normal((Fi, Fo))
+    dW, _ = oracle.forward(x.T, dy, [], "KN")
+    h = 1e-6
+    fd = np.zeros((Fi, Fo))
+    for i in range(Fi):
+        for j in range(Fo):
+            E = np.zeros((Fi, Fo))
+            E[i, j] = h
+            fd[i, j] = (np.sum(dy * (x @ (W + E))) - np.sum(dy * (x @ (W - E)))) / (2 * h)
+    assert np.allclose(dW, fd, rtol=1e-6, atol=1e-8)
+
+
 def test_planted_column_sum_over_the_wrong_axis_is_caught(monkeypatch):
     real = oracle.apply_epilogue
 
