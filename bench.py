@@ -118,6 +118,84 @@ def cpu_baseline(spec, inputs, budget_s: float = 10.0):
     }
 
 
+def bench_weight_grad(args):
+    """dW_acc += X^T dY for the GPT-2-small MLP up-projection (X [8192 tokens x
+    768], dY [8192 x 3072], dW [768 x 3072], K = 8192 tokens): A stored [K x M]
+    and the accumulation into the gradient buffer fused as an in-place ADD_MAT."""
+    import torch
+    import oracle
+    import workloads as w
+    from gemm_epilogue_transformer_bf16_amd import coda, runner
+
+    T, Fi, Fo = 8192, 768, 3072
+    rng = np.random.default_rng(2001)
+    x = w.bf16_bits_from_f64(rng.standard_normal((T, Fi)))
+    dy = w.bf16_bits_from_f64(rng.standard_normal((T, Fo)) / np.sqrt(Fo))
+    acc = w.bf16_bits_from_f64(0.01 * rng.standard_normal((Fi, Fo)))
+    to_dev = lambda b: runner.storage_to_tensor(b, "bf16")
+    X, dY, ACC = to_dev(x), to_dev(dy), to_dev(acc)
+    call = runner.Call(X, dY, [("add_mat", {"mat": ACC, "beta": 1.0})], "KN", a_layout="KM", D=ACC,
+                       tile=args.tile)
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+
+    def timed(fn, n_warm, n):
+        def step():
+            if not args.no_flush:
+                flush.zero_()
+            s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s0.record()
+            coda.check(fn(), "launch")
+            s1.record()
+            return s0, s1
+        for _ in range(n_warm):
+            step()
+        torch.cuda.synchronize()
+        evs = [step() for _ in range(n)]
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in evs])
+
+    print("[bench] weight gradient: fused", file=sys.stderr, flush=True)
+    fused_ms = timed(call.fused, args.warmup, args.steps)
+    ms = float(fused_ms.mean())
+    unfused_ms = None
+    if not args.no_unfused:
+        print("[bench] weight gradient: unfused", file=sys.stderr, flush=True)
+        unfused_ms = float(timed(call.unfused, max(2, args.warmup // 2), args.steps).mean())
+    flops = 2.0 * T * Fi * Fo
+    tflops = flops / (ms * 1e-3) / 1e12
+    alg_bytes = 2.0 * (T * Fi + T * Fo + 2 * Fi * Fo)   # X, dY, the accumulator read and written
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        xs, dys, accs = (w.bf16_bits_to_f64(b) for b in (x, dy, acc))
+        rows = np.random.default_rng(0).permutation(Fi)[:192]
+        t0 = time.perf_counter()
+        oracle.forward(xs[:, rows].T, dys, [("add_mat", {"mat": accs[rows], "beta": 1.0})], "KN")
+        el = time.perf_counter() - t0
+        cpu = {"value": round(2.0 * T * len(rows) * Fo / el / 1e12, 5), "unit": "TFLOP/s",
+               "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+               "sample": f"{len(rows)} of {Fi} rows of dW (fp64 numpy: X^T dY + accumulator), {el:.1f} s"}
+    line = {
+        "metric": "fused GEMM+epilogue TFLOP/s, % bf16 MFMA peak; speedup vs unfused HIP",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "gpt2s_mlp_up weight gradient: dW_acc += X^T dY, X [8192 tokens x 768], "
+                               "dY [8192 x 3072], A stored [K x M], in-place accumulation, bf16",
+                   "M": Fi, "N": Fo, "K": T, "cache_flush_between_steps": not args.no_flush,
+                   "tile": coda.coda_selected_tile(Fi, Fo, T, call.desc)},
+        "pct_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "unfused_ms_per_step": None if unfused_ms is None else round(unfused_ms, 4),
+        "speedup_vs_unfused": None if unfused_ms is None else round(unfused_ms / ms, 3),
+        "effective_GBps": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -131,6 +209,8 @@ def main():
     ap.add_argument("--bias-grad", action="store_true",
                     help="GPT-2-medium backward layer (workload 5) with the bias gradient: a column sum of dH "
                          "appended to its epilogue")
+    ap.add_argument("--weight-grad", action="store_true",
+                    help="the GPT-2-small MLP up-projection's weight gradient, dW_acc += X^T dY, instead")
     ap.add_argument("--in-loop-gain", action="store_true",
                     help="time the RMSNorm gain applied to A in the main loop instead of folded into a copy of the "
                          "weights once (coda_fold_gain, outside the timed region; the default)")
@@ -152,6 +232,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.weight_grad:
+        bench_weight_grad(args)
+        return
 
     spec = w.get_config(args.workload)
     if args.bias_grad:
