@@ -16,6 +16,8 @@ dev::FusedArgs make_args(const Plan& p) {
   a.D = p.D;
   a.gamma = p.gamma;
   a.ln_u = p.ln_u;
+  a.row_ss = p.row_ss;
+  a.row_ss_stride = p.row_ss_stride;
   a.lda = p.lda;
   a.ldb = p.ldb;
   a.ldd = p.ldd;
@@ -68,6 +70,7 @@ int launch_args(const Plan& p, const dev::FusedArgs& a, hipStream_t stream) {
   const bool bkn = p.b_layout == CODA_B_KN;
   const bool akm = p.a_layout == CODA_A_KM;
   const int norm = p.has_ln      ? dev::kNormLn
+                   : p.row_ss    ? dev::kNormRmsGiven
                    : p.gain_in_b ? dev::kNormRmsB
                    : p.has_norm  ? dev::kNormRms
                                  : dev::kNormNone;
@@ -104,6 +107,7 @@ int launch_plain_gemm(const Plan& p, const void* A, int64_t lda, void* out, int6
   q.gain_in_b = false;
   q.gamma = nullptr;
   q.ln_u = nullptr;
+  q.row_ss = nullptr;
   q.n_ops = 0;
   q.n_red = 0;
   q.n_colred = 0;

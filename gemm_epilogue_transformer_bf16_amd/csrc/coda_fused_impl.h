@@ -85,6 +85,9 @@ typedef __attribute__((address_space(3))) i16x4_t LdsI16x4;
 // deferred row norm in front of the GEMM: none, RMSNorm (gain applied to A in
 // the main loop), LayerNorm, RMSNorm with the gain already folded into B's rows
 constexpr int kNormNone = 0, kNormRms = 1, kNormLn = 2, kNormRmsB = 3;
+// RMSNorm with the gain in B and the row sums of squares given (a cross-layer
+// chain): the main loop is the plain GEMM
+constexpr int kNormRmsGiven = 4;
 
 template <int BM_, int BN_, int WM_, int WN_, bool F32_, bool BKN_, int NORM_, bool AKM_ = false>
 struct Cfg {
@@ -102,6 +105,7 @@ struct Cfg {
   // sums of squares come from the X fragments the MFMAs read
   static constexpr bool RMS = NORM_ == kNormRms || NORM_ == kNormLn, LN = NORM_ == kNormLn;
   static constexpr bool SSF = NORM_ == kNormRmsB;
+  static constexpr bool GIVEN = NORM_ == kNormRmsGiven;
   static constexpr int NW = WM * WN;
   static constexpr int NT = 64 * NW;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -1100,7 +1104,14 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
   };
   int* flag = reinterpret_cast<int*>(smem1 + C::EPI_FLAG_OFF);
 
-  if constexpr (C::SSF && !C::F32) {
+  if constexpr (C::GIVEN) {
+    for (int t = tid; t < BM; t += C::NT) {
+      const int row = m0 + t;
+      const float v = row < M ? a->row_ss[(long long)row * a->row_ss_stride] : 0.0f;
+      row_factors(t, v, 0.0f);
+    }
+    __syncthreads();
+  } else if constexpr (C::SSF && !C::F32) {
     for (int t = tid; t < BM; t += C::NT) {
       float v = smem_ss[t];
 #pragma unroll
@@ -1209,7 +1220,7 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
         const float s = rinv[ch.mloc[j]], mr = rmu[ch.mloc[j]];
 #pragma unroll
         for (int e = 0; e < 8; ++e) ch.v[j][e] = fmaf(ch.v[j][e], s, -mr * uv[e]);
-      } else if constexpr (C::RMS || C::SSF) {
+      } else if constexpr (C::RMS || C::SSF || C::GIVEN) {
         const float s = rinv[ch.mloc[j]];
 #pragma unroll
         for (int e = 0; e < 8; ++e) ch.v[j][e] *= s;
@@ -1364,6 +1375,7 @@ int launch_norms(const FusedArgs& args, int64_t nwg, int norm, hipStream_t s) {
     case kNormRms: return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormRms>>(args, nwg, s);
     case kNormLn: return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormLn>>(args, nwg, s);
     case kNormRmsB: return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormRmsB>>(args, nwg, s);
+    case kNormRmsGiven: return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormRmsGiven>>(args, nwg, s);
     default: return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormNone>>(args, nwg, s);
   }
 }

@@ -233,7 +233,7 @@ int build_plan(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
       return CODA_ERR_INVALID_ARG;
     }
     const bool ln = o.kind == CODA_OP_LN_ROWSCALE;
-    if (!ln && o.in2) {
+    if (!ln && o.kind != CODA_OP_RMS_ROWSCALE && o.in2) {
       set_error("op %d: in2 must be NULL", i);
       return CODA_ERR_INVALID_ARG;
     }
@@ -271,11 +271,23 @@ int build_plan(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
           return CODA_ERR_UNSUPPORTED;
         }
       }
+      if (!ln && o.in2) {   // given row sums of squares: the gain must be in B
+        if (o.in) {
+          set_error("RMS_ROWSCALE with given row sums of squares (in2) needs the gain folded into B (in = NULL)");
+          return CODA_ERR_UNSUPPORTED;
+        }
+        if (o.ld < 0 || !aligned(o.in2, 4)) {
+          set_error("RMS_ROWSCALE row sums of squares: ld >= 0 (0 = 1) and 4-byte alignment");
+          return CODA_ERR_INVALID_ARG;
+        }
+        p->row_ss = static_cast<const float*>(o.in2);
+        p->row_ss_stride = o.ld > 0 ? o.ld : 1;
+      }
       p->has_norm = true;
       p->has_ln = ln;
       p->gain_in_b = folded;
       p->gamma = o.in;
-      p->ln_u = static_cast<const float*>(o.in2);
+      p->ln_u = ln ? static_cast<const float*>(o.in2) : nullptr;
       p->eps = o.scalar;
       continue;
     }

@@ -59,6 +59,8 @@ struct Plan {
   bool gain_in_b;            // RMS_ROWSCALE with gamma NULL: the gain is folded into B
   const void* gamma;
   const float* ln_u;         // LN_ROWSCALE: u = gamma^T B [N]
+  const float* row_ss;       // RMS_ROWSCALE with given row sums of squares (stride row_ss_stride)
+  int64_t row_ss_stride;
   float eps;
   int n_ops;                 // ops after the norm op
   Op ops[CODA_MAX_OPS];

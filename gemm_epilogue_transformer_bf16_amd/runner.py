@@ -132,6 +132,12 @@ class Call:
                 o.scalar = float(args["eps"])
             if name == "ln_rowscale":
                 o.in2 = args["u"].data_ptr()
+            if name == "rms_rowscale" and args.get("row_ss") is not None:
+                # given row sums of squares: column `row_ss_col` of a 2-D fp32 tensor
+                t = args["row_ss"]
+                self._keep.append(t)
+                o.in2 = t.data_ptr() + 4 * int(args.get("row_ss_col", 0))
+                o.ld = t.stride(0)
             if name in ("row_sum", "row_sumsq", "row_mean", "col_sum", "col_sumsq"):
                 out = args["out"]
                 self._keep.append(out)

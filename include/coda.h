@@ -110,8 +110,12 @@ typedef enum {
                                  to the GEMM.  in = NULL: the gain is already in the
                                  rows of B (B = diag(gamma) W, see coda_fold_gain), A
                                  is fed unchanged and the row sums of squares come from
-                                 the A fragments the matrix cores read.  Must be the
-                                 first op, at most once, and needs K > 0.             */
+                                 the A fragments the matrix cores read.  With in = NULL
+                                 and in2 != NULL, the row sums of squares are inputs:
+                                 in2 = fp32 sum_k A[i,k]^2 at in2[i*ld] (ld >= 1), e.g.
+                                 the ROW_SUMSQ output of the layer that produced A, and
+                                 the main loop is the plain GEMM (a cross-layer chain).
+                                 Must be the first op, at most once, and needs K > 0. */
   /* accumulation (agentlenshq.com page, "How it works": accumulation) */
   CODA_OP_ADD_COL = 4,        /* v += in[j]          (bias)                          */
   CODA_OP_ADD_ROW = 5,        /* v += in[i]                                          */
@@ -159,7 +163,8 @@ typedef struct {
   int32_t reserved0;    /* must be 0                                                 */
   void* out;            /* reductions: fp32 output (device)                          */
   int64_t out_stride;   /* reductions: element stride between rows of `out`, >= 1   */
-  const void* in2;      /* LN_ROWSCALE: fp32 u [N] (device); NULL for every other op */
+  const void* in2;      /* LN_ROWSCALE: fp32 u [N]; RMS_ROWSCALE: optional fp32 row
+                           sums of squares [M] (stride ld); NULL for every other op */
 } coda_op;
 
 typedef struct {

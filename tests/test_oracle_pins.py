@@ -412,6 +412,16 @@ def test_column_reduction_of_a_backward_layer_is_the_bias_gradient():
     assert np.allclose(reds[0][2], fd, rtol=1e-6, atol=1e-8)
 
 
+def test_chained_row_sumsq_is_the_rms_of_the_next_layer():
+    # a layer's ROW_SUMSQ output, divided by the width, is the mean square the
+    # next layer's RMS normalisation of that output needs (the cross-layer chain)
+    rng = np.random.default_rng(15)
+    A, B = rng.standard_normal((5, 6)), rng.standard_normal((6, 8))
+    D1, reds = oracle.forward(A, B, [("add_col", {"vec": rng.standard_normal(8)}), ("row_sumsq", {})], "KN")
+    eps = 1e-6
+    assert np.allclose(oracle.rms(D1, eps), np.sqrt(reds[0][2] / D1.shape[1] + eps), rtol=1e-14)
+
+
 def test_weight_gradient_is_the_transposed_product():
     # y = x W: dL/dW for L = sum(dy * y) is x^T dy; the oracle's GEMM of the
     # transposed storage against finite differences (pins which operand is
