@@ -209,6 +209,10 @@ def main():
     ap.add_argument("--bias-grad", action="store_true",
                     help="GPT-2-medium backward layer (workload 5) with the bias gradient: a column sum of dH "
                          "appended to its epilogue")
+    ap.add_argument("--given-row-sumsq", action="store_true",
+                    help="RMS layers: the row sums of squares of A are given (as the previous layer's ROW_SUMSQ "
+                         "output provides them in a chain of layers; computed here before timing) and the gain is "
+                         "folded, so the main loop is the plain GEMM")
     ap.add_argument("--weight-grad", action="store_true",
                     help="the GPT-2-small MLP up-projection's weight gradient, dW_acc += X^T dY, instead")
     ap.add_argument("--in-loop-gain", action="store_true",
@@ -228,6 +232,7 @@ def main():
     import torch
     import workloads as w
     from gemm_epilogue_transformer_bf16_amd import coda, runner
+    TORCH_DT_OF = runner.TORCH_DT
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -247,8 +252,19 @@ def main():
     print(f"[bench] generating {spec.name} inputs", file=sys.stderr, flush=True)
     inputs = w.make_inputs(spec)
     has_rms = any(op == "rms_rowscale" for op, _ in spec.program)
-    fold = has_rms and not args.in_loop_gain
+    fold = has_rms and (not args.in_loop_gain or args.given_row_sumsq)
     call = runner.WorkloadCall(spec, inputs, tile=args.tile, fold_gain=fold)
+    if args.given_row_sumsq:
+        if not has_rms:
+            print("--given-row-sumsq applies to layers with an RMSNorm", file=sys.stderr)
+            sys.exit(2)
+        # setup outside the timed region: the row sums of squares a previous
+        # layer's ROW_SUMSQ epilogue would have written
+        A = call.tensors[spec.a_name]
+        row_ss = (A.float() * A.float()).sum(dim=1, keepdim=True).contiguous()
+        prog = [(n, dict(a)) for n, a in call.ops]
+        prog[0][1]["row_ss"] = row_ss
+        call = runner.Call(A, call.B, prog, spec.b_layout, d_dtype=TORCH_DT_OF[spec.d_dtype], tile=args.tile)
     flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
     if args.copy_calibration:
@@ -293,7 +309,7 @@ def main():
 
     # the other placement of the RMSNorm gain, for comparison (not the headline)
     other_ms = None
-    if has_rms and not args.no_unfused:
+    if has_rms and not args.no_unfused and not args.given_row_sumsq:
         print("[bench] fused, other gain placement", file=sys.stderr, flush=True)
         other = runner.WorkloadCall(spec, inputs, tile=args.tile, fold_gain=not fold)
         for _ in range(max(2, args.warmup // 2)):
@@ -336,6 +352,7 @@ def main():
             "M": spec.M, "N": spec.N, "K": spec.K,
             "cache_flush_between_steps": not args.no_flush,
             "gain_folded_into_weights": bool(fold),
+            "row_sumsq_given": bool(args.given_row_sumsq),
             "tile": tile_used,
         },
         "pct_peak": round(100.0 * tflops / peak, 2),

@@ -104,13 +104,14 @@ def bench_profiles(out_dir: str, kt_db: str, fetch_db: str, write_db: str, comma
         "# rocprofv3 kernel trace of bench.py (LLaMA-7B SwiGLU gate/up: M=4096, N=22016, K=4096)",
         f"# command: {command}",
         "#   (runs: rocprofv3 --kernel-trace --stats -- python3 bench.py --steps 10 --warmup 20 --no-cpu-baseline)",
-        "# fused kernel: Cfg<256,256,2,4,fp32 operands=false,B[KxN]=true,norm=3 (RMS, gain folded into B)>; the",
-        "# <..., 1> kernel is the same layer with the gain applied to A in the main loop (timed for comparison),",
-        "# the <..., 0> kernel the plain GEMM of the unfused sequence, ew_kernel / rownorm_kernel its other passes;",
+        "# fused kernel: Cfg<256,256,2,4,fp32 operands=false,B[KxN]=true,norm=3 (RMS, gain folded into B),A[KxM]=false>;",
+        "# the <..., 1, false> kernel is the same layer with the gain applied to A in the main loop (timed for",
+        "# comparison), the <..., 0, false> kernel the plain GEMM of the unfused sequence, ew_kernel /",
+        "# rownorm_kernel its other passes;",
         "# FillFunctor<float> is the 512 MiB cache flush between steps; averages include the warm-up steps.",
         f"# kernel source hash: {khash}",
     ]
-    fused = "false, true, 3>"   # Cfg<..., fp32 operands, B stored [K x N], norm>: RMS, gain folded into B
+    fused = "false, true, 3, false>"   # Cfg<..., fp32 operands, B stored [K x N], norm 3 (RMS, gain in B), A stored [K x M]>
     timed = "# timed steps: " + last_dispatches(kt_db, fused, 10)
     with open(os.path.join(out_dir, "fused_llama7b_gate_up_kernel_trace.txt"), "w") as f:
         f.write("\n".join(header) + "\n" + trace(kt_db) + "\n" + timed + "\n")

@@ -20,7 +20,7 @@ timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE -d "$OUT/write" -o p -- \
 echo "write pass done"
 cd "$R"
 python3 -m gemm_epilogue_transformer_bf16_amd.prof_summary trace "$OUT"/kt/*.db > "$OUT/trace.txt"
-python3 -m gemm_epilogue_transformer_bf16_amd.prof_summary traffic "$OUT"/fetch/*.db "$OUT"/write/*.db "false, true, 3>" 268435456 > "$OUT/traffic.json"
+python3 -m gemm_epilogue_transformer_bf16_amd.prof_summary traffic "$OUT"/fetch/*.db "$OUT"/write/*.db "false, true, 3, false>" 268435456 > "$OUT/traffic.json"
 python3 -m gemm_epilogue_transformer_bf16_amd.prof_summary bench-profiles "$OUT" "$(ls "$OUT"/kt/*.db)" \
   "$(ls "$OUT"/fetch/*.db)" "$(ls "$OUT"/write/*.db)" "bash gemm_epilogue_transformer_bf16_amd/profile_bench.sh <out-dir>"
 echo "summaries done"
