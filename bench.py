@@ -216,8 +216,8 @@ def main():
     ap.add_argument("--weight-grad", action="store_true",
                     help="the GPT-2-small MLP up-projection's weight gradient, dW_acc += X^T dY, instead")
     ap.add_argument("--in-loop-gain", action="store_true",
-                    help="time the RMSNorm gain applied to A in the main loop instead of folded into a copy of the "
-                         "weights once (coda_fold_gain, outside the timed region; the default)")
+                    help="time the RMSNorm / LayerNorm gain applied to A in the main loop instead of folded into a "
+                         "copy of the weights once (coda_fold_gain, outside the timed region; the default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unfused", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -252,7 +252,8 @@ def main():
     print(f"[bench] generating {spec.name} inputs", file=sys.stderr, flush=True)
     inputs = w.make_inputs(spec)
     has_rms = any(op == "rms_rowscale" for op, _ in spec.program)
-    fold = has_rms and (not args.in_loop_gain or args.given_row_sumsq)
+    has_norm = has_rms or any(op == "ln_rowscale" for op, _ in spec.program)
+    fold = has_norm and (not args.in_loop_gain or args.given_row_sumsq)
     call = runner.WorkloadCall(spec, inputs, tile=args.tile, fold_gain=fold)
     if args.given_row_sumsq:
         if not has_rms:
@@ -309,7 +310,7 @@ def main():
 
     # the other placement of the RMSNorm gain, for comparison (not the headline)
     other_ms = None
-    if has_rms and not args.no_unfused and not args.given_row_sumsq:
+    if has_norm and not args.no_unfused and not args.given_row_sumsq:
         print("[bench] fused, other gain placement", file=sys.stderr, flush=True)
         other = runner.WorkloadCall(spec, inputs, tile=args.tile, fold_gain=not fold)
         for _ in range(max(2, args.warmup // 2)):

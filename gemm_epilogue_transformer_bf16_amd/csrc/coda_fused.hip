@@ -69,7 +69,7 @@ int launch_args(const Plan& p, const dev::FusedArgs& a, hipStream_t stream) {
   const int64_t nwg = p.full_tiles + p.split_tiles * p.split_s;
   const bool bkn = p.b_layout == CODA_B_KN;
   const bool akm = p.a_layout == CODA_A_KM;
-  const int norm = p.has_ln      ? dev::kNormLn
+  const int norm = p.has_ln      ? (p.gain_in_b ? dev::kNormLnB : dev::kNormLn)
                    : p.row_ss    ? dev::kNormRmsGiven
                    : p.gain_in_b ? dev::kNormRmsB
                    : p.has_norm  ? dev::kNormRms

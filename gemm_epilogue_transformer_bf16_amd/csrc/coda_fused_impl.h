@@ -88,6 +88,9 @@ constexpr int kNormNone = 0, kNormRms = 1, kNormLn = 2, kNormRmsB = 3;
 // RMSNorm with the gain in B and the row sums of squares given (a cross-layer
 // chain): the main loop is the plain GEMM
 constexpr int kNormRmsGiven = 4;
+// LayerNorm with the gain folded into B: row sums and sums of squares (about a
+// per-row shift) from the X fragments, like kNormRmsB
+constexpr int kNormLnB = 5;
 
 template <int BM_, int BN_, int WM_, int WN_, bool F32_, bool BKN_, int NORM_, bool AKM_ = false>
 struct Cfg {
@@ -104,7 +107,9 @@ struct Cfg {
   // LayerNorm; SSF: A goes to the MFMAs unchanged (the gain is in B) and the
   // sums of squares come from the X fragments the MFMAs read
   static constexpr bool RMS = NORM_ == kNormRms || NORM_ == kNormLn, LN = NORM_ == kNormLn;
-  static constexpr bool SSF = NORM_ == kNormRmsB;
+  static constexpr bool LNF = NORM_ == kNormLnB;
+  static constexpr bool SSF = NORM_ == kNormRmsB || LNF;   // sums from the X fragments
+  static constexpr bool LNE = LN || LNF;                   // LayerNorm epilogue
   static constexpr bool GIVEN = NORM_ == kNormRmsGiven;
   static constexpr int NW = WM * WN;
   static constexpr int NT = 64 * NW;
@@ -153,7 +158,8 @@ struct Cfg {
   // converted (gain, bf16 rounding, sum of squares) from there into the stage
   static constexpr int RAW_BYTES = (RMS && !F32) ? A_BYTES : 16;
   // SSF: per-row partial sums of squares, one row of BM per wave column
-  static constexpr int SS_BYTES = (SSF && !F32) ? WN * BM * 4 : 16;
+  // (LNF: then the row sums [WN][BM] and the per-row shift [BM])
+  static constexpr int SS_BYTES = (SSF && !F32) ? (LNF ? 2 * WN + 1 : WN) * BM * 4 : 16;
   // (arrays a variant never touches are dropped by the compiler: the raw A array
   // without RMS, the sums array without SSF, the 256-byte warm-up word with RMS)
   static_assert(ARR0_BYTES + ARR1_BYTES + (RMS ? RAW_BYTES : 0) + (SSF ? SS_BYTES : 0) + (RMS ? 0 : 256) <=
@@ -709,14 +715,19 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
     // the work has no branch and can sit between the slice's MFMAs; the sum
     // goes to ss[kk * (MI / WN) + t].
     static_assert(C::F32 || !C::SSF || MI % C::WN == 0, "row blocks must split over the wave columns");
+    static_assert(C::F32 || !C::LNF || NSS >= MI, "one shift per row block");
     const int wn_s = __builtin_amdgcn_readfirstlane(wn);
-    auto sumsq_frags = [&](auto kkc, const bf16x8_t (&xf)[MI]) {
+    // LNF: the sums are of x - s, s the row's first element (sh[mi], taken from
+    // the first slice of the first K step), over the K indices below K only.
+    auto sumsq_frags = [&](auto kkc, const bf16x8_t (&xf)[MI], int k0) {
       constexpr int kk = decltype(kkc)::value;
       constexpr int TPW = MI / C::WN;
       const int sel = (wn_s - kk + 4 * C::WN) % C::WN;   // wave-uniform
+      const bool kin = k0 + 16 * kk + 8 * hi < K;
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
         u32x4_t v = __builtin_bit_cast(u32x4_t, xf[C::WN * t]);
+        uint32_t shb = __float_as_uint(sh[C::WN * t]);
 #pragma unroll
         for (int c = 1; c < C::WN; ++c) {
           // a bitwise select on a wave-uniform mask (indexing the fragment
@@ -725,22 +736,34 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
           const u32x4_t o = __builtin_bit_cast(u32x4_t, xf[C::WN * t + c]);
 #pragma unroll
           for (int w = 0; w < 4; ++w) v[w] = (o[w] & m) | (v[w] & ~m);
+          if constexpr (C::LNF) shb = (__float_as_uint(sh[C::WN * t + c]) & m) | (shb & ~m);
         }
+        const float s0 = (C::LNF && kin) ? __uint_as_float(shb) : 0.0f;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          const float lo = bf16_lo(v[w]), hv = bf16_hi(v[w]);
+          const float lo = bf16_lo(v[w]) - s0, hv = bf16_hi(v[w]) - s0;
           ss[kk * TPW + t] = fmaf(lo, lo, ss[kk * TPW + t]);
           ss[kk * TPW + t] = fmaf(hv, hv, ss[kk * TPW + t]);
+          if constexpr (C::LNF) sx[kk * TPW + t] += lo + hv;
         }
-        // keeps the sum computed inside this slice's scheduling region (the
+        // keeps the sums computed inside this slice's scheduling region (the
         // arithmetic would otherwise be sunk past the MFMAs of the whole step)
         asm volatile("" ::"v"(ss[kk * TPW + t]));
+        if constexpr (C::LNF) asm volatile("" ::"v"(sx[kk * TPW + t]));
       }
     };
 
-    auto compute = [&](const char* stage) {
+    auto compute = [&](const char* stage, int kt) {
       bf16x8_t xf[2][MI], wf[2][NI];
       read_frags(stage, 0, xf[0], wf[0]);
+      if constexpr (C::LNF) {
+        if (kt == 0) {   // the row's first element: lane l32 (lower half) holds K indices 0..7
+#pragma unroll
+          for (int mi = 0; mi < MI; ++mi)
+            sh[mi] = __shfl(bf16_lo(__builtin_bit_cast(u32x4_t, xf[0][mi])[0]), l32);
+        }
+      }
+      const int k0 = (kt_lo + kt) * 64;
       static_for<0, 4>([&](auto kkc) {
         constexpr int kk = decltype(kkc)::value;
         // the next step's fragment reads are issued before this step's MFMAs
@@ -754,7 +777,7 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
             acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[kk & 1][ni], xf[kk & 1][mi], acc[mi][ni], 0, 0, 0);
         if constexpr (C::SSF) {
           // the slice's squares between its MFMAs: one MFMA, then up to 4 VALU
-          sumsq_frags(kkc, xf[kk & 1]);
+          sumsq_frags(kkc, xf[kk & 1], k0);
 #pragma unroll
           for (int q = 0; q < MI * NI; ++q) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -810,7 +833,7 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
       if constexpr (C::RMS) {
         if (more && convert_first) convert_phase(kt, nxt);
       }
-      compute(cur);
+      compute(cur, kt);
       if constexpr (C::RMS) {
         if (more && !convert_first) convert_phase(kt, nxt);
       }
@@ -841,9 +864,13 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
       // the WN rows add up to the whole sum
       constexpr int TPW = MI / C::WN;
       float* col = smem_ss + wn * BM + wm * C::WTM + l32;
+      float* colx = col + C::WN * BM;   // LNF: row sums
       if (hi == 0) {
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi) col[32 * mi] = 0.0f;
+        for (int mi = 0; mi < MI; ++mi) {
+          col[32 * mi] = 0.0f;
+          if constexpr (C::LNF) colx[32 * mi] = 0.0f;
+        }
       }
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
@@ -852,7 +879,17 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
           const float v = ss[kk * TPW + t] + __shfl_xor(ss[kk * TPW + t], 32);
           const int mi = (wn - kk + 4 * C::WN) % C::WN + C::WN * t;
           if (hi == 0) col[32 * mi] += v;
+          if constexpr (C::LNF) {
+            const float u = sx[kk * TPW + t] + __shfl_xor(sx[kk * TPW + t], 32);
+            if (hi == 0) colx[32 * mi] += u;
+          }
         }
+      if constexpr (C::LNF) {   // the shifts, once per row (wave column 0)
+        if (wn == 0 && hi == 0) {
+#pragma unroll
+          for (int mi = 0; mi < MI; ++mi) smem_ss[2 * C::WN * BM + wm * C::WTM + 32 * mi + l32] = sh[mi];
+        }
+      }
     }
     __syncthreads();
   } else {
@@ -984,7 +1021,7 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
   // out and come back as agent-scope atomic accesses, which are coherent across
   // the XCDs' L2 caches; waiting for the stores to complete before the count
   // publishes them without writing back or invalidating a whole L2.
-  if constexpr (!C::F32 && !C::LN) {   // LN tiles are never split
+  if constexpr (!C::F32 && !C::LNE) {   // LN tiles are never split
     if (split >= 0) {
       const int S = a->split_s;
       constexpr int NG = MI * NI * 8;   // pairs of accumulator registers per thread
@@ -1091,13 +1128,15 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
   float* colp = reinterpret_cast<float*>(smem1 + C::EPI_COL_OFF);
   // row factors from the sums: RMS 1/sqrt(ss/K + eps); LN rstd = 1/sqrt(var + eps)
   // with mean m = sx/K and var = ss/K - m^2 (of the shifted values), and m * rstd
-  auto row_factors = [&](int row, float v, float s) {
-    if constexpr (C::LN) {
+  // (LNF: the accumulators hold the unshifted product, so the mean term is
+  // (shift + m) * rstd)
+  auto row_factors = [&](int row, float v, float s, float shift) {
+    if constexpr (C::LNE) {
       const float m = s / float(K);
       const float var = fmaxf(v / float(K) - m * m, 0.0f);
       const float r = 1.0f / sqrtf(var + a->eps);
       rinv[row] = r;
-      rmu[row] = m * r;
+      rmu[row] = (shift + m) * r;
     } else {
       rinv[row] = 1.0f / sqrtf(v / float(K) + a->eps);
     }
@@ -1108,15 +1147,20 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
     for (int t = tid; t < BM; t += C::NT) {
       const int row = m0 + t;
       const float v = row < M ? a->row_ss[(long long)row * a->row_ss_stride] : 0.0f;
-      row_factors(t, v, 0.0f);
+      row_factors(t, v, 0.0f, 0.0f);
     }
     __syncthreads();
   } else if constexpr (C::SSF && !C::F32) {
     for (int t = tid; t < BM; t += C::NT) {
-      float v = smem_ss[t];
+      float v = smem_ss[t], s = 0.0f, shift = 0.0f;
 #pragma unroll
       for (int w = 1; w < C::WN; ++w) v += smem_ss[w * BM + t];
-      row_factors(t, v, 0.0f);
+      if constexpr (C::LNF) {
+#pragma unroll
+        for (int w = 0; w < C::WN; ++w) s += smem_ss[(C::WN + w) * BM + t];
+        shift = smem_ss[2 * C::WN * BM + t];
+      }
+      row_factors(t, v, s, shift);
     }
     __syncthreads();
   } else if constexpr (C::RMS || C::SSF) {
@@ -1133,7 +1177,7 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
           s += __shfl_xor(s, 2);
           s += __shfl_xor(s, 4);
         }
-        if ((lane & 7) == 0) row_factors(8 * (wave + C::NW * i) + (lane >> 3), v, s);
+        if ((lane & 7) == 0) row_factors(8 * (wave + C::NW * i) + (lane >> 3), v, s, 0.0f);
       }
     } else {
       constexpr int KCH = BK / 4;
@@ -1145,7 +1189,7 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
           v += __shfl_xor(v, off);
           if constexpr (C::LN) s += __shfl_xor(s, off);
         }
-        if (tid % KCH == 0) row_factors(tid / KCH + i * (C::NT / KCH), v, s);
+        if (tid % KCH == 0) row_factors(tid / KCH + i * (C::NT / KCH), v, s, 0.0f);
       }
     }
     __syncthreads();
@@ -1178,7 +1222,7 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
   if (pf_op >= 0) prefetch(0, pf_buf[0]);
   // LN: u[j] for the lane's 8 columns (the same in every block)
   float uv[8];
-  if constexpr (C::LN) load_cols<false>(a->ln_u, CODA_F32, n0 + wn * C::WTN + 8 * (lane % C::CPR), N, uv);
+  if constexpr (C::LNE) load_cols<false>(a->ln_u, CODA_F32, n0 + wn * C::WTN + 8 * (lane % C::CPR), N, uv);
 
   static_for<0, MI>([&](auto mic) {
     constexpr int mi = decltype(mic)::value;
@@ -1216,7 +1260,7 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
         ch.v[j][e] = lo[e];
         ch.v[j][4 + e] = hv[e];
       }
-      if constexpr (C::LN) {
+      if constexpr (C::LNE) {
         const float s = rinv[ch.mloc[j]], mr = rmu[ch.mloc[j]];
 #pragma unroll
         for (int e = 0; e < 8; ++e) ch.v[j][e] = fmaf(ch.v[j][e], s, -mr * uv[e]);
@@ -1376,6 +1420,7 @@ int launch_norms(const FusedArgs& args, int64_t nwg, int norm, hipStream_t s) {
     case kNormLn: return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormLn>>(args, nwg, s);
     case kNormRmsB: return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormRmsB>>(args, nwg, s);
     case kNormRmsGiven: return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormRmsGiven>>(args, nwg, s);
+    case kNormLnB: return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormLnB>>(args, nwg, s);
     default: return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormNone>>(args, nwg, s);
   }
 }

@@ -247,8 +247,8 @@ int build_plan(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
         set_error("%s needs K > 0", name);
         return CODA_ERR_INVALID_ARG;
       }
-      // RMS_ROWSCALE may leave gamma NULL: the gain is then already in B's rows
-      const bool folded = !ln && !o.in;
+      // gamma NULL: the gain is already in B's rows (coda_fold_gain)
+      const bool folded = !o.in;
       if (!folded && (!o.in || o.in_dtype != d->ab_dtype)) {
         set_error("%s needs gamma[K] in the A/B dtype", name);
         return CODA_ERR_INVALID_ARG;

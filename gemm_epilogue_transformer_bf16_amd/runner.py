@@ -89,7 +89,11 @@ class Call:
         if ldb is None:
             inner = self.N if b_layout == "KN" else self.K
             ldb = B.stride(0) if B.dim() == 2 and B.numel() > 0 else max((inner + 7) // 8 * 8, 8)
-        self.ops = self._expand_layernorm(list(ops), B, ldb)
+        if fold_gain and ops and ops[0][0] == "ln_rowscale":
+            B, ldb = self._fold_layernorm(B, ldb, list(ops))
+            self.B = B
+        else:
+            self.ops = self._expand_layernorm(list(ops), B, ldb)
         if fold_gain:
             B, ldb = self._fold_gain(B, ldb)
             self.B = B
@@ -174,6 +178,39 @@ class Call:
         if c is not None:
             out.append(("add_col", {"vec": c}))
         return out + list(ops[1:])
+
+    def _fold_layernorm(self, B: torch.Tensor, ldb: int, ops):
+        """ln_rowscale(gamma, beta) on B -> LN_ROWSCALE(NULL, u') on B' = diag(gamma) B
+        with u' the column sums of B' and, with beta, ADD_COL(beta^T B)."""
+        args = dict(ops[0][1])
+        gamma = args["gamma"]
+        layout = C.CODA_B_KN if self.b_layout == "KN" else C.CODA_B_NK
+        Bf = torch.empty_like(B)
+        ldo = Bf.stride(0) if Bf.dim() == 2 and Bf.numel() else ldb
+        self._keep += [gamma, B]
+        st = C.coda_fold_gain(B.data_ptr() if B.numel() else None, self.K, self.N, ldb, layout, CODA_DT[B.dtype],
+                              gamma.data_ptr() if gamma.numel() else None, Bf.data_ptr() if Bf.numel() else None,
+                              ldo, current_stream_ptr())
+        C.check(st, "coda_fold_gain")
+        ones = torch.ones(max(self.K, 1), dtype=B.dtype, device=B.device)
+        u = torch.empty(max(self.N, 1), dtype=torch.float32, device=B.device)
+        self._keep += [ones, u]
+        st = C.coda_ln_fold(Bf.data_ptr() if Bf.numel() else None, self.K, self.N, ldo, layout, CODA_DT[B.dtype],
+                            ones.data_ptr(), None, u.data_ptr(), None, current_stream_ptr())
+        C.check(st, "coda_ln_fold (column sums of the folded weights)")
+        out = [("ln_rowscale", {"gamma": None, "eps": args["eps"], "u": u})]
+        beta = args.get("beta")
+        if beta is not None:
+            c = torch.empty(max(self.N, 1), dtype=torch.float32, device=B.device)
+            uu = torch.empty_like(c)
+            self._keep += [beta, c, uu]
+            st = C.coda_ln_fold(B.data_ptr() if B.numel() else None, self.K, self.N, ldb, layout, CODA_DT[B.dtype],
+                                gamma.data_ptr() if gamma.numel() else None, beta.data_ptr(), uu.data_ptr(),
+                                c.data_ptr(), current_stream_ptr())
+            C.check(st, "coda_ln_fold")
+            out.append(("add_col", {"vec": c}))
+        self.ops = out + list(ops[1:])
+        return Bf, ldo
 
     def _fold_gain(self, B: torch.Tensor, ldb: int):
         """rms_rowscale(gamma) on B -> rms_rowscale(NULL) on diag(gamma) B."""

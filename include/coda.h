@@ -142,8 +142,11 @@ typedef enum {
      the mean of row i of A over K and var_i the mean squared deviation from it:
      the GEMM of the normalised, gained A.  The shift beta is not part of the
      op: its term beta^T B is a column vector (coda_ln_fold's c) that a later
-     CODA_OP_ADD_COL adds.  Must be the first op and needs K > 0; at most one
-     of RMS_ROWSCALE / LN_ROWSCALE. */
+     CODA_OP_ADD_COL adds.  in = NULL: the gain is already in the rows of B
+     (coda_fold_gain), and in2 must then hold the column sums of that B
+     (coda_ln_fold with gamma = 1); A is fed unchanged and its row sums and sums
+     of squares come from the fragments the matrix cores read.  Must be the
+     first op and needs K > 0; at most one of RMS_ROWSCALE / LN_ROWSCALE. */
   CODA_OP_LN_ROWSCALE = 14,
   /* reductions over the rows (the survey's backward set: the bias gradient of a
      layer is the column sum of its output gradient).  Each writes an fp32 value

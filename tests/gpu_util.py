@@ -95,7 +95,7 @@ def unfused_extra(spec, inputs, rows, fold_gain: bool = False):
         # the unfused pass stores the beta-free normalised A; beta's term beta^T B
         # is its own column pass, so the GEMM output without it is stored too
         Y = oracle.layernorm(A, ops[0][1]["gamma"], ops[0][1]["eps"])
-        extra = u_ab * (np.abs(Y) @ np.abs(B))
+        extra = (2 if fold_gain else 1) * u_ab * (np.abs(Y) @ np.abs(B))
         if ops[0][1].get("beta") is not None:
             extra = extra + 2 * u * np.abs(Y @ B)
         body = ops[1:]

@@ -44,25 +44,29 @@ def oracle_ops(ops):
 SMALL = [(136, 264, 72), (300, 520, 200), (64, 128, 64), (520, 392, 256)]
 
 
+@pytest.mark.parametrize("fold", [False, True])
 @pytest.mark.parametrize("shape", SMALL)
 @pytest.mark.parametrize("mode", ["fused", "unfused"])
-def test_layernorm_workload_small(CR, shape, mode):
+def test_layernorm_workload_small(CR, shape, mode, fold):
     spec = w.scaled_config(6, *shape)
-    run_and_compare(spec, w.make_inputs(spec), mode=mode, label=f"ln small {shape}",
-                    check_determinism=(mode == "fused"))
+    run_and_compare(spec, w.make_inputs(spec), mode=mode, label=f"ln small {shape} fold={fold}",
+                    check_determinism=(mode == "fused"), fold_gain=fold)
 
 
+@pytest.mark.parametrize("fold", [False, True])
 @pytest.mark.parametrize("tile", [1, 2, 3])
-def test_layernorm_every_tile(CR, tile):
+def test_layernorm_every_tile(CR, tile, fold):
     spec = w.scaled_config(6, 300, 520, 200)
-    run_and_compare(spec, w.make_inputs(spec), tile=tile, label=f"ln tile{tile}")
+    run_and_compare(spec, w.make_inputs(spec), tile=tile, label=f"ln tile{tile} fold={fold}", fold_gain=fold)
 
 
+@pytest.mark.parametrize("fold", [False, True])
 @pytest.mark.parametrize("mode", ["fused", "unfused"])
-def test_layernorm_full_size_sampled_rows(CR, mode):
+def test_layernorm_full_size_sampled_rows(CR, mode, fold):
     spec = w.get_config(6)
     rows = sample_rows(spec.M, 64)
-    run_and_compare(spec, w.make_inputs(spec), mode=mode, rows=rows, label="ln full", check_determinism=True)
+    run_and_compare(spec, w.make_inputs(spec), mode=mode, rows=rows, label=f"ln full fold={fold}",
+                    check_determinism=True, fold_gain=fold)
 
 
 @pytest.mark.parametrize("layout", ["KN", "NK"])
@@ -94,10 +98,10 @@ def test_ln_fold_matches_oracle(CR, layout, dtype):
     assert np.all(np.abs(f64(c) - c_ref) <= bound_c)
 
 
-def _ln_case(CR, A, B, layout, gamma, beta, eps, extra_ops=(), tile=0, d_dtype=None, label=""):
+def _ln_case(CR, A, B, layout, gamma, beta, eps, extra_ops=(), tile=0, d_dtype=None, label="", fold=False):
     coda, runner = CR
     ops = [("ln_rowscale", {"gamma": gamma, "beta": beta, "eps": eps})] + list(extra_ops)
-    call = runner.Call(A, B, ops, layout, tile=tile, d_dtype=d_dtype)
+    call = runner.Call(A, B, ops, layout, tile=tile, d_dtype=d_dtype, fold_gain=fold)
     coda.check(call.fused(), f"fused {label}")
     torch.cuda.synchronize()
     ref, reds = oracle.forward(f64(A), f64(B), oracle_ops(ops), layout)
@@ -169,8 +173,11 @@ def test_layernorm_degenerate_rows(CR):
     b = rng.standard_normal((K, N)) / np.sqrt(K)
     A, B = bf16(a), bf16(b)
     for tile in (0, 1, 3):
-        _ln_case(CR, A, B, "KN", bf16(1 + 0.1 * rng.standard_normal(K)), bf16(0.2 * rng.standard_normal(K)), 1e-5,
-                 [("add_col", {"vec": bf16(0.1 * rng.standard_normal(N))})], tile=tile, label=f"ln degenerate tile{tile}")
+        g, bt = bf16(1 + 0.1 * rng.standard_normal(K)), bf16(0.2 * rng.standard_normal(K))
+        bias = bf16(0.1 * rng.standard_normal(N))
+        for fold in (False, True):
+            _ln_case(CR, A, B, "KN", g, bt, 1e-5, [("add_col", {"vec": bias})], tile=tile, fold=fold,
+                     label=f"ln degenerate tile{tile} fold={fold}")
 
 
 @pytest.mark.parametrize("layout", ["KN", "NK"])
