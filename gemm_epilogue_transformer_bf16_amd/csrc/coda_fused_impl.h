@@ -17,12 +17,22 @@
 //     slots, which the row swizzle swz(r) = (r & 7) ^ ((r >> 3) & 1) provides;
 //   * MFMA fragments for the next k16 step are read while the current step's
 //     v_mfma_f32_32x32x16_bf16 instructions run.
-// With the deferred RMS op, A instead goes through registers: each element is
-// multiplied by gamma[k] and rounded to bf16 on its way into LDS, and its raw
-// square is added to an fp32 per-row sum (the per-row scale of a row-wise norm
-// moved past the projection: the "augment_me" comment on the zeli.app page;
-// the agentlenshq.com page, "CODA's approach").  fp32 operands (a small tile,
-// v_mfma_f32_32x32x2f32) use a register-staged, padded LDS layout.
+// A stored [K x M] (the X^T of a weight gradient) is staged like the
+// N-contiguous W tile and read with the same transposing LDS reads.
+// Deferred row norms (the per-row factors of a row-wise norm moved past the
+// projection: the "augment_me" comment on the zeli.app page; the
+// agentlenshq.com page, "CODA's approach"), one compile-time mode each:
+//   * gain in the loop (RMS, LayerNorm): raw A lands in a third LDS array one
+//     K step ahead; each wave multiplies its blocks by gamma[k], rounds them to
+//     bf16 into the stage and adds the raw squares (and, for LayerNorm, the
+//     values, both about a per-row shift) to fp32 per-row sums;
+//   * gain folded into B (RMS, LayerNorm): A reaches the MFMAs unchanged and
+//     the sums come from the X fragments the MFMAs read, between the MFMAs;
+//   * row sums of squares given (RMS with the gain in B): the plain main loop.
+// The epilogue scales each row by 1/rms (RMS) or applies
+// rstd * (acc - mean * u) with u the column sums of the gained weights
+// (LayerNorm).  fp32 operands (a small tile, v_mfma_f32_32x32x2f32) use a
+// register-staged, padded LDS layout.
 //
 // Epilogue: each wave moves its accumulators, one 32-row block at a time,
 // through a private LDS region into a row-major layout where every lane owns
@@ -31,7 +41,9 @@
 // as whole 16-byte row chunks, and row reductions combine the lanes of a row,
 // then the waves of the tile through LDS, then the workgroups of a tile row
 // through a workspace of partial sums finished by the last workgroup to arrive
-// (a fixed summation order, so results are bitwise repeatable).
+// (a fixed summation order, so results are bitwise repeatable).  Column
+// reductions combine the lanes of a column, then the row blocks of the tile in
+// LDS, then the workgroups of a tile column the same way.
 #pragma once
 
 #include "coda_device.h"
@@ -705,9 +717,6 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
       }
     };
 
-    // MFMAs of one K step.  With the RMS op, the next step's A chunks (already in
-    // registers) are scaled and written to `rms_dst` between the MFMAs of the
-    // last k16 step, so that VALU work overlaps the matrix pipe.
     // SSF: squares of the X fragments (rows wm*WTM + 32 mi + l32, K indices
     // 16 kk + 8 (lane >> 5) + 0..7).  The WN waves that share those rows split
     // the (row block, slice) pairs: at slice kk wave wn takes the blocks

@@ -4,7 +4,8 @@
 // back by the next operator's kernel).
 //
 //   [row norm pass]  ->  plain GEMM (same main loop as the fused kernel)
-//   ->  one pass per elementwise op  ->  one pass per row reduction
+//   ->  one pass per elementwise op  ->  one pass per row reduction, two per
+//   column reduction (partial sums over chunks of rows, then the chunks)
 //
 // Every pass streams its operands with 16-byte vector accesses.
 #include "coda_device.h"
