@@ -6,7 +6,7 @@ import torch
 
 import workloads as w
 
-from gpu_util import announce, assert_close, lib, run_and_compare, sample_rows
+from gpu_util import lib, run_and_compare, sample_rows
 
 pytestmark = pytest.mark.gpu
 

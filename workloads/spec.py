@@ -24,7 +24,7 @@ order they are drawn), and the ordered epilogue program as a list of
 from __future__ import annotations
 
 import dataclasses
-from typing import Dict, List, Optional, Tuple
+from typing import Dict, Tuple
 
 
 @dataclasses.dataclass(frozen=True)
