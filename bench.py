@@ -210,9 +210,9 @@ def main():
                     help="GPT-2-medium backward layer (workload 5) with the bias gradient: a column sum of dH "
                          "appended to its epilogue")
     ap.add_argument("--given-row-sumsq", action="store_true",
-                    help="RMS layers: the row sums of squares of A are given (as the previous layer's ROW_SUMSQ "
-                         "output provides them in a chain of layers; computed here before timing) and the gain is "
-                         "folded, so the main loop is the plain GEMM")
+                    help="RMSNorm / LayerNorm layers: the row sums of squares (and sums) of A are given (as the "
+                         "previous layer's ROW_SUMSQ / ROW_SUM outputs provide them in a chain of layers; computed "
+                         "here before timing) and the gain is folded, so the main loop is the plain GEMM")
     ap.add_argument("--weight-grad", action="store_true",
                     help="the GPT-2-small MLP up-projection's weight gradient, dW_acc += X^T dY, instead")
     ap.add_argument("--in-loop-gain", action="store_true",
@@ -256,15 +256,15 @@ def main():
     fold = has_norm and (not args.in_loop_gain or args.given_row_sumsq)
     call = runner.WorkloadCall(spec, inputs, tile=args.tile, fold_gain=fold)
     if args.given_row_sumsq:
-        if not has_rms:
-            print("--given-row-sumsq applies to layers with an RMSNorm", file=sys.stderr)
+        if not has_norm:
+            print("--given-row-sumsq applies to layers with an RMSNorm or LayerNorm", file=sys.stderr)
             sys.exit(2)
-        # setup outside the timed region: the row sums of squares a previous
-        # layer's ROW_SUMSQ epilogue would have written
+        # setup outside the timed region: the row sums and sums of squares a
+        # previous layer's ROW_SUM / ROW_SUMSQ epilogue would have written
         A = call.tensors[spec.a_name]
-        row_ss = (A.float() * A.float()).sum(dim=1, keepdim=True).contiguous()
+        row_stats = torch.stack([A.float().sum(dim=1), (A.float() * A.float()).sum(dim=1)], dim=1).contiguous()
         prog = [(n, dict(a)) for n, a in call.ops]
-        prog[0][1]["row_ss"] = row_ss
+        prog[0][1].update({"row_ss": row_stats, "row_ss_col": 1, "row_s_col": 0})
         call = runner.Call(A, call.B, prog, spec.b_layout, d_dtype=TORCH_DT_OF[spec.d_dtype], tile=args.tile)
     flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()

@@ -69,6 +69,9 @@ class coda_op(ctypes.Structure):
         ("out", ctypes.c_void_p),
         ("out_stride", ctypes.c_int64),
         ("in2", ctypes.c_void_p),
+        ("row_sum", ctypes.c_void_p),
+        ("row_sumsq", ctypes.c_void_p),
+        ("row_ld", ctypes.c_int64),
     ]
 
 

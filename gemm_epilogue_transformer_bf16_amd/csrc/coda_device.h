@@ -106,7 +106,8 @@ struct FusedArgs {
   void* D;
   const void* gamma;
   const float* ln_u;    // LayerNorm: u = gamma^T B [N]
-  const float* row_ss;  // RMS with given row sums of squares: row_ss[i * row_ss_stride]
+  const float* row_ss;  // given row sums of squares: row_ss[i * row_ss_stride]
+  const float* row_s;   // LayerNorm: given row sums (same stride)
   long long row_ss_stride;
   float* partials;      // [n_red][grid_n][M]
   unsigned* counters;   // [grid_m]

@@ -17,6 +17,7 @@ dev::FusedArgs make_args(const Plan& p) {
   a.gamma = p.gamma;
   a.ln_u = p.ln_u;
   a.row_ss = p.row_ss;
+  a.row_s = p.row_s;
   a.row_ss_stride = p.row_ss_stride;
   a.lda = p.lda;
   a.ldb = p.ldb;
@@ -69,7 +70,7 @@ int launch_args(const Plan& p, const dev::FusedArgs& a, hipStream_t stream) {
   const int64_t nwg = p.full_tiles + p.split_tiles * p.split_s;
   const bool bkn = p.b_layout == CODA_B_KN;
   const bool akm = p.a_layout == CODA_A_KM;
-  const int norm = p.has_ln      ? (p.gain_in_b ? dev::kNormLnB : dev::kNormLn)
+  const int norm = p.has_ln      ? (p.row_ss ? dev::kNormLnGiven : p.gain_in_b ? dev::kNormLnB : dev::kNormLn)
                    : p.row_ss    ? dev::kNormRmsGiven
                    : p.gain_in_b ? dev::kNormRmsB
                    : p.has_norm  ? dev::kNormRms
@@ -108,6 +109,7 @@ int launch_plain_gemm(const Plan& p, const void* A, int64_t lda, void* out, int6
   q.gamma = nullptr;
   q.ln_u = nullptr;
   q.row_ss = nullptr;
+  q.row_s = nullptr;
   q.n_ops = 0;
   q.n_red = 0;
   q.n_colred = 0;

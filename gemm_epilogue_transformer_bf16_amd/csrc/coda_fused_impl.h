@@ -103,6 +103,8 @@ constexpr int kNormRmsGiven = 4;
 // LayerNorm with the gain folded into B: row sums and sums of squares (about a
 // per-row shift) from the X fragments, like kNormRmsB
 constexpr int kNormLnB = 5;
+// LayerNorm with the gain in B and the row sums and sums of squares given
+constexpr int kNormLnGiven = 6;
 
 template <int BM_, int BN_, int WM_, int WN_, bool F32_, bool BKN_, int NORM_, bool AKM_ = false>
 struct Cfg {
@@ -121,8 +123,8 @@ struct Cfg {
   static constexpr bool RMS = NORM_ == kNormRms || NORM_ == kNormLn, LN = NORM_ == kNormLn;
   static constexpr bool LNF = NORM_ == kNormLnB;
   static constexpr bool SSF = NORM_ == kNormRmsB || LNF;   // sums from the X fragments
-  static constexpr bool LNE = LN || LNF;                   // LayerNorm epilogue
-  static constexpr bool GIVEN = NORM_ == kNormRmsGiven;
+  static constexpr bool LNE = LN || LNF || NORM_ == kNormLnGiven;   // LayerNorm epilogue
+  static constexpr bool GIVEN = NORM_ == kNormRmsGiven || NORM_ == kNormLnGiven;
   static constexpr int NW = WM * WN;
   static constexpr int NT = 64 * NW;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -1156,7 +1158,8 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
     for (int t = tid; t < BM; t += C::NT) {
       const int row = m0 + t;
       const float v = row < M ? a->row_ss[(long long)row * a->row_ss_stride] : 0.0f;
-      row_factors(t, v, 0.0f, 0.0f);
+      const float sm = (C::LNE && row < M) ? a->row_s[(long long)row * a->row_ss_stride] : 0.0f;
+      row_factors(t, v, sm, 0.0f);
     }
     __syncthreads();
   } else if constexpr (C::SSF && !C::F32) {
@@ -1430,6 +1433,7 @@ int launch_norms(const FusedArgs& args, int64_t nwg, int norm, hipStream_t s) {
     case kNormRmsB: return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormRmsB>>(args, nwg, s);
     case kNormRmsGiven: return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormRmsGiven>>(args, nwg, s);
     case kNormLnB: return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormLnB>>(args, nwg, s);
+    case kNormLnGiven: return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormLnGiven>>(args, nwg, s);
     default: return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormNone>>(args, nwg, s);
   }
 }

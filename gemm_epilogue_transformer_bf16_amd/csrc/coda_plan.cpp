@@ -233,8 +233,9 @@ int build_plan(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
       return CODA_ERR_INVALID_ARG;
     }
     const bool ln = o.kind == CODA_OP_LN_ROWSCALE;
-    if (!ln && o.kind != CODA_OP_RMS_ROWSCALE && o.in2) {
-      set_error("op %d: in2 must be NULL", i);
+    const bool norm_op = ln || o.kind == CODA_OP_RMS_ROWSCALE;
+    if ((!ln && o.in2) || (!norm_op && (o.row_sum || o.row_sumsq)) || (!ln && o.row_sum)) {
+      set_error("op %d: in2 / row_sum / row_sumsq not used by this op must be NULL", i);
       return CODA_ERR_INVALID_ARG;
     }
     if (o.kind == CODA_OP_RMS_ROWSCALE || ln) {
@@ -271,17 +272,22 @@ int build_plan(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
           return CODA_ERR_UNSUPPORTED;
         }
       }
-      if (!ln && o.in2) {   // given row sums of squares: the gain must be in B
+      if (o.row_sumsq || o.row_sum) {   // given row statistics: the gain must be in B
         if (o.in) {
-          set_error("RMS_ROWSCALE with given row sums of squares (in2) needs the gain folded into B (in = NULL)");
+          set_error("%s with given row statistics needs the gain folded into B (in = NULL)", name);
           return CODA_ERR_UNSUPPORTED;
         }
-        if (o.ld < 0 || !aligned(o.in2, 4)) {
-          set_error("RMS_ROWSCALE row sums of squares: ld >= 0 (0 = 1) and 4-byte alignment");
+        if (!o.row_sumsq || (ln && !o.row_sum)) {
+          set_error("%s: given row statistics need row_sumsq%s", name, ln ? " and row_sum" : "");
           return CODA_ERR_INVALID_ARG;
         }
-        p->row_ss = static_cast<const float*>(o.in2);
-        p->row_ss_stride = o.ld > 0 ? o.ld : 1;
+        if (o.row_ld < 1 || !aligned(o.row_sumsq, 4) || !aligned(o.row_sum, 4)) {
+          set_error("%s row statistics: row_ld >= 1 and 4-byte alignment", name);
+          return CODA_ERR_INVALID_ARG;
+        }
+        p->row_ss = static_cast<const float*>(o.row_sumsq);
+        p->row_s = static_cast<const float*>(o.row_sum);
+        p->row_ss_stride = o.row_ld;
       }
       p->has_norm = true;
       p->has_ln = ln;

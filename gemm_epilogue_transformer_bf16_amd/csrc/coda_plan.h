@@ -59,7 +59,8 @@ struct Plan {
   bool gain_in_b;            // RMS_ROWSCALE with gamma NULL: the gain is folded into B
   const void* gamma;
   const float* ln_u;         // LN_ROWSCALE: u = gamma^T B [N]
-  const float* row_ss;       // RMS_ROWSCALE with given row sums of squares (stride row_ss_stride)
+  const float* row_ss;       // given row sums of squares (stride row_ss_stride), or null
+  const float* row_s;        // LN_ROWSCALE: given row sums (same stride), or null
   int64_t row_ss_stride;
   float eps;
   int n_ops;                 // ops after the norm op

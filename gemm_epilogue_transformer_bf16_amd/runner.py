@@ -61,6 +61,9 @@ class Call:
     ``gamma``/``vec``/``mat`` inputs, ``out`` a 2-D fp32 tensor with ``col``
     selecting the column a reduction writes (its rows index the output's rows
     for row_* reductions and the output's columns for col_* reductions).  Scalars: ``alpha``, ``beta``, ``eps``.
+    ``rms_rowscale`` / ``ln_rowscale`` may take given row statistics: ``row_ss``
+    a 2-D fp32 tensor with the sums of squares in column ``row_ss_col`` and
+    (LayerNorm) the sums in column ``row_s_col`` (with ``fold_gain``).
     ``ln_rowscale`` takes ``gamma``, ``eps`` and an optional shift ``beta``
     tensor: the call computes u = gamma^T B and c = beta^T B once with
     coda_ln_fold and passes LN_ROWSCALE(gamma, u) followed by ADD_COL(c).
@@ -136,12 +139,15 @@ class Call:
                 o.scalar = float(args["eps"])
             if name == "ln_rowscale":
                 o.in2 = args["u"].data_ptr()
-            if name == "rms_rowscale" and args.get("row_ss") is not None:
-                # given row sums of squares: column `row_ss_col` of a 2-D fp32 tensor
+            if name in ("rms_rowscale", "ln_rowscale") and args.get("row_ss") is not None:
+                # given row statistics: columns of a 2-D fp32 tensor, the sums of
+                # squares in `row_ss_col` and (LayerNorm) the sums in `row_s_col`
                 t = args["row_ss"]
                 self._keep.append(t)
-                o.in2 = t.data_ptr() + 4 * int(args.get("row_ss_col", 0))
-                o.ld = t.stride(0)
+                o.row_sumsq = t.data_ptr() + 4 * int(args.get("row_ss_col", 0))
+                if name == "ln_rowscale":
+                    o.row_sum = t.data_ptr() + 4 * int(args["row_s_col"])
+                o.row_ld = t.stride(0)
             if name in ("row_sum", "row_sumsq", "row_mean", "col_sum", "col_sumsq"):
                 out = args["out"]
                 self._keep.append(out)
@@ -198,7 +204,8 @@ class Call:
         st = C.coda_ln_fold(Bf.data_ptr() if Bf.numel() else None, self.K, self.N, ldo, layout, CODA_DT[B.dtype],
                             ones.data_ptr(), None, u.data_ptr(), None, current_stream_ptr())
         C.check(st, "coda_ln_fold (column sums of the folded weights)")
-        out = [("ln_rowscale", {"gamma": None, "eps": args["eps"], "u": u})]
+        out = [("ln_rowscale", {"gamma": None, "eps": args["eps"], "u": u,
+                                **{k: args[k] for k in ("row_ss", "row_ss_col", "row_s_col") if k in args}})]
         beta = args.get("beta")
         if beta is not None:
             c = torch.empty(max(self.N, 1), dtype=torch.float32, device=B.device)

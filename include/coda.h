@@ -111,8 +111,8 @@ typedef enum {
                                  rows of B (B = diag(gamma) W, see coda_fold_gain), A
                                  is fed unchanged and the row sums of squares come from
                                  the A fragments the matrix cores read.  With in = NULL
-                                 and in2 != NULL, the row sums of squares are inputs:
-                                 in2 = fp32 sum_k A[i,k]^2 at in2[i*ld] (ld >= 1), e.g.
+                                 and row_sumsq != NULL, the row sums of squares are
+                                 inputs (sum_k A[i,k]^2 at row_sumsq[i*row_ld]), e.g.
                                  the ROW_SUMSQ output of the layer that produced A, and
                                  the main loop is the plain GEMM (a cross-layer chain).
                                  Must be the first op, at most once, and needs K > 0. */
@@ -145,8 +145,13 @@ typedef enum {
      CODA_OP_ADD_COL adds.  in = NULL: the gain is already in the rows of B
      (coda_fold_gain), and in2 must then hold the column sums of that B
      (coda_ln_fold with gamma = 1); A is fed unchanged and its row sums and sums
-     of squares come from the fragments the matrix cores read.  Must be the
-     first op and needs K > 0; at most one of RMS_ROWSCALE / LN_ROWSCALE. */
+     of squares come from the fragments the matrix cores read.  With in = NULL
+     and row_sum, row_sumsq != NULL the row sums and sums of squares of A are
+     inputs (at [i*row_ld]; e.g. the ROW_SUM / ROW_SUMSQ outputs of the layer
+     that produced A) and the main loop is the plain GEMM; the variance is then
+     sumsq/K - mean^2 in fp32, which loses accuracy on rows whose mean is large
+     against their spread.  Must be the first op and needs K > 0; at most one
+     of RMS_ROWSCALE / LN_ROWSCALE. */
   CODA_OP_LN_ROWSCALE = 14,
   /* reductions over the rows (the survey's backward set: the bias gradient of a
      layer is the column sum of its output gradient).  Each writes an fp32 value
@@ -166,8 +171,10 @@ typedef struct {
   int32_t reserved0;    /* must be 0                                                 */
   void* out;            /* reductions: fp32 output (device)                          */
   int64_t out_stride;   /* reductions: element stride between rows of `out`, >= 1   */
-  const void* in2;      /* LN_ROWSCALE: fp32 u [N]; RMS_ROWSCALE: optional fp32 row
-                           sums of squares [M] (stride ld); NULL for every other op */
+  const void* in2;      /* LN_ROWSCALE: fp32 u [N]; NULL for every other op          */
+  const void* row_sum;  /* LN_ROWSCALE: given fp32 row sums of A, or NULL            */
+  const void* row_sumsq;/* RMS/LN_ROWSCALE: given fp32 row sums of squares, or NULL  */
+  int64_t row_ld;       /* element stride between rows of row_sum / row_sumsq (>= 1) */
 } coda_op;
 
 typedef struct {

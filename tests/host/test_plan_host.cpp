@@ -311,6 +311,29 @@ int main() {
     f = e; f.D = Pm(0x10000000 + 2 * 304 * 8);                               // D inside A's [K x M] extent
     EXPECT(coda_validate(A, B, 304, N, K, &f, 0) == CODA_ERR_INVALID_ARG);
   }
+  {  // given row statistics: gain folded, row_sumsq (and for LN row_sum), row_ld >= 1
+    coda_epi_desc e = base_desc(N, K); e.n_ops = 1;
+    e.ops[0].kind = CODA_OP_RMS_ROWSCALE; e.ops[0].scalar = 1e-6f;
+    e.ops[0].row_sumsq = P(0x50000004); e.ops[0].row_ld = 2;
+    EXPECT(coda_validate(A, B, M, N, K, &e, 0) == CODA_OK);
+    coda::Plan q = plan_of(M, N, K, e);
+    EXPECT(q.gain_in_b && q.row_ss == P(0x50000004) && q.row_s == nullptr && q.row_ss_stride == 2);
+    coda_epi_desc f = e; f.ops[0].in = P(0x40000000); f.ops[0].in_dtype = CODA_BF16;   // gain not folded
+    EXPECT(coda_validate(A, B, M, N, K, &f, 0) == CODA_ERR_UNSUPPORTED);
+    f = e; f.ops[0].row_ld = 0;
+    EXPECT(coda_validate(A, B, M, N, K, &f, 0) == CODA_ERR_INVALID_ARG);
+    f = e; f.ops[0].row_sum = P(0x50000000);                                         // RMS takes no row sums
+    EXPECT(coda_validate(A, B, M, N, K, &f, 0) == CODA_ERR_INVALID_ARG);
+    coda_epi_desc l = e; l.ops[0].kind = CODA_OP_LN_ROWSCALE; l.ops[0].in2 = P(0x60000000);
+    l.ops[0].row_sum = P(0x50000000);
+    EXPECT(coda_validate(A, B, M, N, K, &l, 0) == CODA_OK);
+    coda::Plan r = plan_of(M, N, K, l);
+    EXPECT(r.has_ln && r.gain_in_b && r.row_s == P(0x50000000) && r.row_ss == P(0x50000004));
+    f = l; f.ops[0].row_sum = nullptr;                                               // LN needs both
+    EXPECT(coda_validate(A, B, M, N, K, &f, 0) == CODA_ERR_INVALID_ARG);
+    f = e; f.n_ops = 2; f.ops[1].kind = CODA_OP_GELU_TANH; f.ops[1].row_sumsq = P(0x50000004);
+    EXPECT(coda_validate(A, B, M, N, K, &f, 0) == CODA_ERR_INVALID_ARG);               // only on a norm op
+  }
   {  // coda_fold_gain validation
     const void* g = P(0x40000000);
     EXPECT(coda::validate_fold_gain(B, 768, 3072, 3072, CODA_B_KN, CODA_BF16, g, Pm(0x70000000), 3072) == CODA_OK);

@@ -52,8 +52,9 @@ def test_struct_layout_matches_c(C, tmp_path):
 #include <stddef.h>
 #include "coda.h"
 int main(void) {
-  printf("%zu %zu %zu %zu %zu %zu %zu\\n", sizeof(coda_op), offsetof(coda_op, out), offsetof(coda_op, out_stride),
-         offsetof(coda_op, in2), sizeof(coda_epi_desc), offsetof(coda_epi_desc, tile), offsetof(coda_epi_desc, ops));
+  printf("%zu %zu %zu %zu %zu %zu %zu %zu\\n", sizeof(coda_op), offsetof(coda_op, out), offsetof(coda_op, out_stride),
+         offsetof(coda_op, in2), offsetof(coda_op, row_ld), sizeof(coda_epi_desc), offsetof(coda_epi_desc, tile),
+         offsetof(coda_epi_desc, ops));
   return 0;
 }
 """)
@@ -61,7 +62,8 @@ int main(void) {
     subprocess.run([gcc, f"-I{os.path.join(ROOT, 'include')}", str(src), "-o", str(exe)], check=True)
     vals = list(map(int, subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()))
     assert vals == [ctypes.sizeof(C.coda_op), C.coda_op.out.offset, C.coda_op.out_stride.offset, C.coda_op.in2.offset,
-                    ctypes.sizeof(C.coda_epi_desc), C.coda_epi_desc.tile.offset, C.coda_epi_desc.ops.offset]
+                    C.coda_op.row_ld.offset, ctypes.sizeof(C.coda_epi_desc), C.coda_epi_desc.tile.offset,
+                    C.coda_epi_desc.ops.offset]
 
 
 def test_validation_status_codes_via_library(C):

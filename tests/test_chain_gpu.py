@@ -71,6 +71,35 @@ def test_bert_stats_feed_the_next_rmsnorm(CR, shape, tile):
     assert_close(f64(c3.D), ref, "layer 2 own sums")
 
 
+@pytest.mark.parametrize("tile", [0, 1, 3])
+def test_bert_stats_feed_the_next_layernorm(CR, tile):
+    """The BERT-style layer's (row sum, row sum of squares) output is exactly
+    what the next layer's deferred LayerNorm needs: mean and variance."""
+    coda, runner = CR
+    T, H, Dm, N2 = 520, 136, 392, 264
+    announce(f"chain LayerNorm tile{tile}")
+    rng = np.random.default_rng(102)
+    Hin = bf16(np.abs(rng.standard_normal((T, H))))
+    W1 = bf16(rng.standard_normal((H, Dm)) / np.sqrt(H))
+    R = bf16(rng.standard_normal((T, Dm)) + rng.standard_normal((T, 1)))   # rows with offsets
+    stats = torch.zeros((T, 2), dtype=torch.float32, device="cuda")
+    ops1 = [("add_mat", {"mat": R, "beta": 1.0}), ("row_sum", {"out": stats, "col": 0}),
+            ("row_sumsq", {"out": stats, "col": 1})]
+    c1 = runner.Call(Hin, W1, ops1, "KN", tile=tile)
+    coda.check(c1.fused(), "layer 1")
+    W2 = bf16(rng.standard_normal((Dm, N2)) / np.sqrt(Dm))
+    gamma = bf16(1 + 0.1 * rng.standard_normal(Dm))
+    beta = bf16(0.1 * rng.standard_normal(Dm))
+    ops2 = [("ln_rowscale", {"gamma": gamma, "beta": beta, "eps": 1e-5, "row_ss": stats, "row_ss_col": 1,
+                             "row_s_col": 0}), ("gelu_tanh", {})]
+    c2 = runner.Call(c1.D, W2, ops2, "KN", tile=tile, fold_gain=True)
+    coda.check(c2.fused(), "layer 2")
+    torch.cuda.synchronize()
+    ref, _ = oracle.forward(f64(c1.D), f64(W2), [("ln_rowscale", {"gamma": f64(gamma), "beta": f64(beta),
+                                                                  "eps": 1e-5}), ("gelu_tanh", {})], "KN")
+    assert_close(f64(c2.D), ref, f"chained LayerNorm layer 2 tile{tile}")
+
+
 def test_given_sums_need_the_folded_gain(CR):
     coda, runner = CR
     A = bf16(np.ones((64, 64)))

@@ -31,7 +31,7 @@ def f64(t):
 
 def oracle_ops(ops):
     return [(n, {k: (f64(v) if isinstance(v, torch.Tensor) else v) for k, v in a.items()
-                 if k not in ("out", "row_ss", "row_ss_col")}) for n, a in ops]
+                 if k not in ("out", "row_ss", "row_ss_col", "row_s_col")}) for n, a in ops]
 
 
 def run(CR, A, B, ops, layout="KN", **kw):
