@@ -1,0 +1,96 @@
+"""The text front end (host only): programs of statements on the running value
+lower to the op lists the workloads describe, resolve operands by shape, and
+reject what is not a primitive."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as w
+from gemm_epilogue_transformer_bf16_amd.frontend import FrontendError, lower, parse
+
+
+def operands(M, N, K):
+    rng = np.random.default_rng(3)
+    return {"gamma": np.ones(K), "beta": np.zeros(K), "bias": rng.standard_normal(N), "R": rng.standard_normal((M, N)),
+            "P": rng.standard_normal((M, N)), "rs": rng.standard_normal(M), "stats": np.zeros((M, 2)),
+            "db": np.zeros((N, 1)), "half_bias": rng.standard_normal(N // 2)}
+
+
+def test_the_pages_statement_style_lowers_in_order():
+    M, N, K = 6, 8, 4
+    ops = lower("""EPILOGUE {
+        output = gelu(input);      // the activation of the GEMM result
+        output = output + R;       // a residual matrix
+      }""", operands(M, N, K), M, N)
+    assert [n for n, _ in ops] == ["gelu_tanh", "add_mat"]
+    assert ops[1][1]["beta"] == 1.0
+
+
+@pytest.mark.parametrize("idx,text", [
+    (1, "output = rmsnorm(input, gamma, 1e-6); output = output + bias; output = gelu(output); output = output + R;"),
+    (3, "output = output + bias; output = output + R; stats[0] = rowsum(output); stats[1] = rowsumsq(output);"),
+    (4, "output = rmsnorm(input, gamma, 1e-6); output = swiglu(output);"),
+    (5, "output = output * dgelu(P); rowsum_out[0] = rowsum(output);"),
+    (6, "output = layernorm(input, gamma, beta, 1e-5); output = output + bias; output = gelu(output);"),
+])
+def test_lowering_reproduces_the_workload_programs(idx, text):
+    """The lowered list computes what the workload's program computes (the
+    oracle on both, bit for bit)."""
+    M, N, K = 8, 16, 8
+    spec = w.scaled_config(idx, M, N, K)
+    inputs = w.make_inputs(spec)
+    from oracle.run import resolve_program
+    from workloads.gen import to_f64
+    ref_ops = resolve_program(spec, inputs)
+    named = {}
+    for name, args in ref_ops:
+        for key in ("gamma", "beta", "vec", "mat"):
+            if isinstance(args.get(key), np.ndarray):
+                named[{"vec": "bias", "mat": "R" if name == "add_mat" else "P"}.get(key, key)] = args[key]
+    outs = {o: np.zeros(shape) for o, shape in spec.outputs}
+    named.update(outs)
+    named["rowsum_out"] = outs.get("rowsum", np.zeros((M, 1)))
+    ops = lower(text, named, spec.M, spec.N)
+    dtypes = {t.name: t.dtype for t in spec.tensors}
+    A = to_f64(inputs[spec.a_name], dtypes[spec.a_name])
+    B = to_f64(inputs[spec.b_name], dtypes[spec.b_name])
+    strip = lambda o: [(n, {k: v for k, v in a.items() if k not in ("out", "col")}) for n, a in o]
+    D1, r1 = oracle.forward(A, B, strip(ref_ops), spec.b_layout)
+    D2, r2 = oracle.forward(A, B, strip(ops), spec.b_layout)
+    assert [n for n, _ in ops] == [n for n, _ in ref_ops]
+    assert np.array_equal(D1, D2)
+    for (_, _, a), (_, _, b) in zip(r1, r2):
+        assert np.array_equal(a, b)
+
+
+def test_operands_resolve_by_shape():
+    M, N, K = 6, 8, 4
+    o = operands(M, N, K)
+    ops = lower("""output = output * bias; output = output * rs; output = output + rs; output = 2.5 * output;
+                   output = output + 0.5 * R; output = swiglu(output); output = output + half_bias;
+                   db[0] = colsum(output); stats[1] = rowmean(output);""", o, M, N)
+    assert [n for n, _ in ops] == ["scale_col", "scale_row", "add_row", "scale", "add_mat", "swiglu_pair",
+                                   "add_col", "col_sum", "row_mean"]
+    assert ops[3][1]["alpha"] == 2.5 and ops[4][1]["beta"] == 0.5
+    assert ops[7][1]["col"] == 0 and ops[8][1]["col"] == 1
+
+
+@pytest.mark.parametrize("text,msg", [
+    ("output = dropout(output, 0.1);", "dropout"),
+    ("output = gelu(output); output = rmsnorm(input, gamma, 1e-6);", "first statement"),
+    ("output = output + nothing;", "unbound"),
+    ("output = output + 1.0;", "constant"),
+    ("output = output * R;", "not a primitive"),
+    ("stats[0] = gelu(output);", "reduction"),
+    ("output = gelu(output)", "';'"),
+    ("output = tanh(output);", "expected"),
+])
+def test_errors(text, msg):
+    M, N, K = 6, 8, 4
+    with pytest.raises(FrontendError, match=msg):
+        lower(text, operands(M, N, K), M, N)
+
+
+def test_parse_is_pure_syntax():
+    assert parse("EPILOGUE { output = silu(input); }") == [("func", "silu")]
+    assert parse("") == []

@@ -95,3 +95,29 @@ def test_given_row_sums_one_row(CR):
     call = run(CR, A, B, ops, fold_gain=True)
     ref, _ = oracle.forward(f64(A), f64(B), oracle_ops(ops), "KN")
     assert_close(f64(call.D), ref, "D")
+
+
+def test_text_program_end_to_end(CR):
+    """An epilogue program written as statements, lowered by the front end and
+    run through the C ABI, against the oracle of the same lowered list."""
+    from gemm_epilogue_transformer_bf16_amd.frontend import lower
+    announce("text program end to end")
+    rng = np.random.default_rng(115)
+    M, N, K = 300, 264, 136
+    A, B = bf16(rng.standard_normal((M, K))), bf16(rng.standard_normal((K, N)) / np.sqrt(K))
+    stats = torch.zeros((M, 2), dtype=torch.float32, device="cuda")
+    names = {"gamma": bf16(1 + 0.1 * rng.standard_normal(K)), "bias": bf16(0.1 * rng.standard_normal(N)),
+             "R": bf16(rng.standard_normal((M, N))), "stats": stats}
+    ops = lower("""EPILOGUE {
+        output = rmsnorm(input, gamma, 1e-6);
+        output = output + bias;
+        output = gelu(output);
+        output = output + 0.5 * R;
+        stats[0] = rowsum(output);
+        stats[1] = rowsumsq(output);
+    }""", names, M, N)
+    call = run(CR, A, B, ops)
+    ref, reds = oracle.forward(f64(A), f64(B), oracle_ops(ops), "KN")
+    assert_close(f64(call.D), ref, "D")
+    assert_close(f64(stats)[:, 0], reds[0][2], "rowsum")
+    assert_close(f64(stats)[:, 1], reds[1][2], "rowsumsq")
