@@ -1,13 +1,13 @@
 """fp64 CPU oracle (test infrastructure only; never imported by the product path)."""
 from .coda_oracle import (
     gelu_tanh, gelu_tanh_grad, sigmoid, silu, swiglu_pair, rms, rmsnorm,
-    deferred_rmsnorm_gemm, layernorm, ln_fold, deferred_layernorm_gemm,
+    deferred_rmsnorm_gemm, rmsnorm_backward, layernorm, ln_fold, deferred_layernorm_gemm,
     logical_b, gemm, apply_epilogue, forward,
 )
 from .run import run_workload, resolve_program
 
 __all__ = [
     "gelu_tanh", "gelu_tanh_grad", "sigmoid", "silu", "swiglu_pair", "rms", "rmsnorm",
-    "deferred_rmsnorm_gemm", "layernorm", "ln_fold", "deferred_layernorm_gemm", "logical_b", "gemm", "apply_epilogue", "forward",
+    "deferred_rmsnorm_gemm", "rmsnorm_backward", "layernorm", "ln_fold", "deferred_layernorm_gemm", "logical_b", "gemm", "apply_epilogue", "forward",
     "run_workload", "resolve_program",
 ]

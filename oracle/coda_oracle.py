@@ -36,6 +36,8 @@ Readings of points the pages leave open (each also listed in the design notes):
     per feature (beta optional, zero when absent).
   * A reduction observes the running value at its position in the list, over
     the current width (half the GEMM width after swiglu_pair).
+  * The RMS norm's backward (rmsnorm_backward) is the chain-rule gradient of
+    that same forward form; no epilogue op of the GPU path computes it yet.
 """
 from __future__ import annotations
 
@@ -126,6 +128,34 @@ def deferred_rmsnorm_gemm(X: np.ndarray, gamma: np.ndarray, B: np.ndarray, eps: 
     X = np.asarray(X, dtype=np.float64)
     C = (X * np.asarray(gamma, dtype=np.float64)[None, :]) @ np.asarray(B, dtype=np.float64)
     return C / rms(X, eps)[:, None]
+
+
+def rmsnorm_backward(X: np.ndarray, gamma: np.ndarray, eps: float, dY: np.ndarray):
+    """Gradients of the RMS norm's inputs, given dY = dL/dY for Y = rmsnorm(X, gamma, eps).
+
+    The backward half of the norm: the d9bl.com page's Fig. 4 counts gradients
+    among the Transformer operators split into a GEMM and an epilogue, and the
+    agentlenshq.com page ("How it works") has the primitives covering nearly
+    all non-attention work of both the forward and the backward pass.  The chain
+    rule through Y[i,k] = X[i,k] gamma[k] / r_i, with r_i = sqrt(mean_k X[i,k]^2
+    + eps) and dr_i/dX[i,k] = X[i,k] / (K r_i), gives
+
+        dgamma[k] = sum_i dY[i,k] X[i,k] / r_i
+        dX[i,k]   = gamma[k] dY[i,k] / r_i - X[i,k] * s_i / (K r_i^3),
+        s_i       = sum_j gamma[j] dY[i,j] X[i,j].
+
+    Returns (dX, dgamma).
+    """
+    X = np.asarray(X, dtype=np.float64)
+    dY = np.asarray(dY, dtype=np.float64)
+    g = np.asarray(gamma, dtype=np.float64)
+    K = X.shape[1]
+    r = rms(X, eps)
+    G = dY * g[None, :]                       # dL/d(X / r): the gain's factor
+    s = np.sum(G * X, axis=1)                 # the row dot product of the second term
+    dX = G / r[:, None] - X * (s / (K * r ** 3))[:, None]
+    dgamma = np.sum(dY * X / r[:, None], axis=0)
+    return dX, dgamma
 
 
 # --- mean-centred row norm (LayerNorm; zeli.app comment, d9bl.com Fig. 4) ---

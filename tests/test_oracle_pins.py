@@ -621,3 +621,98 @@ def test_run_workload_matches_brute_force_on_every_program(idx):
     for name in outs:
         assert np.array_equal(outs_sub[name], outs[name][rows])
         assert np.all(np.isfinite(outs[name]))
+
+
+# --- RMSNorm backward (gradients among d9bl.com Fig. 4's operators; agentlenshq.com "How it works") ---
+
+def _rms_bwd_fd_error(bwd, seed=21, T=5, K=6, eps=1e-2):
+    """Largest relative error of ``bwd``'s (dX, dgamma) against central
+    differences of L = sum(dY * rmsnorm(X, gamma, eps))."""
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((T, K)) * np.array([0.05, 0.3, 1.0, 3.0, 10.0])[:T, None]
+    g = 1 + 0.3 * rng.standard_normal(K)
+    dY = rng.standard_normal((T, K))
+    dX, dg = bwd(X, g, eps, dY)
+    h = 1e-6
+
+    def L(Xp, gp):
+        return float(np.sum(dY * oracle.rmsnorm(Xp, gp, eps)))
+    fdX = np.zeros((T, K))
+    for i in range(T):
+        for k in range(K):
+            E = np.zeros((T, K))
+            E[i, k] = h * max(1.0, abs(X[i, k]))
+            fdX[i, k] = (L(X + E, g) - L(X - E, g)) / (2 * E[i, k])
+    fdg = np.array([(L(X, g + h * e) - L(X, g - h * e)) / (2 * h) for e in np.eye(K)])
+    scale = max(np.abs(fdX).max(), np.abs(fdg).max())
+    return max(np.abs(dX - fdX).max(), np.abs(dg - fdg).max()) / scale
+
+
+def test_rmsnorm_backward_matches_finite_differences():
+    assert _rms_bwd_fd_error(oracle.rmsnorm_backward) < 1e-6
+
+
+def test_rmsnorm_backward_closed_forms():
+    rng = np.random.default_rng(22)
+    T, K = 9, 40
+    X = rng.standard_normal((T, K)) * rng.uniform(0.1, 5.0, (T, 1))
+    g = 1 + 0.2 * rng.standard_normal(K)
+    dY = rng.standard_normal((T, K))
+    eps = 1e-3
+    dX, _ = oracle.rmsnorm_backward(X, g, eps, dY)
+    r = oracle.rms(X, eps)
+    s = np.sum(dY * g * X, axis=1)
+    # x . dx = eps s / r^3: zero without eps, where the norm is scale invariant
+    assert np.allclose(np.sum(X * dX, axis=1), eps * s / r ** 3, rtol=1e-10, atol=1e-13)
+    dX0, _ = oracle.rmsnorm_backward(X, g, 0.0, dY)
+    assert np.allclose(np.sum(X * dX0, axis=1), 0.0, atol=1e-12 * np.abs(dX0).max() * np.abs(X).max() * K)
+    # without eps the norm is homogeneous of degree 0: dX(cX) = dX(X) / c
+    dXc, dgc = oracle.rmsnorm_backward(3.5 * X, g, 0.0, dY)
+    assert np.allclose(dXc, dX0 / 3.5, rtol=1e-12, atol=1e-15)
+    assert np.allclose(dgc, oracle.rmsnorm_backward(X, g, 0.0, dY)[1], rtol=1e-12)
+    # one feature without eps: y = sign(x) gamma, constant in x
+    dX1, dg1 = oracle.rmsnorm_backward(np.array([[2.0], [-0.5]]), np.array([1.7]), 0.0, np.array([[0.3], [-2.0]]))
+    assert np.allclose(dX1, 0.0, atol=1e-15)
+    assert np.allclose(dg1, [0.3 * 1.0 + (-2.0) * (-1.0)])
+
+
+def test_rmsnorm_backward_row_dot_through_the_projection():
+    # With Y = rmsnorm(X) feeding P = Y W and dY = dP W^T, the row dot product
+    # s_i = sum_j gamma_j dY_ij X_ij equals r_i * sum_l dP_il P_il: the term of
+    # the norm's gradient that spans the whole row can be gathered from the
+    # projection's output side, where each row is one tile row of the GEMM.
+    rng = np.random.default_rng(23)
+    T, K, Nn = 6, 10, 7
+    X, W = rng.standard_normal((T, K)), rng.standard_normal((K, Nn))
+    g, dP, eps = 1 + 0.1 * rng.standard_normal(K), rng.standard_normal((T, Nn)), 1e-5
+    P = oracle.rmsnorm(X, g, eps) @ W
+    dY = dP @ W.T
+    s = np.sum(g * dY * X, axis=1)
+    assert np.allclose(s, oracle.rms(X, eps) * np.sum(dP * P, axis=1), rtol=1e-12)
+
+
+def test_planted_rmsnorm_backward_mistakes_are_caught():
+    def dropped_term(X, g, eps, dY):
+        dX, dg = oracle.rmsnorm_backward(X, g, eps, dY)
+        r = oracle.rms(X, eps)
+        return dY * g / r[:, None], dg
+
+    def unbiased_mean(X, g, eps, dY):
+        dX, dg = oracle.rmsnorm_backward(X, g, eps, dY)
+        K = X.shape[1]
+        r = oracle.rms(X, eps)
+        s = np.sum(dY * g * X, axis=1)
+        return dX + X * (s / (K * r ** 3) - s / ((K - 1) * r ** 3))[:, None], dg
+
+    def r_squared(X, g, eps, dY):
+        dX, dg = oracle.rmsnorm_backward(X, g, eps, dY)
+        K = X.shape[1]
+        r = oracle.rms(X, eps)
+        s = np.sum(dY * g * X, axis=1)
+        return dX + X * (s / (K * r ** 3) - s / (K * r ** 2))[:, None], dg
+
+    def gain_gradient_without_norm(X, g, eps, dY):
+        dX, _ = oracle.rmsnorm_backward(X, g, eps, dY)
+        return dX, np.sum(dY * X, axis=0)
+    for planted in (dropped_term, unbiased_mean, r_squared, gain_gradient_without_norm):
+        assert _rms_bwd_fd_error(planted) > 1e-3, planted.__name__
