@@ -51,8 +51,9 @@ GELU_CUBIC = 0.044715
 
 # op names understood by the oracle (its own vocabulary; the HIP path has its own enum)
 ELEMENTWISE_OPS = ("scale", "scale_row", "scale_col", "add_col", "add_row", "add_mat",
-                   "gelu_tanh", "silu", "swiglu_pair", "mul_dgelu_tanh")
-REDUCTION_OPS = ("row_sum", "row_sumsq", "row_mean")
+                   "gelu_tanh", "silu", "swiglu_pair", "mul_dgelu_tanh", "rms_bwd")
+# row_dot: sum over the row of the running value times a matrix operand
+REDUCTION_OPS = ("row_sum", "row_sumsq", "row_mean", "row_dot")
 # reductions over the rows of the output, one value per column (the bias
 # gradient of a backward layer is the column sum of its output gradient)
 COLUMN_REDUCTION_OPS = ("col_sum", "col_sumsq")
@@ -253,6 +254,10 @@ def apply_epilogue(C: np.ndarray, ops: Sequence[Tuple[str, Dict]]) -> Tuple[np.n
             v = swiglu_pair(v)
         elif name == "mul_dgelu_tanh":
             v = v * gelu_tanh_grad(np.asarray(args["mat"], dtype=np.float64))
+        elif name == "rms_bwd":
+            # v is dL/dY of Y = rmsnorm(x, gamma, eps); the op's value is dL/dx
+            # (the plain gradient; row statistics a caller may pass are ignored)
+            v = rmsnorm_backward(args["x"], args["gamma"], float(args["eps"]), v)[0]
         elif name == "row_sum":
             reductions.append((name, args, np.sum(v, axis=1)))
         elif name == "row_sumsq":
@@ -262,6 +267,8 @@ def apply_epilogue(C: np.ndarray, ops: Sequence[Tuple[str, Dict]]) -> Tuple[np.n
             if width == 0:
                 raise ValueError("row_mean over an empty row is undefined")
             reductions.append((name, args, np.sum(v, axis=1) / width))
+        elif name == "row_dot":
+            reductions.append((name, args, np.sum(v * np.asarray(args["mat"], dtype=np.float64), axis=1)))
         elif name == "col_sum":
             reductions.append((name, args, np.sum(v, axis=0)))
         elif name == "col_sumsq":

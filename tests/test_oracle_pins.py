@@ -716,3 +716,40 @@ def test_planted_rmsnorm_backward_mistakes_are_caught():
         return dX, np.sum(dY * X, axis=0)
     for planted in (dropped_term, unbiased_mean, r_squared, gain_gradient_without_norm):
         assert _rms_bwd_fd_error(planted) > 1e-3, planted.__name__
+
+
+def test_rms_bwd_epilogue_is_the_gradient_through_the_projection():
+    # D = rms_bwd(dP W^T) is dL/dX for L = sum(dP * (rmsnorm(X) W)): central
+    # differences through the whole forward, W stored [N x K] as the backward
+    # GEMM reads it
+    rng = np.random.default_rng(24)
+    T, K, Nn, eps = 4, 6, 5, 1e-3
+    X = rng.standard_normal((T, K)) * np.array([0.2, 1.0, 4.0, 0.05])[:, None]
+    W, g, dP = rng.standard_normal((K, Nn)), 1 + 0.3 * rng.standard_normal(K), rng.standard_normal((T, Nn))
+    D, _ = oracle.forward(dP, W, [("rms_bwd", {"x": X, "gamma": g, "eps": eps})], "NK")
+    h = 1e-6
+
+    def L(Xp):
+        return float(np.sum(dP * (oracle.rmsnorm(Xp, g, eps) @ W)))
+    fd = np.zeros((T, K))
+    for i in range(T):
+        for k in range(K):
+            E = np.zeros((T, K))
+            E[i, k] = h * max(1.0, abs(X[i, k]))
+            fd[i, k] = (L(X + E) - L(X - E)) / (2 * E[i, k])
+    assert np.allclose(D, fd, rtol=1e-6, atol=1e-7 * np.abs(fd).max())
+
+
+def test_row_dot_brute_force():
+    rng = np.random.default_rng(25)
+    M, N, K = 3, 5, 4
+    A, B, Mat = rng.integers(-3, 4, (M, K)), rng.integers(-3, 4, (K, N)), rng.integers(-3, 4, (M, N))
+    _, reds = oracle.forward(A, B, [("add_col", {"vec": np.arange(N)}), ("row_dot", {"mat": Mat})], "KN")
+    want = []
+    for i in range(M):
+        t = 0
+        for j in range(N):
+            c = sum(int(A[i, k]) * int(B[k, j]) for k in range(K)) + j
+            t += c * int(Mat[i, j])
+        want.append(t)
+    assert np.array_equal(reds[0][2], np.array(want, dtype=np.float64))
