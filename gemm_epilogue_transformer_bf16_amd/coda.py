@@ -50,6 +50,8 @@ CODA_OP_ROW_MEAN = 13
 CODA_OP_LN_ROWSCALE = 14
 CODA_OP_COL_SUM = 15
 CODA_OP_COL_SUMSQ = 16
+CODA_OP_ROW_DOT = 17
+CODA_OP_RMS_BWD = 18
 
 EXPORTED = (
     "coda_gemm_epi", "coda_gemm_unfused", "coda_validate", "coda_workspace_size",

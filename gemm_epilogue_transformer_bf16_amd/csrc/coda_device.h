@@ -98,6 +98,10 @@ struct DevOp {
   long long out_stride;
   int red_slot;         // reductions: 0..n_red-1
   int pad_;
+  const void* in2;      // RMS_BWD: gamma [width] (dtype)
+  const float* row_s;   // RMS_BWD: t per row (row_ld apart)
+  const float* row_ss;  // RMS_BWD: sum of squares of x per row
+  long long row_ld;
 };
 
 struct FusedArgs {

@@ -45,6 +45,10 @@ dev::FusedArgs make_args(const Plan& p) {
     d.out = static_cast<float*>(q.out);
     d.out_stride = q.out_stride;
     d.red_slot = q.red_slot;
+    d.in2 = q.in2;
+    d.row_s = q.row_s;
+    d.row_ss = q.row_ss;
+    d.row_ld = q.row_ld;
   }
   char* ws = static_cast<char*>(p.workspace);
   if (p.n_red > 0 && p.grid_n > 1) {

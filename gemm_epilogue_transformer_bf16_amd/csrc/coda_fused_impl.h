@@ -217,6 +217,10 @@ __device__ __forceinline__ void load_cols(const void* p, int dtype, long long co
   }
 }
 
+__device__ __forceinline__ bool is_row_reduction(int kind) {
+  return (kind >= CODA_OP_ROW_SUM && kind <= CODA_OP_ROW_MEAN) || kind == CODA_OP_ROW_DOT;
+}
+
 // Applies ops[o..] until the end of the list or a SWIGLU_PAIR (returned index).
 template <class C, bool PAIRED>
 __device__ __forceinline__ int run_ops(Chunks<C::CPL>& ch, KArgs a, int o, int M, int lane, int wn, float* red,
@@ -320,6 +324,55 @@ __device__ __forceinline__ int run_ops(Chunks<C::CPL>& ch, KArgs a, int o, int M
 #pragma unroll
           for (int off = 1; off < C::CPR; off <<= 1) p += __shfl_xor(p, off);
           if ((lane & (C::CPR - 1)) == 0) dst[ch.mloc[j]] = p;
+        }
+        break;
+      }
+      case CODA_OP_ROW_DOT: {
+        // ROW_SUM of the running value times the matrix operand
+        const int esz = op.dtype == CODA_BF16 ? 2 : 4;
+        float* dst = red + (op.red_slot * C::WN + wn) * C::BM;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+          float x[8];
+          if (ch.row[j] < M) {
+            load_cols<PAIRED>(static_cast<const char*>(op.in) + (long long)ch.row[j] * op.ld * esz, op.dtype, col,
+                              width, x);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = 0.0f;
+          }
+          float p = 0.0f;
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) p += (col + e < width) ? ch.v[j][e] * x[e] : 0.0f;
+#pragma unroll
+          for (int off = 1; off < C::CPR; off <<= 1) p += __shfl_xor(p, off);
+          if ((lane & (C::CPR - 1)) == 0) dst[ch.mloc[j]] = p;
+        }
+        break;
+      }
+      case CODA_OP_RMS_BWD: {
+        // v = gamma_j v / r_i - x_ij t_i / (width r_i^2), r_i^2 = sumsq_i / width + eps
+        const int esz = op.dtype == CODA_BF16 ? 2 : 4;
+        const float inv_w = 1.0f / float(width);
+        float g[8];
+        load_cols<PAIRED>(op.in2, op.dtype, col, width, g);
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+          float x[8];
+          float rinv = 0.0f, coef = 0.0f;
+          if (ch.row[j] < M) {
+            load_cols<PAIRED>(static_cast<const char*>(op.in) + (long long)ch.row[j] * op.ld * esz, op.dtype, col,
+                              width, x);
+            const long long ro = (long long)ch.row[j] * op.row_ld;
+            const float r2 = op.row_ss[ro] * inv_w + op.scalar;
+            rinv = 1.0f / sqrtf(r2);
+            coef = op.row_s[ro] * inv_w / r2;
+          } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = 0.0f;
+          }
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) ch.v[j][e] = g[e] * ch.v[j][e] * rinv - x[e] * coef;
         }
         break;
       }
@@ -1298,7 +1351,7 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
     const bool multi = a->grid_n > 1;
     for (int q = 0; q < a->n_ops; ++q) {
       KOp op = a->ops[q];
-      if (op.kind < CODA_OP_ROW_SUM || op.kind > CODA_OP_ROW_MEAN) continue;
+      if (!is_row_reduction(op.kind)) continue;
       const int s = op.red_slot;
       for (int t = tid; t < BM; t += C::NT) {
         float v = 0.0f;
@@ -1331,7 +1384,7 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
         // last workgroup of the tile row: sum the partials in tile order
         for (int q = 0; q < a->n_ops; ++q) {
           KOp op = a->ops[q];
-          if (op.kind < CODA_OP_ROW_SUM || op.kind > CODA_OP_ROW_MEAN) continue;
+          if (!is_row_reduction(op.kind)) continue;
           const int s = op.red_slot;
           for (int t = tid; t < BM; t += C::NT) {
             const int row = m0 + t;

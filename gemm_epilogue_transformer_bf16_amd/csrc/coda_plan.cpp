@@ -18,7 +18,8 @@ constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
 constexpr int64_t kMaxLd = int64_t(1) << 21;
 
 bool is_reduction(int kind) {
-  return kind == CODA_OP_ROW_SUM || kind == CODA_OP_ROW_SUMSQ || kind == CODA_OP_ROW_MEAN;
+  return kind == CODA_OP_ROW_SUM || kind == CODA_OP_ROW_SUMSQ || kind == CODA_OP_ROW_MEAN ||
+         kind == CODA_OP_ROW_DOT;
 }
 
 bool is_col_reduction(int kind) { return kind == CODA_OP_COL_SUM || kind == CODA_OP_COL_SUMSQ; }
@@ -28,7 +29,10 @@ bool needs_vector(int kind) {
          kind == CODA_OP_ADD_ROW;
 }
 
-bool needs_matrix(int kind) { return kind == CODA_OP_ADD_MAT || kind == CODA_OP_MUL_DGELU_TANH; }
+bool needs_matrix(int kind) {
+  return kind == CODA_OP_ADD_MAT || kind == CODA_OP_MUL_DGELU_TANH || kind == CODA_OP_ROW_DOT ||
+         kind == CODA_OP_RMS_BWD;
+}
 
 bool valid_dtype(int dt) { return dt == CODA_BF16 || dt == CODA_F32; }
 
@@ -224,7 +228,7 @@ int build_plan(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
   int n_red = 0, n_col = 0;
   for (int i = 0; i < d->n_ops; ++i) {
     const coda_op& o = d->ops[i];
-    if (o.kind < CODA_OP_SCALE || o.kind > CODA_OP_COL_SUMSQ) {
+    if (o.kind < CODA_OP_SCALE || o.kind > CODA_OP_RMS_BWD) {
       set_error("op %d: unknown kind %d", i, o.kind);
       return CODA_ERR_INVALID_ARG;
     }
@@ -234,7 +238,9 @@ int build_plan(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
     }
     const bool ln = o.kind == CODA_OP_LN_ROWSCALE;
     const bool norm_op = ln || o.kind == CODA_OP_RMS_ROWSCALE;
-    if ((!ln && o.in2) || (!norm_op && (o.row_sum || o.row_sumsq)) || (!ln && o.row_sum)) {
+    const bool bwd = o.kind == CODA_OP_RMS_BWD;
+    if ((!ln && !bwd && o.in2) || (!norm_op && !bwd && (o.row_sum || o.row_sumsq)) ||
+        (!ln && !bwd && o.row_sum)) {
       set_error("op %d: in2 / row_sum / row_sumsq not used by this op must be NULL", i);
       return CODA_ERR_INVALID_ARG;
     }
@@ -307,6 +313,35 @@ int build_plan(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
     q.out_stride = o.out_stride;
     q.red_slot = -1;
     q.width = width;
+    q.in2 = nullptr;
+    q.row_s = q.row_ss = nullptr;
+    q.row_ld = 0;
+    if (bwd) {
+      if (width == 0) {
+        set_error("op %d: RMS_BWD needs width > 0", i);
+        return CODA_ERR_INVALID_ARG;
+      }
+      if (!o.in2 || !o.row_sum || !o.row_sumsq) {
+        set_error("op %d: RMS_BWD needs gamma in in2 and the row vectors row_sum (t) and row_sumsq", i);
+        return CODA_ERR_INVALID_ARG;
+      }
+      if (!aligned(o.in2, 16)) {
+        set_error("op %d: RMS_BWD gamma must be 16-byte aligned", i);
+        return CODA_ERR_UNSUPPORTED;
+      }
+      if (o.row_ld < 1 || !aligned(o.row_sumsq, 4) || !aligned(o.row_sum, 4)) {
+        set_error("op %d: RMS_BWD row vectors: row_ld >= 1 and 4-byte alignment", i);
+        return CODA_ERR_INVALID_ARG;
+      }
+      if (!(std::isfinite(o.scalar) && o.scalar >= 0.0f)) {
+        set_error("op %d: RMS_BWD eps must be finite and >= 0", i);
+        return CODA_ERR_INVALID_ARG;
+      }
+      q.in2 = o.in2;
+      q.row_s = static_cast<const float*>(o.row_sum);
+      q.row_ss = static_cast<const float*>(o.row_sumsq);
+      q.row_ld = o.row_ld;
+    }
     if (needs_vector(o.kind) || needs_matrix(o.kind)) {
       if (!o.in) {
         set_error("op %d: input is NULL", i);
@@ -482,6 +517,13 @@ int build_plan(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
           set_error("op %d input overlaps D (only an exact in-place ADD_MAT is allowed)", i);
           return CODA_ERR_INVALID_ARG;
         }
+      }
+      if (q.kind == CODA_OP_RMS_BWD &&
+          (overlap(matrix_extent(q.in2, 1, q.width, q.width, dtype_size(q.dtype)), eD) ||
+           overlap(matrix_extent(q.row_s, M, 1, q.row_ld, 4), eD) ||
+           overlap(matrix_extent(q.row_ss, M, 1, q.row_ld, 4), eD))) {
+        set_error("op %d: RMS_BWD gamma or row vectors overlap D", i);
+        return CODA_ERR_INVALID_ARG;
       }
       if (is_reduction(q.kind) || is_col_reduction(q.kind)) {
         Extent e = is_col_reduction(q.kind) ? matrix_extent(q.out, q.width, 1, q.out_stride, 4)

@@ -45,6 +45,10 @@ struct Op {
   int64_t out_stride;
   int red_slot;      // index among the row (or, for COL_*, the column) reductions, -1 otherwise
   int64_t width;     // width of the running value when the op runs
+  const void* in2;   // RMS_BWD: gamma [width] (dtype)
+  const float* row_s;   // RMS_BWD: t per row
+  const float* row_ss;  // RMS_BWD: sum of squares of x per row
+  int64_t row_ld;
 };
 
 struct Plan {

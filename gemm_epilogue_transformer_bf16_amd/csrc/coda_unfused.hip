@@ -173,6 +173,19 @@ __global__ void __launch_bounds__(kPassThreads) ew_kernel(const void* in, long l
           v[e] = op.kind == CODA_OP_ADD_MAT ? v[e] + op.scalar * s[e] : v[e] * gelu_tanh_grad_f(s[e]);
         break;
       }
+      case CODA_OP_RMS_BWD: {
+        float x[8], g[8];
+        const int sz = op.dtype == CODA_BF16 ? 2 : 4;
+        load8(static_cast<const char*>(op.in) + (long long)row * op.ld * sz, op.dtype, c, width, x);
+        load8(op.in2, op.dtype, c, width, g);
+        const long long ro = (long long)row * op.row_ld;
+        const float r2 = op.row_ss[ro] / float(width) + op.scalar;
+        const float rinv = 1.0f / sqrtf(r2);
+        const float coef = op.row_s[ro] / float(width) / r2;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = g[e] * v[e] * rinv - x[e] * coef;
+        break;
+      }
       case CODA_OP_GELU_TANH:
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = gelu_tanh_f(v[e]);
@@ -204,12 +217,22 @@ __global__ void __launch_bounds__(kPassThreads) rowred_kernel(const void* in, lo
   const int esz = io_dtype == CODA_BF16 ? 2 : 4;
   const char* r = static_cast<const char*>(in) + (long long)row * ldi * esz;
   const bool sq = op.kind == CODA_OP_ROW_SUMSQ;
+  const bool dot = op.kind == CODA_OP_ROW_DOT;
+  const char* mrow = dot ? static_cast<const char*>(op.in) + (long long)row * op.ld * (op.dtype == CODA_BF16 ? 2 : 4)
+                         : nullptr;
   float acc = 0.0f;
   for (long long c = lane * 8LL; c < width; c += 64 * 8) {
     float v[8];
     load8(r, io_dtype, c, width, v);
+    if (dot) {
+      float m[8];
+      load8(mrow, op.dtype, c, width, m);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc += sq ? v[e] * v[e] : v[e];
+      for (int e = 0; e < 8; ++e) acc += v[e] * m[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc += sq ? v[e] * v[e] : v[e];
+    }
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
@@ -256,7 +279,8 @@ __global__ void __launch_bounds__(kPassThreads) colred_final_kernel(const float*
 namespace {
 
 bool is_row_reduction(int kind) {
-  return kind == CODA_OP_ROW_SUM || kind == CODA_OP_ROW_SUMSQ || kind == CODA_OP_ROW_MEAN;
+  return kind == CODA_OP_ROW_SUM || kind == CODA_OP_ROW_SUMSQ || kind == CODA_OP_ROW_MEAN ||
+         kind == CODA_OP_ROW_DOT;
 }
 
 bool is_col_reduction(int kind) { return kind == CODA_OP_COL_SUM || kind == CODA_OP_COL_SUMSQ; }
@@ -277,6 +301,10 @@ dev::DevOp to_dev(const Op& q) {
   d.out = static_cast<float*>(q.out);
   d.out_stride = q.out_stride;
   d.red_slot = q.red_slot;
+  d.in2 = q.in2;
+  d.row_s = q.row_s;
+  d.row_ss = q.row_ss;
+  d.row_ld = q.row_ld;
   return d;
 }
 

@@ -31,6 +31,8 @@ OPCODES = {
     "ln_rowscale": C.CODA_OP_LN_ROWSCALE,
     "col_sum": C.CODA_OP_COL_SUM,
     "col_sumsq": C.CODA_OP_COL_SUMSQ,
+    "row_dot": C.CODA_OP_ROW_DOT,
+    "rms_bwd": C.CODA_OP_RMS_BWD,
 }
 
 TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
@@ -148,7 +150,23 @@ class Call:
                 if name == "ln_rowscale":
                     o.row_sum = t.data_ptr() + 4 * int(args["row_s_col"])
                 o.row_ld = t.stride(0)
-            if name in ("row_sum", "row_sumsq", "row_mean", "col_sum", "col_sumsq"):
+            if name == "rms_bwd":
+                # in = x [M x width], in2 = gamma [width] (x's dtype); the row
+                # statistics are columns of a 2-D fp32 tensor: the sums of squares
+                # of x in `sumsq_col`, t in `t_col`
+                x, g, st = args["x"], args["gamma"], args["stats"]
+                if g.dtype != x.dtype:
+                    raise ValueError("rms_bwd: gamma must have x's dtype")
+                self._keep += [x, g, st]
+                o.in_ = x.data_ptr()
+                o.in_dtype = CODA_DT[x.dtype]
+                o.ld = x.stride(0)
+                o.in2 = g.data_ptr()
+                o.scalar = float(args["eps"])
+                o.row_sumsq = st.data_ptr() + 4 * int(args.get("sumsq_col", 0))
+                o.row_sum = st.data_ptr() + 4 * int(args.get("t_col", 1))
+                o.row_ld = st.stride(0)
+            if name in ("row_sum", "row_sumsq", "row_mean", "col_sum", "col_sumsq", "row_dot"):
                 out = args["out"]
                 self._keep.append(out)
                 col = int(args.get("col", 0))

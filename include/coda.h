@@ -159,7 +159,24 @@ typedef enum {
      rows of the running value (COL_SUM) or of its square (COL_SUMSQ) at the
      op's position.  At most CODA_MAX_COL_REDUCTIONS per list. */
   CODA_OP_COL_SUM = 15,
-  CODA_OP_COL_SUMSQ = 16
+  CODA_OP_COL_SUMSQ = 16,
+  /* the RMS norm's backward (gradients are among the operators the d9bl.com
+     page's Fig. 4 splits into a GEMM and an epilogue; the agentlenshq.com page,
+     "How it works", has the primitives cover the backward pass too).
+     ROW_DOT is a row reduction like ROW_SUM, counted among them: it writes
+     sum_j v[i,j] * in[i*ld + j] over the current width, in a matrix [M x width]
+     of in_dtype.  RMS_BWD takes v = dL/dY of Y = x * gamma / r (the RMS norm,
+     r_i = sqrt(sum_k x[i,k]^2 / width + eps)) and makes it dL/dx:
+       v = gamma[j] v / r_i - x[i,j] * t_i / (width * r_i^2)
+     with in = x [M x width] (in_dtype, ld), in2 = gamma [width] (in_dtype),
+     scalar = eps, row_sumsq[i*row_ld] = sum_k x[i,k]^2 and
+     row_sum[i*row_ld] = t_i, both fp32.  t_i is s_i / r_i with
+     s_i = sum_j gamma[j] v[i,j] x[i,j], the part of the gradient that spans
+     the row.  When v = dP W^T for P = Y W, t_i = sum_l dP[i,l] P[i,l]: the
+     ROW_DOT of dP against P in the epilogue of the GEMM that produced dP,
+     so this op needs no pass over its own row. */
+  CODA_OP_ROW_DOT = 17,
+  CODA_OP_RMS_BWD = 18
 } coda_op_kind;
 
 typedef struct {
@@ -171,9 +188,10 @@ typedef struct {
   int32_t reserved0;    /* must be 0                                                 */
   void* out;            /* reductions: fp32 output (device)                          */
   int64_t out_stride;   /* reductions: element stride between rows of `out`, >= 1   */
-  const void* in2;      /* LN_ROWSCALE: fp32 u [N]; NULL for every other op          */
-  const void* row_sum;  /* LN_ROWSCALE: given fp32 row sums of A, or NULL            */
-  const void* row_sumsq;/* RMS/LN_ROWSCALE: given fp32 row sums of squares, or NULL  */
+  const void* in2;      /* LN_ROWSCALE: fp32 u [N]; RMS_BWD: gamma; else NULL         */
+  const void* row_sum;  /* LN_ROWSCALE: given fp32 row sums of A, or NULL; RMS_BWD: t */
+  const void* row_sumsq;/* RMS/LN_ROWSCALE: given fp32 row sums of squares, or NULL;
+                           RMS_BWD: sum_k x[i,k]^2                                   */
   int64_t row_ld;       /* element stride between rows of row_sum / row_sumsq (>= 1) */
 } coda_op;
 

@@ -36,8 +36,8 @@ Readings of points the pages leave open (each also listed in the design notes):
     per feature (beta optional, zero when absent).
   * A reduction observes the running value at its position in the list, over
     the current width (half the GEMM width after swiglu_pair).
-  * The RMS norm's backward (rmsnorm_backward) is the chain-rule gradient of
-    that same forward form; no epilogue op of the GPU path computes it yet.
+  * The RMS norm's backward (rmsnorm_backward, the rms_bwd op) is the
+    chain-rule gradient of that same forward form.
 """
 from __future__ import annotations
 

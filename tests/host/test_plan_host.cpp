@@ -293,6 +293,37 @@ int main() {
     // the unfused sequence keeps column partials per chunk of rows
     EXPECT(coda_workspace_size(M, N, K, &e, 1) > coda_workspace_size(M, N, K, &d, 1));
   }
+  {  // the RMS norm's backward: ROW_DOT is a row reduction with a matrix; RMS_BWD needs x, gamma and two row vectors
+    coda_epi_desc e = base_desc(N, K);
+    e.n_ops = 2;
+    e.ops[0].kind = CODA_OP_ROW_DOT; e.ops[0].in = P(0x40000000); e.ops[0].ld = N; e.ops[0].in_dtype = CODA_BF16;
+    e.ops[0].out = Pm(0x50000000); e.ops[0].out_stride = 2;
+    e.ops[1].kind = CODA_OP_RMS_BWD; e.ops[1].in = P(0x41000000); e.ops[1].ld = N; e.ops[1].in_dtype = CODA_BF16;
+    e.ops[1].in2 = P(0x42000000); e.ops[1].row_sumsq = P(0x50000000); e.ops[1].row_sum = P(0x50000004);
+    e.ops[1].row_ld = 2; e.ops[1].scalar = 1e-5f;
+    e.workspace = Pm(0x70000000); e.workspace_bytes = coda_workspace_size(100, N, K, &e, 0);
+    coda::Plan q = plan_of(100, N, K, e);
+    EXPECT(q.n_red == 1 && q.ops[0].red_slot == 0 && q.ops[1].red_slot == -1 && q.ops[1].row_ld == 2);
+    EXPECT(coda_validate(A, B, 100, N, K, &e, 0) == CODA_OK);
+    coda_epi_desc f = e; f.ops[1].in2 = nullptr;
+    EXPECT(coda_validate(A, B, 100, N, K, &f, 0) == CODA_ERR_INVALID_ARG);   // no gamma
+    f = e; f.ops[1].row_sum = nullptr;
+    EXPECT(coda_validate(A, B, 100, N, K, &f, 0) == CODA_ERR_INVALID_ARG);   // no t
+    f = e; f.ops[1].row_ld = 0;
+    EXPECT(coda_validate(A, B, 100, N, K, &f, 0) == CODA_ERR_INVALID_ARG);
+    f = e; f.ops[1].scalar = -1.0f;
+    EXPECT(coda_validate(A, B, 100, N, K, &f, 0) == CODA_ERR_INVALID_ARG);   // eps < 0
+    f = e; f.ops[1].ld = N - 8;
+    EXPECT(coda_validate(A, B, 100, N, K, &f, 0) == CODA_ERR_INVALID_ARG);   // x narrower than the row
+    f = e; f.ops[0].in = nullptr;
+    EXPECT(coda_validate(A, B, 100, N, K, &f, 0) == CODA_ERR_INVALID_ARG);   // ROW_DOT without its matrix
+    f = e; f.ops[0].in2 = P(0x42000000);
+    EXPECT(coda_validate(A, B, 100, N, K, &f, 0) == CODA_ERR_INVALID_ARG);   // in2 only on LN_ROWSCALE / RMS_BWD
+    f = e; f.ops[1].in2 = P(0x30000000);
+    EXPECT(coda_validate(A, B, 100, N, K, &f, 0) == CODA_ERR_INVALID_ARG);   // gamma over D
+    f = e; f.ops[1].kind = 19;
+    EXPECT(coda_validate(A, B, 100, N, K, &f, 0) == CODA_ERR_INVALID_ARG);   // unknown kind
+  }
   {  // A stored [K x M] (weight gradient): M % 8, lda >= M, bf16, no row norm
     coda_epi_desc e = base_desc(N, K); e.a_layout = CODA_A_KM; e.lda = 304;
     EXPECT(coda_validate(A, B, 304, N, K, &e, 0) == CODA_OK);
