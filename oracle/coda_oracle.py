@@ -56,7 +56,7 @@ ELEMENTWISE_OPS = ("scale", "scale_row", "scale_col", "add_col", "add_row", "add
 REDUCTION_OPS = ("row_sum", "row_sumsq", "row_mean", "row_dot")
 # reductions over the rows of the output, one value per column (the bias
 # gradient of a backward layer is the column sum of its output gradient)
-COLUMN_REDUCTION_OPS = ("col_sum", "col_sumsq")
+COLUMN_REDUCTION_OPS = ("col_sum", "col_sumsq", "rms_dgamma")
 
 
 # --- pairwise / elementwise transforms (agentlenshq.com, "How it works": pairwise) ---
@@ -273,6 +273,10 @@ def apply_epilogue(C: np.ndarray, ops: Sequence[Tuple[str, Dict]]) -> Tuple[np.n
             reductions.append((name, args, np.sum(v, axis=0)))
         elif name == "col_sumsq":
             reductions.append((name, args, np.sum(v * v, axis=0)))
+        elif name == "rms_dgamma":
+            # v is dL/dY of Y = rmsnorm(x, gamma, eps): dL/dgamma, one value per column
+            x = np.asarray(args["x"], dtype=np.float64)
+            reductions.append((name, args, np.sum(v * x / rms(x, float(args["eps"]))[:, None], axis=0)))
         elif name in ("rms_rowscale", "ln_rowscale"):
             raise ValueError(f"{name} is applied to A by forward(); it must come first")
         else:

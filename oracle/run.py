@@ -12,7 +12,7 @@ import numpy as np
 
 from workloads.gen import to_f64
 
-from .coda_oracle import forward
+from .coda_oracle import COLUMN_REDUCTION_OPS, forward
 
 
 def _row_shaped(spec, name: str) -> bool:
@@ -57,7 +57,7 @@ def run_workload(spec, inputs: Dict[str, np.ndarray], rows: Optional[Sequence[in
     D, reds = forward(A, B, ops, spec.b_layout)
     # outputs of column reductions are indexed by column (over the rows given);
     # all others by row
-    col_outs = {args["out"] for name, args in spec.program if name in ("col_sum", "col_sumsq")}
+    col_outs = {args["out"] for name, args in spec.program if name in COLUMN_REDUCTION_OPS}
     outs = {}
     for oname, shape in spec.outputs:
         outs[oname] = np.full((shape[0] if oname in col_outs else A.shape[0], shape[1]), np.nan)

@@ -753,3 +753,20 @@ def test_row_dot_brute_force():
             t += c * int(Mat[i, j])
         want.append(t)
     assert np.array_equal(reds[0][2], np.array(want, dtype=np.float64))
+
+
+def test_rms_dgamma_is_the_gain_gradient_through_the_projection():
+    # the rms_dgamma column reduction of dP W^T is dL/dgamma for
+    # L = sum(dP * (rmsnorm(X, gamma) W)), by central differences in gamma
+    rng = np.random.default_rng(26)
+    T, K, Nn, eps = 5, 6, 4, 1e-3
+    X = rng.standard_normal((T, K)) * np.array([0.2, 1.0, 4.0, 0.05, 2.0])[:, None]
+    W, g, dP = rng.standard_normal((K, Nn)), 1 + 0.3 * rng.standard_normal(K), rng.standard_normal((T, Nn))
+    _, reds = oracle.forward(dP, W, [("rms_dgamma", {"x": X, "eps": eps}), ("rms_bwd", {"x": X, "gamma": g, "eps": eps})],
+                             "NK")
+    h = 1e-6
+
+    def L(gp):
+        return float(np.sum(dP * (oracle.rmsnorm(X, gp, eps) @ W)))
+    fd = np.array([(L(g + h * e) - L(g - h * e)) / (2 * h) for e in np.eye(K)])
+    assert np.allclose(reds[0][2], fd, rtol=1e-6, atol=1e-8)
