@@ -52,6 +52,7 @@ CODA_OP_COL_SUM = 15
 CODA_OP_COL_SUMSQ = 16
 CODA_OP_ROW_DOT = 17
 CODA_OP_RMS_BWD = 18
+CODA_OP_RMS_DGAMMA = 19
 
 EXPORTED = (
     "coda_gemm_epi", "coda_gemm_unfused", "coda_validate", "coda_workspace_size",

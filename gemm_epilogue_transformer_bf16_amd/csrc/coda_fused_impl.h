@@ -221,6 +221,10 @@ __device__ __forceinline__ bool is_row_reduction(int kind) {
   return (kind >= CODA_OP_ROW_SUM && kind <= CODA_OP_ROW_MEAN) || kind == CODA_OP_ROW_DOT;
 }
 
+__device__ __forceinline__ bool is_col_reduction(int kind) {
+  return kind == CODA_OP_COL_SUM || kind == CODA_OP_COL_SUMSQ || kind == CODA_OP_RMS_DGAMMA;
+}
+
 // Applies ops[o..] until the end of the list or a SWIGLU_PAIR (returned index).
 template <class C, bool PAIRED>
 __device__ __forceinline__ int run_ops(Chunks<C::CPL>& ch, KArgs a, int o, int M, int lane, int wn, float* red,
@@ -373,6 +377,35 @@ __device__ __forceinline__ int run_ops(Chunks<C::CPL>& ch, KArgs a, int o, int M
           }
 #pragma unroll
           for (int e = 0; e < EPC; ++e) ch.v[j][e] = g[e] * ch.v[j][e] * rinv - x[e] * coef;
+        }
+        break;
+      }
+      case CODA_OP_RMS_DGAMMA: {
+        // column sums of v * x / r_i, r_i^2 = sumsq_i / width + eps, reduced as COL_SUM
+        const int esz = op.dtype == CODA_BF16 ? 2 : 4;
+        const float inv_w = 1.0f / float(width);
+        float p[EPC];
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) p[e] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j)
+          if (ch.row[j] < M) {
+            float x[8];
+            load_cols<PAIRED>(static_cast<const char*>(op.in) + (long long)ch.row[j] * op.ld * esz, op.dtype, col,
+                              width, x);
+            const float rinv = 1.0f / sqrtf(op.row_ss[(long long)ch.row[j] * op.row_ld] * inv_w + op.scalar);
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) p[e] += ch.v[j][e] * x[e] * rinv;
+          }
+#pragma unroll
+        for (int off = C::CPR; off < 64; off <<= 1)
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) p[e] += __shfl_xor(p[e], off);
+        if (lane < C::CPR) {
+          const int tcol = wn * C::WTN + 8 * lane;
+          float* dst = colp + ((op.red_slot * C::WM + wm) * C::MI + mi) * C::BN + (PAIRED ? tcol / 2 : tcol);
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) dst[e] = p[e];
         }
         break;
       }
@@ -1411,7 +1444,7 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
     const bool multi = a->grid_m > 1;
     for (int q = 0; q < a->n_ops; ++q) {
       KOp op = a->ops[q];
-      if (op.kind != CODA_OP_COL_SUM && op.kind != CODA_OP_COL_SUMSQ) continue;
+      if (!is_col_reduction(op.kind)) continue;
       const int s = op.red_slot;
       const bool paired = op.width != N;   // after SWIGLU_PAIR: half the columns
       const int cols = paired ? BN / 2 : BN;
@@ -1446,7 +1479,7 @@ __global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
       if (*flag) {
         for (int q = 0; q < a->n_ops; ++q) {
           KOp op = a->ops[q];
-          if (op.kind != CODA_OP_COL_SUM && op.kind != CODA_OP_COL_SUMSQ) continue;
+          if (!is_col_reduction(op.kind)) continue;
           const int s = op.red_slot;
           const bool paired = op.width != N;
           const int cols = paired ? BN / 2 : BN;

@@ -22,7 +22,9 @@ bool is_reduction(int kind) {
          kind == CODA_OP_ROW_DOT;
 }
 
-bool is_col_reduction(int kind) { return kind == CODA_OP_COL_SUM || kind == CODA_OP_COL_SUMSQ; }
+bool is_col_reduction(int kind) {
+  return kind == CODA_OP_COL_SUM || kind == CODA_OP_COL_SUMSQ || kind == CODA_OP_RMS_DGAMMA;
+}
 
 bool needs_vector(int kind) {
   return kind == CODA_OP_SCALE_ROW || kind == CODA_OP_SCALE_COL || kind == CODA_OP_ADD_COL ||
@@ -31,7 +33,7 @@ bool needs_vector(int kind) {
 
 bool needs_matrix(int kind) {
   return kind == CODA_OP_ADD_MAT || kind == CODA_OP_MUL_DGELU_TANH || kind == CODA_OP_ROW_DOT ||
-         kind == CODA_OP_RMS_BWD;
+         kind == CODA_OP_RMS_BWD || kind == CODA_OP_RMS_DGAMMA;
 }
 
 bool valid_dtype(int dt) { return dt == CODA_BF16 || dt == CODA_F32; }
@@ -228,7 +230,7 @@ int build_plan(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
   int n_red = 0, n_col = 0;
   for (int i = 0; i < d->n_ops; ++i) {
     const coda_op& o = d->ops[i];
-    if (o.kind < CODA_OP_SCALE || o.kind > CODA_OP_RMS_BWD) {
+    if (o.kind < CODA_OP_SCALE || o.kind > CODA_OP_RMS_DGAMMA) {
       set_error("op %d: unknown kind %d", i, o.kind);
       return CODA_ERR_INVALID_ARG;
     }
@@ -239,7 +241,8 @@ int build_plan(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
     const bool ln = o.kind == CODA_OP_LN_ROWSCALE;
     const bool norm_op = ln || o.kind == CODA_OP_RMS_ROWSCALE;
     const bool bwd = o.kind == CODA_OP_RMS_BWD;
-    if ((!ln && !bwd && o.in2) || (!norm_op && !bwd && (o.row_sum || o.row_sumsq)) ||
+    const bool dgam = o.kind == CODA_OP_RMS_DGAMMA;
+    if ((!ln && !bwd && o.in2) || (!norm_op && !bwd && !dgam && o.row_sumsq) ||
         (!ln && !bwd && o.row_sum)) {
       set_error("op %d: in2 / row_sum / row_sumsq not used by this op must be NULL", i);
       return CODA_ERR_INVALID_ARG;
@@ -339,6 +342,18 @@ int build_plan(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
       }
       q.in2 = o.in2;
       q.row_s = static_cast<const float*>(o.row_sum);
+      q.row_ss = static_cast<const float*>(o.row_sumsq);
+      q.row_ld = o.row_ld;
+    }
+    if (dgam) {
+      if (!o.row_sumsq || o.row_ld < 1 || !aligned(o.row_sumsq, 4)) {
+        set_error("op %d: RMS_DGAMMA needs row_sumsq (4-byte aligned) and row_ld >= 1", i);
+        return CODA_ERR_INVALID_ARG;
+      }
+      if (!(std::isfinite(o.scalar) && o.scalar >= 0.0f)) {
+        set_error("op %d: RMS_DGAMMA eps must be finite and >= 0", i);
+        return CODA_ERR_INVALID_ARG;
+      }
       q.row_ss = static_cast<const float*>(o.row_sumsq);
       q.row_ld = o.row_ld;
     }
@@ -517,6 +532,10 @@ int build_plan(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
           set_error("op %d input overlaps D (only an exact in-place ADD_MAT is allowed)", i);
           return CODA_ERR_INVALID_ARG;
         }
+      }
+      if (q.kind == CODA_OP_RMS_DGAMMA && overlap(matrix_extent(q.row_ss, M, 1, q.row_ld, 4), eD)) {
+        set_error("op %d: RMS_DGAMMA row_sumsq overlaps D", i);
+        return CODA_ERR_INVALID_ARG;
       }
       if (q.kind == CODA_OP_RMS_BWD &&
           (overlap(matrix_extent(q.in2, 1, q.width, q.width, dtype_size(q.dtype)), eD) ||

@@ -253,12 +253,22 @@ __global__ void __launch_bounds__(kPassThreads) colred_partial_kernel(const void
   const int r1 = min(M, r0 + kColChunk);
   const int esz = io_dtype == CODA_BF16 ? 2 : 4;
   const bool sq = op.kind == CODA_OP_COL_SUMSQ;
+  const bool dg = op.kind == CODA_OP_RMS_DGAMMA;   // sum of v * x / r over the rows
+  const int xsz = op.dtype == CODA_BF16 ? 2 : 4;
   float acc[8] = {};
   for (int r = r0; r < r1; ++r) {
     float v[8];
     load8(static_cast<const char*>(in) + (long long)r * ldi * esz, io_dtype, c, width, v);
+    if (dg) {
+      float x[8];
+      load8(static_cast<const char*>(op.in) + (long long)r * op.ld * xsz, op.dtype, c, width, x);
+      const float rinv = 1.0f / sqrtf(op.row_ss[(long long)r * op.row_ld] / float(width) + op.scalar);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] += sq ? v[e] * v[e] : v[e];
+      for (int e = 0; e < 8; ++e) acc[e] += v[e] * x[e] * rinv;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += sq ? v[e] * v[e] : v[e];
+    }
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e)
@@ -283,7 +293,9 @@ bool is_row_reduction(int kind) {
          kind == CODA_OP_ROW_DOT;
 }
 
-bool is_col_reduction(int kind) { return kind == CODA_OP_COL_SUM || kind == CODA_OP_COL_SUMSQ; }
+bool is_col_reduction(int kind) {
+  return kind == CODA_OP_COL_SUM || kind == CODA_OP_COL_SUMSQ || kind == CODA_OP_RMS_DGAMMA;
+}
 
 bool is_reduction(int kind) { return is_row_reduction(kind) || is_col_reduction(kind); }
 

@@ -33,6 +33,7 @@ OPCODES = {
     "col_sumsq": C.CODA_OP_COL_SUMSQ,
     "row_dot": C.CODA_OP_ROW_DOT,
     "rms_bwd": C.CODA_OP_RMS_BWD,
+    "rms_dgamma": C.CODA_OP_RMS_DGAMMA,
 }
 
 TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
@@ -166,7 +167,18 @@ class Call:
                 o.row_sumsq = st.data_ptr() + 4 * int(args.get("sumsq_col", 0))
                 o.row_sum = st.data_ptr() + 4 * int(args.get("t_col", 1))
                 o.row_ld = st.stride(0)
-            if name in ("row_sum", "row_sumsq", "row_mean", "col_sum", "col_sumsq", "row_dot"):
+            if name == "rms_dgamma":
+                # in = x [M x width]; the sums of squares of x in column
+                # `sumsq_col` of a 2-D fp32 tensor
+                x, st = args["x"], args["stats"]
+                self._keep += [x, st]
+                o.in_ = x.data_ptr()
+                o.in_dtype = CODA_DT[x.dtype]
+                o.ld = x.stride(0)
+                o.scalar = float(args["eps"])
+                o.row_sumsq = st.data_ptr() + 4 * int(args.get("sumsq_col", 0))
+                o.row_ld = st.stride(0)
+            if name in ("row_sum", "row_sumsq", "row_mean", "col_sum", "col_sumsq", "row_dot", "rms_dgamma"):
                 out = args["out"]
                 self._keep.append(out)
                 col = int(args.get("col", 0))

@@ -176,7 +176,13 @@ typedef enum {
      ROW_DOT of dP against P in the epilogue of the GEMM that produced dP,
      so this op needs no pass over its own row. */
   CODA_OP_ROW_DOT = 17,
-  CODA_OP_RMS_BWD = 18
+  CODA_OP_RMS_BWD = 18,
+  /* the RMS norm's gain gradient, a column reduction (counted among them):
+     with v = dL/dY as for RMS_BWD, writes sum_i v[i,j] * x[i,j] / r_i to
+     ((float*)out)[j*out_stride], in = x [M x width] (in_dtype, ld),
+     row_sumsq[i*row_ld] = sum_k x[i,k]^2 (fp32), scalar = eps.  Placed before
+     RMS_BWD in the same list, it reads the same x and row statistics. */
+  CODA_OP_RMS_DGAMMA = 19
 } coda_op_kind;
 
 typedef struct {
@@ -191,7 +197,7 @@ typedef struct {
   const void* in2;      /* LN_ROWSCALE: fp32 u [N]; RMS_BWD: gamma; else NULL         */
   const void* row_sum;  /* LN_ROWSCALE: given fp32 row sums of A, or NULL; RMS_BWD: t */
   const void* row_sumsq;/* RMS/LN_ROWSCALE: given fp32 row sums of squares, or NULL;
-                           RMS_BWD: sum_k x[i,k]^2                                   */
+                           RMS_BWD, RMS_DGAMMA: sum_k x[i,k]^2                       */
   int64_t row_ld;       /* element stride between rows of row_sum / row_sumsq (>= 1) */
 } coda_op;
 

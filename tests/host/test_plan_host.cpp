@@ -321,8 +321,23 @@ int main() {
     EXPECT(coda_validate(A, B, 100, N, K, &f, 0) == CODA_ERR_INVALID_ARG);   // in2 only on LN_ROWSCALE / RMS_BWD
     f = e; f.ops[1].in2 = P(0x30000000);
     EXPECT(coda_validate(A, B, 100, N, K, &f, 0) == CODA_ERR_INVALID_ARG);   // gamma over D
-    f = e; f.ops[1].kind = 19;
+    f = e; f.ops[1].kind = 20;
     EXPECT(coda_validate(A, B, 100, N, K, &f, 0) == CODA_ERR_INVALID_ARG);   // unknown kind
+    // RMS_DGAMMA: a column reduction over x / r, before RMS_BWD
+    f = e; f.n_ops = 3; f.ops[2] = f.ops[1]; f.ops[1] = coda_op{};
+    f.ops[1].kind = CODA_OP_RMS_DGAMMA; f.ops[1].in = P(0x41000000); f.ops[1].ld = N; f.ops[1].in_dtype = CODA_BF16;
+    f.ops[1].row_sumsq = P(0x50000000); f.ops[1].row_ld = 2; f.ops[1].scalar = 1e-5f;
+    f.ops[1].out = Pm(0x52000000); f.ops[1].out_stride = 1;
+    f.workspace_bytes = coda_workspace_size(100, N, K, &f, 0);
+    coda::Plan q2 = plan_of(100, N, K, f);
+    EXPECT(q2.n_colred == 1 && q2.n_red == 1 && q2.ops[1].red_slot == 0);
+    EXPECT(coda_validate(A, B, 100, N, K, &f, 0) == CODA_OK);
+    coda_epi_desc g2 = f; g2.ops[1].row_sumsq = nullptr;
+    EXPECT(coda_validate(A, B, 100, N, K, &g2, 0) == CODA_ERR_INVALID_ARG);   // no sums of squares
+    g2 = f; g2.ops[1].row_sum = P(0x50000004);
+    EXPECT(coda_validate(A, B, 100, N, K, &g2, 0) == CODA_ERR_INVALID_ARG);   // row_sum is RMS_BWD's
+    g2 = f; g2.ops[1].out = nullptr;
+    EXPECT(coda_validate(A, B, 100, N, K, &g2, 0) == CODA_ERR_INVALID_ARG);
   }
   {  // A stored [K x M] (weight gradient): M % 8, lda >= M, bf16, no row norm
     coda_epi_desc e = base_desc(N, K); e.a_layout = CODA_A_KM; e.lda = 304;

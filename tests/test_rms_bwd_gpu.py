@@ -1,6 +1,6 @@
 """The RMS norm's backward on the GPU: ROW_DOT (a row reduction of the running
-value times a matrix) and RMS_BWD (the norm's input gradient given its row
-statistics), through the C ABI, against the fp64 oracle.  Gradients are among
+value times a matrix), RMS_BWD (the norm's input gradient given its row
+statistics) and RMS_DGAMMA (its gain gradient), through the C ABI, against the fp64 oracle.  Gradients are among
 the operators the d9bl.com page's Fig. 4 splits into a GEMM and an epilogue;
 the agentlenshq.com page ("How it works") has the primitives cover the backward
 pass as well as the forward."""
@@ -119,17 +119,24 @@ def test_rms_bwd_op(CR, shape, mode):
     X, G, W, dP = _rms_bwd_inputs(rng, M, Kf, Np)
     eps = 1e-5
     stats = f32(_stats_from_oracle(X, G, W, dP, eps))
-    ops = [("rms_bwd", {"x": X, "gamma": G, "eps": eps, "stats": stats, "sumsq_col": 0, "t_col": 1})]
+    dg = torch.zeros((Kf, 1), dtype=torch.float32, device="cuda")
+    ops = [("rms_dgamma", {"x": X, "eps": eps, "stats": stats, "sumsq_col": 0, "out": dg, "col": 0}),
+           ("rms_bwd", {"x": X, "gamma": G, "eps": eps, "stats": stats, "sumsq_col": 0, "t_col": 1})]
     call = runner.Call(dP, W, ops, "NK")
     coda.check(call.fused() if mode == "fused" else call.unfused(), mode)
     torch.cuda.synchronize()
-    ref, _ = oracle.forward(f64(dP), f64(W), [("rms_bwd", {"x": f64(X), "gamma": f64(G), "eps": eps})], "NK")
-    extra = None
+    ref, reds = oracle.forward(f64(dP), f64(W), [("rms_dgamma", {"x": f64(X), "eps": eps}),
+                                                 ("rms_bwd", {"x": f64(X), "gamma": f64(G), "eps": eps})], "NK")
+    extra = extra_g = None
     if mode == "unfused":
-        # the sequence stores dP W^T in bf16 before the norm's backward scales it by gamma / r
+        # the sequence stores dP W^T in bf16 before the norm's backward scales
+        # it by gamma / r and before the gain gradient sums it times x / r
         r = oracle.rms(f64(X), eps)
-        extra = 2.0 ** -8 * np.abs(f64(G))[None, :] * np.abs(f64(dP) @ f64(W).T) / r[:, None]
+        e_dy = 2.0 ** -8 * np.abs(f64(dP) @ f64(W).T)
+        extra = np.abs(f64(G))[None, :] * e_dy / r[:, None]
+        extra_g = np.sum(e_dy * np.abs(f64(X)) / r[:, None], axis=0)
     assert_close(f64(call.D), ref, f"rms_bwd {shape} {mode}", extra)
+    assert_close(f64(dg)[:, 0], reds[0][2], f"rms_dgamma {shape} {mode}", extra_g)
 
 
 @pytest.mark.parametrize("tile", [1, 2, 3])
@@ -141,12 +148,17 @@ def test_rms_bwd_every_tile_f32(CR, tile):
     X, G, W, dP = _rms_bwd_inputs(rng, M, Kf, Np, "f32")
     eps = 1e-6
     stats = f32(_stats_from_oracle(X, G, W, dP, eps))
-    ops = [("rms_bwd", {"x": X, "gamma": G, "eps": eps, "stats": stats})]
+    dg = torch.zeros((Kf, 2), dtype=torch.float32, device="cuda")
+    ops = [("rms_dgamma", {"x": X, "eps": eps, "stats": stats, "out": dg, "col": 1}),
+           ("rms_bwd", {"x": X, "gamma": G, "eps": eps, "stats": stats})]
     call = runner.Call(dP, W, ops, "NK", tile=tile, d_dtype=torch.float32)
     coda.check(call.fused(), "fused")
     torch.cuda.synchronize()
-    ref, _ = oracle.forward(f64(dP), f64(W), [("rms_bwd", {"x": f64(X), "gamma": f64(G), "eps": eps})], "NK")
+    ref, reds = oracle.forward(f64(dP), f64(W), [("rms_dgamma", {"x": f64(X), "eps": eps}),
+                                                 ("rms_bwd", {"x": f64(X), "gamma": f64(G), "eps": eps})], "NK")
     assert_close(f64(call.D), ref, f"rms_bwd tile{tile} f32")
+    assert_close(f64(dg)[:, 1], reds[0][2], f"rms_dgamma tile{tile} f32")
+    assert np.all(f64(dg)[:, 0] == 0.0)
 
 
 def test_rms_bwd_chain_with_row_dot(CR):
@@ -173,11 +185,13 @@ def test_rms_bwd_chain_with_row_dot(CR):
     coda.check(up.fused(), "dP with ROW_DOT")
     torch.cuda.synchronize()
     dP = up.D
-    dn = runner.Call(dP, W, [("rms_bwd", {"x": X, "gamma": Gm, "eps": eps, "stats": stats})], "NK")
+    dg = torch.zeros((Kf, 1), dtype=torch.float32, device="cuda")
+    dn = runner.Call(dP, W, [("rms_dgamma", {"x": X, "eps": eps, "stats": stats, "out": dg, "col": 0}),
+                             ("rms_bwd", {"x": X, "gamma": Gm, "eps": eps, "stats": stats})], "NK")
     coda.check(dn.fused(), "dX with RMS_BWD")
     torch.cuda.synchronize()
     dP_ref = f64(Gup) @ f64(Hup)
-    dX_ref, _ = oracle.rmsnorm_backward(x, g, eps, dP_ref @ Wf.T)
+    dX_ref, dg_ref = oracle.rmsnorm_backward(x, g, eps, dP_ref @ Wf.T)
     r = oracle.rms(x, eps)
     u = 2.0 ** -8
     # dP rounded once (u |dP|) in both terms; P rounded once inside t
@@ -185,6 +199,7 @@ def test_rms_bwd_chain_with_row_dot(CR):
     e_t = u * np.sum(np.abs(dP_ref) * (np.abs(P_exact) + np.abs(P_exact)), axis=1)
     extra = np.abs(g)[None, :] * e_dy / r[:, None] + np.abs(x) * (e_t / (Kf * r ** 2))[:, None]
     assert_close(f64(dn.D), dX_ref, "rms_bwd chain dX", extra)
+    assert_close(f64(dg)[:, 0], dg_ref, "rms_bwd chain dgamma", np.sum(e_dy * np.abs(x) / r[:, None], axis=0))
     # t itself against the oracle's row dot of the exact dP with the stored P
     t_ref = np.sum(dP_ref * f64(P), axis=1)
     assert_close(f64(stats)[:, 1], t_ref, "chain t")
