@@ -118,6 +118,33 @@ def cpu_baseline(spec, inputs, budget_s: float = 10.0):
     }
 
 
+def _event_timer(args):
+    """timed(fn, n_warm, n): per-step times (ms) of a C-ABI launch from events on
+    torch's current stream (the one the binding launches on), with the caches
+    flushed before each step unless --no-flush."""
+    import torch
+    from gemm_epilogue_transformer_bf16_amd import coda
+
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+
+    def timed(fn, n_warm, n):
+        def step():
+            if not args.no_flush:
+                flush.zero_()
+            s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s0.record()
+            coda.check(fn(), "launch")
+            s1.record()
+            return s0, s1
+        for _ in range(n_warm):
+            step()
+        torch.cuda.synchronize()
+        evs = [step() for _ in range(n)]
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in evs])
+    return timed
+
+
 def bench_weight_grad(args):
     """dW_acc += X^T dY for the GPT-2-small MLP up-projection (X [8192 tokens x
     768], dY [8192 x 3072], dW [768 x 3072], K = 8192 tokens): A stored [K x M]
@@ -136,23 +163,7 @@ def bench_weight_grad(args):
     X, dY, ACC = to_dev(x), to_dev(dy), to_dev(acc)
     call = runner.Call(X, dY, [("add_mat", {"mat": ACC, "beta": 1.0})], "KN", a_layout="KM", D=ACC,
                        tile=args.tile)
-    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
-
-    def timed(fn, n_warm, n):
-        def step():
-            if not args.no_flush:
-                flush.zero_()
-            s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            s0.record()
-            coda.check(fn(), "launch")
-            s1.record()
-            return s0, s1
-        for _ in range(n_warm):
-            step()
-        torch.cuda.synchronize()
-        evs = [step() for _ in range(n)]
-        torch.cuda.synchronize()
-        return np.array([a.elapsed_time(b) for a, b in evs])
+    timed = _event_timer(args)
 
     print("[bench] weight gradient: fused", file=sys.stderr, flush=True)
     fused_ms = timed(call.fused, args.warmup, args.steps)
@@ -196,6 +207,77 @@ def bench_weight_grad(args):
     print(json.dumps(line), flush=True)
 
 
+def bench_rms_backward(args):
+    """The RMS norm's backward through the LLaMA-7B gate/up projection:
+    dX = RMS_BWD(dP W^T) with dgamma = RMS_DGAMMA(dP W^T) in the same epilogue;
+    dP = d[gate|up] [4096 tokens x 22016], W [4096 x 22016] read as the [N x K]
+    operand (N = 4096 features, K = 22016), x [4096 x 4096] the norm's input.
+    The row statistics (sum of squares of x, and t = sum dP * P, which the GEMM
+    producing dP would reduce) are given; they are prepared before timing."""
+    import torch
+    import oracle
+    import workloads as w
+    from gemm_epilogue_transformer_bf16_amd import coda, runner
+
+    T, F, Np, eps = 4096, 4096, 2 * 11008, 1e-6
+    rng = np.random.default_rng(2002)
+    xb = w.bf16_bits_from_f64(rng.standard_normal((T, F)))
+    gb = w.bf16_bits_from_f64(1 + 0.1 * rng.standard_normal(F))
+    wb = w.bf16_bits_from_f64(rng.standard_normal((F, Np)) / np.sqrt(F))
+    dpb = w.bf16_bits_from_f64(rng.standard_normal((T, Np)) / np.sqrt(Np))
+    to_dev = lambda b: runner.storage_to_tensor(b, "bf16")
+    X, G, W, dP = to_dev(xb), to_dev(gb), to_dev(wb), to_dev(dpb)
+    stats = torch.empty((T, 2), dtype=torch.float32, device="cuda")
+    stats[:, 0] = X.float().pow(2).sum(dim=1)
+    stats[:, 1] = torch.from_numpy(rng.standard_normal(T).astype(np.float32)).cuda()
+    dg = torch.zeros((F, 1), dtype=torch.float32, device="cuda")
+    ops = [("rms_dgamma", {"x": X, "eps": eps, "stats": stats, "sumsq_col": 0, "out": dg, "col": 0}),
+           ("rms_bwd", {"x": X, "gamma": G, "eps": eps, "stats": stats, "sumsq_col": 0, "t_col": 1})]
+    call = runner.Call(dP, W, ops, "NK", tile=args.tile)
+    timed = _event_timer(args)
+
+    print("[bench] rms backward: fused", file=sys.stderr, flush=True)
+    ms = float(timed(call.fused, args.warmup, args.steps).mean())
+    unfused_ms = None
+    if not args.no_unfused:
+        print("[bench] rms backward: unfused", file=sys.stderr, flush=True)
+        unfused_ms = float(timed(call.unfused, max(2, args.warmup // 2), args.steps).mean())
+    tflops = 2.0 * T * F * Np / (ms * 1e-3) / 1e12
+    alg_bytes = 2.0 * (T * Np + F * Np + 2 * T * F)   # dP, W, x read; dX written
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        rows = np.random.default_rng(0).permutation(T)[:512]
+        x64, g64, w64, dp64 = (w.bf16_bits_to_f64(b) for b in (xb, gb, wb, dpb))
+        t0 = time.perf_counter()
+        oracle.forward(dp64[rows], w64.T, [("rms_dgamma", {"x": x64[rows], "eps": eps}),
+                                           ("rms_bwd", {"x": x64[rows], "gamma": g64, "eps": eps})], "KN")
+        el = time.perf_counter() - t0
+        cpu = {"value": round(2.0 * len(rows) * F * Np / el / 1e12, 5), "unit": "TFLOP/s",
+               "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+               "sample": f"{len(rows)} of {T} rows of dX (fp64 numpy: dP W^T, the norm's backward), {el:.1f} s"}
+    line = {
+        "metric": "fused GEMM+epilogue TFLOP/s, % bf16 MFMA peak; speedup vs unfused HIP",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "llama7b RMSNorm backward through the gate/up projection: dX = RMS_BWD(dP W^T) "
+                               "and dgamma = RMS_DGAMMA(dP W^T), dP [4096 tokens x 22016], W [4096 x 22016], "
+                               "row statistics given, bf16",
+                   "M": T, "N": F, "K": Np, "cache_flush_between_steps": not args.no_flush,
+                   "tile": coda.coda_selected_tile(T, F, Np, call.desc)},
+        "pct_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
+        "unfused_ms_per_step": None if unfused_ms is None else round(unfused_ms, 4),
+        "speedup_vs_unfused": None if unfused_ms is None else round(unfused_ms / ms, 3),
+        "effective_GBps": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -215,6 +297,8 @@ def main():
                          "here before timing) and the gain is folded, so the main loop is the plain GEMM")
     ap.add_argument("--weight-grad", action="store_true",
                     help="the GPT-2-small MLP up-projection's weight gradient, dW_acc += X^T dY, instead")
+    ap.add_argument("--rms-backward", action="store_true",
+                    help="time the RMS norm's backward through the LLaMA-7B gate/up projection instead")
     ap.add_argument("--in-loop-gain", action="store_true",
                     help="time the RMSNorm / LayerNorm gain applied to A in the main loop instead of folded into a "
                          "copy of the weights once (coda_fold_gain, outside the timed region; the default)")
@@ -237,6 +321,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.rms_backward:
+        bench_rms_backward(args)
+        return
     if args.weight_grad:
         bench_weight_grad(args)
         return

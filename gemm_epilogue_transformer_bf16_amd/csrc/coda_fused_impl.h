@@ -127,6 +127,10 @@ struct Cfg {
   static constexpr bool GIVEN = NORM_ == kNormRmsGiven || NORM_ == kNormLnGiven;
   static constexpr int NW = WM * WN;
   static constexpr int NT = 64 * NW;
+  // the bf16 128 x 128 tile of 4 waves runs two workgroups per CU: two waves
+  // per SIMD, so VGPRs + AGPRs must stay within 256 (the epilogue's rarely
+  // used ops may not push the whole kernel to one wave per SIMD)
+  static constexpr int MIN_WAVES_PER_EU = (BM == 128 && BN == 128 && NW == 4 && !F32) ? 2 : 1;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int MI = WTM / 32, NI = WTN / 32;
   static constexpr int BK = F32 ? 32 : 64;
@@ -506,7 +510,8 @@ __device__ __forceinline__ void write_reduction(KOp op, int row, float v) {
 // ---------------------------------------------------------------------------
 
 template <class C>
-__global__ void __launch_bounds__(C::NT) fused_kernel(FusedArgs args) {
+__global__ void __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::MIN_WAVES_PER_EU)))
+fused_kernel(FusedArgs args) {
   (void)args;
   const KArgs a = (KArgs)__builtin_amdgcn_kernarg_segment_ptr();
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, MI = C::MI, NI = C::NI;
