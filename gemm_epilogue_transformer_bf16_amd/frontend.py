@@ -11,8 +11,12 @@ operand's shape; nothing is computed here.
 Grammar (whitespace and ``//`` comments ignored; the braces are optional)::
 
     program := ["EPILOGUE"] "{" stmt* "}" | stmt*
-    stmt    := "output" "=" value ";"  |  NAME "[" INT "]" "=" REDUCE "(" "output" ")" ";"
+    stmt    := "output" "=" value ";"  |  NAME "[" INT "]" "=" reduce ";"
+    reduce  := REDUCE "(" "output" ")"
+             | "rowdot" "(" "output" "," NAME ")"
+             | "rmsdgamma" "(" "output" "," NAME "," NAME "," NUMBER ")"
     value   := FN "(" ("input" | "output") ")"
+             | "rmsnorm_backward" "(" "output" "," NAME "," NAME "," NAME "," NUMBER ")"
              | "rmsnorm" "(" "input" "," NAME "," NUMBER ")"          (first statement only)
              | "layernorm" "(" "input" "," NAME ["," NAME] "," NUMBER ")"   (first statement only)
              | "output" ("+" | "*") term  |  term ("+" | "*") "output"
@@ -23,7 +27,12 @@ Grammar (whitespace and ``//`` comments ignored; the braces are optional)::
 
 ``output + NAME`` adds a matrix (residual), a column vector [N] (bias) or a
 row vector [M]; ``output * NAME`` scales by a column or row vector;
-``output + b * NAME`` adds b times a matrix.  ``dropout`` is rejected: the
+``output + b * NAME`` adds b times a matrix.  The RMS norm's backward:
+``rowdot(output, P)`` is the row sum of output times the matrix P;
+``rmsnorm_backward(output, x, gamma, stats, eps)`` turns dL/dY into dL/dx given
+``stats`` [M x 2] (column 0 the sums of squares of x, column 1 t = rowdot of
+the upstream gradient with P); ``rmsdgamma(output, x, stats, eps)`` is the
+gain gradient, one value per column.  ``dropout`` is rejected: the
 pages give no random-number generator for it.
 """
 from __future__ import annotations
@@ -37,6 +46,8 @@ _TOKEN = re.compile(r"\s*(?:(//[^\n]*)|(\d+\.\d*(?:[eE][-+]?\d+)?|\d*\.\d+(?:[eE
 _FUNCS = {"gelu": "gelu_tanh", "silu": "silu", "swiglu": "swiglu_pair"}
 _REDUCE = {"rowsum": "row_sum", "rowsumsq": "row_sumsq", "rowmean": "row_mean",
            "colsum": "col_sum", "colsumsq": "col_sumsq"}
+# reductions with operands: name -> (op, number of arguments after output)
+_REDUCE_ARGS = {"rowdot": ("row_dot", 1), "rmsdgamma": ("rms_dgamma", 3)}
 
 
 class FrontendError(ValueError):
@@ -107,12 +118,25 @@ class _Parser:
             self.take("]")
             self.take("=")
             fn = self.take()
-            if fn not in _REDUCE:
-                raise FrontendError(f"{target}[{col}] must be assigned a reduction ({', '.join(_REDUCE)})")
+            if fn not in _REDUCE and fn not in _REDUCE_ARGS:
+                raise FrontendError(f"{target}[{col}] must be assigned a reduction "
+                                    f"({', '.join(list(_REDUCE) + list(_REDUCE_ARGS))})")
             self.take("(")
             self.take("output")
+            args = []
+            while self.peek() == ",":
+                self.take(",")
+                args.append(self.take())
             self.take(")")
-            st = ("reduce", _REDUCE[fn], target, int(col))
+            if fn in _REDUCE:
+                if args:
+                    raise FrontendError(f"{fn} takes only the running value")
+                st = ("reduce", _REDUCE[fn], target, int(col))
+            else:
+                op, nargs = _REDUCE_ARGS[fn]
+                if len(args) != nargs:
+                    raise FrontendError(f"{fn} takes output and {nargs} more argument(s)")
+                st = ("reduce", op, target, int(col), tuple(args))
         self.take(";")
         return st
 
@@ -147,6 +171,20 @@ class _Parser:
                 raise FrontendError(f"eps must be a number, found {eps!r}")
             self.take(")")
             return ("norm", "rms_rowscale" if tok == "rmsnorm" else "ln_rowscale", gamma, beta, float(eps))
+        if tok == "rmsnorm_backward":
+            self.take()
+            self.take("(")
+            self.take("output")
+            names = []
+            for _ in range(3):
+                self.take(",")
+                names.append(self.take())
+            self.take(",")
+            eps = self.take()
+            if not self.is_number(eps):
+                raise FrontendError(f"eps must be a number, found {eps!r}")
+            self.take(")")
+            return ("rmsbwd", *names, float(eps))
         if tok in _FUNCS:
             self.take()
             self.take("(")
@@ -212,9 +250,21 @@ def lower(text: str, operands: Dict[str, object], M: int, N: int) -> List[Tuple[
                 width //= 2
         elif kind == "dgelu":
             ops.append(("mul_dgelu_tanh", {"mat": get(st[1])}))
+        elif kind == "rmsbwd":
+            _, x, gamma, stats, eps = st
+            ops.append(("rms_bwd", {"x": get(x), "gamma": get(gamma), "stats": get(stats), "eps": eps,
+                                    "sumsq_col": 0, "t_col": 1}))
         elif kind == "reduce":
-            _, op, target, col = st
-            ops.append((op, {"out": get(target), "col": col}))
+            op, target, col = st[1], st[2], st[3]
+            args = {"out": get(target), "col": col}
+            if op == "row_dot":
+                args["mat"] = get(st[4][0])
+            elif op == "rms_dgamma":
+                x, stats, eps = st[4]
+                if not _Parser.is_number(eps):
+                    raise FrontendError(f"eps must be a number, found {eps!r}")
+                args.update({"x": get(x), "stats": get(stats), "eps": float(eps), "sumsq_col": 0})
+            ops.append((op, args))
         else:   # ("bin", sym, term)
             _, sym, term = st
             if term[0] == "number":

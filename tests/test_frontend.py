@@ -84,6 +84,10 @@ def test_operands_resolve_by_shape():
     ("stats[0] = gelu(output);", "reduction"),
     ("output = gelu(output)", "';'"),
     ("output = tanh(output);", "expected"),
+    ("stats[1] = rowdot(output);", "1 more argument"),
+    ("stats[0] = rowsum(output, P);", "only the running value"),
+    ("db[0] = rmsdgamma(output, P, stats, eps);", "eps must be a number"),
+    ("output = rmsnorm_backward(output, P, gamma, stats, P);", "eps must be a number"),
 ])
 def test_errors(text, msg):
     M, N, K = 6, 8, 4
@@ -94,3 +98,29 @@ def test_errors(text, msg):
 def test_parse_is_pure_syntax():
     assert parse("EPILOGUE { output = silu(input); }") == [("func", "silu")]
     assert parse("") == []
+
+
+def test_rms_backward_statements_lower_to_the_norms_gradients():
+    # the lowered program, run by the oracle on dP W^T, gives dL/dx and
+    # dL/dgamma of the RMS norm (rmsnorm_backward), and rowdot gives t
+    rng = np.random.default_rng(4)
+    M, F, Np, eps = 5, 8, 6, 1e-3
+    x, g = rng.standard_normal((M, F)), 1 + 0.1 * rng.standard_normal(F)
+    W, dP = rng.standard_normal((F, Np)), rng.standard_normal((M, Np))
+    ops_in = {"x": x, "g": g, "st": np.zeros((M, 2)), "dg": np.zeros((F, 1))}
+    text = """EPILOGUE {
+        dg[0] = rmsdgamma(output, x, st, 1e-3);   // the gain gradient first: it reads dL/dY
+        output = rmsnorm_backward(output, x, g, st, 1e-3);
+    }"""
+    ops = lower(text, ops_in, M, F)
+    assert [n for n, _ in ops] == ["rms_dgamma", "rms_bwd"]
+    assert ops[1][1]["sumsq_col"] == 0 and ops[1][1]["t_col"] == 1 and ops[0][1]["col"] == 0
+    D, reds = oracle.forward(dP, W, ops, "NK")
+    dX, dg = oracle.rmsnorm_backward(x, g, eps, dP @ W.T)
+    assert np.allclose(D, dX, rtol=1e-12, atol=1e-12)
+    assert np.allclose(reds[0][2], dg, rtol=1e-12, atol=1e-12)
+    P = oracle.rmsnorm(x, g, eps) @ W
+    up = lower("st[1] = rowdot(output, P);", {"st": np.zeros((M, 2)), "P": P}, M, Np)
+    assert up[0][0] == "row_dot" and up[0][1]["col"] == 1
+    _, reds = oracle.forward(dP, np.eye(Np), up, "KN")
+    assert np.allclose(reds[0][2] * oracle.rms(x, eps), np.sum(g * (dP @ W.T) * x, axis=1), rtol=1e-10)
