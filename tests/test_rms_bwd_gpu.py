@@ -203,3 +203,26 @@ def test_rms_bwd_chain_with_row_dot(CR):
     # t itself against the oracle's row dot of the exact dP with the stored P
     t_ref = np.sum(dP_ref * f64(P), axis=1)
     assert_close(f64(stats)[:, 1], t_ref, "chain t")
+
+
+def test_rms_backward_text_program_end_to_end(CR):
+    """The front end's backward statements, lowered with device operands and run
+    through the C ABI, against the oracle's gradients."""
+    from gemm_epilogue_transformer_bf16_amd.frontend import lower
+    coda, runner = CR
+    announce("rms backward text program")
+    rng = np.random.default_rng(76)
+    M, Kf, Np, eps = 136, 264, 72, 1e-5
+    X, G, W, dP = _rms_bwd_inputs(rng, M, Kf, Np)
+    st = f32(_stats_from_oracle(X, G, W, dP, eps))
+    dg = torch.zeros((Kf, 1), dtype=torch.float32, device="cuda")
+    ops = lower("""EPILOGUE {
+        dg[0] = rmsdgamma(output, x, st, 1e-5);
+        output = rmsnorm_backward(output, x, g, st, 1e-5);
+    }""", {"x": X, "g": G, "st": st, "dg": dg}, M, Kf)
+    call = runner.Call(dP, W, ops, "NK")
+    coda.check(call.fused(), "text program")
+    torch.cuda.synchronize()
+    dX_ref, dg_ref = oracle.rmsnorm_backward(f64(X), f64(G), eps, f64(dP) @ f64(W).T)
+    assert_close(f64(call.D), dX_ref, "text program dX")
+    assert_close(f64(dg)[:, 0], dg_ref, "text program dgamma")
