@@ -38,6 +38,16 @@ Readings of points the pages leave open (each also listed in the design notes):
     the current width (half the GEMM width after swiglu_pair).
   * The RMS norm's backward (rmsnorm_backward, the rms_bwd op) is the
     chain-rule gradient of that same forward form.
+  * Dropout (the statement ``output = dropout(output, 0.1)`` of the d9bl.com
+    page's section 3.2 example) zeroes an element with probability p and scales
+    the kept ones by 1 / (1 - p) (inverted dropout, so the expectation is
+    unchanged).  The pages name no generator; the mask here is drawn from the
+    counter-based Philox-4x64-10 (Salmon, Moraes, Dror and Shaw, "Parallel
+    random numbers: as easy as 1, 2, 3", SC 2011), keyed by (seed, 0) and
+    counted by (column // 8, row, offset, 0) of the element in the running
+    value; column j takes the 32-bit word j % 8 of the block (the low half of
+    64-bit word (j % 8) // 2 for even j % 8, the high half for odd), and the
+    element is kept when that word is >= floor(p * 2^32), p taken at fp32.
 """
 from __future__ import annotations
 
@@ -51,7 +61,7 @@ GELU_CUBIC = 0.044715
 
 # op names understood by the oracle (its own vocabulary; the HIP path has its own enum)
 ELEMENTWISE_OPS = ("scale", "scale_row", "scale_col", "add_col", "add_row", "add_mat",
-                   "gelu_tanh", "silu", "swiglu_pair", "mul_dgelu_tanh", "rms_bwd")
+                   "gelu_tanh", "silu", "swiglu_pair", "mul_dgelu_tanh", "rms_bwd", "dropout")
 # row_dot: sum over the row of the running value times a matrix operand
 REDUCTION_OPS = ("row_sum", "row_sumsq", "row_mean", "row_dot")
 # reductions over the rows of the output, one value per column (the bias
@@ -98,6 +108,101 @@ def swiglu_pair(v: np.ndarray) -> np.ndarray:
     gate = v[:, 0::2]
     up = v[:, 1::2]
     return silu(gate) * up
+
+
+# --- dropout's generator: Philox-4x64-10 (Salmon et al., SC 2011) ---
+
+MASK32 = np.uint64(0xFFFFFFFF)
+# round multipliers and the two key increments (the golden ratio and sqrt(3) - 1
+# as 64-bit fractions), as the generator's definition gives them
+PHILOX_M0, PHILOX_M1 = 0xD2E7470EE14C6C93, 0xCA5A826395121157
+PHILOX_W0, PHILOX_W1 = 0x9E3779B97F4A7C15, 0xBB67AE8584CAA73B
+PHILOX_ROUNDS = 10
+
+
+def philox4x64_scalar(counter, key, rounds: int = PHILOX_ROUNDS):
+    """One Philox-4x64 block on Python integers (small cases and pins).
+
+    Each round multiplies counter words 0 and 2 by the two multipliers into
+    128-bit products (hi, lo); the new counter is (hi(M1 c2) ^ c1 ^ k0,
+    lo(M1 c2), hi(M0 c0) ^ c3 ^ k1, lo(M0 c0)); the key then advances by
+    (W0, W1) modulo 2^64.
+    """
+    m64 = (1 << 64) - 1
+    c = [int(x) & m64 for x in counter]
+    k0, k1 = (int(x) & m64 for x in key)
+    for _ in range(rounds):
+        p0 = PHILOX_M0 * c[0]
+        p1 = PHILOX_M1 * c[2]
+        c = [(p1 >> 64) ^ c[1] ^ k0, p1 & m64, (p0 >> 64) ^ c[3] ^ k1, p0 & m64]
+        k0 = (k0 + PHILOX_W0) & m64
+        k1 = (k1 + PHILOX_W1) & m64
+    return c
+
+
+def _mulhilo64(a: np.ndarray, b: int):
+    """128-bit products of uint64 arrays by a 64-bit constant, as (hi, lo), from 32-bit limbs."""
+    a = a.astype(np.uint64)
+    a0, a1 = a & MASK32, a >> np.uint64(32)
+    b0, b1 = np.uint64(b & 0xFFFFFFFF), np.uint64(b >> 32)
+    p00, p01, p10, p11 = a0 * b0, a0 * b1, a1 * b0, a1 * b1
+    mid = (p00 >> np.uint64(32)) + (p01 & MASK32) + (p10 & MASK32)
+    lo = (p00 & MASK32) | ((mid & MASK32) << np.uint64(32))
+    hi = p11 + (p01 >> np.uint64(32)) + (p10 >> np.uint64(32)) + (mid >> np.uint64(32))
+    return hi, lo
+
+
+def philox4x64(c0, c1, c2, c3, key, rounds: int = PHILOX_ROUNDS):
+    """Philox-4x64 blocks for arrays of counters (broadcast), the key a pair of ints."""
+    c = [np.asarray(x, dtype=np.uint64) for x in np.broadcast_arrays(c0, c1, c2, c3)]
+    k0, k1 = int(key[0]) & ((1 << 64) - 1), int(key[1]) & ((1 << 64) - 1)
+    with np.errstate(over="ignore"):
+        for _ in range(rounds):
+            hi0, lo0 = _mulhilo64(c[0], PHILOX_M0)
+            hi1, lo1 = _mulhilo64(c[2], PHILOX_M1)
+            c = [hi1 ^ c[1] ^ np.uint64(k0), lo1, hi0 ^ c[3] ^ np.uint64(k1), lo0]
+            k0 = (k0 + PHILOX_W0) & ((1 << 64) - 1)
+            k1 = (k1 + PHILOX_W1) & ((1 << 64) - 1)
+    return c
+
+
+def dropout_words(rows: np.ndarray, width: int, seed: int, offset: int = 0) -> np.ndarray:
+    """The 32-bit uniform word of every element (row i in ``rows``, column j < width)."""
+    rows = np.asarray(rows, dtype=np.uint64)
+    nblk = (width + 7) // 8
+    blk = np.arange(nblk, dtype=np.uint64)
+    words = philox4x64(blk[None, :], rows[:, None], np.uint64(offset), np.uint64(0), (seed, 0))
+    # [rows, blocks, 8]: 32-bit word 2w is the low half of 64-bit word w, 2w + 1 the high half
+    out = np.empty((len(rows), nblk, 8), dtype=np.uint64)
+    for w in range(4):
+        out[:, :, 2 * w] = words[w] & MASK32
+        out[:, :, 2 * w + 1] = words[w] >> np.uint64(32)
+    return out.reshape(len(rows), nblk * 8)[:, :width]
+
+
+def dropout_threshold(p: float) -> int:
+    """floor(p * 2^32) for p taken at fp32: an element is kept when its word is >= this."""
+    p32 = float(np.float32(p))
+    if not 0.0 <= p32 < 1.0:
+        raise ValueError("dropout probability must be in [0, 1)")
+    return int(math.floor(p32 * 4294967296.0))
+
+
+def dropout_keep(rows: np.ndarray, width: int, p: float, seed: int, offset: int = 0) -> np.ndarray:
+    """Boolean keep-mask [len(rows) x width]."""
+    return dropout_words(rows, width, seed, offset) >= np.uint64(dropout_threshold(p))
+
+
+def dropout(v: np.ndarray, p: float, seed: int, offset: int = 0, rows=None) -> np.ndarray:
+    """Inverted dropout of the running value: kept elements times 1 / (1 - p), the rest 0.
+
+    ``rows`` are the global row indices of v's rows (default 0 .. len(v) - 1).
+    """
+    v = np.asarray(v, dtype=np.float64)
+    rows = np.arange(v.shape[0]) if rows is None else np.asarray(rows)
+    keep = dropout_keep(rows, v.shape[1], p, seed, offset)
+    p32 = float(np.float32(p))
+    return np.where(keep, v / (1.0 - p32), 0.0)
 
 
 # --- row-wise norm (zeli.app comment; d9bl.com section 3.1 / Fig. 4) ---
@@ -223,13 +328,16 @@ def gemm(Y: np.ndarray, B: np.ndarray, alpha: float = 1.0) -> np.ndarray:
 
 # --- the ordered epilogue (d9bl.com section 3.2; agentlenshq.com "How it works") ---
 
-def apply_epilogue(C: np.ndarray, ops: Sequence[Tuple[str, Dict]]) -> Tuple[np.ndarray, List[Tuple[str, Dict, np.ndarray]]]:
+def apply_epilogue(C: np.ndarray, ops: Sequence[Tuple[str, Dict]],
+                   row_ids=None) -> Tuple[np.ndarray, List[Tuple[str, Dict, np.ndarray]]]:
     """Apply ``ops`` in order to the running value v = C.
 
     Returns the final value and, for each reduction op in list order, a tuple
     (op name, its args, the fp64 result): one value per row for row_*, one per
     column (over all rows given) for col_*.  ``rms_rowscale`` is not an
-    epilogue op here: the oracle applies it to A before the GEMM.
+    epilogue op here: the oracle applies it to A before the GEMM.  ``row_ids``
+    are the global indices of C's rows (dropout's counter uses them; default
+    0 .. rows - 1).
     """
     v = np.array(C, dtype=np.float64, copy=True)
     reductions = []
@@ -254,6 +362,8 @@ def apply_epilogue(C: np.ndarray, ops: Sequence[Tuple[str, Dict]]) -> Tuple[np.n
             v = swiglu_pair(v)
         elif name == "mul_dgelu_tanh":
             v = v * gelu_tanh_grad(np.asarray(args["mat"], dtype=np.float64))
+        elif name == "dropout":
+            v = dropout(v, float(args["p"]), int(args.get("seed", 0)), int(args.get("offset", 0)), row_ids)
         elif name == "rms_bwd":
             # v is dL/dY of Y = rmsnorm(x, gamma, eps); the op's value is dL/dx
             # (the plain gradient; row statistics a caller may pass are ignored)
@@ -285,10 +395,11 @@ def apply_epilogue(C: np.ndarray, ops: Sequence[Tuple[str, Dict]]) -> Tuple[np.n
 
 
 def forward(A: np.ndarray, B_stored: np.ndarray, ops: Sequence[Tuple[str, Dict]],
-            b_layout: str = "KN", alpha: float = 1.0):
+            b_layout: str = "KN", alpha: float = 1.0, row_ids=None):
     """Normalise (if the list starts with rms_rowscale or ln_rowscale) -> GEMM -> ordered epilogue.
 
-    ``ops`` items are (name, args) with array-valued args already resolved.
+    ``ops`` items are (name, args) with array-valued args already resolved;
+    ``row_ids`` are the global indices of A's rows when A is a row subset.
     Returns (D fp64, list of (name, args, fp64 per-row result)).
     """
     A = np.asarray(A, dtype=np.float64)
@@ -305,4 +416,4 @@ def forward(A: np.ndarray, B_stored: np.ndarray, ops: Sequence[Tuple[str, Dict]]
         if name in ("rms_rowscale", "ln_rowscale"):
             raise ValueError(f"{name} must be the first op")
     C = gemm(Y, logical_b(B_stored, b_layout), alpha)
-    return apply_epilogue(C, ops)
+    return apply_epilogue(C, ops, row_ids)

@@ -54,7 +54,7 @@ def run_workload(spec, inputs: Dict[str, np.ndarray], rows: Optional[Sequence[in
         A = A[rows_arr]
     B = to_f64(inputs[spec.b_name], dtypes[spec.b_name])
     ops = resolve_program(spec, inputs, rows_arr)
-    D, reds = forward(A, B, ops, spec.b_layout)
+    D, reds = forward(A, B, ops, spec.b_layout, row_ids=rows_arr)
     # outputs of column reductions are indexed by column (over the rows given);
     # all others by row
     col_outs = {args["out"] for name, args in spec.program if name in COLUMN_REDUCTION_OPS}

@@ -20,6 +20,9 @@ order they are drawn), and the ordered epilogue program as a list of
   mul_dgelu_tanh(mat)       v[i,j] *= GELU_tanh'(mat[i,j])
   row_sum/row_sumsq/row_mean(out, col)   fp32 per-row reduction written to
                             out[i, col] of an [M x ncols] fp32 array
+  dropout(p, seed, offset)  inverted dropout with a counter-based mask (element
+                            (i, j) kept with probability 1 - p, kept values
+                            scaled by 1 / (1 - p))
 """
 from __future__ import annotations
 
