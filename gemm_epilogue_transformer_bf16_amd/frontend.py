@@ -21,19 +21,27 @@ Grammar (whitespace and ``//`` comments ignored; the braces are optional)::
              | "layernorm" "(" "input" "," NAME ["," NAME] "," NUMBER ")"   (first statement only)
              | "output" ("+" | "*") term  |  term ("+" | "*") "output"
              | "output" "*" "dgelu" "(" NAME ")"
-    term    := NUMBER | NAME | NUMBER "*" NAME
+             | "dropout" "(" "output" "," NUMBER ["," INT] ")"
+    term    := NUMBER | NAME | NUMBER "*" NAME | "row" "(" NAME ")" | "col" "(" NAME ")"
     FN      := "gelu" | "silu" | "swiglu"
     REDUCE  := "rowsum" | "rowsumsq" | "rowmean" | "colsum" | "colsumsq"
 
-``output + NAME`` adds a matrix (residual), a column vector [N] (bias) or a
-row vector [M]; ``output * NAME`` scales by a column or row vector;
-``output + b * NAME`` adds b times a matrix.  The RMS norm's backward:
+``input`` (the GEMM result) may appear only in the first statement: later
+statements see the running value ``output``.  ``output + NAME`` adds a matrix
+(residual), a column vector [width] (bias) or a row vector [M];
+``output * NAME`` scales by a column or row vector; ``output + b * NAME`` adds
+b times a matrix.  When M equals the running width a vector's length does not
+say which it is: write ``col(NAME)`` or ``row(NAME)`` (an unmarked vector is
+then an error).  ``dropout(output, p[, seed])`` zeroes each element with
+probability p and scales the kept ones by 1 / (1 - p); the mask comes from the
+counter-based Philox-4x64-10 generator keyed by the seed (default 0, or the
+``seed`` argument of ``lower``) and counted by the element's row and column, so
+it is reproducible and needs no stored state.  The RMS norm's backward:
 ``rowdot(output, P)`` is the row sum of output times the matrix P;
 ``rmsnorm_backward(output, x, gamma, stats, eps)`` turns dL/dY into dL/dx given
 ``stats`` [M x 2] (column 0 the sums of squares of x, column 1 t = rowdot of
 the upstream gradient with P); ``rmsdgamma(output, x, stats, eps)`` is the
-gain gradient, one value per column.  ``dropout`` is rejected: the
-pages give no random-number generator for it.
+gain gradient, one value per column.
 """
 from __future__ import annotations
 
@@ -142,6 +150,11 @@ class _Parser:
 
     def term(self):
         tok = self.take()
+        if tok in ("row", "col") and self.peek() == "(":
+            self.take("(")
+            name = self.take()
+            self.take(")")
+            return ("vec", tok, name)
         if self.is_number(tok):
             if self.peek() == "*" and self.peek(1) not in (None, "output"):
                 self.take("*")
@@ -152,7 +165,24 @@ class _Parser:
     def value(self, first: bool):
         tok = self.peek()
         if tok == "dropout":
-            raise FrontendError("dropout is not supported: no random-number generator is specified for it")
+            self.take()
+            self.take("(")
+            self.take("output")
+            self.take(",")
+            p = self.take()
+            if not self.is_number(p):
+                raise FrontendError(f"dropout probability must be a number, found {p!r}")
+            seed = None
+            if self.peek() == ",":
+                self.take(",")
+                seed = self.take()
+                if not seed.isdigit():
+                    raise FrontendError(f"dropout seed must be a non-negative integer, found {seed!r}")
+                seed = int(seed)
+            self.take(")")
+            if not 0.0 <= float(p) < 1.0:
+                raise FrontendError(f"dropout probability must be in [0, 1), found {p}")
+            return ("dropout", float(p), seed)
         if tok in ("rmsnorm", "layernorm"):
             if not first:
                 raise FrontendError(f"{tok} normalises the GEMM's A operand and must be the first statement")
@@ -191,6 +221,9 @@ class _Parser:
             arg = self.take()
             if arg not in ("input", "output"):
                 raise FrontendError(f"{tok} applies to the running value, found {arg!r}")
+            if arg == "input" and not first:
+                raise FrontendError(f"'input' names the GEMM result and is valid only in the first statement; "
+                                    f"use {tok}(output)")
             self.take(")")
             return ("func", _FUNCS[tok])
         if tok == "output":
@@ -218,12 +251,13 @@ def parse(text: str):
     return _Parser(text).program()
 
 
-def lower(text: str, operands: Dict[str, object], M: int, N: int) -> List[Tuple[str, Dict]]:
+def lower(text: str, operands: Dict[str, object], M: int, N: int, seed: int = 0) -> List[Tuple[str, Dict]]:
     """Lower a program to the op list of ``runner.Call`` / the workloads vocabulary.
 
     ``operands`` maps names to bound values (tensors or arrays: anything with
     ``.shape``); M and N are the GEMM's output rows and columns, used to tell a
-    row vector [M] from a column vector [N] and a matrix [M x width].
+    row vector [M] from a column vector [N] and a matrix [M x width].  ``seed``
+    keys every dropout statement that names no seed of its own.
     """
     ops: List[Tuple[str, Dict]] = []
     width = N
@@ -250,6 +284,9 @@ def lower(text: str, operands: Dict[str, object], M: int, N: int) -> List[Tuple[
                 width //= 2
         elif kind == "dgelu":
             ops.append(("mul_dgelu_tanh", {"mat": get(st[1])}))
+        elif kind == "dropout":
+            _, p, own_seed = st
+            ops.append(("dropout", {"p": p, "seed": seed if own_seed is None else own_seed}))
         elif kind == "rmsbwd":
             _, x, gamma, stats, eps = st
             ops.append(("rms_bwd", {"x": get(x), "gamma": get(gamma), "stats": get(stats), "eps": eps,
@@ -267,6 +304,17 @@ def lower(text: str, operands: Dict[str, object], M: int, N: int) -> List[Tuple[
             ops.append((op, args))
         else:   # ("bin", sym, term)
             _, sym, term = st
+            if term[0] == "vec":
+                _, which, name = term
+                shp = shape(name)
+                want = width if which == "col" else M
+                if len(shp) != 1 or shp[0] != want:
+                    raise FrontendError(f"{which}({name}) must be a vector of length {want}, found shape {shp}")
+                if which == "col":
+                    ops.append(("add_col" if sym == "+" else "scale_col", {"vec": get(name)}))
+                else:
+                    ops.append(("add_row" if sym == "+" else "scale_row", {"vec": get(name)}))
+                continue
             if term[0] == "number":
                 if sym == "*":
                     ops.append(("scale", {"alpha": term[1]}))
@@ -285,6 +333,9 @@ def lower(text: str, operands: Dict[str, object], M: int, N: int) -> List[Tuple[
                     if sym == "*":
                         raise FrontendError("elementwise products with a matrix are not a primitive (use dgelu)")
                     ops.append(("add_mat", {"mat": get(name), "beta": 1.0}))
+                elif len(shp) == 1 and shp[0] == width == M:
+                    raise FrontendError(f"{name!r} of length {shp[0]} could be a row vector [M] or a column vector "
+                                        f"[width]; write row({name}) or col({name})")
                 elif len(shp) == 1 and shp[0] == width:
                     ops.append(("add_col" if sym == "+" else "scale_col", {"vec": get(name)}))
                 elif len(shp) == 1 and shp[0] == M:

@@ -76,7 +76,11 @@ def test_operands_resolve_by_shape():
 
 
 @pytest.mark.parametrize("text,msg", [
-    ("output = dropout(output, 0.1);", "dropout"),
+    ("output = dropout(output, 1.0);", "dropout probability"),
+    ("output = dropout(output, p);", "dropout probability must be a number"),
+    ("output = dropout(output, 0.1, s);", "seed"),
+    ("output = output + bias; output = gelu(input);", "first statement"),
+    ("output = silu(output); output = swiglu(input);", "first statement"),
     ("output = gelu(output); output = rmsnorm(input, gamma, 1e-6);", "first statement"),
     ("output = output + nothing;", "unbound"),
     ("output = output + 1.0;", "constant"),
@@ -124,3 +128,45 @@ def test_rms_backward_statements_lower_to_the_norms_gradients():
     assert up[0][0] == "row_dot" and up[0][1]["col"] == 1
     _, reds = oracle.forward(dP, np.eye(Np), up, "KN")
     assert np.allclose(reds[0][2] * oracle.rms(x, eps), np.sum(g * (dP @ W.T) * x, axis=1), rtol=1e-10)
+
+
+def test_input_only_in_the_first_statement():
+    M, N, K = 6, 8, 4
+    assert [n for n, _ in lower("output = gelu(input); output = output + R;", operands(M, N, K), M, N)] == \
+        ["gelu_tanh", "add_mat"]
+
+
+def test_square_output_needs_explicit_vector_orientation():
+    # with M == width, a vector of that length could be a row vector or a column vector
+    M = N = 8
+    o = {"v": np.arange(8.0), "R": np.zeros((8, 8))}
+    with pytest.raises(FrontendError, match="row\\(v\\) or col\\(v\\)"):
+        lower("output = output + v;", o, M, N)
+    with pytest.raises(FrontendError, match="row\\(v\\) or col\\(v\\)"):
+        lower("output = output * v;", o, M, N)
+    ops = lower("output = output + col(v); output = output * row(v); output = output + row(v); "
+                "output = output * col(v);", o, M, N)
+    assert [n for n, _ in ops] == ["add_col", "scale_row", "add_row", "scale_col"]
+    # the oracle sees the intended orientation
+    C = np.arange(64.0).reshape(8, 8)
+    D, _ = oracle.apply_epilogue(C, ops[:1])
+    assert np.array_equal(D, C + np.arange(8.0)[None, :])
+    D, _ = oracle.apply_epilogue(C, ops[1:2])
+    assert np.array_equal(D, C * np.arange(8.0)[:, None])
+    with pytest.raises(FrontendError, match="length 6"):
+        lower("output = output + row(v);", o, 6, 8)
+
+
+def test_dropout_statement_lowers_with_seed():
+    M, N, K = 6, 8, 4
+    ops = lower("output = gelu(input); output = dropout(output, 0.1); output = dropout(output, 0.25, 7);",
+                operands(M, N, K), M, N, seed=42)
+    assert ops[1] == ("dropout", {"p": 0.1, "seed": 42})
+    assert ops[2] == ("dropout", {"p": 0.25, "seed": 7})
+    # the oracle runs the lowered program: the mask of the seeded generator
+    rng = np.random.default_rng(0)
+    A, B = rng.standard_normal((M, K)), rng.standard_normal((K, N))
+    D, _ = oracle.forward(A, B, ops[:2])
+    keep = oracle.dropout_keep(np.arange(M), N, 0.1, 42)
+    ref = np.where(keep, oracle.gelu_tanh(A @ B) / (1 - float(np.float32(0.1))), 0.0)
+    assert np.allclose(D, ref, rtol=1e-14, atol=0)
