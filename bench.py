@@ -1,18 +1,27 @@
 """Benchmark of the fused GEMM + epilogue path on one MI355X.
 
-One step = one fused call (operand staging, in-loop sum of squares and gain,
+One step = one fused call (operand staging, in-loop gain and sum of squares,
 MFMA main loop, ordered epilogue, one store of D) on the LLaMA-7B-shaped
 SwiGLU gate/up layer: M = 4096 tokens, K = 4096, [W_gate | W_up] column
-interleaved, N = 2 x 11008, deferred RMSNorm row scale then SiLU(gate) * up,
-bf16 storage and fp32 accumulation.  Inputs are seeded synthetic tensors with
-the layer's shapes and value distributions, resident in HBM before timing.
-``--workload`` times another of the synthetic transformer layers instead (the
-default line is the LLaMA layer's).
+interleaved, N = 2 x 11008, deferred RMSNorm ((x * gamma) @ W in the main loop,
+the per-row 1/rms in the epilogue) then SiLU(gate) * up, bf16 storage and fp32
+accumulation.  Inputs are seeded synthetic tensors with the layer's shapes and
+value distributions, resident in HBM before timing.  ``--workload`` times
+another of the synthetic transformer layers instead.
 
-Prints one JSON line: fused TFLOP/s (2 M N K / kernel time), the share of the
-bf16 dense MFMA peak, the speedup over the in-run unfused HIP sequence (same
-main loop, one kernel per operator, bf16 intermediates), the roofline object
-and the CPU-oracle baseline.
+Timing: the fused call, the in-run unfused HIP sequence (same main loop, one
+kernel per operator, bf16 intermediates) and, for norm layers, the fused call
+with the gain folded into a copy of the weights run round-robin, one step of
+each per round, each step preceded by a cache flush and bracketed by HIP
+events on the stream the library launches on.  The warm-up lasts at least
+``--warmup`` rounds and ``--warmup-seconds`` of wall time, so the GPU clock has
+settled whatever the round count.  Times are medians over the timed rounds
+(p10 / p90 beside them).
+
+Prints one JSON line: fused TFLOP/s (2 M N K / median kernel time), the share
+of the bf16 dense MFMA peak (and of the peak at the clock measured during the
+run), the speedup over the unfused sequence, the roofline object and the
+CPU-oracle baseline.
 """
 from __future__ import annotations
 
@@ -65,17 +74,32 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel_hash: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", "fused_llama7b_gate_up_traffic.json")
+def _profile_record(workload: str, kind: str):
+    path = os.path.join(ROOT, "profiles", f"{workload}_{kind}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
-        rec = json.load(f)
-    if rec.get("kernel_source_hash") != kernel_hash:
+        return json.load(f)
+
+
+def load_traffic(workload: str, kernel_hash: str):
+    """L2-to-fabric bytes per launch of the fused kernel (FETCH_SIZE + WRITE_SIZE,
+    each calibrated against a plain device copy) from the committed rocprofv3
+    counter runs of this workload, if they were taken on the current kernel
+    sources."""
+    rec = _profile_record(workload, "traffic")
+    if not rec or rec.get("kernel_source_hash") != kernel_hash:
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec.get("bytes_per_launch")
+
+
+def load_counter_clock(workload: str, kernel_hash: str):
+    """Shader clock (GHz) of the fused kernel from the committed counter run:
+    GRBM_GUI_ACTIVE cycles (per XCD) over the dispatch duration."""
+    rec = _profile_record(workload, "counters")
+    if not rec or rec.get("kernel_source_hash") != kernel_hash:
+        return None
+    return rec.get("fused", {}).get("clock_ghz")
 
 
 def cpu_baseline(spec, inputs, budget_s: float = 10.0):
@@ -118,38 +142,156 @@ def cpu_baseline(spec, inputs, budget_s: float = 10.0):
     }
 
 
-def _event_timer(args):
-    """timed(fn, n_warm, n): per-step times (ms) of a C-ABI launch from events on
-    torch's current stream (the one the binding launches on), with the caches
-    flushed before each step unless --no-flush."""
-    import torch
-    from gemm_epilogue_transformer_bf16_amd import coda
+class ClockSampler:
+    """Samples the GPU shader clock (MHz, torch.cuda.clock_rate, which reads
+    amdsmi on ROCm) from a background thread while kernels run; None when the
+    query is unavailable."""
 
-    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    def __init__(self, period_s: float = 0.002):
+        import threading
+        self.period_s = period_s
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = None
+        self._threading = threading
 
-    def timed(fn, n_warm, n):
-        def step():
-            if not args.no_flush:
-                flush.zero_()
-            s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            s0.record()
-            coda.check(fn(), "launch")
-            s1.record()
-            return s0, s1
-        for _ in range(n_warm):
-            step()
+    def _loop(self):
+        import torch
+        while not self._stop.is_set():
+            try:
+                self.samples.append(float(torch.cuda.clock_rate(0)))
+            except Exception:     # pragma: no cover - query not available
+                return
+            self._stop.wait(self.period_s)
+
+    def start(self):
+        self.samples = []
+        self._stop.clear()
+        self._thread = self._threading.Thread(target=self._loop, daemon=True)
+        self._thread.start()
+
+    def stop(self):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join()
+        return float(np.median(self.samples)) if self.samples else None
+
+
+class Timer:
+    """Times C-ABI launch functions round-robin: per round one step of each, every
+    step preceded by a cache flush (a 512 MiB fill, unless --no-flush) and
+    bracketed by HIP events on torch's current stream, the stream the binding
+    launches on.  The warm-up runs at least ``warmup`` rounds and
+    ``warmup_seconds`` of wall time; then exactly ``steps`` rounds are timed
+    between two device synchronisations."""
+
+    def __init__(self, args):
+        import torch
+        self.args = args
+        self.flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+        self.clock = ClockSampler()
+        self.wall_s = None
+        self.clock_mhz = None
+
+    def _step(self, fn):
+        import torch
+        from gemm_epilogue_transformer_bf16_amd import coda
+        if not self.args.no_flush:
+            self.flush.zero_()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
+        coda.check(fn(), "launch")
+        s1.record()
+        return s0, s1
+
+    def run(self, fns):
+        """fns: {name: launch function}; returns {name: per-step times in ms}."""
+        import torch
+        args = self.args
         torch.cuda.synchronize()
-        evs = [step() for _ in range(n)]
+        t0 = time.perf_counter()
+        rounds = 0
+        while rounds < args.warmup or time.perf_counter() - t0 < args.warmup_seconds:
+            for fn in fns.values():
+                self._step(fn)
+            rounds += 1
+            if rounds % 8 == 0:
+                torch.cuda.synchronize()
         torch.cuda.synchronize()
-        return np.array([a.elapsed_time(b) for a, b in evs])
-    return timed
+        self.clock.start()
+        t1 = time.perf_counter()
+        evs = {name: [] for name in fns}
+        for _ in range(args.steps):
+            for name, fn in fns.items():
+                evs[name].append(self._step(fn))
+        torch.cuda.synchronize()
+        self.wall_s = time.perf_counter() - t1
+        self.clock_mhz = self.clock.stop()
+        self.warmup_rounds = rounds
+        self.warmup_s = t1 - t0
+        return {name: np.array([a.elapsed_time(b) for a, b in e]) for name, e in evs.items()}
+
+
+def stats(ms):
+    return {"median": round(float(np.median(ms)), 4), "mean": round(float(np.mean(ms)), 4),
+            "p10": round(float(np.percentile(ms, 10)), 4), "p90": round(float(np.percentile(ms, 90)), 4)}
+
+
+def result_line(args, timer, flops, fused_ms, unfused_ms, config, peak, alg_bytes, cpu, traffic=None,
+                counter_clock=None, extra=None):
+    """The JSON line: value = flops / median fused time."""
+    ms = float(np.median(fused_ms))
+    tflops = flops / (ms * 1e-3) / 1e12
+    umed = None if unfused_ms is None else float(np.median(unfused_ms))
+    clock_ghz = counter_clock if counter_clock else (None if timer.clock_mhz is None else timer.clock_mhz / 1e3)
+    line = {
+        "metric": "fused GEMM+epilogue TFLOP/s, % bf16 MFMA peak; speedup vs unfused HIP",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if peak == PEAK_F32_TFLOPS else "bf16",
+        "data": "synthetic",
+        "config": config,
+        "pct_peak": round(100.0 * tflops / peak, 2),
+        "fused_ms": stats(fused_ms),
+        "unfused_ms": None if unfused_ms is None else stats(unfused_ms),
+        "unfused_ms_per_step": None if umed is None else round(umed, 4),
+        "speedup_vs_unfused": None if umed is None else round(umed / ms, 3),
+        "effective_GBps": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
+        "clock_ghz_smi": None if timer.clock_mhz is None else round(timer.clock_mhz / 1e3, 3),
+        "clock_ghz_counters": counter_clock,
+        # dense peak at the measured clock: 256 CUs x 4096 bf16 flop per clock (x 256 fp32)
+        "pct_peak_at_measured_clock": None if clock_ghz is None else round(
+            100.0 * tflops / ((4096.0 if peak != PEAK_F32_TFLOPS else 256.0) * 256 * clock_ghz * 1e-3), 2),
+        "timing": {"warmup_rounds": timer.warmup_rounds, "warmup_s": round(timer.warmup_s, 3),
+                   "timed_rounds_wall_s": round(timer.wall_s, 4), "interleaved": True,
+                   "cache_flush_between_steps": not args.no_flush},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / peak, 4),
+            "traffic": traffic,
+        },
+        "cpu_baseline": cpu,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if extra:
+        line.update(extra)
+    return line
 
 
 def bench_weight_grad(args):
     """dW_acc += X^T dY for the GPT-2-small MLP up-projection (X [8192 tokens x
     768], dY [8192 x 3072], dW [768 x 3072], K = 8192 tokens): A stored [K x M]
     and the accumulation into the gradient buffer fused as an in-place ADD_MAT."""
-    import torch
     import oracle
     import workloads as w
     from gemm_epilogue_transformer_bf16_amd import coda, runner
@@ -163,17 +305,13 @@ def bench_weight_grad(args):
     X, dY, ACC = to_dev(x), to_dev(dy), to_dev(acc)
     call = runner.Call(X, dY, [("add_mat", {"mat": ACC, "beta": 1.0})], "KN", a_layout="KM", D=ACC,
                        tile=args.tile)
-    timed = _event_timer(args)
-
-    print("[bench] weight gradient: fused", file=sys.stderr, flush=True)
-    fused_ms = timed(call.fused, args.warmup, args.steps)
-    ms = float(fused_ms.mean())
-    unfused_ms = None
+    timer = Timer(args)
+    fns = {"fused": call.fused}
     if not args.no_unfused:
-        print("[bench] weight gradient: unfused", file=sys.stderr, flush=True)
-        unfused_ms = float(timed(call.unfused, max(2, args.warmup // 2), args.steps).mean())
+        fns["unfused"] = call.unfused
+    print("[bench] weight gradient: fused and unfused, interleaved", file=sys.stderr, flush=True)
+    t = timer.run(fns)
     flops = 2.0 * T * Fi * Fo
-    tflops = flops / (ms * 1e-3) / 1e12
     alg_bytes = 2.0 * (T * Fi + T * Fo + 2 * Fi * Fo)   # X, dY, the accumulator read and written
     cpu = None
     if not args.no_cpu_baseline:
@@ -186,24 +324,10 @@ def bench_weight_grad(args):
         cpu = {"value": round(2.0 * T * len(rows) * Fo / el / 1e12, 5), "unit": "TFLOP/s",
                "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
                "sample": f"{len(rows)} of {Fi} rows of dW (fp64 numpy: X^T dY + accumulator), {el:.1f} s"}
-    line = {
-        "metric": "fused GEMM+epilogue TFLOP/s, % bf16 MFMA peak; speedup vs unfused HIP",
-        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "gpt2s_mlp_up weight gradient: dW_acc += X^T dY, X [8192 tokens x 768], "
-                               "dY [8192 x 3072], A stored [K x M], in-place accumulation, bf16",
-                   "M": Fi, "N": Fo, "K": T, "cache_flush_between_steps": not args.no_flush,
-                   "tile": coda.coda_selected_tile(Fi, Fo, T, call.desc)},
-        "pct_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
-        "unfused_ms_per_step": None if unfused_ms is None else round(unfused_ms, 4),
-        "speedup_vs_unfused": None if unfused_ms is None else round(unfused_ms / ms, 3),
-        "effective_GBps": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
-        "cpu_baseline": cpu,
-        "kernel_source_hash": kernel_source_hash(),
-    }
+    config = {"workload": "gpt2s_mlp_up weight gradient: dW_acc += X^T dY, X [8192 tokens x 768], "
+                          "dY [8192 x 3072], A stored [K x M], in-place accumulation, bf16",
+              "M": Fi, "N": Fo, "K": T, "tile": coda.coda_selected_tile(Fi, Fo, T, call.desc)}
+    line = result_line(args, timer, flops, t["fused"], t.get("unfused"), config, PEAK_BF16_TFLOPS, alg_bytes, cpu)
     print(json.dumps(line), flush=True)
 
 
@@ -227,22 +351,20 @@ def bench_rms_backward(args):
     dpb = w.bf16_bits_from_f64(rng.standard_normal((T, Np)) / np.sqrt(Np))
     to_dev = lambda b: runner.storage_to_tensor(b, "bf16")
     X, G, W, dP = to_dev(xb), to_dev(gb), to_dev(wb), to_dev(dpb)
-    stats = torch.empty((T, 2), dtype=torch.float32, device="cuda")
-    stats[:, 0] = X.float().pow(2).sum(dim=1)
-    stats[:, 1] = torch.from_numpy(rng.standard_normal(T).astype(np.float32)).cuda()
+    stats_t = torch.empty((T, 2), dtype=torch.float32, device="cuda")
+    stats_t[:, 0] = X.float().pow(2).sum(dim=1)
+    stats_t[:, 1] = torch.from_numpy(rng.standard_normal(T).astype(np.float32)).cuda()
     dg = torch.zeros((F, 1), dtype=torch.float32, device="cuda")
-    ops = [("rms_dgamma", {"x": X, "eps": eps, "stats": stats, "sumsq_col": 0, "out": dg, "col": 0}),
-           ("rms_bwd", {"x": X, "gamma": G, "eps": eps, "stats": stats, "sumsq_col": 0, "t_col": 1})]
+    ops = [("rms_dgamma", {"x": X, "eps": eps, "stats": stats_t, "sumsq_col": 0, "out": dg, "col": 0}),
+           ("rms_bwd", {"x": X, "gamma": G, "eps": eps, "stats": stats_t, "sumsq_col": 0, "t_col": 1})]
     call = runner.Call(dP, W, ops, "NK", tile=args.tile)
-    timed = _event_timer(args)
-
-    print("[bench] rms backward: fused", file=sys.stderr, flush=True)
-    ms = float(timed(call.fused, args.warmup, args.steps).mean())
-    unfused_ms = None
+    timer = Timer(args)
+    fns = {"fused": call.fused}
     if not args.no_unfused:
-        print("[bench] rms backward: unfused", file=sys.stderr, flush=True)
-        unfused_ms = float(timed(call.unfused, max(2, args.warmup // 2), args.steps).mean())
-    tflops = 2.0 * T * F * Np / (ms * 1e-3) / 1e12
+        fns["unfused"] = call.unfused
+    print("[bench] rms backward: fused and unfused, interleaved", file=sys.stderr, flush=True)
+    t = timer.run(fns)
+    flops = 2.0 * T * F * Np
     alg_bytes = 2.0 * (T * Np + F * Np + 2 * T * F)   # dP, W, x read; dX written
     cpu = None
     if not args.no_cpu_baseline:
@@ -256,34 +378,25 @@ def bench_rms_backward(args):
         cpu = {"value": round(2.0 * len(rows) * F * Np / el / 1e12, 5), "unit": "TFLOP/s",
                "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
                "sample": f"{len(rows)} of {T} rows of dX (fp64 numpy: dP W^T, the norm's backward), {el:.1f} s"}
-    line = {
-        "metric": "fused GEMM+epilogue TFLOP/s, % bf16 MFMA peak; speedup vs unfused HIP",
-        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "llama7b RMSNorm backward through the gate/up projection: dX = RMS_BWD(dP W^T) "
-                               "and dgamma = RMS_DGAMMA(dP W^T), dP [4096 tokens x 22016], W [4096 x 22016], "
-                               "row statistics given, bf16",
-                   "M": T, "N": F, "K": Np, "cache_flush_between_steps": not args.no_flush,
-                   "tile": coda.coda_selected_tile(T, F, Np, call.desc)},
-        "pct_peak": round(100.0 * tflops / PEAK_BF16_TFLOPS, 2),
-        "unfused_ms_per_step": None if unfused_ms is None else round(unfused_ms, 4),
-        "speedup_vs_unfused": None if unfused_ms is None else round(unfused_ms / ms, 3),
-        "effective_GBps": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
-        "cpu_baseline": cpu,
-        "kernel_source_hash": kernel_source_hash(),
-    }
+    config = {"workload": "llama7b RMSNorm backward through the gate/up projection: dX = RMS_BWD(dP W^T) "
+                          "and dgamma = RMS_DGAMMA(dP W^T), dP [4096 tokens x 22016], W [4096 x 22016], "
+                          "row statistics given, bf16",
+              "M": T, "N": F, "K": Np, "tile": coda.coda_selected_tile(T, F, Np, call.desc)}
+    line = result_line(args, timer, flops, t["fused"], t.get("unfused"), config, PEAK_BF16_TFLOPS, alg_bytes, cpu)
     print(json.dumps(line), flush=True)
+
+
+WORKLOAD_KEY = {1: "tiny_fwd", 2: "gpt2s_mlp_up", 3: "bertl_mlp_down", 4: "llama7b_gate_up",
+                5: "gpt2m_mlp_bwd", 6: "gpt2s_mlp_up_layernorm"}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=40,
-                    help="untimed steps first; the clock needs a few tens of steps to settle under this load")
+    ap.add_argument("--steps", type=int, default=20, help="timed rounds (one step of each variant per round)")
+    ap.add_argument("--warmup", type=int, default=10, help="untimed rounds first (at least)")
+    ap.add_argument("--warmup-seconds", type=float, default=0.6,
+                    help="the warm-up lasts at least this long: the clock needs a few hundred ms to settle")
     ap.add_argument("--tile", type=int, default=0, help="force a tile configuration (0 = automatic)")
     ap.add_argument("--workload", type=int, default=WORKLOAD_INDEX, choices=sorted(WORKLOAD_TEXT),
                     help="synthetic layer to time (default: the LLaMA-7B gate/up layer)")
@@ -299,9 +412,10 @@ def main():
                     help="the GPT-2-small MLP up-projection's weight gradient, dW_acc += X^T dY, instead")
     ap.add_argument("--rms-backward", action="store_true",
                     help="time the RMS norm's backward through the LLaMA-7B gate/up projection instead")
-    ap.add_argument("--in-loop-gain", action="store_true",
-                    help="time the RMSNorm / LayerNorm gain applied to A in the main loop instead of folded into a "
-                         "copy of the weights once (coda_fold_gain, outside the timed region; the default)")
+    ap.add_argument("--fold-gain", action="store_true",
+                    help="headline = the RMSNorm / LayerNorm gain folded into a copy of the weights once "
+                         "(coda_fold_gain, outside the timed region) instead of applied to A in the main loop; "
+                         "the other placement is timed beside it either way")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unfused", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -340,7 +454,7 @@ def main():
     inputs = w.make_inputs(spec)
     has_rms = any(op == "rms_rowscale" for op, _ in spec.program)
     has_norm = has_rms or any(op == "ln_rowscale" for op, _ in spec.program)
-    fold = has_norm and (not args.in_loop_gain or args.given_row_sumsq)
+    fold = has_norm and (args.fold_gain or args.given_row_sumsq)
     call = runner.WorkloadCall(spec, inputs, tile=args.tile, fold_gain=fold)
     if args.given_row_sumsq:
         if not has_norm:
@@ -353,7 +467,6 @@ def main():
         prog = [(n, dict(a)) for n, a in call.ops]
         prog[0][1].update({"row_ss": row_stats, "row_ss_col": 1, "row_s_col": 0})
         call = runner.Call(A, call.B, prog, spec.b_layout, d_dtype=TORCH_DT_OF[spec.d_dtype], tile=args.tile)
-    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
     if args.copy_calibration:
         src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
@@ -364,105 +477,46 @@ def main():
         del src, dst
     tile_used = coda.coda_selected_tile(spec.M, spec.N, spec.K, call.desc)
 
-    def step(fn):
-        if not args.no_flush:
-            flush.zero_()
-        start = torch.cuda.Event(enable_timing=True)
-        end = torch.cuda.Event(enable_timing=True)
-        start.record()
-        coda.check(fn(), "launch")
-        end.record()
-        return start, end
-
-    print(f"[bench] fused warm-up {args.warmup}, timed {args.steps}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        step(call.fused)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    evs = [step(call.fused) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    fused_ms = np.array([s.elapsed_time(e) for s, e in evs])
-    ms = float(fused_ms.mean())
-
-    unfused_ms = None
+    fns = {"fused": call.fused}
     if not args.no_unfused:
-        print("[bench] unfused sequence", file=sys.stderr, flush=True)
-        for _ in range(max(2, args.warmup // 2)):
-            step(call.unfused)
-        torch.cuda.synchronize()
-        uevs = [step(call.unfused) for _ in range(args.steps)]
-        torch.cuda.synchronize()
-        unfused_ms = float(np.mean([s.elapsed_time(e) for s, e in uevs]))
-
-    # the other placement of the RMSNorm gain, for comparison (not the headline)
-    other_ms = None
-    if has_norm and not args.no_unfused and not args.given_row_sumsq:
-        print("[bench] fused, other gain placement", file=sys.stderr, flush=True)
+        fns["unfused"] = call.unfused
+    other = None
+    if has_norm and not args.given_row_sumsq and not args.no_unfused:
+        # the other placement of the norm's gain, for comparison (not the headline)
         other = runner.WorkloadCall(spec, inputs, tile=args.tile, fold_gain=not fold)
-        for _ in range(max(2, args.warmup // 2)):
-            step(other.fused)
-        torch.cuda.synchronize()
-        oevs = [step(other.fused) for _ in range(args.steps)]
-        torch.cuda.synchronize()
-        other_ms = float(np.mean([s.elapsed_time(e) for s, e in oevs]))
-        del other
+        fns["other"] = other.fused
+    timer = Timer(args)
+    print(f"[bench] {', '.join(fns)}: warm-up >= {args.warmup} rounds and {args.warmup_seconds} s, "
+          f"then {args.steps} timed rounds", file=sys.stderr, flush=True)
+    t = timer.run(fns)
 
     flops = float(spec.flops)
-    tflops = flops / (ms * 1e-3) / 1e12
     peak = PEAK_F32_TFLOPS if spec.ab_dtype == "f32" else PEAK_BF16_TFLOPS
     alg_bytes = algorithmic_bytes(spec)
     khash = kernel_source_hash()
-    # the committed counter runs cover the LLaMA layer's kernel
-    traffic = load_traffic(khash) if args.workload == WORKLOAD_INDEX else None
+    key = WORKLOAD_KEY[args.workload]
+    plain_variant = not (args.bias_grad or args.given_row_sumsq or args.fold_gain or args.tile or args.no_flush)
+    traffic = load_traffic(key, khash) if plain_variant else None
+    counter_clock = load_counter_clock(key, khash) if plain_variant else None
 
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         cpu = cpu_baseline(spec, inputs)
 
-    line = {
-        "metric": "fused GEMM+epilogue TFLOP/s, % bf16 MFMA peak; speedup vs unfused HIP",
-        "value": round(tflops, 2),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32" if spec.ab_dtype == "f32" else "bf16",
-        "data": "synthetic",
-        "config": {
-            "workload": WORKLOAD_TEXT[args.workload] + (" + bias gradient (column sum of dH)"
-                                                        if args.bias_grad else ""),
-            "M": spec.M, "N": spec.N, "K": spec.K,
-            "cache_flush_between_steps": not args.no_flush,
-            "gain_folded_into_weights": bool(fold),
-            "row_sumsq_given": bool(args.given_row_sumsq),
-            "tile": tile_used,
-        },
-        "pct_peak": round(100.0 * tflops / peak, 2),
-        "unfused_ms_per_step": None if unfused_ms is None else round(unfused_ms, 4),
-        "speedup_vs_unfused": None if unfused_ms is None else round(unfused_ms / ms, 3),
-        "effective_GBps": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
-        ("fused_in_loop_gain_ms_per_step" if fold else "fused_folded_gain_ms_per_step"):
-            None if other_ms is None else round(other_ms, 4),
-        "fused_ms_p10_p90": [round(float(np.percentile(fused_ms, 10)), 4),
-                             round(float(np.percentile(fused_ms, 90)), 4)],
-        "wall_s_timed_region": round(wall, 4),
-        "roofline": {
-            "bound": "mfma",
-            "achieved": round(tflops, 2),
-            "peak": peak,
-            "unit": "TFLOP/s",
-            "frac": round(tflops / peak, 4),
-            "traffic": traffic,
-        },
-        "cpu_baseline": cpu,
-        "kernel_source_hash": khash,
+    config = {
+        "workload": WORKLOAD_TEXT[args.workload] + (" + bias gradient (column sum of dH)" if args.bias_grad else ""),
+        "M": spec.M, "N": spec.N, "K": spec.K,
+        "gain": ("folded into a copy of the weights" if fold else "applied to A in the main loop")
+                if has_norm else None,
+        "row_sumsq_given": bool(args.given_row_sumsq),
+        "tile": tile_used,
     }
+    extra = {}
+    if other is not None:
+        extra[("fused_in_loop_gain_ms" if fold else "fused_folded_gain_ms")] = stats(t["other"])
+    line = result_line(args, timer, flops, t["fused"], t.get("unfused"), config, peak, alg_bytes, cpu,
+                       traffic=traffic, counter_clock=counter_clock, extra=extra)
     print(json.dumps(line), flush=True)
 
 

@@ -1,9 +1,11 @@
-"""Host-side checks of bench.py (no GPU): the multi-GPU refusal and the
-traffic record's source-hash gate."""
+"""Host-side checks of bench.py (no GPU): the multi-GPU refusal, the profile
+records' source-hash gate and the timing statistics."""
 import json
 import os
 import subprocess
 import sys
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -14,15 +16,27 @@ def test_more_than_one_gpu_is_refused():
     assert "one GPU" in r.stderr
 
 
-def test_traffic_record_only_used_for_matching_sources(tmp_path, monkeypatch):
+def test_profile_records_only_used_for_matching_sources():
     sys.path.insert(0, ROOT)
     import bench
     h = bench.kernel_source_hash()
     assert len(h) == 16 and h == bench.kernel_source_hash()
-    rec_path = os.path.join(ROOT, "profiles", "fused_llama7b_gate_up_traffic.json")
-    if os.path.exists(rec_path):
-        rec = json.load(open(rec_path))
-        got = bench.load_traffic(h)
-        assert got is None or got == rec["hbm_bytes_per_launch"]
-        assert got == (rec["hbm_bytes_per_launch"] if rec["kernel_source_hash"] == h else None)
-    assert bench.load_traffic("0" * 16) is None
+    for key in bench.WORKLOAD_KEY.values():
+        for kind, getter, field in (("traffic", bench.load_traffic, "bytes_per_launch"),):
+            path = os.path.join(ROOT, "profiles", f"{key}_{kind}.json")
+            got = getter(key, h)
+            if os.path.exists(path):
+                rec = json.load(open(path))
+                assert got == (rec[field] if rec["kernel_source_hash"] == h else None)
+            else:
+                assert got is None
+            assert getter(key, "0" * 16) is None
+        assert bench.load_counter_clock(key, "0" * 16) is None
+
+
+def test_stats_median_and_percentiles():
+    sys.path.insert(0, ROOT)
+    import bench
+    s = bench.stats(np.array([1.0, 2.0, 3.0, 4.0, 100.0]))
+    assert s["median"] == 3.0 and s["mean"] == 22.0
+    assert s["p10"] <= s["median"] <= s["p90"]
