@@ -53,6 +53,7 @@ CODA_OP_COL_SUMSQ = 16
 CODA_OP_ROW_DOT = 17
 CODA_OP_RMS_BWD = 18
 CODA_OP_RMS_DGAMMA = 19
+CODA_OP_DROPOUT = 20
 
 EXPORTED = (
     "coda_gemm_epi", "coda_gemm_unfused", "coda_validate", "coda_workspace_size",
@@ -75,6 +76,8 @@ class coda_op(ctypes.Structure):
         ("row_sum", ctypes.c_void_p),
         ("row_sumsq", ctypes.c_void_p),
         ("row_ld", ctypes.c_int64),
+        ("seed", ctypes.c_uint64),
+        ("offset", ctypes.c_uint64),
     ]
 
 

@@ -67,6 +67,55 @@ __device__ __forceinline__ float gelu_tanh_grad_f(float p) {
 }
 
 // ---------------------------------------------------------------------------
+// Dropout's generator: Philox-4x64 with 10 rounds (Salmon, Moraes, Dror and
+// Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011).  A round
+// multiplies counter words 0 and 2 by the two round multipliers into 128-bit
+// products and recombines them with words 1 and 3 and the key; the key then
+// advances by the two Weyl increments (the golden ratio and sqrt(3) - 1 as
+// 64-bit fractions).
+// ---------------------------------------------------------------------------
+constexpr unsigned long long kPhiloxM0 = 0xD2E7470EE14C6C93ull, kPhiloxM1 = 0xCA5A826395121157ull;
+constexpr unsigned long long kPhiloxW0 = 0x9E3779B97F4A7C15ull, kPhiloxW1 = 0xBB67AE8584CAA73Bull;
+
+__device__ __forceinline__ void philox4x64_10(unsigned long long (&c)[4], unsigned long long k0,
+                                              unsigned long long k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const unsigned long long hi0 = __umul64hi(kPhiloxM0, c[0]), lo0 = kPhiloxM0 * c[0];
+    const unsigned long long hi1 = __umul64hi(kPhiloxM1, c[2]), lo1 = kPhiloxM1 * c[2];
+    c[0] = hi1 ^ c[1] ^ k0;
+    c[1] = lo1;
+    c[2] = hi0 ^ c[3] ^ k1;
+    c[3] = lo0;
+    k0 += kPhiloxW0;
+    k1 += kPhiloxW1;
+  }
+}
+
+// Inverted dropout of n consecutive values v[0..n) of row `row`, columns
+// col .. col + n - 1, with n = 8 and col % 8 == 0, or n = 4 and col % 4 == 0
+// (one generator block either way): the block has key (seed, 0) and counter
+// (col / 8, row, offset, 0), column j takes 32-bit word j % 8 (the low half of
+// 64-bit word (j % 8) / 2 when even, the high half when odd), and a value is
+// kept, times `scale`, when its word is >= thr.
+template <int n>
+__device__ __forceinline__ void dropout_values(float* v, long long row, long long col, unsigned thr, float scale,
+                                               unsigned long long seed, unsigned long long offset) {
+  static_assert(n == 8 || n == 4, "one generator block per call");
+  unsigned long long c[4] = {(unsigned long long)(col >> 3), (unsigned long long)row, offset, 0ull};
+  philox4x64_10(c, seed, 0ull);
+  // the upper half of a block (col % 8 == 4) takes 64-bit words 2 and 3; a
+  // select rather than a runtime index keeps the words in registers
+  const bool upper = n == 4 && (col & 4) != 0;
+  const unsigned long long x[4] = {upper ? c[2] : c[0], upper ? c[3] : c[1], c[2], c[3]};
+#pragma unroll
+  for (int e = 0; e < n; ++e) {
+    const unsigned word = unsigned(x[e >> 1] >> (32 * (e & 1)));
+    v[e] = word >= thr ? v[e] * scale : 0.0f;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Buffer resources: raw (stride 0) buffers whose out-of-range loads return 0.
 // Offsets at or above num_records read as zero instead of faulting, which is
 // how tile tails and masked K chunks are zero-filled.
@@ -97,11 +146,12 @@ struct DevOp {
   float* out;
   long long out_stride;
   int red_slot;         // reductions: 0..n_red-1
-  int pad_;
+  unsigned thr;         // DROPOUT: keep when the element's 32-bit word >= thr
   const void* in2;      // RMS_BWD: gamma [width] (dtype)
   const float* row_s;   // RMS_BWD: t per row (row_ld apart)
   const float* row_ss;  // RMS_BWD: sum of squares of x per row
   long long row_ld;
+  unsigned long long seed, offset;   // DROPOUT: key word 0, counter word 2 (scalar = 1 / (1 - p))
 };
 
 struct FusedArgs {

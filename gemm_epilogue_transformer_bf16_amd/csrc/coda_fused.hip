@@ -49,6 +49,9 @@ dev::FusedArgs make_args(const Plan& p) {
     d.row_s = q.row_s;
     d.row_ss = q.row_ss;
     d.row_ld = q.row_ld;
+    d.thr = q.thr;
+    d.seed = q.seed;
+    d.offset = q.offset;
   }
   char* ws = static_cast<char*>(p.workspace);
   if (p.n_red > 0 && p.grid_n > 1) {
@@ -102,27 +105,13 @@ int launch_fused(const Plan& p, hipStream_t stream) {
 
 int launch_plain_gemm(const Plan& p, const void* A, int64_t lda, void* out, int64_t ldo, hipStream_t stream) {
   if (p.M == 0 || p.N == 0) return CODA_OK;
-  Plan q = p;
+  // the fused kernel with an empty list, split like a fused call of this GEMM
+  Plan q = plain_gemm_plan(p);
   q.A = A;
   q.lda = lda;
   q.D = out;
   q.ldd = ldo;
-  q.has_norm = false;
-  q.has_ln = false;
-  q.gain_in_b = false;
-  q.gamma = nullptr;
-  q.ln_u = nullptr;
-  q.row_ss = nullptr;
-  q.row_s = nullptr;
-  q.n_ops = 0;
-  q.n_red = 0;
-  q.n_colred = 0;
-  q.has_swiglu = false;
-  q.out_width = p.N;
-  // no workspace here: the tiles are computed whole
-  q.full_tiles = q.grid_m * q.grid_n;
-  q.split_tiles = 0;
-  q.split_s = 1;
+  q.workspace = static_cast<char*>(p.workspace) + unfused_split_offset(p);
   dev::FusedArgs a = make_args(q);
   return launch_args(q, a, stream);
 }

@@ -306,6 +306,13 @@ __device__ __forceinline__ int run_ops(Chunks<C::CPL>& ch, KArgs a, int o, int M
             ch.v[j][e] = addm ? ch.v[j][e] + beta * x[j][e] : ch.v[j][e] * gelu_tanh_grad_f(x[j][e]);
         break;
       }
+      case CODA_OP_DROPOUT: {
+        // the lane's chunk of each row: 8 columns (4 after SWIGLU_PAIR), one
+        // generator block
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) dropout_values<EPC>(ch.v[j], ch.row[j], col, op.thr, op.scalar, op.seed, op.offset);
+        break;
+      }
       case CODA_OP_GELU_TANH:
       case CODA_OP_SILU: {
         const bool gelu = kind == CODA_OP_GELU_TANH;
@@ -615,12 +622,15 @@ fused_kernel(FusedArgs args) {
         return;
       }
       const __amdgpu_buffer_rsrc_t ra = make_rsrc(Abase + (long long)k0 * 2, a_ext0 - (long long)k0 * 2);
+      // chunks past K read as zero (an offset with the top bit set is out of
+      // range); whole K steps take the wave-uniform first branch, so the
+      // offsets carry no per-lane select (one compiled as a divergent branch
+      // around every load)
+      const uint32_t kmask = (k0 + 64 <= K) ? 0u : ((k0 + 8 * kq_chunk < K) ? 0u : kOobOffset);
 #pragma unroll
       for (int i = 0; i < C::A_BPW; ++i) {
         const int q = wave + C::NW * i;
-        const uint32_t off = (k0 + 8 * kq_chunk < K)
-                                 ? uint32_t(8 * q + kq_row) * uint32_t(lda * 2) + uint32_t(kq_chunk * 16)
-                                 : kOobOffset;
+        const uint32_t off = (uint32_t(8 * q + kq_row) * uint32_t(lda * 2) + uint32_t(kq_chunk * 16)) | kmask;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (LdsPtr)(dst + q * 1024), 16, (int)off, 0, 0, 0);
       }
       if constexpr (C::RMS) {
@@ -644,12 +654,11 @@ fused_kernel(FusedArgs args) {
         }
       } else {
         const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bbase + (long long)k0 * 2, b_ext0 - (long long)k0 * 2);
+        const uint32_t kmask = (k0 + 64 <= K) ? 0u : ((k0 + 8 * kq_chunk < K) ? 0u : kOobOffset);
 #pragma unroll
         for (int i = 0; i < C::B_BPW; ++i) {
           const int q = wave + C::NW * i;
-          const uint32_t off = (k0 + 8 * kq_chunk < K)
-                                   ? uint32_t(8 * q + kq_row) * uint32_t(ldb * 2) + uint32_t(kq_chunk * 16)
-                                   : kOobOffset;
+          const uint32_t off = (uint32_t(8 * q + kq_row) * uint32_t(ldb * 2) + uint32_t(kq_chunk * 16)) | kmask;
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (LdsPtr)(Bs + q * 1024), 16, (int)off, 0, 0, 0);
         }
       }

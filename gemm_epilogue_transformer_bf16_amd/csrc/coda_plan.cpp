@@ -56,6 +56,33 @@ bool overlap(const Extent& a, const Extent& b) {
   return a.lo < b.hi && b.lo < a.hi;
 }
 
+// n elements of `elem` bytes, `stride` bytes apart (a dense block: n = 1)
+struct Strided {
+  uintptr_t lo;
+  int64_t n, stride, elem;
+  Extent extent() const {
+    if (lo == 0 || n <= 0) return {0, 0};
+    return {lo, lo + uintptr_t((n - 1) * stride + elem)};
+  }
+};
+
+Strided dense(const Extent& e) { return {e.lo, e.empty() ? 0 : 1, 0, int64_t(e.hi - e.lo)}; }
+Strided column(const void* p, int64_t n, int64_t stride_elems) {
+  return {reinterpret_cast<uintptr_t>(p), n, stride_elems * 4, 4};
+}
+
+// Two strided vectors of one stride whose elements fall in disjoint byte
+// ranges of every period (columns of one row-major array) do not overlap.
+bool strided_overlap(const Strided& a, const Strided& b) {
+  if (!overlap(a.extent(), b.extent())) return false;
+  if (a.stride == b.stride && a.stride > 0 && a.n > 1 && b.n > 1 && a.elem <= a.stride && b.elem <= b.stride) {
+    intptr_t d = (intptr_t(b.lo) - intptr_t(a.lo)) % intptr_t(a.stride);
+    if (d < 0) d += intptr_t(a.stride);
+    if (d >= a.elem && intptr_t(a.stride) - d >= b.elem) return false;
+  }
+  return true;
+}
+
 // Automatic tile choice, from measurements on MI355X: the 8-wave 256 x 256
 // tile (config 3) is fastest once its grid fills the 256 CUs at least once;
 // smaller grids do better with 128 x 128 tiles (config 2), which give four
@@ -134,7 +161,7 @@ size_t fused_workspace_bytes(const Plan& p) {
 // round of r = T % slots tiles.  Splitting each of those r tiles over K into s
 // parts (s <= slots / r, each part at least kMinSplitSteps K steps) lets the
 // last round take about 1/s of a round.
-void plan_split(Plan* p, bool allow) {
+void plan_split(Plan* p, bool allow, int max_split) {
   p->full_tiles = p->grid_m * p->grid_n;
   p->split_tiles = 0;
   p->split_s = 1;
@@ -144,7 +171,7 @@ void plan_split(Plan* p, bool allow) {
   const int64_t r = tiles % slots;
   if (r == 0) return;
   int64_t s = slots / r;
-  if (s > kMaxSplit) s = kMaxSplit;
+  if (s > max_split) s = max_split;
   if (s > p->k_steps / kMinSplitSteps) s = p->k_steps / kMinSplitSteps;
   if (s < 2) return;
   p->split_tiles = r;
@@ -161,16 +188,37 @@ size_t unfused_col_partials_offset(const Plan& p) {
   return bytes;
 }
 
-size_t unfused_workspace_bytes(const Plan& p) {
-  if (p.M == 0 || p.N == 0) return 0;
+Plan plain_gemm_plan(const Plan& p) {
+  Plan q = p;
+  q.has_norm = q.has_ln = q.gain_in_b = false;
+  q.gamma = nullptr;
+  q.ln_u = q.row_ss = q.row_s = nullptr;
+  q.n_ops = q.n_red = q.n_colred = 0;
+  q.has_swiglu = false;
+  q.out_width = p.N;
+  plan_split(&q, p.split_allowed, kMaxSplit);
+  return q;
+}
+
+size_t unfused_split_offset(const Plan& p) {
   size_t bytes = unfused_col_partials_offset(p);
   if (p.n_colred > 0)
     bytes += align256(size_t((p.M + kColChunk - 1) / kColChunk) * size_t(unfused_ld(p)) * sizeof(float));
   return bytes;
 }
 
+size_t unfused_workspace_bytes(const Plan& p) {
+  if (p.M == 0 || p.N == 0) return 0;
+  return unfused_split_offset(p) + fused_workspace_bytes(plain_gemm_plan(p));
+}
+
 int build_plan(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
                const coda_epi_desc* d, int unfused, bool check_pointers, Plan* p) {
+  return build_plan_split(A, B, M, N, K, d, unfused, check_pointers, kMaxSplit, p);
+}
+
+int build_plan_split(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
+                     const coda_epi_desc* d, int unfused, bool check_pointers, int max_split, Plan* p) {
   clear_error();
   if (!d || !p) {
     set_error("descriptor is NULL");
@@ -230,7 +278,7 @@ int build_plan(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
   int n_red = 0, n_col = 0;
   for (int i = 0; i < d->n_ops; ++i) {
     const coda_op& o = d->ops[i];
-    if (o.kind < CODA_OP_SCALE || o.kind > CODA_OP_RMS_DGAMMA) {
+    if (o.kind < CODA_OP_SCALE || o.kind > CODA_OP_DROPOUT) {
       set_error("op %d: unknown kind %d", i, o.kind);
       return CODA_ERR_INVALID_ARG;
     }
@@ -319,6 +367,25 @@ int build_plan(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
     q.in2 = nullptr;
     q.row_s = q.row_ss = nullptr;
     q.row_ld = 0;
+    q.seed = q.offset = 0;
+    q.thr = 0;
+    if (o.kind == CODA_OP_DROPOUT) {
+      // keep when the element's 32-bit word >= floor(p * 2^32); kept values
+      // are scaled by 1 / (1 - p), rounded once to fp32
+      if (!(std::isfinite(o.scalar) && o.scalar >= 0.0f && o.scalar < 1.0f)) {
+        set_error("op %d: DROPOUT probability must be in [0, 1)", i);
+        return CODA_ERR_INVALID_ARG;
+      }
+      if (o.in) {
+        set_error("op %d: DROPOUT takes no input (in must be NULL)", i);
+        return CODA_ERR_INVALID_ARG;
+      }
+      const double pd = double(o.scalar);
+      q.thr = uint32_t(std::floor(pd * 4294967296.0));
+      q.scalar = float(1.0 / (1.0 - pd));
+      q.seed = o.seed;
+      q.offset = o.offset;
+    }
     if (bwd) {
       if (width == 0) {
         set_error("op %d: RMS_BWD needs width > 0", i);
@@ -494,7 +561,8 @@ int build_plan(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
     return CODA_ERR_UNSUPPORTED;
   }
   p->k_steps = (K + p->cfg.bk - 1) / p->cfg.bk;
-  plan_split(p, !unfused && !(d->flags & CODA_FLAG_NO_SPLIT_K));
+  p->split_allowed = !(d->flags & CODA_FLAG_NO_SPLIT_K);
+  plan_split(p, !unfused && p->split_allowed, max_split);
 
   // ---- overlap ----
   if (check_pointers) {
@@ -565,6 +633,38 @@ int build_plan(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
         outs[no] = e;
         strides[no] = q.out_stride;
         ++no;
+      }
+    }
+    // A reduction output must not overlap anything the same call reads: the
+    // fused kernel and the unfused sequence read inputs at different times
+    // relative to the writes, so the two paths would disagree.
+    Strided ins[4 + 4 * CODA_MAX_OPS];
+    int ni = 0;
+    if (p->gamma) ins[ni++] = dense(matrix_extent(p->gamma, 1, K, K, abs));
+    if (p->ln_u) ins[ni++] = dense(matrix_extent(p->ln_u, 1, N, N, 4));
+    if (p->row_ss) ins[ni++] = column(p->row_ss, M, p->row_ss_stride);
+    if (p->row_s) ins[ni++] = column(p->row_s, M, p->row_ss_stride);
+    for (int i = 0; i < p->n_ops; ++i) {
+      const Op& q = p->ops[i];
+      if (q.in && (needs_vector(q.kind) || needs_matrix(q.kind))) {
+        const size_t es = dtype_size(q.dtype);
+        if (q.kind == CODA_OP_SCALE_ROW || q.kind == CODA_OP_ADD_ROW) ins[ni++] = dense(matrix_extent(q.in, 1, M, M, es));
+        else if (needs_vector(q.kind)) ins[ni++] = dense(matrix_extent(q.in, 1, q.width, q.width, es));
+        else ins[ni++] = dense(matrix_extent(q.in, M, q.width, q.ld, es));
+      }
+      if (q.in2) ins[ni++] = dense(matrix_extent(q.in2, 1, q.width, q.width, dtype_size(q.dtype)));
+      if (q.row_s) ins[ni++] = column(q.row_s, M, q.row_ld);
+      if (q.row_ss) ins[ni++] = column(q.row_ss, M, q.row_ld);
+    }
+    for (int i = 0; i < p->n_ops; ++i) {
+      const Op& q = p->ops[i];
+      if (!is_reduction(q.kind) && !is_col_reduction(q.kind)) continue;
+      const Strided o = column(q.out, is_col_reduction(q.kind) ? q.width : M, q.out_stride);
+      for (int j = 0; j < ni; ++j) {
+        if (strided_overlap(o, ins[j])) {
+          set_error("reduction output of op %d overlaps an input read by the same call", i);
+          return CODA_ERR_INVALID_ARG;
+        }
       }
     }
   }

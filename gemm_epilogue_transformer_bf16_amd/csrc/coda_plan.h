@@ -49,6 +49,8 @@ struct Op {
   const float* row_s;   // RMS_BWD: t per row
   const float* row_ss;  // RMS_BWD: sum of squares of x per row
   int64_t row_ld;
+  uint64_t seed, offset;   // DROPOUT: the generator's key word 0 and counter word 2
+  uint32_t thr;            // DROPOUT: keep when the element's 32-bit word >= thr (scalar = 1 / (1 - p))
 };
 
 struct Plan {
@@ -83,6 +85,7 @@ struct Plan {
   int64_t full_tiles;        // tiles computed whole
   int64_t split_tiles;       // tiles split over K
   int split_s;               // parts per split tile (1: no split)
+  bool split_allowed;        // the caller did not set CODA_FLAG_NO_SPLIT_K
   void* workspace;
   size_t workspace_bytes;
 };
@@ -91,6 +94,10 @@ struct Plan {
 // message retrievable through coda_last_error().
 int build_plan(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
                const coda_epi_desc* desc, int unfused, bool check_pointers, Plan* plan);
+// The same, with the split of the last round limited to max_split parts per
+// tile (1: no split), e.g. to fit a fixed scratch buffer.
+int build_plan_split(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
+                     const coda_epi_desc* desc, int unfused, bool check_pointers, int max_split, Plan* plan);
 
 // Workspace layout of the fused path, each region 256-byte aligned: fp32 row
 // reduction partials [n_red][grid_n][M], uint32 counters [grid_m]; then for
@@ -116,6 +123,12 @@ constexpr int kColChunk = 128;
 size_t unfused_workspace_bytes(const Plan& p);
 int64_t unfused_ld(const Plan& p);
 size_t unfused_col_partials_offset(const Plan& p);
+// The plain GEMM of the unfused sequence: the call's plan without a row norm
+// or ops, with the split of the last round a fused call of that GEMM would
+// use; its workspace (split partial tiles and counters, zero counters on
+// entry and exit) sits at unfused_split_offset(p) in the unfused workspace.
+Plan plain_gemm_plan(const Plan& p);
+size_t unfused_split_offset(const Plan& p);
 
 // Validates a coda_ln_fold call.  Returns a coda_status.
 int validate_ln_fold(const void* B, int64_t K, int64_t N, int64_t ldb, int32_t b_layout, int32_t dtype,

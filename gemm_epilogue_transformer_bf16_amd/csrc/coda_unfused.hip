@@ -190,6 +190,9 @@ __global__ void __launch_bounds__(kPassThreads) ew_kernel(const void* in, long l
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = gelu_tanh_f(v[e]);
         break;
+      case CODA_OP_DROPOUT:
+        dropout_values<8>(v, row, c, op.thr, op.scalar, op.seed, op.offset);
+        break;
       case CODA_OP_SILU:
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = silu_f(v[e]);
@@ -317,6 +320,9 @@ dev::DevOp to_dev(const Op& q) {
   d.row_s = q.row_s;
   d.row_ss = q.row_ss;
   d.row_ld = q.row_ld;
+  d.thr = q.thr;
+  d.seed = q.seed;
+  d.offset = q.offset;
   return d;
 }
 

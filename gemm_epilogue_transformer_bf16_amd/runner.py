@@ -34,6 +34,7 @@ OPCODES = {
     "row_dot": C.CODA_OP_ROW_DOT,
     "rms_bwd": C.CODA_OP_RMS_BWD,
     "rms_dgamma": C.CODA_OP_RMS_DGAMMA,
+    "dropout": C.CODA_OP_DROPOUT,
 }
 
 TORCH_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
@@ -123,6 +124,7 @@ class Call:
         if len(self.ops) > C.CODA_MAX_OPS:
             raise ValueError(f"at most {C.CODA_MAX_OPS} ops")
         d.n_ops = len(self.ops)
+        self._validate_operands(width_in=self.N)
         for i, (name, args) in enumerate(self.ops):
             o = d.ops[i]
             o.kind = OPCODES[name]
@@ -140,6 +142,10 @@ class Call:
                 o.scalar = float(args.get("beta", 1.0))
             elif name in ("rms_rowscale", "ln_rowscale"):
                 o.scalar = float(args["eps"])
+            elif name == "dropout":
+                o.scalar = float(args["p"])
+                o.seed = int(args.get("seed", 0)) & ((1 << 64) - 1)
+                o.offset = int(args.get("offset", 0)) & ((1 << 64) - 1)
             if name == "ln_rowscale":
                 o.in2 = args["u"].data_ptr()
             if name in ("rms_rowscale", "ln_rowscale") and args.get("row_ss") is not None:
@@ -191,6 +197,81 @@ class Call:
         for unfused in (0, 1):
             nbytes = C.coda_workspace_size(self.M, self.N, self.K, d, unfused)
             self.ws[unfused] = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=A.device) if nbytes else None
+
+    def _validate_operands(self, width_in: int):
+        """Shapes, dtypes and strides of every tensor an op reads or writes.
+
+        The C ABI sees raw pointers only and cannot check extents, so a tensor
+        that is too small, of the wrong dtype or with a strided inner dimension
+        is rejected here, before a descriptor points at it.
+        """
+        M, K = self.M, self.K
+        width = width_in
+
+        def check(t, what, *, rows=None, cols=None, length=None, dtype=None):
+            if not isinstance(t, torch.Tensor):
+                raise ValueError(f"{what}: expected a tensor, got {type(t).__name__}")
+            if dtype is not None and t.dtype != dtype:
+                raise ValueError(f"{what}: dtype {t.dtype}, expected {dtype}")
+            if t.dtype not in CODA_DT:
+                raise ValueError(f"{what}: dtype {t.dtype} is neither bfloat16 nor float32")
+            if length is not None:
+                if t.dim() != 1 or t.shape[0] < length or (t.numel() > 1 and t.stride(0) != 1):
+                    raise ValueError(f"{what}: expected a contiguous vector of at least {length} elements, "
+                                     f"got shape {tuple(t.shape)}")
+                return
+            if t.dim() != 2:
+                raise ValueError(f"{what}: expected a 2-D tensor, got shape {tuple(t.shape)}")
+            if t.shape[1] > 1 and t.stride(1) != 1:
+                raise ValueError(f"{what}: the inner dimension must be contiguous (stride {t.stride(1)})")
+            if rows is not None and t.shape[0] < rows:
+                raise ValueError(f"{what}: {t.shape[0]} rows, at least {rows} needed")
+            if cols is not None and t.shape[1] < cols:
+                raise ValueError(f"{what}: {t.shape[1]} columns, at least {cols} needed")
+
+        def check_col(t, col, what):
+            if not 0 <= int(col) < t.shape[1]:
+                raise ValueError(f"{what}: column {col} outside 0..{t.shape[1] - 1}")
+
+        for name, args in self.ops:
+            if name not in OPCODES:
+                raise ValueError(f"unknown op {name!r}")
+            if name in ("rms_rowscale", "ln_rowscale"):
+                if args.get("gamma") is not None:
+                    check(args["gamma"], f"{name} gamma", length=K, dtype=self.A.dtype)
+                if args.get("u") is not None:
+                    check(args["u"], f"{name} u", length=self.N, dtype=torch.float32)
+                if args.get("row_ss") is not None:
+                    st = args["row_ss"]
+                    check(st, f"{name} row statistics", rows=M, dtype=torch.float32)
+                    check_col(st, args.get("row_ss_col", 0), f"{name} row_ss_col")
+                    if name == "ln_rowscale":
+                        check_col(st, args["row_s_col"], f"{name} row_s_col")
+            elif name in ("scale_row", "add_row"):
+                check(args["vec"], f"{name} vec", length=M)
+            elif name in ("scale_col", "add_col"):
+                check(args["vec"], f"{name} vec", length=width)
+            elif name in ("add_mat", "mul_dgelu_tanh", "row_dot"):
+                check(args["mat"], f"{name} mat", rows=M, cols=width)
+            elif name in ("rms_bwd", "rms_dgamma"):
+                check(args["x"], f"{name} x", rows=M, cols=width)
+                st = args["stats"]
+                check(st, f"{name} stats", rows=M, dtype=torch.float32)
+                check_col(st, args.get("sumsq_col", 0), f"{name} sumsq_col")
+                if name == "rms_bwd":
+                    check(args["gamma"], f"{name} gamma", length=width)
+                    check_col(st, args.get("t_col", 1), f"{name} t_col")
+            elif name == "dropout":
+                p = float(args["p"])
+                if not 0.0 <= p < 1.0:
+                    raise ValueError(f"dropout probability {p} outside [0, 1)")
+            if name in ("row_sum", "row_sumsq", "row_mean", "row_dot", "col_sum", "col_sumsq", "rms_dgamma"):
+                out = args["out"]
+                col_red = name in ("col_sum", "col_sumsq", "rms_dgamma")
+                check(out, f"{name} out", rows=width if col_red else M, dtype=torch.float32)
+                check_col(out, args.get("col", 0), f"{name} out col")
+            if name == "swiglu_pair":
+                width //= 2
 
     def _expand_layernorm(self, ops, B: torch.Tensor, ldb: int):
         """ln_rowscale(gamma, beta, eps) -> LN_ROWSCALE(gamma, u) [+ ADD_COL(c)],

@@ -49,8 +49,11 @@
  *    CODA_OK.  Sizes that are not tile multiples (ragged M, N, K) are supported.
  *  - Aliasing: D may coincide exactly with the matrix of a CODA_OP_ADD_MAT op
  *    (same pointer, same dtype, same leading dimension: an in-place residual
- *    update).  Any other overlap between D and an input, or between outputs,
- *    is CODA_ERR_INVALID_ARG.
+ *    update).  Any other overlap between D and an input, between outputs,
+ *    or between a reduction output and any input the same call reads (the
+ *    columns of one row-major array may interleave: a reduction may write one
+ *    column of a stats array whose other columns an op reads), is
+ *    CODA_ERR_INVALID_ARG.
  *  - The library is stateless and reentrant, except for the workspace rule
  *    of coda_gemm_epi below.
  */
@@ -182,7 +185,20 @@ typedef enum {
      ((float*)out)[j*out_stride], in = x [M x width] (in_dtype, ld),
      row_sumsq[i*row_ld] = sum_k x[i,k]^2 (fp32), scalar = eps.  Placed before
      RMS_BWD in the same list, it reads the same x and row statistics. */
-  CODA_OP_RMS_DGAMMA = 19
+  CODA_OP_RMS_DGAMMA = 19,
+  /* dropout (the d9bl.com page, section 3.2: the EPILOGUE example's
+     `output = dropout(output, 0.1)`): element (i, j) of the running value is
+     kept with probability 1 - p and scaled by 1 / (1 - p), or set to 0; p is
+     `scalar`, 0 <= p < 1.  The mask comes from the counter-based generator
+     Philox-4x64-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers:
+     as easy as 1, 2, 3", SC 2011) with key (seed, 0) and counter
+     (j / 8, i, offset, 0): j indexes the current width, and the element takes
+     32-bit word j % 8 of the 256-bit block (the low half of 64-bit word
+     (j % 8) / 2 when j % 8 is even, the high half when odd); it is kept when
+     that word is >= floor(p * 2^32).  The mask depends on (seed, offset, i, j)
+     only, so it is reproducible, needs no stored state, and a backward pass
+     regenerates it; vary `offset` (or `seed`) to draw a new mask. */
+  CODA_OP_DROPOUT = 20
 } coda_op_kind;
 
 typedef struct {
@@ -199,6 +215,8 @@ typedef struct {
   const void* row_sumsq;/* RMS/LN_ROWSCALE: given fp32 row sums of squares, or NULL;
                            RMS_BWD, RMS_DGAMMA: sum_k x[i,k]^2                       */
   int64_t row_ld;       /* element stride between rows of row_sum / row_sumsq (>= 1) */
+  uint64_t seed;        /* DROPOUT: the generator's key word 0 (ignored by other ops) */
+  uint64_t offset;      /* DROPOUT: counter word 2, e.g. a step count (ignored by other ops) */
 } coda_op;
 
 typedef struct {
@@ -219,16 +237,20 @@ typedef struct {
 
 /*
  * coda_gemm_epi - one fused kernel: D = f(A * B) with f = desc->ops in order.
- * The GEMM runs on MFMA with fp32 accumulators; every op runs on the fp32
- * accumulators in registers; D is written once, rounded to d_dtype
+ * The GEMM runs on MFMA with fp32 accumulators.  The ops run on fp32 values
+ * on-chip: each wave passes its accumulators once through its own region of
+ * LDS into a row-major layout (every lane then holds runs of 8 consecutive
+ * columns, so side operands and D move as whole 16-byte row chunks), and the
+ * list runs there before D is written once, rounded to d_dtype
  * (round-to-nearest-even for bf16).  With CODA_OP_RMS_ROWSCALE first, the
  * GEMM operand is A*gamma rounded to ab_dtype and the row factor is applied
  * to the accumulators.  With CODA_OP_LN_ROWSCALE first and bf16 operands, the
- * GEMM operand is (A - s_i)*gamma rounded to bf16, s_i being the row's first
- * element (a shift that leaves the norm unchanged and keeps rows whose spread
- * is small against their mean accurate); the row mean and variance come from
- * sums of A - s_i gathered in the main loop.  LN_ROWSCALE tiles are never
- * split over K.
+ * GEMM operand is (A - s_i)*gamma rounded to bf16, s_i being a per-row shift
+ * (a constant that leaves the norm unchanged and keeps rows whose spread is
+ * small against their mean accurate): the mean of the row's first 64 stored
+ * values with the gain applied in the loop, the row's first element with the
+ * gain folded into B; the row mean and variance come from sums of A - s_i
+ * gathered in the main loop.  LN_ROWSCALE tiles are never split over K.
  * Load balance: when the output tiles do not fill a whole number of rounds
  * of the GPU's compute units, each tile of the last, partial round is split
  * over K between up to 4 workgroups (bf16 operands only, unless flags holds
@@ -254,9 +276,15 @@ int coda_gemm_epi(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
  * memory and read straight back): an RMS or LayerNorm normalisation pass over
  * A (when the list starts with CODA_OP_RMS_ROWSCALE or CODA_OP_LN_ROWSCALE;
  * the latter writes (A - mu) / sqrt(var + eps) * gamma), the plain GEMM with the same main
- * loop as coda_gemm_epi, then one pass per remaining op.  Intermediates are
- * stored in d_dtype in the workspace (coda_workspace_size(..., 1) bytes).
- * Meant as the in-run comparison for coda_gemm_epi.  Returns a coda_status.
+ * loop as coda_gemm_epi (split over K in its last, partial round exactly as
+ * a fused call of that GEMM would be, unless flags holds
+ * CODA_FLAG_NO_SPLIT_K), then one pass per remaining op.  Intermediates are
+ * stored in d_dtype in the workspace (coda_workspace_size(..., 1) bytes),
+ * which also holds the split's partial tiles and counters: as for
+ * coda_gemm_epi, the workspace must be zero before the first call (every
+ * call leaves the counters zero again) and concurrent calls must not share
+ * it.  Meant as the in-run comparison for coda_gemm_epi.  Returns a
+ * coda_status.
  */
 int coda_gemm_unfused(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
                       const coda_epi_desc* desc, void* stream);

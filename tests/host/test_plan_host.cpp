@@ -297,7 +297,7 @@ int main() {
     coda_epi_desc e = base_desc(N, K);
     e.n_ops = 2;
     e.ops[0].kind = CODA_OP_ROW_DOT; e.ops[0].in = P(0x40000000); e.ops[0].ld = N; e.ops[0].in_dtype = CODA_BF16;
-    e.ops[0].out = Pm(0x50000000); e.ops[0].out_stride = 2;
+    e.ops[0].out = Pm(0x51000000); e.ops[0].out_stride = 2;
     e.ops[1].kind = CODA_OP_RMS_BWD; e.ops[1].in = P(0x41000000); e.ops[1].ld = N; e.ops[1].in_dtype = CODA_BF16;
     e.ops[1].in2 = P(0x42000000); e.ops[1].row_sumsq = P(0x50000000); e.ops[1].row_sum = P(0x50000004);
     e.ops[1].row_ld = 2; e.ops[1].scalar = 1e-5f;
@@ -321,8 +321,26 @@ int main() {
     EXPECT(coda_validate(A, B, 100, N, K, &f, 0) == CODA_ERR_INVALID_ARG);   // in2 only on LN_ROWSCALE / RMS_BWD
     f = e; f.ops[1].in2 = P(0x30000000);
     EXPECT(coda_validate(A, B, 100, N, K, &f, 0) == CODA_ERR_INVALID_ARG);   // gamma over D
-    f = e; f.ops[1].kind = 20;
+    f = e; f.ops[1].kind = 21;
     EXPECT(coda_validate(A, B, 100, N, K, &f, 0) == CODA_ERR_INVALID_ARG);   // unknown kind
+    // a reduction output must not overlap what the same call reads: ROW_DOT
+    // writing the t column (or the sums of squares) RMS_BWD reads is rejected
+    f = e; f.ops[0].out = Pm(0x50000004);
+    EXPECT(coda_validate(A, B, 100, N, K, &f, 0) == CODA_ERR_INVALID_ARG);
+    EXPECT(coda_validate(A, B, 100, N, K, &f, 1) == CODA_ERR_INVALID_ARG);
+    f = e; f.ops[0].out = Pm(0x50000000);
+    EXPECT(coda_validate(A, B, 100, N, K, &f, 0) == CODA_ERR_INVALID_ARG);
+    // a third column of the same [M x 3] array is fine: the columns interleave
+    f = e; f.ops[0].out = Pm(0x50000008); f.ops[0].out_stride = 3; f.ops[1].row_ld = 3;
+    EXPECT(coda_validate(A, B, 100, N, K, &f, 0) == CODA_OK);
+    // ... and so is a column that only starts inside another's period
+    f = e; f.ops[0].out = Pm(0x50000004); f.ops[0].out_stride = 3; f.ops[1].row_ld = 3;
+    EXPECT(coda_validate(A, B, 100, N, K, &f, 0) == CODA_ERR_INVALID_ARG);
+    // a reduction output inside ROW_DOT's own matrix or RMS_BWD's x
+    f = e; f.ops[0].out = Pm(0x40000100);
+    EXPECT(coda_validate(A, B, 100, N, K, &f, 0) == CODA_ERR_INVALID_ARG);
+    f = e; f.ops[0].out = Pm(0x41000100);
+    EXPECT(coda_validate(A, B, 100, N, K, &f, 0) == CODA_ERR_INVALID_ARG);
     // RMS_DGAMMA: a column reduction over x / r, before RMS_BWD
     f = e; f.n_ops = 3; f.ops[2] = f.ops[1]; f.ops[1] = coda_op{};
     f.ops[1].kind = CODA_OP_RMS_DGAMMA; f.ops[1].in = P(0x41000000); f.ops[1].ld = N; f.ops[1].in_dtype = CODA_BF16;
@@ -416,6 +434,40 @@ int main() {
     EXPECT(coda::validate_ln_fold(B, 768, 3072, 3072, CODA_B_KN, CODA_BF16, g, nullptr,
                                   static_cast<float*>(Pm(0x20000010)), nullptr) == CODA_ERR_INVALID_ARG);   // u in B
     EXPECT(coda::validate_ln_fold(B, 768, 0, 8, CODA_B_KN, CODA_BF16, g, nullptr, nullptr, nullptr) == CODA_OK);
+  }
+  {  // DROPOUT: 0 <= p < 1, no input; the plan holds the keep threshold and 1 / (1 - p)
+    coda_epi_desc e = base_desc(N, K);
+    e.n_ops = 1;
+    e.ops[0].kind = CODA_OP_DROPOUT; e.ops[0].scalar = 0.5f; e.ops[0].seed = 0x1234; e.ops[0].offset = 9;
+    EXPECT(coda_validate(A, B, M, N, K, &e, 0) == CODA_OK);
+    EXPECT(coda_validate(A, B, M, N, K, &e, 1) == CODA_ERR_WORKSPACE);   // the unfused pass needs its buffer
+    e.workspace = Pm(0x70000000); e.workspace_bytes = coda_workspace_size(M, N, K, &e, 1);
+    EXPECT(coda_validate(A, B, M, N, K, &e, 1) == CODA_OK);
+    coda::Plan q = plan_of(M, N, K, e);
+    EXPECT(q.ops[0].thr == 0x80000000u && q.ops[0].scalar == 2.0f && q.ops[0].seed == 0x1234 &&
+           q.ops[0].offset == 9);
+    e.ops[0].scalar = 0.0f;
+    EXPECT(plan_of(M, N, K, e).ops[0].thr == 0u);
+    e.ops[0].scalar = 0.25f;
+    EXPECT(plan_of(M, N, K, e).ops[0].thr == 0x40000000u);
+    coda_epi_desc f = e; f.ops[0].scalar = 1.0f;
+    EXPECT(coda_validate(A, B, M, N, K, &f, 0) == CODA_ERR_INVALID_ARG);
+    f = e; f.ops[0].scalar = -0.1f;
+    EXPECT(coda_validate(A, B, M, N, K, &f, 0) == CODA_ERR_INVALID_ARG);
+    f = e; f.ops[0].in = P(0x40000000); f.ops[0].in_dtype = CODA_BF16;
+    EXPECT(coda_validate(A, B, M, N, K, &f, 0) == CODA_ERR_INVALID_ARG);
+  }
+  {  // a reduction output over an ADD_MAT residual the same call reads
+    coda_epi_desc e = base_desc(N, K);
+    e.n_ops = 2;
+    e.ops[0].kind = CODA_OP_ADD_MAT; e.ops[0].in = P(0x40000000); e.ops[0].ld = N; e.ops[0].in_dtype = CODA_BF16;
+    e.ops[0].scalar = 1.0f;
+    e.ops[1].kind = CODA_OP_ROW_SUM; e.ops[1].out = Pm(0x40000400); e.ops[1].out_stride = 1;
+    e.workspace = Pm(0x70000000); e.workspace_bytes = coda_workspace_size(M, N, K, &e, 0) + 256;
+    EXPECT(coda_validate(A, B, M, N, K, &e, 0) == CODA_ERR_INVALID_ARG);
+    e.ops[1].out = Pm(0x50000000);
+    e.workspace_bytes = coda_workspace_size(M, N, K, &e, 0);
+    EXPECT(coda_validate(A, B, M, N, K, &e, 0) == CODA_OK);
   }
   EXPECT(std::strcmp(coda_status_string(CODA_ERR_WORKSPACE), "CODA_ERR_WORKSPACE") == 0);
   if (failures == 0) std::printf("ALL OK\n");
