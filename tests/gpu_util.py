@@ -103,7 +103,8 @@ def unfused_extra(spec, inputs, rows, fold_gain: bool = False):
     last_ew = ew[-1] if ew else -1
 
     def value_after(i):   # oracle value after body[:i]
-        v, _ = oracle.forward(A, oracle.logical_b(B, "KN"), ([ops[0]] if body is not ops else []) + body[:i], "KN")
+        v, _ = oracle.forward(A, oracle.logical_b(B, "KN"), ([ops[0]] if body is not ops else []) + body[:i], "KN",
+                              row_ids=rows)
         return v
 
     if last_ew >= 0:
@@ -133,6 +134,43 @@ def unfused_extra(spec, inputs, rows, fold_gain: bool = False):
     return extra, red_extra
 
 
+def bf16_round(x: np.ndarray) -> np.ndarray:
+    """Round-to-nearest-even to bf16, from fp64 (the storage rounding of the workloads)."""
+    return w.bf16_bits_to_f64(w.bf16_bits_from_f64(x))
+
+
+def operand_rounding_extra(spec, inputs, rows, fold_gain: bool):
+    """Exact effect on D (and on the row reductions) of the one bf16 rounding
+    the deferred RMSNorm's GEMM operand takes on bf16 matrix cores.
+
+    The method feeds the matrix cores bf16 operands, so the gained operand is
+    rounded once: x * gamma in the main loop, or gamma * w when the gain is
+    folded into the weights.  The bar for bf16 outputs from fp32 accumulation
+    does not cover that rounding, which at K = 4096 reaches the bar's edge on
+    a few tens of the LLaMA layer's 45 M outputs.  This is its exact effect:
+    the oracle's epilogue on the product of the rounded operand, minus the
+    oracle's result; the kernel must then be within the bar of the latter
+    plus this.  Computed from the stored inputs and the rounding rule alone.
+    Returns (extra for D, {reduction index: extra per row}), or (None, {}).
+    """
+    if spec.ab_dtype != "bf16" or not spec.program or spec.program[0][0] != "rms_rowscale":
+        return None, {}
+    dtypes = {t.name: t.dtype for t in spec.tensors}
+    X = to_f64(inputs[spec.a_name], dtypes[spec.a_name])[rows]
+    B = oracle.logical_b(to_f64(inputs[spec.b_name], dtypes[spec.b_name]), spec.b_layout)
+    ops = oracle.resolve_program(spec, inputs, rows)
+    g, eps = ops[0][1]["gamma"], float(ops[0][1]["eps"])
+    r = oracle.rms(X, eps)
+    if fold_gain:
+        C = (X / r[:, None]) @ bf16_round(g[:, None] * B)
+    else:
+        C = (bf16_round(X * g[None, :]) / r[:, None]) @ B
+    D_rounded, reds_rounded = oracle.apply_epilogue(C, ops[1:], rows)
+    D_exact, reds_exact = oracle.forward(X, B, ops, "KN", row_ids=rows)
+    red_extra = {i: np.abs(a[2] - b[2]) for i, (a, b) in enumerate(zip(reds_rounded, reds_exact))}
+    return np.abs(D_rounded - D_exact), red_extra
+
+
 def run_and_compare(spec, inputs, mode: str = "fused", tile: int = 0, rows=None, label: str = "",
                     check_determinism: bool = False, flags: int = 0, return_call: bool = False,
                     fold_gain: bool = False):
@@ -160,14 +198,17 @@ def run_and_compare(spec, inputs, mode: str = "fused", tile: int = 0, rows=None,
             assert torch.equal(o1[k], call.outputs[k]), f"{k} not bitwise repeatable"
     rows_idx = np.arange(spec.M) if rows is None else np.asarray(rows)
     D_ref, outs_ref = oracle.run_workload(spec, inputs, rows_idx)
-    d_extra, red_extra = (None, {}) if mode == "fused" else unfused_extra(spec, inputs, rows_idx, fold_gain)
+    if mode == "fused":
+        d_extra, red_extra = operand_rounding_extra(spec, inputs, rows_idx, fold_gain)
+    else:
+        d_extra, red_extra = unfused_extra(spec, inputs, rows_idx, fold_gain)
     stats = {"D": assert_close(D, D_ref, f"{spec.name}/{mode}/D", d_extra)}
     red_i = 0
     for name, args in spec.program:
         if name not in ("row_sum", "row_sumsq", "row_mean"):
             continue
         o, col = args["out"], args["col"]
-        extra = red_extra.get(red_i) if mode == "unfused" else None
+        extra = red_extra.get(red_i)
         stats[f"{o}[{col}]"] = assert_close(outs[o][:, col], outs_ref[o][:, col], f"{spec.name}/{mode}/{o}[:,{col}]",
                                             extra)
         red_i += 1

@@ -8,7 +8,7 @@ import torch
 
 import workloads as w
 
-from gpu_util import announce, lib, run_and_compare, sample_rows
+from gpu_util import announce, lib, run_and_compare
 
 pytestmark = pytest.mark.gpu
 
@@ -78,15 +78,13 @@ def test_folded_split_round(CR, flags):
     # 12 x 12 = 144 tiles of 256 x 256 with 32 K steps: the last, partial round
     # is split over K (flags 0) or computed whole (CODA_FLAG_NO_SPLIT_K)
     spec = w.scaled_config(4, 2944, 2944, 2048)
-    rows = sample_rows(spec.M, 32)
-    run_and_compare(spec, w.make_inputs(spec), tile=3, flags=flags, rows=rows, fold_gain=True,
+    run_and_compare(spec, w.make_inputs(spec), tile=3, flags=flags, fold_gain=True,
                     check_determinism=True, label=f"folded split flags={flags}")
 
 
 @pytest.mark.parametrize("idx", [2, 4])
 @pytest.mark.parametrize("mode", ["fused", "unfused"])
-def test_folded_full_size_sampled_rows(CR, idx, mode):
+def test_folded_full_size_every_row(CR, idx, mode):
     spec = w.get_config(idx)
-    rows = sample_rows(spec.M, 48)
-    run_and_compare(spec, w.make_inputs(spec), mode=mode, rows=rows, fold_gain=True, label=f"folded full cfg{idx}",
+    run_and_compare(spec, w.make_inputs(spec), mode=mode, fold_gain=True, label=f"folded full cfg{idx}",
                     check_determinism=(mode == "fused"))

@@ -6,7 +6,7 @@ import torch
 
 import workloads as w
 
-from gpu_util import lib, run_and_compare, sample_rows
+from gpu_util import lib, run_and_compare
 
 pytestmark = pytest.mark.gpu
 
@@ -42,18 +42,17 @@ def test_small_configs_every_tile(idx, tile):
 
 
 @pytest.mark.parametrize("idx", [2, 3, 4, 5])
-def test_full_size_sampled_rows_fused(idx):
+def test_full_size_every_row_fused(idx):
     spec = w.get_config(idx)
     inputs = w.make_inputs(spec)
-    run_and_compare(spec, inputs, mode="fused", rows=sample_rows(spec.M), label=f"full cfg{idx}",
-                    check_determinism=True)
+    run_and_compare(spec, inputs, mode="fused", label=f"full cfg{idx}", check_determinism=True)
 
 
 @pytest.mark.parametrize("idx", [2, 3, 4, 5])
-def test_full_size_sampled_rows_unfused(idx):
+def test_full_size_every_row_unfused(idx):
     spec = w.get_config(idx)
     inputs = w.make_inputs(spec)
-    run_and_compare(spec, inputs, mode="unfused", rows=sample_rows(spec.M, 24), label=f"full cfg{idx}")
+    run_and_compare(spec, inputs, mode="unfused", label=f"full cfg{idx}")
 
 
 def test_full_cfg1_exact_shape_both_modes():
