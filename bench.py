@@ -19,9 +19,9 @@ settled whatever the round count.  Times are medians over the timed rounds
 (p10 / p90 beside them).
 
 Prints one JSON line: fused TFLOP/s (2 M N K / median kernel time), the share
-of the bf16 dense MFMA peak (and of the peak at the clock measured during the
-run), the speedup over the unfused sequence, the roofline object and the
-CPU-oracle baseline.
+of the bf16 dense MFMA peak (and of the peak at the shader clock the committed
+counter run measured under the same kernel sources), the speedup over the
+unfused sequence, the roofline object and the CPU-oracle baseline.
 """
 from __future__ import annotations
 
@@ -142,41 +142,6 @@ def cpu_baseline(spec, inputs, budget_s: float = 10.0):
     }
 
 
-class ClockSampler:
-    """Samples the GPU shader clock (MHz, torch.cuda.clock_rate, which reads
-    amdsmi on ROCm) from a background thread while kernels run; None when the
-    query is unavailable."""
-
-    def __init__(self, period_s: float = 0.002):
-        import threading
-        self.period_s = period_s
-        self.samples = []
-        self._stop = threading.Event()
-        self._thread = None
-        self._threading = threading
-
-    def _loop(self):
-        import torch
-        while not self._stop.is_set():
-            try:
-                self.samples.append(float(torch.cuda.clock_rate(0)))
-            except Exception:     # pragma: no cover - query not available
-                return
-            self._stop.wait(self.period_s)
-
-    def start(self):
-        self.samples = []
-        self._stop.clear()
-        self._thread = self._threading.Thread(target=self._loop, daemon=True)
-        self._thread.start()
-
-    def stop(self):
-        self._stop.set()
-        if self._thread is not None:
-            self._thread.join()
-        return float(np.median(self.samples)) if self.samples else None
-
-
 class Timer:
     """Times C-ABI launch functions round-robin: per round one step of each, every
     step preceded by a cache flush (a 512 MiB fill, unless --no-flush) and
@@ -189,9 +154,7 @@ class Timer:
         import torch
         self.args = args
         self.flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
-        self.clock = ClockSampler()
         self.wall_s = None
-        self.clock_mhz = None
 
     def _step(self, fn):
         import torch
@@ -218,7 +181,6 @@ class Timer:
             if rounds % 8 == 0:
                 torch.cuda.synchronize()
         torch.cuda.synchronize()
-        self.clock.start()
         t1 = time.perf_counter()
         evs = {name: [] for name in fns}
         for _ in range(args.steps):
@@ -226,7 +188,6 @@ class Timer:
                 evs[name].append(self._step(fn))
         torch.cuda.synchronize()
         self.wall_s = time.perf_counter() - t1
-        self.clock_mhz = self.clock.stop()
         self.warmup_rounds = rounds
         self.warmup_s = t1 - t0
         return {name: np.array([a.elapsed_time(b) for a, b in e]) for name, e in evs.items()}
@@ -243,7 +204,6 @@ def result_line(args, timer, flops, fused_ms, unfused_ms, config, peak, alg_byte
     ms = float(np.median(fused_ms))
     tflops = flops / (ms * 1e-3) / 1e12
     umed = None if unfused_ms is None else float(np.median(unfused_ms))
-    clock_ghz = counter_clock if counter_clock else (None if timer.clock_mhz is None else timer.clock_mhz / 1e3)
     line = {
         "metric": "fused GEMM+epilogue TFLOP/s, % bf16 MFMA peak; speedup vs unfused HIP",
         "value": round(tflops, 2),
@@ -264,11 +224,13 @@ def result_line(args, timer, flops, fused_ms, unfused_ms, config, peak, alg_byte
         "unfused_ms_per_step": None if umed is None else round(umed, 4),
         "speedup_vs_unfused": None if umed is None else round(umed / ms, 3),
         "effective_GBps": round(alg_bytes / (ms * 1e-3) / 1e9, 1),
-        "clock_ghz_smi": None if timer.clock_mhz is None else round(timer.clock_mhz / 1e3, 3),
+        # the shader clock under this kernel (GRBM_GUI_ACTIVE cycles over the
+        # dispatch time, from the committed counter run of the same sources) and
+        # the dense peak at that clock: 256 CUs x 4096 bf16 flop per clock
+        # (x 256 for fp32)
         "clock_ghz_counters": counter_clock,
-        # dense peak at the measured clock: 256 CUs x 4096 bf16 flop per clock (x 256 fp32)
-        "pct_peak_at_measured_clock": None if clock_ghz is None else round(
-            100.0 * tflops / ((4096.0 if peak != PEAK_F32_TFLOPS else 256.0) * 256 * clock_ghz * 1e-3), 2),
+        "pct_peak_at_measured_clock": None if not counter_clock else round(
+            100.0 * tflops / ((4096.0 if peak != PEAK_F32_TFLOPS else 256.0) * 256 * counter_clock * 1e-3), 2),
         "timing": {"warmup_rounds": timer.warmup_rounds, "warmup_s": round(timer.warmup_s, 3),
                    "timed_rounds_wall_s": round(timer.wall_s, 4), "interleaved": True,
                    "cache_flush_between_steps": not args.no_flush},
