@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libcoda.so")
 HIP_SOURCES = [
     "coda_fused_t1.hip", "coda_fused_t2.hip", "coda_fused_t3.hip",
     "coda_fused_tf32.hip", "coda_fused.hip", "coda_unfused.hip", "coda_fold.hip", "coda_api.hip",
+    "coda_noalloc.hip",
 ]
 CPP_SOURCES = ["coda_plan.cpp"]
 

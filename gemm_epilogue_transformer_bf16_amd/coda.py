@@ -58,8 +58,9 @@ CODA_OP_DROPOUT = 20
 EXPORTED = (
     "coda_gemm_epi", "coda_gemm_unfused", "coda_validate", "coda_workspace_size",
     "coda_status_string", "coda_last_error", "coda_num_tile_configs", "coda_tile_config",
-    "coda_selected_tile", "coda_ln_fold", "coda_fold_gain",
+    "coda_selected_tile", "coda_ln_fold", "coda_fold_gain", "coda_gemm_epi_noalloc",
 )
+CODA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class coda_op(ctypes.Structure):
@@ -118,6 +119,8 @@ def _load():
     DESC = ctypes.POINTER(coda_epi_desc)
     lib.coda_gemm_epi.argtypes = [P, P, I64, I64, I64, DESC, P]
     lib.coda_gemm_epi.restype = ctypes.c_int
+    lib.coda_gemm_epi_noalloc.argtypes = [P, P, I64, I64, I64, DESC, P]
+    lib.coda_gemm_epi_noalloc.restype = ctypes.c_int
     lib.coda_gemm_unfused.argtypes = [P, P, I64, I64, I64, DESC, P]
     lib.coda_gemm_unfused.restype = ctypes.c_int
     lib.coda_validate.argtypes = [P, P, I64, I64, I64, DESC, ctypes.c_int]
@@ -152,6 +155,10 @@ def _desc_ptr(desc):
 
 def coda_gemm_epi(A: int, B: int, M: int, N: int, K: int, desc: coda_epi_desc, stream: int = 0) -> int:
     return lib.coda_gemm_epi(A, B, M, N, K, _desc_ptr(desc), stream)
+
+
+def coda_gemm_epi_noalloc(A: int, B: int, M: int, N: int, K: int, desc: coda_epi_desc, stream: int = 0) -> int:
+    return lib.coda_gemm_epi_noalloc(A, B, M, N, K, _desc_ptr(desc), stream)
 
 
 def coda_gemm_unfused(A: int, B: int, M: int, N: int, K: int, desc: coda_epi_desc, stream: int = 0) -> int:

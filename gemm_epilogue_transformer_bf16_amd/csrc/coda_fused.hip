@@ -103,6 +103,18 @@ int launch_fused(const Plan& p, hipStream_t stream) {
   return launch_args(p, a, stream);
 }
 
+int launch_fused_with_counters(const Plan& p, unsigned* counters, hipStream_t stream) {
+  if (p.M == 0 || p.N == 0) return CODA_OK;
+  dev::FusedArgs a = make_args(p);
+  // the counters live in a region the caller keeps zero between calls (every
+  // call leaves the counters it used at zero): row counters, then column
+  // counters, then the split tiles' counters
+  if (a.counters) a.counters = counters;
+  if (a.col_counters) a.col_counters = counters + p.grid_m;
+  if (a.split_cnt) a.split_cnt = counters + p.grid_m + p.grid_n;
+  return launch_args(p, a, stream);
+}
+
 int launch_plain_gemm(const Plan& p, const void* A, int64_t lda, void* out, int64_t ldo, hipStream_t stream) {
   if (p.M == 0 || p.N == 0) return CODA_OK;
   // the fused kernel with an empty list, split like a fused call of this GEMM

@@ -10,6 +10,11 @@ namespace coda {
 // Enqueue the fused kernel for `p` on `stream`.  Returns a coda_status.
 int launch_fused(const Plan& p, hipStream_t stream);
 
+// The same, with the cross-workgroup counters taken from `counters` (at least
+// grid_m + grid_n + split_tiles words, zero on entry and left zero) instead
+// of the workspace, whose counter regions are then unused.
+int launch_fused_with_counters(const Plan& p, unsigned* counters, hipStream_t stream);
+
 // Enqueue the unfused sequence for `p` on `stream`.  Returns a coda_status.
 int launch_unfused(const Plan& p, hipStream_t stream);
 

@@ -71,6 +71,9 @@ extern "C" {
 #define CODA_MAX_REDUCTIONS 8
 #define CODA_MAX_COL_REDUCTIONS 2
 
+/* bytes of the fixed per-GPU scratch of coda_gemm_epi_noalloc (64 MiB) */
+#define CODA_NOALLOC_SCRATCH_BYTES (64u << 20)
+
 /* coda_epi_desc.flags */
 #define CODA_FLAG_NO_SPLIT_K 1   /* coda_gemm_epi: never split the last round of
                                     tiles over K (see coda_gemm_epi)            */
@@ -268,6 +271,29 @@ typedef struct {
  */
 int coda_gemm_epi(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
                   const coda_epi_desc* desc, void* stream);
+
+/*
+ * coda_gemm_epi_noalloc - coda_gemm_epi for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  The same computation and results as
+ * coda_gemm_epi, with the cross-workgroup scratch (row and column reduction
+ * partials and counters, the split round's partial tiles) taken from a fixed
+ * array of CODA_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it
+ * runs on until the process ends; desc->workspace and desc->workspace_bytes
+ * are ignored.  The array's first 1 MiB holds the cross-workgroup counters
+ * at fixed places (zero between calls), the rest a call's partial sums and
+ * tiles.  When the split of the last round would not fit, the tiles are
+ * split into fewer parts, or not at all; when even the unsplit call needs
+ * more scratch than the maximum (row reductions over many tile columns of a
+ * very tall output), it returns CODA_ERR_WORKSPACE and launches nothing.
+ * Calls no allocating routine.  Every call on one GPU shares that GPU's
+ * array: calls that may run at the same time on one GPU (different streams,
+ * or host threads) race and must be serialised by the caller.  The first
+ * call on a device clears the array with a kernel on `stream`.
+ * Returns a coda_status.
+ */
+int coda_gemm_epi_noalloc(const void* A, const void* B, int64_t M, int64_t N, int64_t K,
+                          const coda_epi_desc* desc, void* stream);
 
 /*
  * coda_gemm_unfused - the same computation as the framework-level sequence of
