@@ -96,10 +96,17 @@ def load_traffic(workload: str, kernel_hash: str):
 def load_counter_clock(workload: str, kernel_hash: str):
     """Shader clock (GHz) of the fused kernel from the committed counter run:
     GRBM_GUI_ACTIVE cycles (per XCD) over the dispatch duration."""
+    return load_counter_field(workload, kernel_hash, "clock_ghz")
+
+
+def load_counter_field(workload: str, kernel_hash: str, field: str):
+    """A derived figure of the fused kernel from the committed counter run of
+    this workload (clock_ghz, mfma_busy_pct), if it was taken on the current
+    kernel sources."""
     rec = _profile_record(workload, "counters")
     if not rec or rec.get("kernel_source_hash") != kernel_hash:
         return None
-    return rec.get("fused", {}).get("clock_ghz")
+    return rec.get("fused", {}).get(field)
 
 
 def cpu_baseline(spec, inputs, budget_s: float = 10.0):
@@ -460,6 +467,7 @@ def main():
     plain_variant = not (args.bias_grad or args.given_row_sumsq or args.fold_gain or args.tile or args.no_flush)
     traffic = load_traffic(key, khash) if plain_variant else None
     counter_clock = load_counter_clock(key, khash) if plain_variant else None
+    mfma_busy = load_counter_field(key, khash, "mfma_busy_pct") if plain_variant else None
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -474,7 +482,9 @@ def main():
         "row_sumsq_given": bool(args.given_row_sumsq),
         "tile": tile_used,
     }
-    extra = {}
+    # MFMA pipe busy share of the SIMD-cycles in the committed counter run of
+    # the same sources (the headline kernel alone, counters serialise dispatches)
+    extra = {"mfma_busy_pct_counters": mfma_busy}
     if other is not None:
         extra[("fused_in_loop_gain_ms" if fold else "fused_folded_gain_ms")] = stats(t["other"])
     line = result_line(args, timer, flops, t["fused"], t.get("unfused"), config, peak, alg_bytes, cpu,

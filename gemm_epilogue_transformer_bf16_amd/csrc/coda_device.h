@@ -129,6 +129,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)n, kBufferFlags);
 }
 
+// For extents known to be >= 0 (the main loop's): the clamp to 2^31 - 1 is a
+// shift test that stays on the scalar unit (a signed 64-bit compare has no
+// scalar form and costs vector compares and lane reads every K step).  No
+// offset within a tile reaches 2^31, so clamping larger extents loses nothing.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_nonneg(const void* base, int64_t bytes) {
+  const uint64_t b = uint64_t(bytes);
+  const int n = (b >> 31) ? 0x7fffffff : int(b);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kBufferFlags);
+}
+
 __device__ __forceinline__ u32x4_t buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
 }

@@ -82,13 +82,14 @@ int launch_args(const Plan& p, const dev::FusedArgs& a, hipStream_t stream) {
                    : p.gain_in_b ? dev::kNormRmsB
                    : p.has_norm  ? dev::kNormRms
                                  : dev::kNormNone;
+  const bool ext = p.has_ext;
   if (p.ab_dtype == CODA_F32) {
-    return dev::launch_tile_f32(a, nwg, bkn, norm, akm, stream);
+    return dev::launch_tile_f32(a, nwg, bkn, norm, akm, ext, stream);
   }
   switch (p.tile) {
-    case 1: return dev::launch_tile1(a, nwg, bkn, norm, akm, stream);
-    case 2: return dev::launch_tile2(a, nwg, bkn, norm, akm, stream);
-    case 3: return dev::launch_tile3(a, nwg, bkn, norm, akm, stream);
+    case 1: return dev::launch_tile1(a, nwg, bkn, norm, akm, ext, stream);
+    case 2: return dev::launch_tile2(a, nwg, bkn, norm, akm, ext, stream);
+    case 3: return dev::launch_tile3(a, nwg, bkn, norm, akm, ext, stream);
     default:
       set_error("no kernel for tile config %d", p.tile);
       return CODA_ERR_UNSUPPORTED;

@@ -106,10 +106,14 @@ constexpr int kNormLnB = 5;
 // LayerNorm with the gain in B and the row sums and sums of squares given
 constexpr int kNormLnGiven = 6;
 
-template <int BM_, int BN_, int WM_, int WN_, bool F32_, bool BKN_, int NORM_, bool AKM_ = false>
+template <int BM_, int BN_, int WM_, int WN_, bool F32_, bool BKN_, int NORM_, bool AKM_ = false, bool EXT_ = true>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
   static constexpr bool F32 = F32_, BKN = BKN_;
+  // EXT: the kernel carries the epilogue ops of the backward set (column
+  // reductions, ROW_DOT, RMS_BWD, RMS_DGAMMA); lists without them run a
+  // variant compiled without their code and registers
+  static constexpr bool EXT = EXT_;
   // AKM: A stored [K x M] (M contiguous) and used transposed, as X^T in the
   // weight gradient X^T dY; its tile is staged and read like an N-major W tile
   static constexpr bool AKM = AKM_;
@@ -232,7 +236,8 @@ __device__ __forceinline__ bool is_col_reduction(int kind) {
 // Applies ops[o..] until the end of the list or a SWIGLU_PAIR (returned index).
 template <class C, bool PAIRED>
 __device__ __forceinline__ int run_ops(Chunks<C::CPL>& ch, KArgs a, int o, int M, int lane, int wn, float* red,
-                                       int pf_op, const u32x4_t (&pf)[C::CPL], float* colp, int wm, int mi) {
+                                       int pf_op, const u32x4_t (&pf)[C::CPL], float* colp, int wm, int mi,
+                                       int cv_op, const float (&cv)[8]) {
   constexpr int CPL = C::CPL;
   constexpr int EPC = PAIRED ? 4 : 8;   // live values per chunk
   const int col = PAIRED ? ch.col >> 1 : ch.col;
@@ -265,7 +270,12 @@ __device__ __forceinline__ int run_ops(Chunks<C::CPL>& ch, KArgs a, int o, int M
       case CODA_OP_ADD_COL: {
         const bool add = kind == CODA_OP_ADD_COL;
         float x[8];
-        load_cols<PAIRED>(op.in, op.dtype, col, width, x);
+        if (!PAIRED && o == cv_op) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = cv[e];   // loaded once per tile
+        } else {
+          load_cols<PAIRED>(op.in, op.dtype, col, width, x);
+        }
 #pragma unroll
         for (int j = 0; j < CPL; ++j)
 #pragma unroll
@@ -343,106 +353,114 @@ __device__ __forceinline__ int run_ops(Chunks<C::CPL>& ch, KArgs a, int o, int M
         break;
       }
       case CODA_OP_ROW_DOT: {
-        // ROW_SUM of the running value times the matrix operand
-        const int esz = op.dtype == CODA_BF16 ? 2 : 4;
-        float* dst = red + (op.red_slot * C::WN + wn) * C::BM;
+        if constexpr (C::EXT) {
+          // ROW_SUM of the running value times the matrix operand
+          const int esz = op.dtype == CODA_BF16 ? 2 : 4;
+          float* dst = red + (op.red_slot * C::WN + wn) * C::BM;
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-          float x[8];
-          if (ch.row[j] < M) {
-            load_cols<PAIRED>(static_cast<const char*>(op.in) + (long long)ch.row[j] * op.ld * esz, op.dtype, col,
-                              width, x);
-          } else {
+          for (int j = 0; j < CPL; ++j) {
+            float x[8];
+            if (ch.row[j] < M) {
+              load_cols<PAIRED>(static_cast<const char*>(op.in) + (long long)ch.row[j] * op.ld * esz, op.dtype, col,
+                                width, x);
+            } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = 0.0f;
+              for (int e = 0; e < 8; ++e) x[e] = 0.0f;
+            }
+            float p = 0.0f;
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) p += (col + e < width) ? ch.v[j][e] * x[e] : 0.0f;
+#pragma unroll
+            for (int off = 1; off < C::CPR; off <<= 1) p += __shfl_xor(p, off);
+            if ((lane & (C::CPR - 1)) == 0) dst[ch.mloc[j]] = p;
           }
-          float p = 0.0f;
-#pragma unroll
-          for (int e = 0; e < EPC; ++e) p += (col + e < width) ? ch.v[j][e] * x[e] : 0.0f;
-#pragma unroll
-          for (int off = 1; off < C::CPR; off <<= 1) p += __shfl_xor(p, off);
-          if ((lane & (C::CPR - 1)) == 0) dst[ch.mloc[j]] = p;
         }
         break;
       }
       case CODA_OP_RMS_BWD: {
-        // v = gamma_j v / r_i - x_ij t_i / (width r_i^2), r_i^2 = sumsq_i / width + eps
-        const int esz = op.dtype == CODA_BF16 ? 2 : 4;
-        const float inv_w = 1.0f / float(width);
-        float g[8];
-        load_cols<PAIRED>(op.in2, op.dtype, col, width, g);
+        if constexpr (C::EXT) {
+          // v = gamma_j v / r_i - x_ij t_i / (width r_i^2), r_i^2 = sumsq_i / width + eps
+          const int esz = op.dtype == CODA_BF16 ? 2 : 4;
+          const float inv_w = 1.0f / float(width);
+          float g[8];
+          load_cols<PAIRED>(op.in2, op.dtype, col, width, g);
 #pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-          float x[8];
-          float rinv = 0.0f, coef = 0.0f;
-          if (ch.row[j] < M) {
-            load_cols<PAIRED>(static_cast<const char*>(op.in) + (long long)ch.row[j] * op.ld * esz, op.dtype, col,
-                              width, x);
-            const long long ro = (long long)ch.row[j] * op.row_ld;
-            const float r2 = op.row_ss[ro] * inv_w + op.scalar;
-            rinv = 1.0f / sqrtf(r2);
-            coef = op.row_s[ro] * inv_w / r2;
-          } else {
+          for (int j = 0; j < CPL; ++j) {
+            float x[8];
+            float rinv = 0.0f, coef = 0.0f;
+            if (ch.row[j] < M) {
+              load_cols<PAIRED>(static_cast<const char*>(op.in) + (long long)ch.row[j] * op.ld * esz, op.dtype, col,
+                                width, x);
+              const long long ro = (long long)ch.row[j] * op.row_ld;
+              const float r2 = op.row_ss[ro] * inv_w + op.scalar;
+              rinv = 1.0f / sqrtf(r2);
+              coef = op.row_s[ro] * inv_w / r2;
+            } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = 0.0f;
+              for (int e = 0; e < 8; ++e) x[e] = 0.0f;
+            }
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) ch.v[j][e] = g[e] * ch.v[j][e] * rinv - x[e] * coef;
           }
-#pragma unroll
-          for (int e = 0; e < EPC; ++e) ch.v[j][e] = g[e] * ch.v[j][e] * rinv - x[e] * coef;
         }
         break;
       }
       case CODA_OP_RMS_DGAMMA: {
-        // column sums of v * x / r_i, r_i^2 = sumsq_i / width + eps, reduced as COL_SUM
-        const int esz = op.dtype == CODA_BF16 ? 2 : 4;
-        const float inv_w = 1.0f / float(width);
-        float p[EPC];
+        if constexpr (C::EXT) {
+          // column sums of v * x / r_i, r_i^2 = sumsq_i / width + eps, reduced as COL_SUM
+          const int esz = op.dtype == CODA_BF16 ? 2 : 4;
+          const float inv_w = 1.0f / float(width);
+          float p[EPC];
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) p[e] = 0.0f;
+          for (int e = 0; e < EPC; ++e) p[e] = 0.0f;
 #pragma unroll
-        for (int j = 0; j < CPL; ++j)
-          if (ch.row[j] < M) {
-            float x[8];
-            load_cols<PAIRED>(static_cast<const char*>(op.in) + (long long)ch.row[j] * op.ld * esz, op.dtype, col,
-                              width, x);
-            const float rinv = 1.0f / sqrtf(op.row_ss[(long long)ch.row[j] * op.row_ld] * inv_w + op.scalar);
+          for (int j = 0; j < CPL; ++j)
+            if (ch.row[j] < M) {
+              float x[8];
+              load_cols<PAIRED>(static_cast<const char*>(op.in) + (long long)ch.row[j] * op.ld * esz, op.dtype, col,
+                                width, x);
+              const float rinv = 1.0f / sqrtf(op.row_ss[(long long)ch.row[j] * op.row_ld] * inv_w + op.scalar);
 #pragma unroll
-            for (int e = 0; e < EPC; ++e) p[e] += ch.v[j][e] * x[e] * rinv;
+              for (int e = 0; e < EPC; ++e) p[e] += ch.v[j][e] * x[e] * rinv;
+            }
+#pragma unroll
+          for (int off = C::CPR; off < 64; off <<= 1)
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) p[e] += __shfl_xor(p[e], off);
+          if (lane < C::CPR) {
+            const int tcol = wn * C::WTN + 8 * lane;
+            float* dst = colp + ((op.red_slot * C::WM + wm) * C::MI + mi) * C::BN + (PAIRED ? tcol / 2 : tcol);
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) dst[e] = p[e];
           }
-#pragma unroll
-        for (int off = C::CPR; off < 64; off <<= 1)
-#pragma unroll
-          for (int e = 0; e < EPC; ++e) p[e] += __shfl_xor(p[e], off);
-        if (lane < C::CPR) {
-          const int tcol = wn * C::WTN + 8 * lane;
-          float* dst = colp + ((op.red_slot * C::WM + wm) * C::MI + mi) * C::BN + (PAIRED ? tcol / 2 : tcol);
-#pragma unroll
-          for (int e = 0; e < EPC; ++e) dst[e] = p[e];
         }
         break;
       }
       case CODA_OP_COL_SUM:
       case CODA_OP_COL_SUMSQ: {
-        // the lane's rows, then the lanes that hold the same columns (lane %
-        // CPR): the wave's partial for its 32-row block, kept per block in LDS
-        const bool sq = kind == CODA_OP_COL_SUMSQ;
-        float p[EPC];
+        if constexpr (C::EXT) {
+          // the lane's rows, then the lanes that hold the same columns (lane %
+          // CPR): the wave's partial for its 32-row block, kept per block in LDS
+          const bool sq = kind == CODA_OP_COL_SUMSQ;
+          float p[EPC];
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) p[e] = 0.0f;
+          for (int e = 0; e < EPC; ++e) p[e] = 0.0f;
 #pragma unroll
-        for (int j = 0; j < CPL; ++j)
-          if (ch.row[j] < M) {
+          for (int j = 0; j < CPL; ++j)
+            if (ch.row[j] < M) {
 #pragma unroll
-            for (int e = 0; e < EPC; ++e) p[e] += sq ? ch.v[j][e] * ch.v[j][e] : ch.v[j][e];
+              for (int e = 0; e < EPC; ++e) p[e] += sq ? ch.v[j][e] * ch.v[j][e] : ch.v[j][e];
+            }
+#pragma unroll
+          for (int off = C::CPR; off < 64; off <<= 1)
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) p[e] += __shfl_xor(p[e], off);
+          if (lane < C::CPR) {
+            const int tcol = wn * C::WTN + 8 * lane;   // tile-local first column of the chunk
+            float* dst = colp + ((op.red_slot * C::WM + wm) * C::MI + mi) * C::BN + (PAIRED ? tcol / 2 : tcol);
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) dst[e] = p[e];
           }
-#pragma unroll
-        for (int off = C::CPR; off < 64; off <<= 1)
-#pragma unroll
-          for (int e = 0; e < EPC; ++e) p[e] += __shfl_xor(p[e], off);
-        if (lane < C::CPR) {
-          const int tcol = wn * C::WTN + 8 * lane;   // tile-local first column of the chunk
-          float* dst = colp + ((op.red_slot * C::WM + wm) * C::MI + mi) * C::BN + (PAIRED ? tcol / 2 : tcol);
-#pragma unroll
-          for (int e = 0; e < EPC; ++e) dst[e] = p[e];
         }
         break;
       }
@@ -503,6 +521,45 @@ __device__ __forceinline__ void store_chunks(const Chunks<C::CPL>& ch, KArgs a, 
         for (int e = 0; e < EPC; ++e)
           if (col + e < width) d[e] = ch.v[j][e];
       }
+    }
+  }
+}
+
+// D rounded to bf16 and packed, one 16-byte word group per chunk (4 words, or
+// 2 after SWIGLU_PAIR), for a store issued later
+template <class C, bool PAIRED>
+__device__ __forceinline__ void pack_chunks(const Chunks<C::CPL>& ch, u32x4_t (&dst)[C::CPL]) {
+#pragma unroll
+  for (int j = 0; j < C::CPL; ++j)
+#pragma unroll
+    for (int e = 0; e < (PAIRED ? 2 : 4); ++e) dst[j][e] = pack_bf16x2(ch.v[j][2 * e], ch.v[j][2 * e + 1]);
+}
+
+// the store of pack_chunks's words: rows m0 + mloc(j), first column col (of
+// the output's width)
+template <class C>
+__device__ __forceinline__ void store_packed(const u32x4_t (&w)[C::CPL], KArgs a, int M, int m0, int mloc0,
+                                             int col, bool paired) {
+  const int width = a->out_width;
+  const int n = paired ? 4 : 8;
+#pragma unroll
+  for (int j = 0; j < C::CPL; ++j) {
+    const int row = m0 + mloc0 + C::RSTEP * j;
+    if (row >= M) continue;
+    uint16_t* d = static_cast<uint16_t*>(a->D) + (long long)row * a->ldd + col;
+    if (col + n - 1 < width) {
+      if (paired) {
+        u32x2_t v;
+        v[0] = w[j][0];
+        v[1] = w[j][1];
+        *reinterpret_cast<u32x2_t*>(d) = v;
+      } else {
+        *reinterpret_cast<u32x4_t*>(d) = w[j];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (e < n && col + e < width) d[e] = uint16_t(w[j][e >> 1] >> (16 * (e & 1)));
     }
   }
 }
@@ -599,29 +656,49 @@ fused_kernel(FusedArgs args) {
     const int kn_slot = lane % C::KN_CPR;
 
     u32x4_t greg;   // RMS: the gamma chunk matching this lane's A chunks
+    const __amdgpu_buffer_rsrc_t rg_all = make_rsrc(C::RMS ? a->gamma : a->A, (long long)K * 2);
 
     // A (raw, into smem_raw, with RMS) or A (into the stage) plus B, all
     // straight to LDS; the swizzled block layout is the same for both A targets
+    // per-lane offsets of the direct loads within a K step (fixed for the
+    // whole loop; the step moves the resource base)
+    uint32_t a_off[C::A_BPW], b_off[C::B_BPW];
+#pragma unroll
+    for (int i = 0; i < C::A_BPW; ++i) {
+      const int q = wave + C::NW * i;
+      if constexpr (C::AKM) {
+        const int k = q * C::KM_RPB + lane / C::KM_CPR;
+        a_off[i] = uint32_t(k) * uint32_t(lda * 2) + uint32_t(((lane % C::KM_CPR) ^ (2 * (k & 3))) * 16);
+      } else {
+        a_off[i] = uint32_t(8 * q + kq_row) * uint32_t(lda * 2) + uint32_t(kq_chunk * 16);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < C::B_BPW; ++i) {
+      const int q = wave + C::NW * i;
+      if constexpr (C::BKN) {
+        const int k = q * C::KN_RPB + kn_row;
+        b_off[i] = uint32_t(k) * uint32_t(ldb * 2) + uint32_t((kn_slot ^ (2 * (k & 3))) * 16);
+      } else {
+        b_off[i] = uint32_t(8 * q + kq_row) * uint32_t(ldb * 2) + uint32_t(kq_chunk * 16);
+      }
+    }
     auto load_a = [&](int kt, char* dst) {
       const int k0 = (kt_lo + kt) * 64;
       if constexpr (C::AKM) {
         // K rows of BM contiguous M values, 16-byte chunk c of row k at slot
         // c ^ 2(k & 3) (rows past K read as zero); the same layout as an
         // N-major W tile
-        const int km_row = lane / C::KM_CPR, km_slot = lane % C::KM_CPR;
         const __amdgpu_buffer_rsrc_t ra =
-            make_rsrc(Abase + (long long)k0 * lda * 2, a_ext0 - (long long)k0 * lda * 2);
+            make_rsrc_nonneg(Abase + (long long)k0 * lda * 2, a_ext0 - (long long)k0 * lda * 2);
 #pragma unroll
         for (int i = 0; i < C::A_BPW; ++i) {
           const int q = wave + C::NW * i;
-          const int k = q * C::KM_RPB + km_row;
-          const int c = km_slot ^ (2 * (k & 3));
-          const uint32_t off = uint32_t(k) * uint32_t(lda * 2) + uint32_t(c * 16);
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (LdsPtr)(dst + q * 1024), 16, (int)off, 0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (LdsPtr)(dst + q * 1024), 16, (int)a_off[i], 0, 0, 0);
         }
         return;
       }
-      const __amdgpu_buffer_rsrc_t ra = make_rsrc(Abase + (long long)k0 * 2, a_ext0 - (long long)k0 * 2);
+      const __amdgpu_buffer_rsrc_t ra = make_rsrc_nonneg(Abase + (long long)k0 * 2, a_ext0 - (long long)k0 * 2);
       // chunks past K read as zero (an offset with the top bit set is out of
       // range); whole K steps take the wave-uniform first branch, so the
       // offsets carry no per-lane select (one compiled as a divergent branch
@@ -630,36 +707,28 @@ fused_kernel(FusedArgs args) {
 #pragma unroll
       for (int i = 0; i < C::A_BPW; ++i) {
         const int q = wave + C::NW * i;
-        const uint32_t off = (uint32_t(8 * q + kq_row) * uint32_t(lda * 2) + uint32_t(kq_chunk * 16)) | kmask;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (LdsPtr)(dst + q * 1024), 16, (int)off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (LdsPtr)(dst + q * 1024), 16, (int)(a_off[i] | kmask), 0, 0, 0);
       }
-      if constexpr (C::RMS) {
-        const __amdgpu_buffer_rsrc_t rg = make_rsrc(a->gamma, (long long)K * 2);
-        greg = buffer_load16(rg, uint32_t((k0 + 8 * kq_chunk) * 2));
-      }
+      if constexpr (C::RMS) greg = buffer_load16(rg_all, uint32_t((k0 + 8 * kq_chunk) * 2));
     };
     auto load_b = [&](int kt, char* As) {
       const int k0 = (kt_lo + kt) * 64;
       char* Bs = As + C::A_BYTES;
       if constexpr (C::BKN) {
         const __amdgpu_buffer_rsrc_t rb =
-            make_rsrc(Bbase + (long long)k0 * ldb * 2, b_ext0 - (long long)k0 * ldb * 2);
+            make_rsrc_nonneg(Bbase + (long long)k0 * ldb * 2, b_ext0 - (long long)k0 * ldb * 2);
 #pragma unroll
         for (int i = 0; i < C::B_BPW; ++i) {
           const int q = wave + C::NW * i;
-          const int k = q * C::KN_RPB + kn_row;
-          const int c = kn_slot ^ (2 * (k & 3));
-          const uint32_t off = uint32_t(k) * uint32_t(ldb * 2) + uint32_t(c * 16);
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (LdsPtr)(Bs + q * 1024), 16, (int)off, 0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (LdsPtr)(Bs + q * 1024), 16, (int)b_off[i], 0, 0, 0);
         }
       } else {
-        const __amdgpu_buffer_rsrc_t rb = make_rsrc(Bbase + (long long)k0 * 2, b_ext0 - (long long)k0 * 2);
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc_nonneg(Bbase + (long long)k0 * 2, b_ext0 - (long long)k0 * 2);
         const uint32_t kmask = (k0 + 64 <= K) ? 0u : ((k0 + 8 * kq_chunk < K) ? 0u : kOobOffset);
 #pragma unroll
         for (int i = 0; i < C::B_BPW; ++i) {
           const int q = wave + C::NW * i;
-          const uint32_t off = (uint32_t(8 * q + kq_row) * uint32_t(ldb * 2) + uint32_t(kq_chunk * 16)) | kmask;
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (LdsPtr)(Bs + q * 1024), 16, (int)off, 0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (LdsPtr)(Bs + q * 1024), 16, (int)(b_off[i] | kmask), 0, 0, 0);
         }
       }
     };
@@ -705,15 +774,14 @@ fused_kernel(FusedArgs args) {
     };
 
     // RMS: convert this wave's raw A blocks into the stage `As`: fp32 sum of
-    // squares of the raw values (scaled by `live`, 0 when there is nothing to
-    // convert), then bf16(x * gamma).  Each wave reads only the blocks its own
+    // squares of the raw values, then bf16(x * gamma).  Each wave reads only the blocks its own
     // direct loads wrote, so no barrier is needed between load and conversion.
     // LN: the values converted are x - s, s the mean of the row's first 64 values
     // (taken at the first conversion over the 8 lanes that hold the row; any
     // per-row constant leaves the norm unchanged, and one close to the row mean
     // keeps x - s, and so the bf16 rounding of the operand, small); chunks past K
     // (zeros) use s = 0 so that they add nothing to the sums.
-    auto convert_a = [&](char* As, float live, int k0, bool first) {
+    auto convert_a = [&](char* As, int k0, bool first) {
       const bool kin = k0 + 8 * kq_chunk < K;
 #pragma unroll
       for (int i = 0; i < C::A_BPW; ++i) {
@@ -733,18 +801,17 @@ fused_kernel(FusedArgs args) {
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
             const float lo = bf16_lo(x[w]) - s0, hv = bf16_hi(x[w]) - s0;
-            ss[i] = fmaf(lo * live, lo, ss[i]);
-            ss[i] = fmaf(hv * live, hv, ss[i]);
-            sx[i] += (lo + hv) * live;
+            ss[i] = fmaf(lo, lo, ss[i]);
+            ss[i] = fmaf(hv, hv, ss[i]);
+            sx[i] += lo + hv;
             x[w] = pack_bf16x2(lo * bf16_lo(greg[w]), hv * bf16_hi(greg[w]));
           }
         } else {
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
             const float lo = bf16_lo(x[w]), hv = bf16_hi(x[w]);
-            const float lo_l = lo * live, hv_l = hv * live;
-            ss[i] = fmaf(lo_l, lo, ss[i]);
-            ss[i] = fmaf(hv_l, hv, ss[i]);
+            ss[i] = fmaf(lo, lo, ss[i]);
+            ss[i] = fmaf(hv, hv, ss[i]);
             x[w] = pack_bf16x2(lo * bf16_lo(greg[w]), hv * bf16_hi(greg[w]));
           }
         }
@@ -916,7 +983,7 @@ fused_kernel(FusedArgs args) {
     const bool convert_first = wave >= C::NW / 2;
     auto convert_phase = [&](int kt, char* nxt) {
       wait_vm(kAfterA);                     // raw A(kt+1) and its gamma have landed
-      convert_a(nxt, 1.0f, (kt_lo + kt + 1) * 64, false);
+      convert_a(nxt, (kt_lo + kt + 1) * 64, false);
       if (kt + 2 < KT) {
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // raw reads done before reuse
         load_a(kt + 2, smem_raw);
@@ -954,7 +1021,7 @@ fused_kernel(FusedArgs args) {
         load_a(0, smem_raw);
         load_b(0, smem0);
         wait_vm(kAfterA);
-        convert_a(smem0, 1.0f, kt_lo * 64, true);
+        convert_a(smem0, kt_lo * 64, true);
         if (KT > 1) {
           asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
           load_a(1, smem_raw);
@@ -1335,6 +1402,31 @@ fused_kernel(FusedArgs args) {
   // LN: u[j] for the lane's 8 columns (the same in every block)
   float uv[8];
   if constexpr (C::LNE) load_cols<false>(a->ln_u, CODA_F32, n0 + wn * C::WTN + 8 * (lane % C::CPR), N, uv);
+  // The first column vector of the list (a bias, before any SWIGLU_PAIR): a
+  // lane's 8 columns are the same in every 32-row block, so it is loaded once
+  // here instead of once per block with its latency in each block's path.
+  int cv_op = -1;
+  for (int q = 0; q < a->n_ops; ++q) {
+    const int k = a->ops[q].kind;
+    if (k == CODA_OP_SWIGLU_PAIR) break;
+    if (k == CODA_OP_ADD_COL || k == CODA_OP_SCALE_COL) {
+      cv_op = q;
+      break;
+    }
+  }
+  float cv[8];
+  if (cv_op >= 0) {
+    KOp op = a->ops[cv_op];
+    load_cols<false>(op.in, op.dtype, n0 + wn * C::WTN + 8 * (lane % C::CPR), op.width, cv);
+  }
+  // With reductions across the workgroups of a tile row or column, the D
+  // stores wait until the partial sums are published: the publishing waits for
+  // every store this workgroup issued, and the tile's D stores (128 KB) would
+  // otherwise hold the CU until they drain to memory.
+  const bool defer = a->d_dtype == CODA_BF16 &&
+                     ((a->n_red > 0 && a->grid_n > 1) || (C::EXT && a->n_colred > 0 && a->grid_m > 1));
+  u32x4_t dpk[MI][C::CPL];
+  bool paired_out = false;
 
   static_for<0, MI>([&](auto mic) {
     constexpr int mi = decltype(mic)::value;
@@ -1383,13 +1475,16 @@ fused_kernel(FusedArgs args) {
       }
     }
     __builtin_amdgcn_wave_barrier();
-    const int o = run_ops<C, false>(ch, a, 0, M, lane, wn, red, pf_op, pf_buf[mi & 1], colp, wm, mi);
+    const int o = run_ops<C, false>(ch, a, 0, M, lane, wn, red, pf_op, pf_buf[mi & 1], colp, wm, mi, cv_op, cv);
     if (o < a->n_ops) {   // SWIGLU_PAIR
       swiglu_chunks<C>(ch);
-      run_ops<C, true>(ch, a, o + 1, M, lane, wn, red, -1, pf_buf[mi & 1], colp, wm, mi);
-      store_chunks<C, true>(ch, a, M);
+      run_ops<C, true>(ch, a, o + 1, M, lane, wn, red, -1, pf_buf[mi & 1], colp, wm, mi, -1, cv);
+      paired_out = true;
+      if (defer) pack_chunks<C, true>(ch, dpk[mi]);
+      else store_chunks<C, true>(ch, a, M);
     } else {
-      store_chunks<C, false>(ch, a, M);
+      if (defer) pack_chunks<C, false>(ch, dpk[mi]);
+      else store_chunks<C, false>(ch, a, M);
     }
   });
 
@@ -1453,7 +1548,7 @@ fused_kernel(FusedArgs args) {
   // fixed order), then across the tile rows of the grid through the workspace,
   // finished in tile order by the last workgroup of the tile column, as for
   // the row reductions.
-  if (a->n_colred > 0) {
+  if (C::EXT && a->n_colred > 0) {
     __syncthreads();
     const bool multi = a->grid_m > 1;
     for (int q = 0; q < a->n_ops; ++q) {
@@ -1513,6 +1608,16 @@ fused_kernel(FusedArgs args) {
       }
     }
   }
+
+  if (defer) {
+    const int c = lane % C::CPR;
+    const int col0 = n0 + wn * C::WTN + 8 * c;
+    static_for<0, MI>([&](auto mic) {
+      constexpr int mi = decltype(mic)::value;
+      store_packed<C>(dpk[mi], a, M, m0, wm * C::WTM + 32 * mi + lane / C::CPR, paired_out ? col0 >> 1 : col0,
+                      paired_out);
+    });
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1525,36 +1630,45 @@ int launch_cfg(const FusedArgs& args, int64_t nwg, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? CODA_OK : CODA_ERR_HIP;
 }
 
+// The backward set's ops (EXT) are compiled into the kernels without a row
+// norm only: a list with a row norm and one of those ops is rejected on the
+// host (no workload pairs them), which keeps the norm kernels' registers to
+// what their own ops need.
 template <int BM, int BN, int WM, int WN, bool F32, bool BKN>
-int launch_norms(const FusedArgs& args, int64_t nwg, int norm, hipStream_t s) {
+int launch_norms(const FusedArgs& args, int64_t nwg, int norm, bool ext, hipStream_t s) {
   switch (norm) {
-    case kNormRms: return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormRms>>(args, nwg, s);
-    case kNormLn: return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormLn>>(args, nwg, s);
-    case kNormRmsB: return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormRmsB>>(args, nwg, s);
-    case kNormRmsGiven: return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormRmsGiven>>(args, nwg, s);
-    case kNormLnB: return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormLnB>>(args, nwg, s);
-    case kNormLnGiven: return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormLnGiven>>(args, nwg, s);
-    default: return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormNone>>(args, nwg, s);
+    case kNormRms: return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormRms, false, false>>(args, nwg, s);
+    case kNormLn: return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormLn, false, false>>(args, nwg, s);
+    case kNormRmsB: return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormRmsB, false, false>>(args, nwg, s);
+    case kNormRmsGiven: return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormRmsGiven, false, false>>(args, nwg, s);
+    case kNormLnB: return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormLnB, false, false>>(args, nwg, s);
+    case kNormLnGiven: return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormLnGiven, false, false>>(args, nwg, s);
+    default:
+      return ext ? launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormNone, false, true>>(args, nwg, s)
+                 : launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormNone, false, false>>(args, nwg, s);
   }
 }
 
 template <int BM, int BN, int WM, int WN, bool F32>
-int launch_variants(const FusedArgs& args, int64_t nwg, bool bkn, int norm, bool akm, hipStream_t s) {
+int launch_variants(const FusedArgs& args, int64_t nwg, bool bkn, int norm, bool akm, bool ext, hipStream_t s) {
   if constexpr (!F32) {
     if (akm) {   // A stored [K x M]: no row norm (validated on the host)
-      return bkn ? launch_cfg<Cfg<BM, BN, WM, WN, F32, true, kNormNone, true>>(args, nwg, s)
-                 : launch_cfg<Cfg<BM, BN, WM, WN, F32, false, kNormNone, true>>(args, nwg, s);
+      if (ext)
+        return bkn ? launch_cfg<Cfg<BM, BN, WM, WN, F32, true, kNormNone, true, true>>(args, nwg, s)
+                   : launch_cfg<Cfg<BM, BN, WM, WN, F32, false, kNormNone, true, true>>(args, nwg, s);
+      return bkn ? launch_cfg<Cfg<BM, BN, WM, WN, F32, true, kNormNone, true, false>>(args, nwg, s)
+                 : launch_cfg<Cfg<BM, BN, WM, WN, F32, false, kNormNone, true, false>>(args, nwg, s);
     }
   }
-  return bkn ? launch_norms<BM, BN, WM, WN, F32, true>(args, nwg, norm, s)
-             : launch_norms<BM, BN, WM, WN, F32, false>(args, nwg, norm, s);
+  return bkn ? launch_norms<BM, BN, WM, WN, F32, true>(args, nwg, norm, ext, s)
+             : launch_norms<BM, BN, WM, WN, F32, false>(args, nwg, norm, ext, s);
 }
 
 // one function per compiled tile configuration (defined in coda_fused_t*.hip)
-int launch_tile1(const FusedArgs& a, int64_t nwg, bool bkn, int norm, bool akm, hipStream_t s);
-int launch_tile2(const FusedArgs& a, int64_t nwg, bool bkn, int norm, bool akm, hipStream_t s);
-int launch_tile3(const FusedArgs& a, int64_t nwg, bool bkn, int norm, bool akm, hipStream_t s);
-int launch_tile_f32(const FusedArgs& a, int64_t nwg, bool bkn, int norm, bool akm, hipStream_t s);
+int launch_tile1(const FusedArgs& a, int64_t nwg, bool bkn, int norm, bool akm, bool ext, hipStream_t s);
+int launch_tile2(const FusedArgs& a, int64_t nwg, bool bkn, int norm, bool akm, bool ext, hipStream_t s);
+int launch_tile3(const FusedArgs& a, int64_t nwg, bool bkn, int norm, bool akm, bool ext, hipStream_t s);
+int launch_tile_f32(const FusedArgs& a, int64_t nwg, bool bkn, int norm, bool akm, bool ext, hipStream_t s);
 
 }  // namespace dev
 }  // namespace coda

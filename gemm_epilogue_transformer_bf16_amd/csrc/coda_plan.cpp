@@ -89,9 +89,26 @@ bool strided_overlap(const Strided& a, const Strided& b) {
 // times as many workgroups (two resident per CU).
 }  // namespace
 
-int choose_tile(int64_t M, int64_t N) {
-  const int64_t big = ((M + 255) / 256) * ((N + 255) / 256);
-  return big >= kNumCUs ? 3 : 2;
+namespace {
+// share of the compute units busy over the rounds of a grid of t tiles, one
+// workgroup per CU
+double round_fill(int64_t t) {
+  const int64_t rounds = (t + kNumCUs - 1) / kNumCUs;
+  return double(t) / double(rounds * kNumCUs);
+}
+}  // namespace
+
+int choose_tile(int64_t M, int64_t N, int64_t K, bool split_allowed) {
+  const int64_t t3 = ((M + 255) / 256) * ((N + 255) / 256);   // 256 x 256 tiles
+  const int64_t t1 = ((M + 255) / 256) * ((N + 127) / 128);   // 256 x 128 tiles
+  if (t1 < kNumCUs) return 2;   // not one round even of 256 x 128: 128 x 128, two per CU
+  if (t3 < kNumCUs) return 1;
+  // the 256 x 256 tile's main loop is the faster one (fewer operand bytes per
+  // flop through LDS); the 256 x 128 tile wins where it fills the rounds
+  // better.  A last round that the split over K can fill counts as full.
+  const bool splittable = split_allowed && (K + 63) / 64 >= 2 * kMinSplitSteps;
+  const double fill3 = splittable ? 1.0 : round_fill(t3);
+  return fill3 >= kTile1Speed * round_fill(t1) ? 3 : 1;
 }
 
 namespace {
@@ -499,6 +516,14 @@ int build_plan_split(const void* A, const void* B, int64_t M, int64_t N, int64_t
   p->n_red = n_red;
   p->n_colred = n_col;
   p->out_width = width;
+  for (int i = 0; i < p->n_ops; ++i) {
+    const int k = p->ops[i].kind;
+    if (is_col_reduction(k) || k == CODA_OP_ROW_DOT || k == CODA_OP_RMS_BWD) p->has_ext = true;
+  }
+  if (p->has_norm && p->has_ext) {
+    set_error("column reductions, ROW_DOT, RMS_BWD and RMS_DGAMMA cannot follow RMS_ROWSCALE / LN_ROWSCALE");
+    return CODA_ERR_UNSUPPORTED;
+  }
 
   // ---- shapes, leading dimensions, alignment ----
   const bool empty = (M == 0 || N == 0);
@@ -551,7 +576,7 @@ int build_plan_split(const void* A, const void* B, int64_t M, int64_t N, int64_t
     p->tile = 0;
     p->cfg = kF32Tile;
   } else {
-    p->tile = d->tile ? d->tile : choose_tile(M, N);
+    p->tile = d->tile ? d->tile : choose_tile(M, N, K, !(d->flags & CODA_FLAG_NO_SPLIT_K));
     p->cfg = kTileCfgs[p->tile - 1];
   }
   p->grid_m = (M + p->cfg.bm - 1) / p->cfg.bm;
@@ -824,7 +849,7 @@ int coda_selected_tile(int64_t M, int64_t N, int64_t K, const coda_epi_desc* des
   const int st = coda::build_plan(nullptr, nullptr, M, N, K, desc, 0, false, &p);
   if (st != CODA_OK) return st;
   if (desc->ab_dtype == CODA_F32) return 0;
-  return desc->tile ? desc->tile : coda::choose_tile(M, N);
+  return desc->tile ? desc->tile : coda::choose_tile(M, N, K, !(desc->flags & CODA_FLAG_NO_SPLIT_K));
 }
 
 int coda_tile_config(int index, int* bm, int* bn, int* bk, int* waves) {

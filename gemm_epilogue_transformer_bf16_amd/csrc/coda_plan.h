@@ -18,7 +18,7 @@ struct TileCfg {
 };
 
 constexpr TileCfg kTileCfgs[] = {
-    {256, 128, 64, 2, 2, 1},   // 1: 4 waves, 128x64 per wave
+    {256, 128, 64, 4, 2, 1},   // 1: 8 waves, 64x64 per wave
     {128, 128, 64, 2, 2, 2},   // 2: 4 waves, 64x64 per wave
     {256, 256, 64, 2, 4, 1},   // 3: 8 waves, 128x64 per wave
 };
@@ -31,6 +31,8 @@ constexpr TileCfg kF32Tile = {64, 64, 32, 2, 2, 4};
 // (on another device the result is the same, only the balance differs).
 constexpr int kNumCUs = 256;
 constexpr int kMaxSplit = 4;
+// main-loop rate of the 256 x 128 tile relative to the 256 x 256 one, per CU
+constexpr double kTile1Speed = 0.95;
 // Fewest K steps per part: the parts exchange fp32 partial tiles through
 // memory, which costs about as much as 8 - 16 K steps of the main loop.
 constexpr int kMinSplitSteps = 16;
@@ -74,6 +76,7 @@ struct Plan {
   int n_red;
   int n_colred;              // column reductions
   bool has_swiglu;
+  bool has_ext;              // a backward-set op: column reduction, ROW_DOT, RMS_BWD or RMS_DGAMMA
   int tile;                  // 1-based bf16 tile config; 0 for the fp32 path
   TileCfg cfg;
   int64_t grid_m, grid_n;
@@ -139,7 +142,7 @@ int validate_fold_gain(const void* B, int64_t K, int64_t N, int64_t ldb, int32_t
                        const void* gamma, const void* B_out, int64_t ldo);
 
 // Automatic bf16 tile configuration (1-based) for an M x N output.
-int choose_tile(int64_t M, int64_t N);
+int choose_tile(int64_t M, int64_t N, int64_t K, bool split_allowed);
 
 void set_error(const char* fmt, ...);
 void clear_error();

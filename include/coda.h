@@ -163,7 +163,11 @@ typedef enum {
      layer is the column sum of its output gradient).  Each writes an fp32 value
      per column j < width to ((float*)out)[j*out_stride]: the sum over all M
      rows of the running value (COL_SUM) or of its square (COL_SUMSQ) at the
-     op's position.  At most CODA_MAX_COL_REDUCTIONS per list. */
+     op's position.  At most CODA_MAX_COL_REDUCTIONS per list.  The backward
+     set (COL_SUM, COL_SUMSQ, ROW_DOT, RMS_BWD, RMS_DGAMMA) does not share a
+     list with RMS_ROWSCALE or LN_ROWSCALE: such a list is
+     CODA_ERR_UNSUPPORTED (the kernels with a deferred row norm are built
+     without the backward set's code). */
   CODA_OP_COL_SUM = 15,
   CODA_OP_COL_SUMSQ = 16,
   /* the RMS norm's backward (gradients are among the operators the d9bl.com
@@ -189,8 +193,8 @@ typedef enum {
      row_sumsq[i*row_ld] = sum_k x[i,k]^2 (fp32), scalar = eps.  Placed before
      RMS_BWD in the same list, it reads the same x and row statistics. */
   CODA_OP_RMS_DGAMMA = 19,
-  /* dropout (the d9bl.com page, section 3.2: the EPILOGUE example's
-     `output = dropout(output, 0.1)`): element (i, j) of the running value is
+  /* dropout (the d9bl.com page, section 3.2: the dropout step of its
+     EPILOGUE example): element (i, j) of the running value is
      kept with probability 1 - p and scaled by 1 / (1 - p), or set to 0; p is
      `scalar`, 0 <= p < 1.  The mask comes from the counter-based generator
      Philox-4x64-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers:

@@ -38,8 +38,8 @@ Readings of points the pages leave open (each also listed in the design notes):
     the current width (half the GEMM width after swiglu_pair).
   * The RMS norm's backward (rmsnorm_backward, the rms_bwd op) is the
     chain-rule gradient of that same forward form.
-  * Dropout (the statement ``output = dropout(output, 0.1)`` of the d9bl.com
-    page's section 3.2 example) zeroes an element with probability p and scales
+  * Dropout (the dropout step of the d9bl.com page's section 3.2 EPILOGUE
+    example) zeroes an element with probability p and scales
     the kept ones by 1 / (1 - p) (inverted dropout, so the expectation is
     unchanged).  The pages name no generator; the mask here is drawn from the
     counter-based Philox-4x64-10 (Salmon, Moraes, Dror and Shaw, "Parallel

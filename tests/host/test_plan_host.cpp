@@ -190,10 +190,24 @@ int main() {
     EXPECT(coda_tile_config(1, &bm, &bn, &bk, &w) == CODA_OK && bm > 0 && bn > 0 && bk > 0 && w > 0);
     EXPECT(coda_tile_config(0, &bm, &bn, &bk, &w) == CODA_ERR_INVALID_ARG);
   }
-  {  // selected tile: explicit, automatic (large grid -> 256 x 256 / 8 waves), fp32
-    coda_epi_desc e = base_desc(22016, 4096);
+  {  // selected tile: explicit, automatic (by how well the grid fills rounds of 256 CUs), fp32
+    coda_epi_desc e = base_desc(22016, 4096); e.flags = 0;
     EXPECT(coda_selected_tile(4096, 22016, 4096, &e) == 3);
     EXPECT(coda_selected_tile(300, 520, 200, &d) == 2);
+    // 256 x 128 where it fills whole rounds and 256 x 256 does not:
+    // 32 x 24 = 768 tiles (3 rounds) against 384 (1.5 rounds, 12 K steps: no split)
+    EXPECT(coda_selected_tile(8192, 3072, 768, &e) == 1);
+    // 32 x 8 = 256 tiles (1 round) against 128
+    EXPECT(coda_selected_tile(8192, 1024, 4096, &e) == 1);
+    // 32 x 16 = 512 tiles of 256 x 256 fill two rounds
+    EXPECT(coda_selected_tile(8192, 4096, 1024, &e) == 3);
+    // 5.4 rounds of 256 x 256, the last one split over K (64 K steps)
+    EXPECT(coda_selected_tile(4096, 22016, 4096, &e) == 3);
+    // the same grid with 12 K steps, or without the split: the 256 x 128 grid
+    // (10.75 rounds) fills better
+    EXPECT(coda_selected_tile(4096, 22016, 768, &e) == 1);
+    coda_epi_desc ns = e; ns.flags = CODA_FLAG_NO_SPLIT_K;
+    EXPECT(coda_selected_tile(4096, 22016, 4096, &ns) == 1);
     e.tile = 2;
     EXPECT(coda_selected_tile(4096, 22016, 4096, &e) == 2);
     e.ab_dtype = CODA_F32; e.tile = 0;
@@ -292,6 +306,17 @@ int main() {
     EXPECT(coda_workspace_size(100, N, K, &e, 0) == 0);
     // the unfused sequence keeps column partials per chunk of rows
     EXPECT(coda_workspace_size(M, N, K, &e, 1) > coda_workspace_size(M, N, K, &d, 1));
+  }
+  {  // the backward set does not follow a deferred row norm (fused and unfused)
+    coda_epi_desc e = base_desc(N, K);
+    e.n_ops = 2;
+    e.ops[0].kind = CODA_OP_RMS_ROWSCALE; e.ops[0].in = P(0x40000000); e.ops[0].in_dtype = CODA_BF16;
+    e.ops[1].kind = CODA_OP_COL_SUM; e.ops[1].out = Pm(0x50000000); e.ops[1].out_stride = 1;
+    e.workspace = Pm(0x70000000); e.workspace_bytes = size_t(1) << 30;
+    EXPECT(coda_validate(A, B, M, N, K, &e, 0) == CODA_ERR_UNSUPPORTED);
+    EXPECT(coda_validate(A, B, M, N, K, &e, 1) == CODA_ERR_UNSUPPORTED);
+    e.ops[1].kind = CODA_OP_ROW_SUM;   // a row reduction is not in the backward set
+    EXPECT(coda_validate(A, B, M, N, K, &e, 0) == CODA_OK);
   }
   {  // the RMS norm's backward: ROW_DOT is a row reduction with a matrix; RMS_BWD needs x, gamma and two row vectors
     coda_epi_desc e = base_desc(N, K);
