@@ -387,19 +387,19 @@ def main():
                          "the other placement is timed beside it either way")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unfused", action="store_true")
+    ap.add_argument("--all", action="store_true",
+                    help="every synthetic layer in turn: one line with each layer's fused, unfused and plain-GEMM "
+                         "medians, speedups beside the ceilings, and their geometric mean")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain 256 MiB device copy three times (reference for traffic counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
-              "the fused GEMM + epilogue path is single-GPU in this build.", file=sys.stderr)
+              "the fused GEMM + epilogue path runs on one GPU.", file=sys.stderr)
         sys.exit(2)
 
     import torch
-    import workloads as w
-    from gemm_epilogue_transformer_bf16_amd import coda, runner
-    TORCH_DT_OF = runner.TORCH_DT
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -411,10 +411,26 @@ def main():
         bench_weight_grad(args)
         return
 
-    spec = w.get_config(args.workload)
+    if args.all:
+        bench_all(args)
+        return
+    line = measure_workload(args, args.workload)
+    print(json.dumps(line), flush=True)
+
+
+def measure_workload(args, workload: int, cpu_baseline_on: bool = True):
+    """Times one synthetic layer (fused, the unfused sequence, the plain GEMM
+    with an empty list and, for norm layers, the other gain placement,
+    round-robin) and returns the JSON line as a dict."""
+    import torch
+    import workloads as w
+    from gemm_epilogue_transformer_bf16_amd import coda, runner
+    TORCH_DT_OF = runner.TORCH_DT
+
+    spec = w.get_config(workload)
     if args.bias_grad:
         import dataclasses
-        if args.workload != 5:
+        if workload != 5:
             print("--bias-grad applies to the backward layer (--workload 5)", file=sys.stderr)
             sys.exit(2)
         spec = dataclasses.replace(spec, program=spec.program + (("col_sum", {"out": "db", "col": 0}),),
@@ -425,13 +441,14 @@ def main():
     has_norm = has_rms or any(op == "ln_rowscale" for op, _ in spec.program)
     fold = has_norm and (args.fold_gain or args.given_row_sumsq)
     call = runner.WorkloadCall(spec, inputs, tile=args.tile, fold_gain=fold)
+    tensors = call.tensors
     if args.given_row_sumsq:
         if not has_norm:
             print("--given-row-sumsq applies to layers with an RMSNorm or LayerNorm", file=sys.stderr)
             sys.exit(2)
         # setup outside the timed region: the row sums and sums of squares a
         # previous layer's ROW_SUM / ROW_SUMSQ epilogue would have written
-        A = call.tensors[spec.a_name]
+        A = tensors[spec.a_name]
         row_stats = torch.stack([A.float().sum(dim=1), (A.float() * A.float()).sum(dim=1)], dim=1).contiguous()
         prog = [(n, dict(a)) for n, a in call.ops]
         prog[0][1].update({"row_ss": row_stats, "row_ss_col": 1, "row_s_col": 0})
@@ -447,13 +464,18 @@ def main():
     tile_used = coda.coda_selected_tile(spec.M, spec.N, spec.K, call.desc)
 
     fns = {"fused": call.fused}
+    other = plain = None
     if not args.no_unfused:
         fns["unfused"] = call.unfused
-    other = None
-    if has_norm and not args.given_row_sumsq and not args.no_unfused:
-        # the other placement of the norm's gain, for comparison (not the headline)
-        other = runner.WorkloadCall(spec, inputs, tile=args.tile, fold_gain=not fold)
-        fns["other"] = other.fused
+        # the same main loop with an empty list: the fused kernel's time if its
+        # epilogue were free, so unfused / plain is the most fusion can gain here
+        plain = runner.Call(tensors[spec.a_name], tensors[spec.b_name], [], spec.b_layout,
+                            d_dtype=TORCH_DT_OF[spec.d_dtype], tile=args.tile, M=spec.M, N=spec.N, K=spec.K)
+        fns["plain"] = plain.fused
+        if has_norm and not args.given_row_sumsq:
+            # the other placement of the norm's gain, for comparison (not the headline)
+            other = runner.WorkloadCall(spec, inputs, tile=args.tile, fold_gain=not fold)
+            fns["other"] = other.fused
     timer = Timer(args)
     print(f"[bench] {', '.join(fns)}: warm-up >= {args.warmup} rounds and {args.warmup_seconds} s, "
           f"then {args.steps} timed rounds", file=sys.stderr, flush=True)
@@ -463,19 +485,19 @@ def main():
     peak = PEAK_F32_TFLOPS if spec.ab_dtype == "f32" else PEAK_BF16_TFLOPS
     alg_bytes = algorithmic_bytes(spec)
     khash = kernel_source_hash()
-    key = WORKLOAD_KEY[args.workload]
+    key = WORKLOAD_KEY[workload]
     plain_variant = not (args.bias_grad or args.given_row_sumsq or args.fold_gain or args.tile or args.no_flush)
     traffic = load_traffic(key, khash) if plain_variant else None
     counter_clock = load_counter_clock(key, khash) if plain_variant else None
     mfma_busy = load_counter_field(key, khash, "mfma_busy_pct") if plain_variant else None
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if cpu_baseline_on and not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         cpu = cpu_baseline(spec, inputs)
 
     config = {
-        "workload": WORKLOAD_TEXT[args.workload] + (" + bias gradient (column sum of dH)" if args.bias_grad else ""),
+        "workload": WORKLOAD_TEXT[workload] + (" + bias gradient (column sum of dH)" if args.bias_grad else ""),
         "M": spec.M, "N": spec.N, "K": spec.K,
         "gain": ("folded into a copy of the weights" if fold else "applied to A in the main loop")
                 if has_norm else None,
@@ -485,11 +507,55 @@ def main():
     # MFMA pipe busy share of the SIMD-cycles in the committed counter run of
     # the same sources (the headline kernel alone, counters serialise dispatches)
     extra = {"mfma_busy_pct_counters": mfma_busy}
+    if plain is not None:
+        pmed, fmed, umed = (float(np.median(t[k])) for k in ("plain", "fused", "unfused"))
+        extra["plain_gemm_ms"] = stats(t["plain"])
+        extra["fused_over_plain"] = round(fmed / pmed, 3)
+        extra["unfused_over_plain"] = round(umed / pmed, 3)
     if other is not None:
         extra[("fused_in_loop_gain_ms" if fold else "fused_folded_gain_ms")] = stats(t["other"])
-    line = result_line(args, timer, flops, t["fused"], t.get("unfused"), config, peak, alg_bytes, cpu,
+    return result_line(args, timer, flops, t["fused"], t.get("unfused"), config, peak, alg_bytes, cpu,
                        traffic=traffic, counter_clock=counter_clock, extra=extra)
-    print(json.dumps(line), flush=True)
+
+
+# the per-layer speedup ceilings of fusion for the same main loop, computed from
+# the unfused sequence's extra HBM passes (at 8 and at 5 TB/s) over the GEMM at
+# 70% of the bf16 dense peak
+CEILING = {2: (2.29, 3.06), 3: (1.27, 1.43), 4: (1.13, 1.20), 5: (1.65, 2.03)}
+
+
+def bench_all(args):
+    """Every synthetic layer in turn (fused, unfused, plain GEMM), one JSON
+    line: each layer's medians and speedup beside the ceilings, and the
+    geometric mean of the speedups over the bf16 layers."""
+    if args.no_unfused:
+        print("--all compares fused and unfused: drop --no-unfused", file=sys.stderr)
+        sys.exit(2)
+    rows = []
+    for wl in sorted(WORKLOAD_TEXT):
+        line = measure_workload(args, wl, cpu_baseline_on=False)
+        rows.append({
+            "workload": WORKLOAD_KEY[wl], "tile": line["config"]["tile"],
+            "fused_ms": line["fused_ms"]["median"], "unfused_ms": line["unfused_ms"]["median"],
+            "plain_gemm_ms": line["plain_gemm_ms"]["median"], "speedup_vs_unfused": line["speedup_vs_unfused"],
+            "unfused_over_plain": line["unfused_over_plain"], "fused_over_plain": line["fused_over_plain"],
+            "tflops": line["value"], "pct_peak": line["pct_peak"],
+            "ceiling_at_8_and_5_TBps": CEILING.get(wl),
+            "fused_p10_p90": [line["fused_ms"]["p10"], line["fused_ms"]["p90"]],
+        })
+        print(f"[bench] {WORKLOAD_KEY[wl]}: fused {rows[-1]['fused_ms']} ms, unfused {rows[-1]['unfused_ms']} ms, "
+              f"plain {rows[-1]['plain_gemm_ms']} ms", file=sys.stderr, flush=True)
+    bf = [r["speedup_vs_unfused"] for r in rows if r["workload"] != WORKLOAD_KEY[1]]
+    geo = float(np.exp(np.mean(np.log(bf))))
+    out = {
+        "metric": "fused vs unfused speedup, geometric mean over the bf16 synthetic layers",
+        "value": round(geo, 3), "unit": "x", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "higher_is_better": True, "data": "synthetic", "per_workload": rows,
+        "geomean_unfused_over_plain": round(float(np.exp(np.mean(np.log(
+            [r["unfused_over_plain"] for r in rows if r["workload"] != WORKLOAD_KEY[1]])))), 3),
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":

@@ -225,6 +225,46 @@ __device__ __forceinline__ void load_cols(const void* p, int dtype, long long co
   }
 }
 
+// ---------------------------------------------------------------------------
+// Lane reductions with DPP row moves (inside the VALU) where the partner lane
+// is in the same row of 16, LDS permutes across rows.  The additions pair the
+// lanes as the xor butterfly over the same offsets does, so the sums are the
+// same bit for bit.  (gfx950's permlane16/32 swaps would serve across rows,
+// but the compiler's builtin returns the first half of the swap for both of
+// its results, checked on the GPU, so they are not used.)
+// ---------------------------------------------------------------------------
+template <int ctrl>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), ctrl, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]: lane i <- lane i ^ 1
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]: lane i <- lane i ^ 2
+constexpr int kDppHalfMirror = 0x141; // lane i of 8 <- lane 7 - i
+constexpr int kDppMirror = 0x140;     // lane i of 16 <- lane 15 - i
+constexpr int kDppRor8 = 0x128;       // lane i of 16 <- lane (i + 8) % 16 = lane i ^ 8
+
+// sum over each group of n consecutive lanes (n = 4, 8 or 16), in every lane;
+// after the quad sums, the mirrors bring the other half's (equal) sums
+template <int n>
+__device__ __forceinline__ float group_sum(float p) {
+  static_assert(n == 4 || n == 8 || n == 16, "group of 4, 8 or 16 lanes");
+  p += dpp<kDppXor1>(p);
+  p += dpp<kDppXor2>(p);
+  if constexpr (n >= 8) p += dpp<kDppHalfMirror>(p);
+  if constexpr (n >= 16) p += dpp<kDppMirror>(p);
+  return p;
+}
+
+// sum over the lanes l with the same l % n (n = 4, 8 or 16), in every lane
+template <int n>
+__device__ __forceinline__ float stride_sum(float p) {
+  static_assert(n == 4 || n == 8 || n == 16, "stride of 4, 8 or 16 lanes");
+  if constexpr (n == 4) p += __shfl_xor(p, 4);
+  if constexpr (n <= 8) p += dpp<kDppRor8>(p);
+  p += __shfl_xor(p, 16);
+  return p + __shfl_xor(p, 32);
+}
+
 __device__ __forceinline__ bool is_row_reduction(int kind) {
   return (kind >= CODA_OP_ROW_SUM && kind <= CODA_OP_ROW_MEAN) || kind == CODA_OP_ROW_DOT;
 }
@@ -346,8 +386,7 @@ __device__ __forceinline__ int run_ops(Chunks<C::CPL>& ch, KArgs a, int o, int M
             p += (col + e < width) ? (sq ? x * x : x) : 0.0f;
           }
           // the CPR lanes of a row are consecutive
-#pragma unroll
-          for (int off = 1; off < C::CPR; off <<= 1) p += __shfl_xor(p, off);
+          p = group_sum<C::CPR>(p);
           if ((lane & (C::CPR - 1)) == 0) dst[ch.mloc[j]] = p;
         }
         break;
@@ -370,8 +409,7 @@ __device__ __forceinline__ int run_ops(Chunks<C::CPL>& ch, KArgs a, int o, int M
             float p = 0.0f;
 #pragma unroll
             for (int e = 0; e < EPC; ++e) p += (col + e < width) ? ch.v[j][e] * x[e] : 0.0f;
-#pragma unroll
-            for (int off = 1; off < C::CPR; off <<= 1) p += __shfl_xor(p, off);
+            p = group_sum<C::CPR>(p);
             if ((lane & (C::CPR - 1)) == 0) dst[ch.mloc[j]] = p;
           }
         }
@@ -424,9 +462,7 @@ __device__ __forceinline__ int run_ops(Chunks<C::CPL>& ch, KArgs a, int o, int M
               for (int e = 0; e < EPC; ++e) p[e] += ch.v[j][e] * x[e] * rinv;
             }
 #pragma unroll
-          for (int off = C::CPR; off < 64; off <<= 1)
-#pragma unroll
-            for (int e = 0; e < EPC; ++e) p[e] += __shfl_xor(p[e], off);
+          for (int e = 0; e < EPC; ++e) p[e] = stride_sum<C::CPR>(p[e]);
           if (lane < C::CPR) {
             const int tcol = wn * C::WTN + 8 * lane;
             float* dst = colp + ((op.red_slot * C::WM + wm) * C::MI + mi) * C::BN + (PAIRED ? tcol / 2 : tcol);
@@ -452,9 +488,7 @@ __device__ __forceinline__ int run_ops(Chunks<C::CPL>& ch, KArgs a, int o, int M
               for (int e = 0; e < EPC; ++e) p[e] += sq ? ch.v[j][e] * ch.v[j][e] : ch.v[j][e];
             }
 #pragma unroll
-          for (int off = C::CPR; off < 64; off <<= 1)
-#pragma unroll
-            for (int e = 0; e < EPC; ++e) p[e] += __shfl_xor(p[e], off);
+          for (int e = 0; e < EPC; ++e) p[e] = stride_sum<C::CPR>(p[e]);
           if (lane < C::CPR) {
             const int tcol = wn * C::WTN + 8 * lane;   // tile-local first column of the chunk
             float* dst = colp + ((op.red_slot * C::WM + wm) * C::MI + mi) * C::BN + (PAIRED ? tcol / 2 : tcol);
@@ -1514,6 +1548,13 @@ fused_kernel(FusedArgs args) {
       // The partial sums went out as agent-scope atomic stores, which are
       // coherent across the XCDs' L2s.  Waiting for their completion before the
       // counter increment publishes them without a device-wide L2 write-back.
+      // This is an ISA-level argument, outside the language memory model
+      // (which would ask for a release increment and an acquire read): on
+      // gfx950 an agent-scope store is written through to the memory side of
+      // the XCD L2s, vmcnt counts a store down only when that write is
+      // acknowledged, and the agent-scope loads of the last workgroup read
+      // from the same level, never from a stale L2 line.  A release/acquire
+      // pair would instead write back and invalidate a whole L2 per workgroup.
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       if (tid == 0) {

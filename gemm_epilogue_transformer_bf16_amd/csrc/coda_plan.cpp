@@ -92,17 +92,21 @@ bool strided_overlap(const Strided& a, const Strided& b) {
 namespace {
 // share of the compute units busy over the rounds of a grid of t tiles, one
 // workgroup per CU
-double round_fill(int64_t t) {
-  const int64_t rounds = (t + kNumCUs - 1) / kNumCUs;
-  return double(t) / double(rounds * kNumCUs);
+double round_fill(int64_t t, int64_t per_cu = 1) {
+  const int64_t slots = kNumCUs * per_cu;
+  const int64_t rounds = (t + slots - 1) / slots;
+  return double(t) / double(rounds * slots);
 }
 }  // namespace
 
 int choose_tile(int64_t M, int64_t N, int64_t K, bool split_allowed) {
   const int64_t t3 = ((M + 255) / 256) * ((N + 255) / 256);   // 256 x 256 tiles
   const int64_t t1 = ((M + 255) / 256) * ((N + 127) / 128);   // 256 x 128 tiles
-  if (t1 < kNumCUs) return 2;   // not one round even of 256 x 128: 128 x 128, two per CU
-  if (t3 < kNumCUs) return 1;
+  const int64_t t2 = ((M + 127) / 128) * ((N + 127) / 128);   // 128 x 128 tiles, two per CU
+  if (t1 < kNumCUs) return 2;   // not one round even of 256 x 128
+  // under one round of 256 x 256: two 128 x 128 workgroups per CU, one's
+  // epilogue beside the other's main loop, unless they fill the rounds worse
+  if (t3 < kNumCUs) return round_fill(t2, 2) >= round_fill(t1) ? 2 : 1;
   // the 256 x 256 tile's main loop is the faster one (fewer operand bytes per
   // flop through LDS); the 256 x 128 tile wins where it fills the rounds
   // better.  A last round that the split over K can fill counts as full.

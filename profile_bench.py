@@ -6,9 +6,9 @@ For each workload (default: all of 1 - 6) it runs, each under its own time
 limit and from /tmp (TMPDIR=/tmp):
 
 1. ``rocprofv3 --kernel-trace --stats -- python3 bench.py --workload N
-   --no-cpu-baseline``: the bench exactly as timed (fused, unfused sequence
-   and, for norm layers, the other gain placement, round-robin, a cache flush
-   before every step).  The trace is cut into steps at the flushes
+   --no-cpu-baseline``: the bench exactly as timed (fused, unfused sequence,
+   plain GEMM and, for norm layers, the other gain placement, round-robin, a
+   cache flush before every step).  The trace is cut into steps at the flushes
    (``FillFunctor<float>`` dispatches); the last ``steps x variants`` steps
    are the timed ones, and the summary gives each variant's kernel time per
    step next to the bench's own event timings of the same run.
@@ -119,9 +119,12 @@ def trace_table(db):
 
 
 def summarize_trace(db, line, khash):
+    # the bench's round order: fused, unfused sequence, plain GEMM, other gain placement
     variants = ["fused"]
     if line.get("unfused_ms") is not None:
         variants.append("unfused")
+    if line.get("plain_gemm_ms") is not None:
+        variants.append("plain_gemm")
     other = [k for k in ("fused_in_loop_gain_ms", "fused_folded_gain_ms") if k in line]
     if other:
         variants.append(other[0][:-3])
@@ -155,15 +158,14 @@ def summarize_trace(db, line, khash):
         ms = sorted(per[i])
         mean = sum(ms) / len(ms)
         med = ms[len(ms) // 2] if len(ms) % 2 else 0.5 * (ms[len(ms) // 2 - 1] + ms[len(ms) // 2])
-        bench_stats = line["fused_ms"] if v == "fused" else (line["unfused_ms"] if v == "unfused"
-                                                            else line[v + "_ms"])
+        bench_stats = line[v + "_ms"]
         kinds = ", ".join(f"{n if len(n) < 70 else n[:67] + '...'} x{c // line['steps']}"
                           for n, c in names[i].items())
         tail.append(f"#   {v}: kernel time per step (trace) mean {mean:.4f} ms, median {med:.4f} ms "
                     f"(min {ms[0]:.4f}, max {ms[-1]:.4f}); bench events median {bench_stats['median']:.4f} ms, "
                     f"mean {bench_stats['mean']:.4f} ms")
         tail.append(f"#      kernels per step: {kinds}")
-        rec[v] = {"trace_mean_ms": round(mean, 5), "trace_median_ms": round(med, 5),
+        rec[v] = {"trace_mean_ms": round(mean, 6), "trace_median_ms": round(med, 6),
                   "bench_median_ms": bench_stats["median"], "bench_mean_ms": bench_stats["mean"]}
     tail.append(f"# bench line of this run: value {line['value']} {line['unit']}, "
                 f"speedup_vs_unfused {line.get('speedup_vs_unfused')}, tile {line['config'].get('tile')}")

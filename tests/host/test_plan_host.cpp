@@ -197,8 +197,17 @@ int main() {
     // 256 x 128 where it fills whole rounds and 256 x 256 does not:
     // 32 x 24 = 768 tiles (3 rounds) against 384 (1.5 rounds, 12 K steps: no split)
     EXPECT(coda_selected_tile(8192, 3072, 768, &e) == 1);
-    // 32 x 8 = 256 tiles (1 round) against 128
-    EXPECT(coda_selected_tile(8192, 1024, 4096, &e) == 1);
+    // under one round of 256 x 256 (128 tiles): 64 x 8 = 512 tiles of 128 x 128
+    // fill one round at two per CU, as well as 256 tiles of 256 x 128 do
+    EXPECT(coda_selected_tile(8192, 1024, 4096, &e) == 2);
+    // 31 x 8 = 248 tiles of 256 x 128: under one round
+    EXPECT(coda_selected_tile(7936, 1024, 4096, &e) == 2);
+    // 24 x 12 = 288 of 256 x 128 (2 rounds, 56% busy) against 48 x 12 = 576
+    // of 128 x 128 (2 rounds of 512, 56%): ties go to 128 x 128
+    EXPECT(coda_selected_tile(6144, 1536, 4096, &e) == 2);
+    // 40 x 8 = 320 of 256 x 128 (2 rounds, 62.5%) against 79 x 8 = 632 of
+    // 128 x 128 (2 rounds of 512, 61.7%); 256 x 256: 40 x 4 = 160, under a round
+    EXPECT(coda_selected_tile(10112, 1024, 4096, &e) == 1);
     // 32 x 16 = 512 tiles of 256 x 256 fill two rounds
     EXPECT(coda_selected_tile(8192, 4096, 1024, &e) == 3);
     // 5.4 rounds of 256 x 256, the last one split over K (64 K steps)

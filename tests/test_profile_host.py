@@ -83,3 +83,24 @@ def test_counters_summed_per_dispatch_and_copy_scale(tmp_path):
     assert pb.avg(cnt["fused_kernel<A>"], "FETCH_SIZE") == 4000.0
     ref, scale = pb.copy_scale(cnt, "FETCH_SIZE")
     assert ref == 2000.0 and scale == bench.COPY_BYTES / (2000.0 * 1024)
+
+
+def test_summarize_trace_variants_and_bench_stats(tmp_path):
+    import profile_bench as pb
+    db = str(tmp_path / "t.db")
+    _trace_db(db, rounds=6, variants=4)
+    c = sqlite3.connect(db)
+    c.execute("create table top_kernels (name text, total_calls integer, total_duration real, average real, "
+              "percentage real)")
+    c.execute("insert into top_kernels values ('fused_kernel<Cfg<1>>', 6, 4.2, 0.7, 50.0)")
+    c.commit()
+    c.close()
+    st = {"median": 1.0, "mean": 1.0, "p10": 1.0, "p90": 1.0}
+    line = {"steps": 3, "fused_ms": st, "unfused_ms": st, "plain_gemm_ms": st, "fused_in_loop_gain_ms": st,
+            "value": 1.0, "unit": "TFLOP/s", "speedup_vs_unfused": 1.0,
+            "config": {"workload": pb.bench.WORKLOAD_TEXT[2], "tile": 1}}
+    text, fused_name, rec = pb.summarize_trace(db, line, "0" * 16)
+    assert fused_name == "fused_kernel<Cfg<1>>"
+    assert set(rec) == {"fused", "unfused", "plain_gemm", "fused_in_loop_gain"}
+    # the last three rounds: fused durations 703, 704, 705 ns
+    assert abs(rec["fused"]["trace_mean_ms"] - 704e-6) < 1e-9
