@@ -22,10 +22,10 @@
 // Deferred row norms (the per-row factors of a row-wise norm moved past the
 // projection: the "augment_me" comment on the zeli.app page; the
 // agentlenshq.com page, "CODA's approach"), one compile-time mode each:
-//   * gain in the loop (RMS, LayerNorm): raw A lands in a third LDS array one
-//     K step ahead; each wave multiplies its blocks by gamma[k], rounds them to
-//     bf16 into the stage and adds the raw squares (and, for LayerNorm, the
-//     values, both about a per-row shift) to fp32 per-row sums;
+//   * gain in the loop (RMS, LayerNorm): raw A comes into registers one K
+//     step ahead; each wave multiplies its chunks by gamma[k], rounds them to
+//     bf16, writes them into the stage and adds the raw squares (and, for
+//     LayerNorm, the values, both about a per-row shift) to fp32 per-row sums;
 //   * gain folded into B (RMS, LayerNorm): A reaches the MFMAs unchanged and
 //     the sums come from the X fragments the MFMAs read, between the MFMAs;
 //   * row sums of squares given (RMS with the gain in B): the plain main loop.
@@ -176,15 +176,12 @@ struct Cfg {
   static constexpr int EPI_END = EPI_COL_OFF + CODA_MAX_COL_REDUCTIONS * WM * MI * BN * 4;
   static constexpr int ARR0_BYTES = STAGE_BYTES > NW * REGION_BYTES ? STAGE_BYTES : NW * REGION_BYTES;
   static constexpr int ARR1_BYTES = STAGE_BYTES > EPI_END ? STAGE_BYTES : EPI_END;
-  // RMS: raw A of the next K step lands in a third array by direct loads and is
-  // converted (gain, bf16 rounding, sum of squares) from there into the stage
-  static constexpr int RAW_BYTES = (RMS && !F32) ? A_BYTES : 16;
   // SSF: per-row partial sums of squares, one row of BM per wave column
   // (LNF: then the row sums [WN][BM] and the per-row shift [BM])
   static constexpr int SS_BYTES = (SSF && !F32) ? (LNF ? 2 * WN + 1 : WN) * BM * 4 : 16;
-  // (arrays a variant never touches are dropped by the compiler: the raw A array
-  // without RMS, the sums array without SSF, the 256-byte warm-up word with RMS)
-  static_assert(ARR0_BYTES + ARR1_BYTES + (RMS ? RAW_BYTES : 0) + (SSF ? SS_BYTES : 0) + (RMS ? 0 : 256) <=
+  // (arrays a variant never touches are dropped by the compiler: the sums array
+  // without SSF, the 256-byte warm-up word with RMS)
+  static_assert(ARR0_BYTES + ARR1_BYTES + (SSF ? SS_BYTES : 0) + (RMS ? 0 : 256) <=
                     160 * 1024,
                 "LDS budget");
   static_assert(CPR >= 4 && CPR <= 16 && (CPR & (CPR - 1)) == 0, "epilogue lane layout");
@@ -615,7 +612,6 @@ fused_kernel(FusedArgs args) {
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, MI = C::MI, NI = C::NI;
   __shared__ __attribute__((aligned(1024))) char smem0[C::ARR0_BYTES];
   __shared__ __attribute__((aligned(1024))) char smem1[C::ARR1_BYTES];
-  __shared__ __attribute__((aligned(1024))) char smem_raw[C::RAW_BYTES];
   __shared__ __attribute__((aligned(16))) float smem_ss[C::SS_BYTES / 4];
   __shared__ __attribute__((aligned(256))) char smem_warm[256];
 
@@ -690,10 +686,12 @@ fused_kernel(FusedArgs args) {
     const int kn_slot = lane % C::KN_CPR;
 
     u32x4_t greg;   // RMS: the gamma chunk matching this lane's A chunks
+    u32x4_t araw[C::A_BPW];   // RMS: this lane's raw A chunks of the next K step
     const __amdgpu_buffer_rsrc_t rg_all = make_rsrc(C::RMS ? a->gamma : a->A, (long long)K * 2);
 
-    // A (raw, into smem_raw, with RMS) or A (into the stage) plus B, all
-    // straight to LDS; the swizzled block layout is the same for both A targets
+    // A straight to LDS (into the stage), or with RMS into registers (the chunk
+    // a lane loads is the one it owns in the stage's swizzled block layout, so
+    // its converted values go to LDS at the same place); B straight to LDS
     // per-lane offsets of the direct loads within a K step (fixed for the
     // whole loop; the step moves the resource base)
     uint32_t a_off[C::A_BPW], b_off[C::B_BPW];
@@ -738,12 +736,18 @@ fused_kernel(FusedArgs args) {
       // offsets carry no per-lane select (one compiled as a divergent branch
       // around every load)
       const uint32_t kmask = (k0 + 64 <= K) ? 0u : ((k0 + 8 * kq_chunk < K) ? 0u : kOobOffset);
+      if constexpr (C::RMS) {
 #pragma unroll
-      for (int i = 0; i < C::A_BPW; ++i) {
-        const int q = wave + C::NW * i;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (LdsPtr)(dst + q * 1024), 16, (int)(a_off[i] | kmask), 0, 0, 0);
+        for (int i = 0; i < C::A_BPW; ++i) araw[i] = buffer_load16(ra, a_off[i] | kmask);
+        greg = buffer_load16(rg_all, uint32_t((k0 + 8 * kq_chunk) * 2));
+      } else {
+#pragma unroll
+        for (int i = 0; i < C::A_BPW; ++i) {
+          const int q = wave + C::NW * i;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (LdsPtr)(dst + q * 1024), 16, (int)(a_off[i] | kmask), 0, 0,
+                                                   0);
+        }
       }
-      if constexpr (C::RMS) greg = buffer_load16(rg_all, uint32_t((k0 + 8 * kq_chunk) * 2));
     };
     auto load_b = [&](int kt, char* As) {
       const int k0 = (kt_lo + kt) * 64;
@@ -807,9 +811,9 @@ fused_kernel(FusedArgs args) {
       }
     };
 
-    // RMS: convert this wave's raw A blocks into the stage `As`: fp32 sum of
-    // squares of the raw values, then bf16(x * gamma).  Each wave reads only the blocks its own
-    // direct loads wrote, so no barrier is needed between load and conversion.
+    // RMS: convert this lane's raw A chunks into the stage `As`: fp32 sum of
+    // squares of the raw values, then bf16(x * gamma).  Each lane writes only
+    // its own chunks, so no barrier is needed between load and conversion.
     // LN: the values converted are x - s, s the mean of the row's first 64 values
     // (taken at the first conversion over the 8 lanes that hold the row; any
     // per-row constant leaves the norm unchanged, and one close to the row mean
@@ -820,7 +824,7 @@ fused_kernel(FusedArgs args) {
 #pragma unroll
       for (int i = 0; i < C::A_BPW; ++i) {
         const int q = wave + C::NW * i;
-        u32x4_t x = *reinterpret_cast<const u32x4_t*>(smem_raw + q * 1024 + lane * 16);
+        u32x4_t x = araw[i];
         if constexpr (C::LN) {
           if (first) {
             float t = 0.0f;
@@ -1000,8 +1004,9 @@ fused_kernel(FusedArgs args) {
       });
     };
 
-    // Direct loads complete in issue order, so a wait for a given load is
-    // "at most `later` loads outstanding", `later` being those issued after it.
+    // Buffer loads (to LDS or to registers) complete in issue order, so a wait
+    // for a given load is "at most `later` loads outstanding", `later` being
+    // those issued after it.
     auto wait_vm = [&](auto later_c) {
       constexpr int later = decltype(later_c)::value;
       constexpr int enc = (later & 0xF) | (0x7 << 4) | (0xF << 8) | (((later >> 4) & 3) << 14);
@@ -1018,16 +1023,13 @@ fused_kernel(FusedArgs args) {
     auto convert_phase = [&](int kt, char* nxt) {
       wait_vm(kAfterA);                     // raw A(kt+1) and its gamma have landed
       convert_a(nxt, (kt_lo + kt + 1) * 64, false);
-      if (kt + 2 < KT) {
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // raw reads done before reuse
-        load_a(kt + 2, smem_raw);
-      }
+      if (kt + 2 < KT) load_a(kt + 2, nullptr);   // into araw, which the conversion has consumed
     };
 
     // One K step: tile kt is in `cur`; every wave is done reading `nxt`.
-    // RMS order of a wave's direct loads: B(kt) at the top of step kt-1, then
-    // raw A(kt+1) and gamma after that wave's conversion in step kt-1; so at the
-    // top of step kt only the latter may still be in flight.
+    // RMS order of a wave's loads: B(kt) (to LDS) at the top of step kt-1, then
+    // raw A(kt+1) (to registers) and gamma after that wave's conversion in step
+    // kt-1; so at the top of step kt only the latter may still be in flight.
     auto step = [&](int kt, char* cur, char* nxt) {
       if constexpr (C::RMS) {
         if (kt + 1 < KT) wait_vm(kAfterB);
@@ -1052,14 +1054,11 @@ fused_kernel(FusedArgs args) {
     };
     if (KT > 0) {
       if constexpr (C::RMS) {
-        load_a(0, smem_raw);
+        load_a(0, nullptr);
         load_b(0, smem0);
         wait_vm(kAfterA);
         convert_a(smem0, kt_lo * 64, true);
-        if (KT > 1) {
-          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-          load_a(1, smem_raw);
-        }
+        if (KT > 1) load_a(1, nullptr);
       } else {
         load_a(0, smem0);
         load_b(0, smem0);
