@@ -1,6 +1,6 @@
 """rocprofv3 profiles of bench.py, one workload at a time, summarised as text.
 
-    python3 profile_bench.py --out <dir> [--workload 4 --workload 2 ...]
+    python3 profile_bench.py --out <dir> [--raw <dir>] [--workload 4 --workload 2 ...]
 
 For each workload (default: all of 1 - 6) it runs, each under its own time
 limit and from /tmp (TMPDIR=/tmp):
@@ -221,17 +221,20 @@ def copy_scale(cnt, counter):
 def profile(args, n):
     key = bench.WORKLOAD_KEY[n]
     khash = bench.kernel_source_hash()
-    out = os.path.join(args.out, key)
-    summ = os.path.join(args.out, "summaries")
-    os.makedirs(out, exist_ok=True)
-    os.makedirs(summ, exist_ok=True)
+    # absolute: the profiled processes run from /tmp.  The results databases
+    # (large) go under --raw, the logs and the summaries under --out.
+    out = os.path.join(os.path.abspath(args.raw), key)
+    logs = os.path.join(os.path.abspath(args.out), key)
+    summ = os.path.join(os.path.abspath(args.out), "summaries")
+    for d in (out, logs, summ):
+        os.makedirs(d, exist_ok=True)
     bench_py = os.path.join(ROOT, "bench.py")
     py = sys.executable or "python3"
 
     log(f"{key}: kernel trace")
     run(["rocprofv3", "--kernel-trace", "--stats", "-d", os.path.join(out, "kt"), "-o", "run", "--",
-         py, bench_py, "--workload", str(n), "--no-cpu-baseline"], os.path.join(out, "kt.log"), args.trace_limit)
-    line = bench_line(os.path.join(out, "kt.log"))
+         py, bench_py, "--workload", str(n), "--no-cpu-baseline"], os.path.join(logs, "kt.log"), args.trace_limit)
+    line = bench_line(os.path.join(logs, "kt.log"))
     text, fused_name, trace_rec = summarize_trace(find_db(os.path.join(out, "kt")), line, khash)
     with open(os.path.join(summ, f"{key}_kernel_trace.txt"), "w") as f:
         f.write(text)
@@ -243,7 +246,7 @@ def profile(args, n):
         run(["rocprofv3", "--pmc", *ctrs, "-d", os.path.join(out, name), "-o", "run", "--",
              py, bench_py, "--workload", str(n), "--no-cpu-baseline", "--no-unfused", "--copy-calibration",
              "--steps", "3", "--warmup", "2", "--warmup-seconds", "0.3"],
-            os.path.join(out, name + ".log"), args.counter_limit, kill_signal="KILL")
+            os.path.join(logs, name + ".log"), args.counter_limit, kill_signal="KILL")
         cnt[name] = counters(find_db(os.path.join(out, name)))
         log(f"{key}: counter pass {name} done")
 
@@ -324,7 +327,8 @@ def profile(args, n):
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("--out", required=True)
+    ap.add_argument("--out", required=True, help="logs and summaries")
+    ap.add_argument("--raw", default="/tmp/coda_profile_raw", help="rocprofv3 results databases")
     ap.add_argument("--workload", type=int, action="append", choices=sorted(bench.WORKLOAD_TEXT))
     ap.add_argument("--trace-limit", type=int, default=240, help="seconds for the kernel-trace run")
     ap.add_argument("--counter-limit", type=int, default=90, help="seconds for each counter pass")
