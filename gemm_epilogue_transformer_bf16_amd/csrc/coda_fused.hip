@@ -83,13 +83,14 @@ int launch_args(const Plan& p, const dev::FusedArgs& a, hipStream_t stream) {
                    : p.has_norm  ? dev::kNormRms
                                  : dev::kNormNone;
   const bool ext = p.has_ext;
+  const bool side = p.has_side;
   if (p.ab_dtype == CODA_F32) {
-    return dev::launch_tile_f32(a, nwg, bkn, norm, akm, ext, stream);
+    return dev::launch_tile_f32(a, nwg, bkn, norm, akm, ext, side, stream);
   }
   switch (p.tile) {
-    case 1: return dev::launch_tile1(a, nwg, bkn, norm, akm, ext, stream);
-    case 2: return dev::launch_tile2(a, nwg, bkn, norm, akm, ext, stream);
-    case 3: return dev::launch_tile3(a, nwg, bkn, norm, akm, ext, stream);
+    case 1: return dev::launch_tile1(a, nwg, bkn, norm, akm, ext, side, stream);
+    case 2: return dev::launch_tile2(a, nwg, bkn, norm, akm, ext, side, stream);
+    case 3: return dev::launch_tile3(a, nwg, bkn, norm, akm, ext, side, stream);
     default:
       set_error("no kernel for tile config %d", p.tile);
       return CODA_ERR_UNSUPPORTED;

@@ -106,7 +106,8 @@ constexpr int kNormLnB = 5;
 // LayerNorm with the gain in B and the row sums and sums of squares given
 constexpr int kNormLnGiven = 6;
 
-template <int BM_, int BN_, int WM_, int WN_, bool F32_, bool BKN_, int NORM_, bool AKM_ = false, bool EXT_ = true>
+template <int BM_, int BN_, int WM_, int WN_, bool F32_, bool BKN_, int NORM_, bool AKM_ = false, bool EXT_ = true,
+          bool SIDE_ = false>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
   static constexpr bool F32 = F32_, BKN = BKN_;
@@ -114,6 +115,11 @@ struct Cfg {
   // reductions, ROW_DOT, RMS_BWD, RMS_DGAMMA); lists without them run a
   // variant compiled without their code and registers
   static constexpr bool EXT = EXT_;
+  // SIDE: the list's first bf16 side matrix (ADD_MAT / MUL_DGELU_TANH before
+  // any SWIGLU_PAIR) is read one 32-row block ahead into registers; variants
+  // without it read side matrices chunk by chunk where they are used, and
+  // carry no prefetch registers
+  static constexpr bool SIDE = SIDE_;
   // AKM: A stored [K x M] (M contiguous) and used transposed, as X^T in the
   // weight gradient X^T dY; its tile is staged and read like an N-major W tile
   static constexpr bool AKM = AKM_;
@@ -271,10 +277,13 @@ __device__ __forceinline__ bool is_col_reduction(int kind) {
 }
 
 // Applies ops[o..] until the end of the list or a SWIGLU_PAIR (returned index).
-template <class C, bool PAIRED>
+// pf: the prefetched rows of side matrix op pf_op (SIDE variants); pf_used()
+// runs as soon as they are consumed, and issues the next block's prefetch into
+// the same registers
+template <class C, bool PAIRED, class PfUsed>
 __device__ __forceinline__ int run_ops(Chunks<C::CPL>& ch, KArgs a, int o, int M, int lane, int wn, float* red,
                                        int pf_op, const u32x4_t (&pf)[C::CPL], float* colp, int wm, int mi,
-                                       int cv_op, const float (&cv)[8]) {
+                                       int cv_op, const float (&cv)[8], PfUsed&& pf_used) {
   constexpr int CPL = C::CPL;
   constexpr int EPC = PAIRED ? 4 : 8;   // live values per chunk
   const int col = PAIRED ? ch.col >> 1 : ch.col;
@@ -321,36 +330,45 @@ __device__ __forceinline__ int run_ops(Chunks<C::CPL>& ch, KArgs a, int o, int M
       }
       case CODA_OP_ADD_MAT:
       case CODA_OP_MUL_DGELU_TANH: {
-        const bool addm = kind == CODA_OP_ADD_MAT;
-        const float beta = op.scalar;
-        const int esz = op.dtype == CODA_BF16 ? 2 : 4;
-        float x[CPL][8];
-        if (!PAIRED && o == pf_op) {
-          // prefetched bf16 row chunks
+        // v + beta x, or v * GELU_tanh'(x): the variant is a compile-time flag,
+        // and the side values are applied chunk by chunk so that no whole
+        // block of them is live
+        auto side_mat = [&](auto addc) {
+          constexpr bool ADDM = decltype(addc)::value;
+          const float beta = op.scalar;
+          auto apply = [&](float& v, float x) {
+            if constexpr (ADDM) v = v + beta * x;
+            else v = v * gelu_tanh_grad_f(x);
+          };
+          if (C::SIDE && !PAIRED && o == pf_op) {
+            // prefetched bf16 row chunks
 #pragma unroll
-          for (int j = 0; j < CPL; ++j)
+            for (int j = 0; j < CPL; ++j)
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-              x[j][2 * w] = bf16_lo(pf[j][w]);
-              x[j][2 * w + 1] = bf16_hi(pf[j][w]);
-            }
-        } else {
-#pragma unroll
-        for (int j = 0; j < CPL; ++j) {
-          if (ch.row[j] < M) {
-            load_cols<PAIRED>(static_cast<const char*>(op.in) + (long long)ch.row[j] * op.ld * esz, op.dtype, col,
-                              width, x[j]);
+              for (int w = 0; w < 4; ++w) {
+                apply(ch.v[j][2 * w], bf16_lo(pf[j][w]));
+                apply(ch.v[j][2 * w + 1], bf16_hi(pf[j][w]));
+              }
+            pf_used();
           } else {
+            const int esz = op.dtype == CODA_BF16 ? 2 : 4;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[j][e] = 0.0f;
+            for (int j = 0; j < CPL; ++j) {
+              float x[8];
+              if (ch.row[j] < M) {
+                load_cols<PAIRED>(static_cast<const char*>(op.in) + (long long)ch.row[j] * op.ld * esz, op.dtype,
+                                  col, width, x);
+              } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = 0.0f;
+              }
+#pragma unroll
+              for (int e = 0; e < EPC; ++e) apply(ch.v[j][e], x[e]);
+            }
           }
-        }
-        }
-#pragma unroll
-        for (int j = 0; j < CPL; ++j)
-#pragma unroll
-          for (int e = 0; e < EPC; ++e)
-            ch.v[j][e] = addm ? ch.v[j][e] + beta * x[j][e] : ch.v[j][e] * gelu_tanh_grad_f(x[j][e]);
+        };
+        if (kind == CODA_OP_ADD_MAT) side_mat(std::true_type{});
+        else side_mat(std::false_type{});
         break;
       }
       case CODA_OP_DROPOUT: {
@@ -1407,18 +1425,23 @@ fused_kernel(FusedArgs args) {
     __syncthreads();
   }
 
-  // The first bf16 side matrix of the list (before any SWIGLU_PAIR) is read one
-  // 32-row block ahead, so its load latency overlaps the previous block's work.
+  // SIDE: the first bf16 side matrix of the list (before any SWIGLU_PAIR) is
+  // read ahead: block 0's rows before the block loop, block mi+1's as soon as
+  // block mi has consumed its own (one set of registers), so their latency
+  // overlaps the rest of the block's ops, its stores and the next restage.
   int pf_op = -1;
-  for (int q = 0; q < a->n_ops; ++q) {
-    const int k = a->ops[q].kind;
-    if (k == CODA_OP_SWIGLU_PAIR) break;
-    if ((k == CODA_OP_ADD_MAT || k == CODA_OP_MUL_DGELU_TANH) && a->ops[q].dtype == CODA_BF16) {
-      pf_op = q;
-      break;
+  if constexpr (C::SIDE) {
+    for (int q = 0; q < a->n_ops; ++q) {
+      const int k = a->ops[q].kind;
+      if (k == CODA_OP_SWIGLU_PAIR) break;
+      if ((k == CODA_OP_ADD_MAT || k == CODA_OP_MUL_DGELU_TANH) && a->ops[q].dtype == CODA_BF16) {
+        pf_op = q;
+        break;
+      }
     }
   }
-  u32x4_t pf_buf[2][C::CPL];
+  u32x4_t pf_buf[C::SIDE ? C::CPL : 1][1];
+  u32x4_t(&pfb)[C::CPL] = *reinterpret_cast<u32x4_t(*)[C::CPL]>(&pf_buf[0][0]);
   auto prefetch = [&](int mi_next, u32x4_t (&dst)[C::CPL]) {
     KOp op = a->ops[pf_op];
     // rows from m0 on; reads past the matrix (rows >= M) return zero
@@ -1431,7 +1454,7 @@ fused_kernel(FusedArgs args) {
       dst[j] = buffer_load16(rs, uint32_t(mloc) * uint32_t(op.ld * 2) + uint32_t(colb * 2));
     }
   };
-  if (pf_op >= 0) prefetch(0, pf_buf[0]);
+  if (C::SIDE && pf_op >= 0) prefetch(0, pfb);
   // LN: u[j] for the lane's 8 columns (the same in every block)
   float uv[8];
   if constexpr (C::LNE) load_cols<false>(a->ln_u, CODA_F32, n0 + wn * C::WTN + 8 * (lane % C::CPR), N, uv);
@@ -1463,9 +1486,9 @@ fused_kernel(FusedArgs args) {
 
   static_for<0, MI>([&](auto mic) {
     constexpr int mi = decltype(mic)::value;
-    if constexpr (mi + 1 < MI) {
-      if (pf_op >= 0) prefetch(mi + 1, pf_buf[(mi + 1) & 1]);
-    }
+    auto next_pf = [&]() {
+      if constexpr (C::SIDE && mi + 1 < MI) prefetch(mi + 1, pfb);
+    };
     // accumulators of block mi -> the wave's region, row-major [32][WTN] fp32,
     // 16-byte slot s of row r stored at slot s ^ swz(r)
 #pragma unroll
@@ -1508,10 +1531,10 @@ fused_kernel(FusedArgs args) {
       }
     }
     __builtin_amdgcn_wave_barrier();
-    const int o = run_ops<C, false>(ch, a, 0, M, lane, wn, red, pf_op, pf_buf[mi & 1], colp, wm, mi, cv_op, cv);
+    const int o = run_ops<C, false>(ch, a, 0, M, lane, wn, red, pf_op, pfb, colp, wm, mi, cv_op, cv, next_pf);
     if (o < a->n_ops) {   // SWIGLU_PAIR
       swiglu_chunks<C>(ch);
-      run_ops<C, true>(ch, a, o + 1, M, lane, wn, red, -1, pf_buf[mi & 1], colp, wm, mi, -1, cv);
+      run_ops<C, true>(ch, a, o + 1, M, lane, wn, red, -1, pfb, colp, wm, mi, -1, cv, [] {});
       paired_out = true;
       if (defer) pack_chunks<C, true>(ch, dpk[mi]);
       else store_chunks<C, true>(ch, a, M);
@@ -1675,7 +1698,7 @@ int launch_cfg(const FusedArgs& args, int64_t nwg, hipStream_t stream) {
 // host (no workload pairs them), which keeps the norm kernels' registers to
 // what their own ops need.
 template <int BM, int BN, int WM, int WN, bool F32, bool BKN>
-int launch_norms(const FusedArgs& args, int64_t nwg, int norm, bool ext, hipStream_t s) {
+int launch_norms(const FusedArgs& args, int64_t nwg, int norm, bool ext, bool side, hipStream_t s) {
   switch (norm) {
     case kNormRms: return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormRms, false, false>>(args, nwg, s);
     case kNormLn: return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormLn, false, false>>(args, nwg, s);
@@ -1684,31 +1707,37 @@ int launch_norms(const FusedArgs& args, int64_t nwg, int norm, bool ext, hipStre
     case kNormLnB: return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormLnB, false, false>>(args, nwg, s);
     case kNormLnGiven: return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormLnGiven, false, false>>(args, nwg, s);
     default:
-      return ext ? launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormNone, false, true>>(args, nwg, s)
-                 : launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormNone, false, false>>(args, nwg, s);
+      if (ext) return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormNone, false, true, true>>(args, nwg, s);
+      return side ? launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormNone, false, false, true>>(args, nwg, s)
+                  : launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormNone, false, false>>(args, nwg, s);
   }
 }
 
 template <int BM, int BN, int WM, int WN, bool F32>
-int launch_variants(const FusedArgs& args, int64_t nwg, bool bkn, int norm, bool akm, bool ext, hipStream_t s) {
+int launch_variants(const FusedArgs& args, int64_t nwg, bool bkn, int norm, bool akm, bool ext, bool side,
+                    hipStream_t s) {
   if constexpr (!F32) {
     if (akm) {   // A stored [K x M]: no row norm (validated on the host)
       if (ext)
-        return bkn ? launch_cfg<Cfg<BM, BN, WM, WN, F32, true, kNormNone, true, true>>(args, nwg, s)
-                   : launch_cfg<Cfg<BM, BN, WM, WN, F32, false, kNormNone, true, true>>(args, nwg, s);
-      return bkn ? launch_cfg<Cfg<BM, BN, WM, WN, F32, true, kNormNone, true, false>>(args, nwg, s)
-                 : launch_cfg<Cfg<BM, BN, WM, WN, F32, false, kNormNone, true, false>>(args, nwg, s);
+        return bkn ? launch_cfg<Cfg<BM, BN, WM, WN, F32, true, kNormNone, true, true, true>>(args, nwg, s)
+                   : launch_cfg<Cfg<BM, BN, WM, WN, F32, false, kNormNone, true, true, true>>(args, nwg, s);
+      return bkn ? launch_cfg<Cfg<BM, BN, WM, WN, F32, true, kNormNone, true, false, true>>(args, nwg, s)
+                 : launch_cfg<Cfg<BM, BN, WM, WN, F32, false, kNormNone, true, false, true>>(args, nwg, s);
     }
   }
-  return bkn ? launch_norms<BM, BN, WM, WN, F32, true>(args, nwg, norm, ext, s)
-             : launch_norms<BM, BN, WM, WN, F32, false>(args, nwg, norm, ext, s);
+  return bkn ? launch_norms<BM, BN, WM, WN, F32, true>(args, nwg, norm, ext, side, s)
+             : launch_norms<BM, BN, WM, WN, F32, false>(args, nwg, norm, ext, side, s);
 }
 
 // one function per compiled tile configuration (defined in coda_fused_t*.hip)
-int launch_tile1(const FusedArgs& a, int64_t nwg, bool bkn, int norm, bool akm, bool ext, hipStream_t s);
-int launch_tile2(const FusedArgs& a, int64_t nwg, bool bkn, int norm, bool akm, bool ext, hipStream_t s);
-int launch_tile3(const FusedArgs& a, int64_t nwg, bool bkn, int norm, bool akm, bool ext, hipStream_t s);
-int launch_tile_f32(const FusedArgs& a, int64_t nwg, bool bkn, int norm, bool akm, bool ext, hipStream_t s);
+int launch_tile1(const FusedArgs& a, int64_t nwg, bool bkn, int norm, bool akm, bool ext, bool side,
+                 hipStream_t s);
+int launch_tile2(const FusedArgs& a, int64_t nwg, bool bkn, int norm, bool akm, bool ext, bool side,
+                 hipStream_t s);
+int launch_tile3(const FusedArgs& a, int64_t nwg, bool bkn, int norm, bool akm, bool ext, bool side,
+                 hipStream_t s);
+int launch_tile_f32(const FusedArgs& a, int64_t nwg, bool bkn, int norm, bool akm, bool ext, bool side,
+                 hipStream_t s);
 
 }  // namespace dev
 }  // namespace coda

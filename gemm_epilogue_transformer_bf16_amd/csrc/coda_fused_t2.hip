@@ -5,9 +5,10 @@
 namespace coda {
 namespace dev {
 
-int launch_tile2(const FusedArgs& a, int64_t nwg, bool bkn, int norm, bool akm, bool ext, hipStream_t s) {
+int launch_tile2(const FusedArgs& a, int64_t nwg, bool bkn, int norm, bool akm, bool ext, bool side,
+                 hipStream_t s) {
   constexpr TileCfg t = kTileCfgs[1];
-  return launch_variants<t.bm, t.bn, t.wm, t.wn, false>(a, nwg, bkn, norm, akm, ext, s);
+  return launch_variants<t.bm, t.bn, t.wm, t.wn, false>(a, nwg, bkn, norm, akm, ext, side, s);
 }
 
 }  // namespace dev

@@ -215,7 +215,7 @@ Plan plain_gemm_plan(const Plan& p) {
   q.gamma = nullptr;
   q.ln_u = q.row_ss = q.row_s = nullptr;
   q.n_ops = q.n_red = q.n_colred = 0;
-  q.has_swiglu = false;
+  q.has_swiglu = q.has_ext = q.has_side = false;
   q.out_width = p.N;
   plan_split(&q, p.split_allowed, kMaxSplit);
   return q;
@@ -523,6 +523,14 @@ int build_plan_split(const void* A, const void* B, int64_t M, int64_t N, int64_t
   for (int i = 0; i < p->n_ops; ++i) {
     const int k = p->ops[i].kind;
     if (is_col_reduction(k) || k == CODA_OP_ROW_DOT || k == CODA_OP_RMS_BWD) p->has_ext = true;
+  }
+  for (int i = 0; i < p->n_ops; ++i) {
+    const int k = p->ops[i].kind;
+    if (k == CODA_OP_SWIGLU_PAIR) break;
+    if ((k == CODA_OP_ADD_MAT || k == CODA_OP_MUL_DGELU_TANH) && p->ops[i].dtype == CODA_BF16) {
+      p->has_side = true;
+      break;
+    }
   }
   if (p->has_norm && p->has_ext) {
     set_error("column reductions, ROW_DOT, RMS_BWD and RMS_DGAMMA cannot follow RMS_ROWSCALE / LN_ROWSCALE");

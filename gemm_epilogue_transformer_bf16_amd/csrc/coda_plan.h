@@ -77,6 +77,7 @@ struct Plan {
   int n_colred;              // column reductions
   bool has_swiglu;
   bool has_ext;              // a backward-set op: column reduction, ROW_DOT, RMS_BWD or RMS_DGAMMA
+  bool has_side;             // a bf16 ADD_MAT / MUL_DGELU_TANH before any SWIGLU_PAIR (read ahead)
   int tile;                  // 1-based bf16 tile config; 0 for the fp32 path
   TileCfg cfg;
   int64_t grid_m, grid_n;

@@ -168,9 +168,15 @@ __global__ void __launch_bounds__(kPassThreads) ew_kernel(const void* in, long l
         float s[8];
         const int sz = op.dtype == CODA_BF16 ? 2 : 4;
         load8(static_cast<const char*>(op.in) + (long long)row * op.ld * sz, op.dtype, c, width, s);
+        // the variant is chosen outside the element loop (inside it, the
+        // compiler branches around every element)
+        if (op.kind == CODA_OP_ADD_MAT) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          v[e] = op.kind == CODA_OP_ADD_MAT ? v[e] + op.scalar * s[e] : v[e] * gelu_tanh_grad_f(s[e]);
+          for (int e = 0; e < 8; ++e) v[e] = v[e] + op.scalar * s[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = v[e] * gelu_tanh_grad_f(s[e]);
+        }
         break;
       }
       case CODA_OP_RMS_BWD: {

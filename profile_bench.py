@@ -12,10 +12,10 @@ limit and from /tmp (TMPDIR=/tmp):
    (``FillFunctor<float>`` dispatches); the last ``steps x variants`` steps
    are the timed ones, and the summary gives each variant's kernel time per
    step next to the bench's own event timings of the same run.
-2. Four counter passes over ``bench.py --workload N --no-unfused
+2. Five counter passes over ``bench.py --workload N --no-unfused
    --copy-calibration`` (the headline kernel alone): FETCH_SIZE; WRITE_SIZE;
    GRBM_GUI_ACTIVE with the MFMA and LDS counters; GRBM_GUI_ACTIVE with the
-   VALU / wait counters.  FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are
+   VALU / wait counters; the instruction cache.  FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are
    scaled by 256 MiB / (the same counter for a plain 256 MiB device copy in
    the same process).  They count L2-to-fabric traffic: L2 misses, which the
    Infinity Cache or HBM serve.
@@ -51,6 +51,7 @@ PASSES = {
                     "SQ_LDS_BANK_CONFLICT"],
     "sq_valu_wait": ["GRBM_GUI_ACTIVE", "SQ_WAVES", "SQ_INSTS_VALU", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_VMEM",
                      "SQ_ACTIVE_INST_ANY", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY"],
+    "sqc_icache": ["GRBM_GUI_ACTIVE", "SQ_IFETCH", "SQC_ICACHE_REQ", "SQC_ICACHE_MISSES"],
 }
 FLUSH = "FillFunctor<float>"
 COPY = "copyBuffer"
@@ -285,7 +286,8 @@ def profile(args, n):
     mfma_busy = avg(a, "SQ_VALU_MFMA_BUSY_CYCLES")
     mops = avg(a, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
     raw = {}
-    for name, ds in (("sq_mfma_lds", a), ("sq_valu_wait", b)):
+    ic = headline_dispatches(cnt["sqc_icache"], fused_name)
+    for name, ds in (("sq_mfma_lds", a), ("sq_valu_wait", b), ("sqc_icache", ic)):
         for ctr in PASSES[name]:
             raw[f"{name}.{ctr}"] = avg(ds, ctr)
         raw[f"{name}.duration_us"] = avg(ds, "_duration_ns") / 1e3
@@ -305,6 +307,9 @@ def profile(args, n):
         round(raw["sq_valu_wait.SQ_INSTS_VALU"] / raw["sq_valu_wait.SQ_WAVES"], 1),
         "lds_insts_per_wave": None if not raw["sq_valu_wait.SQ_WAVES"] else
         round(raw["sq_mfma_lds.SQ_INSTS_LDS"] / raw["sq_valu_wait.SQ_WAVES"], 1),
+        # instruction cache: misses per request of the SQCs (each shared by a pair of CUs)
+        "icache_miss_pct": None if not raw["sqc_icache.SQC_ICACHE_REQ"] else
+        round(100.0 * raw["sqc_icache.SQC_ICACHE_MISSES"] / raw["sqc_icache.SQC_ICACHE_REQ"], 2),
     }
     rec = {
         "workload": key,

@@ -316,6 +316,25 @@ int main() {
     // the unfused sequence keeps column partials per chunk of rows
     EXPECT(coda_workspace_size(M, N, K, &e, 1) > coda_workspace_size(M, N, K, &d, 1));
   }
+  {  // the side matrix read ahead: the first bf16 ADD_MAT / MUL_DGELU_TANH before any SWIGLU_PAIR
+    coda_epi_desc e = base_desc(N, K);
+    e.n_ops = 1;
+    e.ops[0].kind = CODA_OP_ADD_MAT; e.ops[0].in = P(0x40000000); e.ops[0].ld = N; e.ops[0].in_dtype = CODA_BF16;
+    e.ops[0].scalar = 1.0f;
+    EXPECT(coda_validate(A, B, M, N, K, &e, 0) == CODA_OK);
+    coda::Plan q = plan_of(M, N, K, e);
+    EXPECT(q.has_side && !q.has_ext);
+    EXPECT(!coda::plain_gemm_plan(q).has_side);
+    e.ops[0].in_dtype = CODA_F32; e.ops[0].ld = N;   // fp32 side matrices are read where used
+    EXPECT(!plan_of(M, N, K, e).has_side);
+    coda_epi_desc f = base_desc(N, K);
+    f.n_ops = 2; f.ldd = 264;   // N / 2 = 260 columns, rows 16-byte aligned
+    f.ops[0].kind = CODA_OP_SWIGLU_PAIR;
+    f.ops[1].kind = CODA_OP_ADD_MAT; f.ops[1].in = P(0x40000000); f.ops[1].ld = 264; f.ops[1].in_dtype = CODA_BF16;
+    f.ops[1].scalar = 1.0f;
+    EXPECT(coda_validate(A, B, M, N, K, &f, 0) == CODA_OK);
+    EXPECT(!plan_of(M, N, K, f).has_side);   // after SWIGLU_PAIR
+  }
   {  // the backward set does not follow a deferred row norm (fused and unfused)
     coda_epi_desc e = base_desc(N, K);
     e.n_ops = 2;
