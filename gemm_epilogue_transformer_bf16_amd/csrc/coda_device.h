@@ -39,31 +39,42 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
 // ---------------------------------------------------------------------------
 // Activations, written from their definitions with the identity
 // 0.5 * (1 + tanh(z)) = 1 / (1 + exp(-2z)), evaluated with the hardware
-// base-2 exponential and reciprocal (about 1 ulp each in fp32).
+// base-2 exponential and reciprocal (about 1 ulp each in fp32).  The constant
+// factors are folded: with z = sqrt(2/pi) (v + 0.044715 v^3),
+//   -2 z log2(e) = v (kG1 + kG3 v^2),
+// so GELU_tanh(v) = v / (1 + 2^(v (kG1 + kG3 v^2))) in 7 operations.
 // ---------------------------------------------------------------------------
-constexpr float kSqrt2OverPi = 0.7978845608028654f;   // sqrt(2/pi)
-constexpr float kGeluCubic = 0.044715f;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr double kSqrt2OverPiD = 0.79788456080286535588;   // sqrt(2 / pi)
+constexpr double kGeluCubicD = 0.044715;
+constexpr double kLog2eD = 1.44269504088896340736;
+constexpr float kG1 = float(-2.0 * kSqrt2OverPiD * kLog2eD);
+constexpr float kG3 = float(-2.0 * kSqrt2OverPiD * kGeluCubicD * kLog2eD);
+// d(2z)/dv = kD0 + kD2 v^2
+constexpr float kD0 = float(2.0 * kSqrt2OverPiD);
+constexpr float kD2 = float(2.0 * kSqrt2OverPiD * 3.0 * kGeluCubicD);
 
 __device__ __forceinline__ float sigmoid_f(float x) {
   // 1 / (1 + 2^(-x log2 e)); saturates cleanly to 0 / 1 at the extremes
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * kLog2e));
 }
 
-__device__ __forceinline__ float gelu_tanh_f(float v) {
-  const float z = kSqrt2OverPi * (v + kGeluCubic * v * v * v);
-  return v * sigmoid_f(2.0f * z);
+// s = sigmoid(2 z(v)) = 0.5 (1 + tanh(z(v)))
+__device__ __forceinline__ float gelu_gate_f(float v, float v2) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(v * fmaf(kG3, v2, kG1)));
 }
+
+__device__ __forceinline__ float gelu_tanh_f(float v) { return v * gelu_gate_f(v, v * v); }
 
 __device__ __forceinline__ float silu_f(float v) { return v * sigmoid_f(v); }
 
 // d/dp [0.5 p (1 + tanh(z(p)))] = s + 2 p s (1 - s) z'(p), with s = sigmoid(2 z)
-// (since 1 - tanh^2 = 4 s (1 - s)) and z'(p) = sqrt(2/pi) (1 + 3 * 0.044715 p^2).
+// (since 1 - tanh^2 = 4 s (1 - s)) and 2 z'(p) = kD0 + kD2 p^2.
 __device__ __forceinline__ float gelu_tanh_grad_f(float p) {
-  const float z = kSqrt2OverPi * (p + kGeluCubic * p * p * p);
-  const float s = sigmoid_f(2.0f * z);
-  const float dz = kSqrt2OverPi * (1.0f + 3.0f * kGeluCubic * p * p);
-  return s + 2.0f * p * s * (1.0f - s) * dz;
+  const float p2 = p * p;
+  const float s = gelu_gate_f(p, p2);
+  const float dz2 = p * fmaf(kD2, p2, kD0);   // 2 p z'(p)
+  return fmaf(dz2, s * (1.0f - s), s);
 }
 
 // ---------------------------------------------------------------------------
