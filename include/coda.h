@@ -93,7 +93,7 @@ typedef enum {
   CODA_A_KM = 1   /* A stored row-major [K x M] and used transposed: the X^T of a
                      weight gradient dW = X^T dY, X being [tokens x features] and
                      tokens the contraction; bf16 only, no RMS/LN_ROWSCALE, and
-                     M % 8 == 0 (the survey's backward set)                      */
+                     M % 8 == 0                                                 */
 } coda_a_layout;
 
 typedef enum {
@@ -159,7 +159,7 @@ typedef enum {
      against their spread.  Must be the first op and needs K > 0; at most one
      of RMS_ROWSCALE / LN_ROWSCALE. */
   CODA_OP_LN_ROWSCALE = 14,
-  /* reductions over the rows (the survey's backward set: the bias gradient of a
+  /* reductions over the rows (for the backward pass: the bias gradient of a
      layer is the column sum of its output gradient).  Each writes an fp32 value
      per column j < width to ((float*)out)[j*out_stride]: the sum over all M
      rows of the running value (COL_SUM) or of its square (COL_SUMSQ) at the

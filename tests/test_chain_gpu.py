@@ -1,4 +1,4 @@
-"""Cross-layer chain (the survey's NEXT-3): a layer's fp32 row sums of squares
+"""Cross-layer chain: a layer's fp32 row sums of squares
 (its ROW_SUMSQ output) feed the next layer's RMSNorm row scale, whose gain is
 folded into the weights, so the next layer's main loop is the plain GEMM.
 Checked against the fp64 oracle of the second layer on the stored output of
