@@ -18,10 +18,12 @@ INCLUDE = os.path.join(REPO, "include")
 OBJ_DIR = os.path.join(REPO, "_build", "obj")
 LIB_PATH = os.path.join(PKG_DIR, "libcoda.so")
 
+# the fused kernel's compilation units first (the longest compiles), so they
+# start together
 HIP_SOURCES = [
-    "coda_fused_t1.hip", "coda_fused_t2.hip", "coda_fused_t3.hip",
-    "coda_fused_tf32.hip", "coda_fused.hip", "coda_unfused.hip", "coda_fold.hip", "coda_api.hip",
-    "coda_noalloc.hip",
+    "coda_fused_t3n.hip", "coda_fused_t3.hip", "coda_fused_t1n.hip", "coda_fused_t1.hip",
+    "coda_fused_t2n.hip", "coda_fused_t2.hip", "coda_fused_tf32.hip", "coda_fused.hip", "coda_unfused.hip",
+    "coda_fold.hip", "coda_api.hip", "coda_noalloc.hip",
 ]
 CPP_SOURCES = ["coda_plan.cpp"]
 

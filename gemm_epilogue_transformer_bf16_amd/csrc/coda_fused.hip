@@ -87,10 +87,20 @@ int launch_args(const Plan& p, const dev::FusedArgs& a, hipStream_t stream) {
   if (p.ab_dtype == CODA_F32) {
     return dev::launch_tile_f32(a, nwg, bkn, norm, akm, ext, side, stream);
   }
+  if (norm != dev::kNormNone) {
+    switch (p.tile) {
+      case 1: return dev::launch_tile1_norm(a, nwg, bkn, norm, stream);
+      case 2: return dev::launch_tile2_norm(a, nwg, bkn, norm, stream);
+      case 3: return dev::launch_tile3_norm(a, nwg, bkn, norm, stream);
+      default:
+        set_error("no kernel for tile config %d", p.tile);
+        return CODA_ERR_UNSUPPORTED;
+    }
+  }
   switch (p.tile) {
-    case 1: return dev::launch_tile1(a, nwg, bkn, norm, akm, ext, side, stream);
-    case 2: return dev::launch_tile2(a, nwg, bkn, norm, akm, ext, side, stream);
-    case 3: return dev::launch_tile3(a, nwg, bkn, norm, akm, ext, side, stream);
+    case 1: return dev::launch_tile1(a, nwg, bkn, akm, ext, side, stream);
+    case 2: return dev::launch_tile2(a, nwg, bkn, akm, ext, side, stream);
+    case 3: return dev::launch_tile3(a, nwg, bkn, akm, ext, side, stream);
     default:
       set_error("no kernel for tile config %d", p.tile);
       return CODA_ERR_UNSUPPORTED;

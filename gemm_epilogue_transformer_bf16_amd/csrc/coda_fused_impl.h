@@ -1698,7 +1698,7 @@ int launch_cfg(const FusedArgs& args, int64_t nwg, hipStream_t stream) {
 // host (no workload pairs them), which keeps the norm kernels' registers to
 // what their own ops need.
 template <int BM, int BN, int WM, int WN, bool F32, bool BKN>
-int launch_norms(const FusedArgs& args, int64_t nwg, int norm, bool ext, bool side, hipStream_t s) {
+int launch_norms(const FusedArgs& args, int64_t nwg, int norm, hipStream_t s) {
   switch (norm) {
     case kNormRms: return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormRms, false, false>>(args, nwg, s);
     case kNormLn: return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormLn, false, false>>(args, nwg, s);
@@ -1706,38 +1706,58 @@ int launch_norms(const FusedArgs& args, int64_t nwg, int norm, bool ext, bool si
     case kNormRmsGiven: return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormRmsGiven, false, false>>(args, nwg, s);
     case kNormLnB: return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormLnB, false, false>>(args, nwg, s);
     case kNormLnGiven: return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormLnGiven, false, false>>(args, nwg, s);
-    default:
-      if (ext) return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormNone, false, true, true>>(args, nwg, s);
-      return side ? launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormNone, false, false, true>>(args, nwg, s)
-                  : launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormNone, false, false>>(args, nwg, s);
+    default: return CODA_ERR_UNSUPPORTED;
   }
+}
+
+// The kernels with a deferred row norm (one per norm kind and B layout).
+template <int BM, int BN, int WM, int WN, bool F32>
+int launch_norm_variants(const FusedArgs& args, int64_t nwg, bool bkn, int norm, hipStream_t s) {
+  return bkn ? launch_norms<BM, BN, WM, WN, F32, true>(args, nwg, norm, s)
+             : launch_norms<BM, BN, WM, WN, F32, false>(args, nwg, norm, s);
+}
+
+// The kernels without a row norm: A stored [M x K] or [K x M], with or
+// without the backward set (ext) and the side-matrix read-ahead (side).
+template <int BM, int BN, int WM, int WN, bool F32, bool BKN>
+int launch_plain_b(const FusedArgs& args, int64_t nwg, bool akm, bool ext, bool side, hipStream_t s) {
+  if constexpr (!F32) {
+    if (akm) {   // A stored [K x M]: no row norm (validated on the host)
+      return ext ? launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormNone, true, true, true>>(args, nwg, s)
+                 : launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormNone, true, false, true>>(args, nwg, s);
+    }
+  }
+  if (ext) return launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormNone, false, true, true>>(args, nwg, s);
+  return side ? launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormNone, false, false, true>>(args, nwg, s)
+              : launch_cfg<Cfg<BM, BN, WM, WN, F32, BKN, kNormNone, false, false>>(args, nwg, s);
 }
 
 template <int BM, int BN, int WM, int WN, bool F32>
-int launch_variants(const FusedArgs& args, int64_t nwg, bool bkn, int norm, bool akm, bool ext, bool side,
-                    hipStream_t s) {
-  if constexpr (!F32) {
-    if (akm) {   // A stored [K x M]: no row norm (validated on the host)
-      if (ext)
-        return bkn ? launch_cfg<Cfg<BM, BN, WM, WN, F32, true, kNormNone, true, true, true>>(args, nwg, s)
-                   : launch_cfg<Cfg<BM, BN, WM, WN, F32, false, kNormNone, true, true, true>>(args, nwg, s);
-      return bkn ? launch_cfg<Cfg<BM, BN, WM, WN, F32, true, kNormNone, true, false, true>>(args, nwg, s)
-                 : launch_cfg<Cfg<BM, BN, WM, WN, F32, false, kNormNone, true, false, true>>(args, nwg, s);
-    }
-  }
-  return bkn ? launch_norms<BM, BN, WM, WN, F32, true>(args, nwg, norm, ext, side, s)
-             : launch_norms<BM, BN, WM, WN, F32, false>(args, nwg, norm, ext, side, s);
+int launch_plain_variants(const FusedArgs& args, int64_t nwg, bool bkn, bool akm, bool ext, bool side,
+                          hipStream_t s) {
+  return bkn ? launch_plain_b<BM, BN, WM, WN, F32, true>(args, nwg, akm, ext, side, s)
+             : launch_plain_b<BM, BN, WM, WN, F32, false>(args, nwg, akm, ext, side, s);
 }
 
-// one function per compiled tile configuration (defined in coda_fused_t*.hip)
-int launch_tile1(const FusedArgs& a, int64_t nwg, bool bkn, int norm, bool akm, bool ext, bool side,
-                 hipStream_t s);
-int launch_tile2(const FusedArgs& a, int64_t nwg, bool bkn, int norm, bool akm, bool ext, bool side,
-                 hipStream_t s);
-int launch_tile3(const FusedArgs& a, int64_t nwg, bool bkn, int norm, bool akm, bool ext, bool side,
-                 hipStream_t s);
+// every variant of one tile configuration
+template <int BM, int BN, int WM, int WN, bool F32>
+int launch_variants(const FusedArgs& args, int64_t nwg, bool bkn, int norm, bool akm, bool ext, bool side,
+                    hipStream_t s) {
+  if (norm == kNormNone) return launch_plain_variants<BM, BN, WM, WN, F32>(args, nwg, bkn, akm, ext, side, s);
+  return launch_norm_variants<BM, BN, WM, WN, F32>(args, nwg, bkn, norm, s);
+}
+
+// per compiled tile configuration (bf16 configurations 1 - 3, defined in
+// coda_fused_t<n>.hip without a row norm and coda_fused_t<n>n.hip with one,
+// so that the two halves compile in parallel; fp32 in coda_fused_tf32.hip)
+int launch_tile1(const FusedArgs& a, int64_t nwg, bool bkn, bool akm, bool ext, bool side, hipStream_t s);
+int launch_tile2(const FusedArgs& a, int64_t nwg, bool bkn, bool akm, bool ext, bool side, hipStream_t s);
+int launch_tile3(const FusedArgs& a, int64_t nwg, bool bkn, bool akm, bool ext, bool side, hipStream_t s);
+int launch_tile1_norm(const FusedArgs& a, int64_t nwg, bool bkn, int norm, hipStream_t s);
+int launch_tile2_norm(const FusedArgs& a, int64_t nwg, bool bkn, int norm, hipStream_t s);
+int launch_tile3_norm(const FusedArgs& a, int64_t nwg, bool bkn, int norm, hipStream_t s);
 int launch_tile_f32(const FusedArgs& a, int64_t nwg, bool bkn, int norm, bool akm, bool ext, bool side,
-                 hipStream_t s);
+                    hipStream_t s);
 
 }  // namespace dev
 }  // namespace coda
