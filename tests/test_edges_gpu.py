@@ -168,6 +168,27 @@ def test_every_op_fused(CR, layout, tile):
 
 
 @pytest.mark.parametrize("layout", ["KN", "NK"])
+@pytest.mark.parametrize("tile", [1, 2, 3])
+def test_every_op_no_norm(CR, layout, tile):
+    # without a row norm the list runs in the kernels that read the first bf16
+    # side matrix ahead (here ADD_MAT), while the fp32 one (MUL_DGELU_TANH) is
+    # read where it is used
+    announce(f"every op, no row norm, {layout} tile{tile}")
+    rng = np.random.default_rng(23)
+    M, N, K = 300, 264, 136
+    a = rng.standard_normal((M, K))
+    b = rng.standard_normal((K, N)) / np.sqrt(K)
+    A = bf16(a)
+    B = bf16(b if layout == "KN" else np.ascontiguousarray(b.T))
+    ops, outs = every_op_program(M, N, K, rng, use_rms=False)
+    call = run(CR, A, B, ops, layout, tile=tile)
+    ref, reds = oracle.forward(f64(A), f64(B), oracle_ops(ops), layout)
+    assert_close(f64(call.D), ref, "every-op (no norm) D")
+    for i, (_, _, r) in enumerate(reds):
+        assert_close(f64(outs)[:, i], r, f"every-op (no norm) reduction {i}")
+
+
+@pytest.mark.parametrize("layout", ["KN", "NK"])
 def test_every_op_f32_operands(CR, layout):
     announce(f"every op f32 operands {layout}")
     rng = np.random.default_rng(22)
