@@ -387,6 +387,8 @@ def main():
                          "the other placement is timed beside it either way")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unfused", action="store_true")
+    ap.add_argument("--no-vendor", action="store_true",
+                    help="skip the torch.matmul timing of the plain product (reported for context)")
     ap.add_argument("--all", action="store_true",
                     help="every synthetic layer in turn: one line with each layer's fused, unfused and plain-GEMM "
                          "medians, speedups beside the ceilings, and their geometric mean")
@@ -476,6 +478,17 @@ def measure_workload(args, workload: int, cpu_baseline_on: bool = True):
             # the other placement of the norm's gain, for comparison (not the headline)
             other = runner.WorkloadCall(spec, inputs, tile=args.tile, fold_gain=not fold)
             fns["other"] = other.fused
+    if not args.no_unfused and not args.no_vendor:
+        # context only: the vendor library's plain product of the same operands
+        # (torch.matmul; B stored [N x K] is given to it transposed once, here)
+        va = tensors[spec.a_name]
+        vb = tensors[spec.b_name] if spec.b_layout == "KN" else tensors[spec.b_name].t().contiguous()
+        vd = torch.empty((spec.M, spec.N), dtype=va.dtype, device=va.device)
+
+        def vendor_gemm():
+            torch.matmul(va, vb, out=vd)
+            return 0
+        fns["vendor"] = vendor_gemm
     timer = Timer(args)
     print(f"[bench] {', '.join(fns)}: warm-up >= {args.warmup} rounds and {args.warmup_seconds} s, "
           f"then {args.steps} timed rounds", file=sys.stderr, flush=True)
@@ -514,6 +527,10 @@ def measure_workload(args, workload: int, cpu_baseline_on: bool = True):
         extra["unfused_over_plain"] = round(umed / pmed, 3)
     if other is not None:
         extra[("fused_in_loop_gain_ms" if fold else "fused_folded_gain_ms")] = stats(t["other"])
+    if "vendor" in t:
+        extra["vendor_gemm_ms"] = stats(t["vendor"])
+        extra["plain_over_vendor"] = round(float(np.median(t["plain"])) / float(np.median(t["vendor"])), 3)
+        extra["vendor_gemm"] = "torch.matmul, the plain product only (context, not a baseline of the speedup)"
     return result_line(args, timer, flops, t["fused"], t.get("unfused"), config, peak, alg_bytes, cpu,
                        traffic=traffic, counter_clock=counter_clock, extra=extra)
 
@@ -542,6 +559,7 @@ def bench_all(args):
             "tflops": line["value"], "pct_peak": line["pct_peak"],
             "ceiling_at_8_and_5_TBps": CEILING.get(wl),
             "fused_p10_p90": [line["fused_ms"]["p10"], line["fused_ms"]["p90"]],
+            "vendor_gemm_ms": line.get("vendor_gemm_ms", {}).get("median"),
         })
         print(f"[bench] {WORKLOAD_KEY[wl]}: fused {rows[-1]['fused_ms']} ms, unfused {rows[-1]['unfused_ms']} ms, "
               f"plain {rows[-1]['plain_gemm_ms']} ms", file=sys.stderr, flush=True)

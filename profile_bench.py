@@ -120,7 +120,8 @@ def trace_table(db):
 
 
 def summarize_trace(db, line, khash):
-    # the bench's round order: fused, unfused sequence, plain GEMM, other gain placement
+    # the bench's round order: fused, unfused sequence, plain GEMM, other gain placement,
+    # the vendor library's plain product
     variants = ["fused"]
     if line.get("unfused_ms") is not None:
         variants.append("unfused")
@@ -129,6 +130,8 @@ def summarize_trace(db, line, khash):
     other = [k for k in ("fused_in_loop_gain_ms", "fused_folded_gain_ms") if k in line]
     if other:
         variants.append(other[0][:-3])
+    if line.get("vendor_gemm_ms") is not None:
+        variants.append("vendor_gemm")
     steps = timed_steps(db, line["steps"], len(variants))
     per = collections.defaultdict(list)
     names = collections.defaultdict(collections.Counter)

@@ -104,3 +104,23 @@ def test_summarize_trace_variants_and_bench_stats(tmp_path):
     assert set(rec) == {"fused", "unfused", "plain_gemm", "fused_in_loop_gain"}
     # the last three rounds: fused durations 703, 704, 705 ns
     assert abs(rec["fused"]["trace_mean_ms"] - 704e-6) < 1e-9
+
+
+def test_summarize_trace_with_vendor_leg(tmp_path):
+    import profile_bench as pb
+    db = str(tmp_path / "t.db")
+    _trace_db(db, rounds=5, variants=5)
+    c = sqlite3.connect(db)
+    c.execute("create table top_kernels (name text, total_calls integer, total_duration real, average real, "
+              "percentage real)")
+    c.commit()
+    c.close()
+    st = {"median": 1.0, "mean": 1.0, "p10": 1.0, "p90": 1.0}
+    line = {"steps": 2, "fused_ms": st, "unfused_ms": st, "plain_gemm_ms": st, "fused_folded_gain_ms": st,
+            "vendor_gemm_ms": st, "value": 1.0, "unit": "TFLOP/s", "speedup_vs_unfused": 1.0,
+            "config": {"workload": pb.bench.WORKLOAD_TEXT[4], "tile": 3}}
+    text, fused_name, rec = pb.summarize_trace(db, line, "0" * 16)
+    assert list(rec) == ["fused", "unfused", "plain_gemm", "fused_folded_gain", "vendor_gemm"]
+    # the vendor leg is the fifth step of each round: rounds 3 and 4 of variant 4
+    assert abs(rec["vendor_gemm"]["trace_mean_ms"] - 743.5e-6) <= 0.5e-6   # rounded to 1 ns
+    assert "vendor_gemm" in text
