@@ -5,6 +5,8 @@
 
 namespace coda {
 
+// the kernel's split finalization holds one slot per part
+static_assert(kMaxSplit <= dev::kMaxSplitParts, "split parts beyond the kernel's slots");
 
 namespace {
 

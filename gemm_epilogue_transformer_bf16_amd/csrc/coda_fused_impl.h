@@ -613,6 +613,30 @@ __device__ __forceinline__ void store_packed(const u32x4_t (&w)[C::CPL], KArgs a
   }
 }
 
+// Parts of a tile split over K: at most this many (the plan's limit)
+constexpr int kMaxSplitParts = 4;
+
+// The sum p[0] + p[stride] + ... + p[(n - 1) stride], added in index order (so
+// the result does not depend on which workgroup adds), read with agent-scope
+// loads.  Those loads go to the memory side of the XCD L2s, about a
+// microsecond each, so they go out eight at a time ahead of their adds: one
+// round trip per eight partials, not one per partial.  (Adding 0 in place of a
+// missing partial leaves the sum unchanged: it starts at +0 and never becomes
+// -0.)
+__device__ __forceinline__ float sum_partials(const float* p, long long stride, int n) {
+  float v = 0.0f;
+  for (int i = 0; i < n; i += 8) {
+    float t[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      t[j] = i + j < n ? __hip_atomic_load(p + (long long)(i + j) * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                       : 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v += t[j];
+  }
+  return v;
+}
+
 __device__ __forceinline__ void write_reduction(KOp op, int row, float v) {
   if (op.kind == CODA_OP_ROW_MEAN) v = v / float(op.width);
   op.out[(long long)row * op.out_stride] = v;
@@ -1298,47 +1322,100 @@ fused_kernel(FusedArgs args) {
       __syncthreads();
       if (*last == 0) return;
       // the parts in part order (this part's own values from its registers)
-      static_for<0, NG>([&](auto gc) {
-        constexpr int gi = decltype(gc)::value;
-        constexpr int mi = gi / (NI * 8), ni = (gi / 8) % NI, g = gi % 8;
-        float s0 = 0.0f, s1 = 0.0f;
-        for (int pp = 0; pp < S; ++pp) {
-          float v0 = acc[mi][ni][2 * g], v1 = acc[mi][ni][2 * g + 1];
-          if (pp != part) {
-            const unsigned long long bits = __hip_atomic_load(accp + ((slot0 + pp) * NG + gi) * C::NT,
-                                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            v0 = __uint_as_float(uint32_t(bits));
-            v1 = __uint_as_float(uint32_t(bits >> 32));
+      if constexpr (C::RMS) {
+        // one pair at a time: the in-loop row norm's kernels sit at the
+        // register limit, and the batches below make them spill
+        static_for<0, NG>([&](auto gc) {
+          constexpr int gi = decltype(gc)::value;
+          constexpr int mi = gi / (NI * 8), ni = (gi / 8) % NI, g = gi % 8;
+          float s0 = 0.0f, s1 = 0.0f;
+          for (int pp = 0; pp < S; ++pp) {
+            float v0 = acc[mi][ni][2 * g], v1 = acc[mi][ni][2 * g + 1];
+            if (pp != part) {
+              const unsigned long long bits = __hip_atomic_load(accp + ((slot0 + pp) * NG + gi) * C::NT,
+                                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              v0 = __uint_as_float(uint32_t(bits));
+              v1 = __uint_as_float(uint32_t(bits >> 32));
+            }
+            s0 = pp == 0 ? v0 : s0 + v0;
+            s1 = pp == 0 ? v1 : s1 + v1;
           }
-          s0 = pp == 0 ? v0 : s0 + v0;
-          s1 = pp == 0 ? v1 : s1 + v1;
-        }
-        acc[mi][ni][2 * g] = s0;
-        acc[mi][ni][2 * g + 1] = s1;
-      });
+          acc[mi][ni][2 * g] = s0;
+          acc[mi][ni][2 * g + 1] = s1;
+        });
+      } else {
+        // the other parts' values of PB register pairs are loaded together, so a
+        // batch costs one round trip to the memory side
+        constexpr int PB = 8;
+        static_assert(NG % PB == 0, "register pairs come in whole batches");
+        static_for<0, NG / PB>([&](auto bc) {
+          constexpr int b = decltype(bc)::value;
+          // (scheduling barriers keep each batch's loads next to its adds)
+          __builtin_amdgcn_sched_barrier(0);
+          unsigned long long t[kMaxSplitParts][PB];
+          static_for<0, kMaxSplitParts>([&](auto pc) {
+            constexpr int pp = decltype(pc)::value;
+            if (pp < S && pp != part) {
+#pragma unroll
+              for (int j = 0; j < PB; ++j)
+                t[pp][j] = __hip_atomic_load(accp + ((slot0 + pp) * NG + PB * b + j) * C::NT, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+            }
+          });
+          static_for<0, PB>([&](auto jc) {
+            constexpr int gi = PB * b + decltype(jc)::value;
+            constexpr int mi = gi / (NI * 8), ni = (gi / 8) % NI, g = gi % 8;
+            const float own0 = acc[mi][ni][2 * g], own1 = acc[mi][ni][2 * g + 1];
+            float s0 = 0.0f, s1 = 0.0f;
+            static_for<0, kMaxSplitParts>([&](auto pc) {
+              constexpr int pp = decltype(pc)::value;
+              if (pp < S) {
+                float v0 = own0, v1 = own1;
+                if (pp != part) {
+                  const unsigned long long bits = t[pp][decltype(jc)::value];
+                  v0 = __uint_as_float(uint32_t(bits));
+                  v1 = __uint_as_float(uint32_t(bits >> 32));
+                }
+                s0 = pp == 0 ? v0 : s0 + v0;
+                s1 = pp == 0 ? v1 : s1 + v1;
+              }
+            });
+            acc[mi][ni][2 * g] = s0;
+            acc[mi][ni][2 * g + 1] = s1;
+          });
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      }
       if constexpr (C::RMS) {
         // whole-row sums in part order, on the first lane of each row (the row
         // sum below adds the zeros of the other lanes)
 #pragma unroll
         for (int i = 0; i < C::A_BPW; ++i) {
           const int row = 8 * (wave + C::NW * i) + (lane >> 3);
+          float x[kMaxSplitParts];
+#pragma unroll
+          for (int pp = 0; pp < kMaxSplitParts; ++pp)
+            if (pp < S)
+              x[pp] = __hip_atomic_load(a->split_ss + (slot0 + pp) * BM + row, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
           float t = 0.0f;
-          for (int pp = 0; pp < S; ++pp) {
-            const float v =
-                __hip_atomic_load(a->split_ss + (slot0 + pp) * BM + row, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            t = pp == 0 ? v : t + v;
-          }
+#pragma unroll
+          for (int pp = 0; pp < kMaxSplitParts; ++pp)
+            if (pp < S) t = pp == 0 ? x[pp] : t + x[pp];
           ss[i] = (lane & 7) == 0 ? t : 0.0f;
         }
       } else if constexpr (C::SSF) {
         // whole-row sums in part order, left in the first wave column's LDS row
         for (int t = tid; t < BM; t += C::NT) {
+          float x[kMaxSplitParts];
+#pragma unroll
+          for (int pp = 0; pp < kMaxSplitParts; ++pp)
+            if (pp < S)
+              x[pp] = __hip_atomic_load(a->split_ss + (slot0 + pp) * BM + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           float v = 0.0f;
-          for (int pp = 0; pp < S; ++pp) {
-            const float x =
-                __hip_atomic_load(a->split_ss + (slot0 + pp) * BM + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            v = pp == 0 ? x : v + x;
-          }
+#pragma unroll
+          for (int pp = 0; pp < kMaxSplitParts; ++pp)
+            if (pp < S) v = pp == 0 ? x[pp] : v + x[pp];
           smem_ss[t] = v;
 #pragma unroll
           for (int w = 1; w < C::WN; ++w) smem_ss[w * BM + t] = 0.0f;
@@ -1594,10 +1671,7 @@ fused_kernel(FusedArgs args) {
           for (int t = tid; t < BM; t += C::NT) {
             const int row = m0 + t;
             if (row >= M) continue;
-            float v = 0.0f;
-            for (int tn = 0; tn < a->grid_n; ++tn)
-              v += __hip_atomic_load(a->partials + ((long long)s * a->grid_n + tn) * M + row, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
+            const float v = sum_partials(a->partials + (long long)s * a->grid_n * M + row, M, a->grid_n);
             write_reduction(op, row, v);
           }
         }
@@ -1659,10 +1733,7 @@ fused_kernel(FusedArgs args) {
           for (int t = tid; t < cols; t += C::NT) {
             const int col = c0 + t;
             if (col >= op.width) continue;
-            float v = 0.0f;
-            for (int tm = 0; tm < a->grid_m; ++tm)
-              v += __hip_atomic_load(a->col_partials + ((long long)s * a->grid_m + tm) * N + col, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
+            const float v = sum_partials(a->col_partials + (long long)s * a->grid_m * N + col, N, a->grid_m);
             op.out[(long long)col * op.out_stride] = v;
           }
         }
