@@ -615,6 +615,18 @@ __device__ __forceinline__ void store_packed(const u32x4_t (&w)[C::CPL], KArgs a
 
 // Parts of a tile split over K: at most this many (the plan's limit)
 constexpr int kMaxSplitParts = 4;
+// cache policy of a buffer load: sc1, coherent at agent scope (the policy of
+// this target's agent-scope atomic loads)
+constexpr int kCachePolicySc1 = 16;
+
+// Register pairs per round trip when a split tile's partials come through LDS:
+// the largest of 8, 4, 2, 1 whose chunk (pairs x threads x 8 bytes) fits a
+// part's LDS slot and divides the pairs
+constexpr int split_chunk_pairs(int slot_bytes, int nt, int pairs) {
+  int c = 8;
+  while (c > 1 && (c * nt * 8 > slot_bytes || pairs % c != 0)) c /= 2;
+  return c;
+}
 
 // The sum p[0] + p[stride] + ... + p[(n - 1) stride], added in index order (so
 // the result does not depend on which workgroup adds), read with agent-scope
@@ -1323,26 +1335,57 @@ fused_kernel(FusedArgs args) {
       if (*last == 0) return;
       // the parts in part order (this part's own values from its registers)
       if constexpr (C::RMS) {
-        // one pair at a time: the in-loop row norm's kernels sit at the
-        // register limit, and the batches below make them spill
-        static_for<0, NG>([&](auto gc) {
-          constexpr int gi = decltype(gc)::value;
-          constexpr int mi = gi / (NI * 8), ni = (gi / 8) % NI, g = gi % 8;
-          float s0 = 0.0f, s1 = 0.0f;
-          for (int pp = 0; pp < S; ++pp) {
-            float v0 = acc[mi][ni][2 * g], v1 = acc[mi][ni][2 * g + 1];
-            if (pp != part) {
-              const unsigned long long bits = __hip_atomic_load(accp + ((slot0 + pp) * NG + gi) * C::NT,
-                                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              v0 = __uint_as_float(uint32_t(bits));
-              v1 = __uint_as_float(uint32_t(bits >> 32));
+        // The in-loop row norm's kernels sit at the register limit, so the
+        // other parts' partials come through LDS instead (the stages are free
+        // now): direct loads of CH register pairs of every part per round trip,
+        // agent-scope coherent like the atomic loads (sc1), then the sums in
+        // part order from LDS.  Part pp's slot: array pp / 2, half pp % 2.
+        constexpr int SLOT = (C::ARR0_BYTES < C::ARR1_BYTES ? C::ARR0_BYTES : C::ARR1_BYTES) / 2;
+        constexpr int CH = split_chunk_pairs(SLOT, C::NT, NG);
+        constexpr int KB_PER_PART = CH * C::NT * 8 / 1024;   // 1 KB direct loads per part and chunk
+        static_assert(NG % CH == 0 && KB_PER_PART % C::NW == 0 && CH * C::NT * 8 <= SLOT, "split chunk layout");
+        static_for<0, NG / CH>([&](auto cc) {
+          constexpr int c = decltype(cc)::value;
+          __syncthreads();   // every read of the previous chunk (or of the flag) is done
+          static_for<0, kMaxSplitParts>([&](auto pc) {
+            constexpr int pp = decltype(pc)::value;
+            if (pp < S && pp != part) {
+              char* slot = (pp < 2 ? smem0 : smem1) + (pp & 1) * SLOT;
+              const char* src = reinterpret_cast<const char*>(accp - tid) +
+                                (((slot0 + pp) * NG + size_t(CH) * c) * C::NT) * 8;
+              const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, CH * C::NT * 8);
+#pragma unroll
+              for (int i = 0; i < KB_PER_PART / C::NW; ++i) {
+                const int k = wave + C::NW * i;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LdsPtr)(slot + k * 1024), 16, k * 1024 + lane * 16, 0,
+                                                         0, kCachePolicySc1);
+              }
             }
-            s0 = pp == 0 ? v0 : s0 + v0;
-            s1 = pp == 0 ? v1 : s1 + v1;
-          }
-          acc[mi][ni][2 * g] = s0;
-          acc[mi][ni][2 * g + 1] = s1;
+          });
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+          __syncthreads();
+          static_for<0, CH>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            constexpr int gi = CH * c + j;
+            constexpr int mi = gi / (NI * 8), ni = (gi / 8) % NI, g = gi % 8;
+            float s0 = 0.0f, s1 = 0.0f;
+            for (int pp = 0; pp < S; ++pp) {
+              float v0 = acc[mi][ni][2 * g], v1 = acc[mi][ni][2 * g + 1];
+              if (pp != part) {
+                const char* slot = (pp < 2 ? smem0 : smem1) + (pp & 1) * SLOT;
+                const unsigned long long bits =
+                    *reinterpret_cast<const unsigned long long*>(slot + (j * C::NT + tid) * 8);
+                v0 = __uint_as_float(uint32_t(bits));
+                v1 = __uint_as_float(uint32_t(bits >> 32));
+              }
+              s0 = pp == 0 ? v0 : s0 + v0;
+              s1 = pp == 0 ? v1 : s1 + v1;
+            }
+            acc[mi][ni][2 * g] = s0;
+            acc[mi][ni][2 * g + 1] = s1;
+          });
         });
+        __syncthreads();   // the slots' last reads are done before the epilogue's LDS use
       } else {
         // the other parts' values of PB register pairs are loaded together, so a
         // batch costs one round trip to the memory side
