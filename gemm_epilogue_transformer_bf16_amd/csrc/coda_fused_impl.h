@@ -185,11 +185,8 @@ struct Cfg {
   // SSF: per-row partial sums of squares, one row of BM per wave column
   // (LNF: then the row sums [WN][BM] and the per-row shift [BM])
   static constexpr int SS_BYTES = (SSF && !F32) ? (LNF ? 2 * WN + 1 : WN) * BM * 4 : 16;
-  // (arrays a variant never touches are dropped by the compiler: the sums array
-  // without SSF, the 256-byte warm-up word with RMS)
-  static_assert(ARR0_BYTES + ARR1_BYTES + (SSF ? SS_BYTES : 0) + (RMS ? 0 : 256) <=
-                    160 * 1024,
-                "LDS budget");
+  // (the compiler drops the sums array from variants without SSF)
+  static_assert(ARR0_BYTES + ARR1_BYTES + (SSF ? SS_BYTES : 0) <= 160 * 1024, "LDS budget");
   static_assert(CPR >= 4 && CPR <= 16 && (CPR & (CPR - 1)) == 0, "epilogue lane layout");
 };
 
@@ -667,7 +664,6 @@ fused_kernel(FusedArgs args) {
   __shared__ __attribute__((aligned(1024))) char smem0[C::ARR0_BYTES];
   __shared__ __attribute__((aligned(1024))) char smem1[C::ARR1_BYTES];
   __shared__ __attribute__((aligned(16))) float smem_ss[C::SS_BYTES / 4];
-  __shared__ __attribute__((aligned(256))) char smem_warm[256];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -821,46 +817,6 @@ fused_kernel(FusedArgs args) {
         for (int i = 0; i < C::B_BPW; ++i) {
           const int q = wave + C::NW * i;
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (LdsPtr)(Bs + q * 1024), 16, (int)(b_off[i] | kmask), 0, 0, 0);
-        }
-      }
-    };
-
-    // Side matrix of the epilogue (the first ADD_MAT / MUL_DGELU_TANH): its
-    // tile is touched during the last 8 K steps, one eighth of the rows per
-    // step, by direct loads into a scratch LDS word, so that the epilogue finds
-    // it in cache and its HBM traffic overlaps the matrix work.
-    int warm_op = -1;
-    if constexpr (!C::RMS) {
-      for (int q = 0; q < a->n_ops; ++q) {
-        const int k = a->ops[q].kind;
-        if (k == CODA_OP_SWIGLU_PAIR) break;
-        if (k == CODA_OP_ADD_MAT || k == CODA_OP_MUL_DGELU_TANH) {
-          warm_op = q;
-          break;
-        }
-      }
-    }
-    auto warm = [&](int chunk) {
-      KOp op = a->ops[warm_op];
-      const int es = op.dtype == CODA_F32 ? 4 : 2;
-      const char* base = static_cast<const char*>(op.in) + (long long)m0 * op.ld * es;
-      const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, ((long long)(M - 1 - m0) * op.ld + op.width) * es);
-      constexpr int ROWS = BM / 8;
-      const int row_bytes = BN * es;
-      const int segs = ROWS * row_bytes / 64;
-      for (int s = tid; s < segs; s += C::NT) {
-        const int r = chunk * ROWS + (s * 64) / row_bytes;
-        const int cb = (s * 64) % row_bytes;
-        const uint32_t off = uint32_t(r) * uint32_t(op.ld * es) + uint32_t(n0 * es + cb);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LdsPtr)smem_warm, 4, (int)off, 0, 0, 0);
-      }
-    };
-    auto warm_step = [&](int kt) {
-      if constexpr (!C::RMS) {
-        if (warm_op >= 0) {
-          const int c = kt + 8 - KT;
-          if (c >= 0)
-            for (int cc = (kt == 0 ? 0 : c); cc <= c; ++cc) warm(cc);
         }
       }
     };
@@ -1097,7 +1053,6 @@ fused_kernel(FusedArgs args) {
         if constexpr (!C::RMS) load_a(kt + 1, nxt);
         load_b(kt + 1, nxt);
       }
-      warm_step(kt);
       if constexpr (C::RMS) {
         if (more && convert_first) convert_phase(kt, nxt);
       }
