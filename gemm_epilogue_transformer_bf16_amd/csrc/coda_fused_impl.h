@@ -571,45 +571,6 @@ __device__ __forceinline__ void store_chunks(const Chunks<C::CPL>& ch, KArgs a, 
   }
 }
 
-// D rounded to bf16 and packed, one 16-byte word group per chunk (4 words, or
-// 2 after SWIGLU_PAIR), for a store issued later
-template <class C, bool PAIRED>
-__device__ __forceinline__ void pack_chunks(const Chunks<C::CPL>& ch, u32x4_t (&dst)[C::CPL]) {
-#pragma unroll
-  for (int j = 0; j < C::CPL; ++j)
-#pragma unroll
-    for (int e = 0; e < (PAIRED ? 2 : 4); ++e) dst[j][e] = pack_bf16x2(ch.v[j][2 * e], ch.v[j][2 * e + 1]);
-}
-
-// the store of pack_chunks's words: rows m0 + mloc(j), first column col (of
-// the output's width)
-template <class C>
-__device__ __forceinline__ void store_packed(const u32x4_t (&w)[C::CPL], KArgs a, int M, int m0, int mloc0,
-                                             int col, bool paired) {
-  const int width = a->out_width;
-  const int n = paired ? 4 : 8;
-#pragma unroll
-  for (int j = 0; j < C::CPL; ++j) {
-    const int row = m0 + mloc0 + C::RSTEP * j;
-    if (row >= M) continue;
-    uint16_t* d = static_cast<uint16_t*>(a->D) + (long long)row * a->ldd + col;
-    if (col + n - 1 < width) {
-      if (paired) {
-        u32x2_t v;
-        v[0] = w[j][0];
-        v[1] = w[j][1];
-        *reinterpret_cast<u32x2_t*>(d) = v;
-      } else {
-        *reinterpret_cast<u32x4_t*>(d) = w[j];
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (e < n && col + e < width) d[e] = uint16_t(w[j][e >> 1] >> (16 * (e & 1)));
-    }
-  }
-}
-
 // Parts of a tile split over K: at most this many (the plan's limit)
 constexpr int kMaxSplitParts = 4;
 // cache policy of a buffer load: sc1, coherent at agent scope (the policy of
@@ -1550,14 +1511,6 @@ fused_kernel(FusedArgs args) {
     KOp op = a->ops[cv_op];
     load_cols<false>(op.in, op.dtype, n0 + wn * C::WTN + 8 * (lane % C::CPR), op.width, cv);
   }
-  // With reductions across the workgroups of a tile row or column, the D
-  // stores wait until the partial sums are published: the publishing waits for
-  // every store this workgroup issued, and the tile's D stores (128 KB) would
-  // otherwise hold the CU until they drain to memory.
-  const bool defer = a->d_dtype == CODA_BF16 &&
-                     ((a->n_red > 0 && a->grid_n > 1) || (C::EXT && a->n_colred > 0 && a->grid_m > 1));
-  u32x4_t dpk[MI][C::CPL];
-  bool paired_out = false;
 
   static_for<0, MI>([&](auto mic) {
     constexpr int mi = decltype(mic)::value;
@@ -1610,12 +1563,9 @@ fused_kernel(FusedArgs args) {
     if (o < a->n_ops) {   // SWIGLU_PAIR
       swiglu_chunks<C>(ch);
       run_ops<C, true>(ch, a, o + 1, M, lane, wn, red, -1, pfb, colp, wm, mi, -1, cv, [] {});
-      paired_out = true;
-      if (defer) pack_chunks<C, true>(ch, dpk[mi]);
-      else store_chunks<C, true>(ch, a, M);
+      store_chunks<C, true>(ch, a, M);
     } else {
-      if (defer) pack_chunks<C, false>(ch, dpk[mi]);
-      else store_chunks<C, false>(ch, a, M);
+      store_chunks<C, false>(ch, a, M);
     }
   });
 
@@ -1739,16 +1689,6 @@ fused_kernel(FusedArgs args) {
         if (tid == 0) __hip_atomic_store(a->col_counters + tile_n, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
-  }
-
-  if (defer) {
-    const int c = lane % C::CPR;
-    const int col0 = n0 + wn * C::WTN + 8 * c;
-    static_for<0, MI>([&](auto mic) {
-      constexpr int mi = decltype(mic)::value;
-      store_packed<C>(dpk[mi], a, M, m0, wm * C::WTM + 32 * mi + lane / C::CPR, paired_out ? col0 >> 1 : col0,
-                      paired_out);
-    });
   }
 }
 
