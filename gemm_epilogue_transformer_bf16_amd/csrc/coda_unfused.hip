@@ -87,6 +87,15 @@ __global__ void __launch_bounds__(kPassThreads) rownorm_kernel(const void* X, lo
 
 // ---- one elementwise op per pass; each thread owns 8 consecutive input columns ----
 __device__ __forceinline__ void load8(const void* p, int dtype, long long i, long long limit, float (&v)[8]) {
+  if (dtype == CODA_BF16 && i + 7 < limit) {   // the group's 16 bytes in one access
+    const u32x4_t w = *reinterpret_cast<const u32x4_t*>(static_cast<const uint16_t*>(p) + i);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] = bf16_lo(w[e]);
+      v[2 * e + 1] = bf16_hi(w[e]);
+    }
+    return;
+  }
   float a[4], b[4];
   load4(p, dtype, i, limit, a);
   load4(p, dtype, i + 4, limit, b);
@@ -129,14 +138,16 @@ __device__ __forceinline__ void store_n(void* p, int dtype, long long i, long lo
   }
 }
 
+// IDX: the index type of the element groups (32-bit when they number under
+// 2^31, which keeps the row / column split of an index cheap)
+template <class IDX>
 __global__ void __launch_bounds__(kPassThreads) ew_kernel(const void* in, long long ldi, int width, int M,
                                                           void* out, long long ldo, int io_dtype, DevOp op) {
-  const long long groups_per_row = (width + 7) / 8;
-  const long long total = groups_per_row * M;
-  for (long long gid = blockIdx.x * (long long)kPassThreads + threadIdx.x; gid < total;
-       gid += (long long)gridDim.x * kPassThreads) {
+  const IDX groups_per_row = IDX((width + 7) / 8);
+  const IDX total = groups_per_row * IDX(M);
+  for (IDX gid = IDX(blockIdx.x) * kPassThreads + threadIdx.x; gid < total; gid += IDX(gridDim.x) * kPassThreads) {
     const int row = int(gid / groups_per_row);
-    const long long c = (gid % groups_per_row) * 8;
+    const long long c = (long long)(gid % groups_per_row) * 8;
     const int esz = io_dtype == CODA_BF16 ? 2 : 4;
     float v[8];
     load8(static_cast<const char*>(in) + (long long)row * ldi * esz, io_dtype, c, width, v);
@@ -412,8 +423,12 @@ int launch_unfused(const Plan& p, hipStream_t stream) {
     const int64_t groups = ((width + 7) / 8) * p.M;
     int64_t blocks = (groups + dev::kPassThreads - 1) / dev::kPassThreads;
     if (blocks > 65536) blocks = 65536;
-    hipLaunchKernelGGL(dev::ew_kernel, dim3((unsigned)blocks), dim3(dev::kPassThreads), 0, stream, cur,
-                       (long long)ldc, (int)width, M, dst, (long long)ldo, p.d_dtype, d);
+    if (groups < (int64_t(1) << 31))
+      hipLaunchKernelGGL(dev::ew_kernel<uint32_t>, dim3((unsigned)blocks), dim3(dev::kPassThreads), 0, stream, cur,
+                         (long long)ldc, (int)width, M, dst, (long long)ldo, p.d_dtype, d);
+    else
+      hipLaunchKernelGGL(dev::ew_kernel<long long>, dim3((unsigned)blocks), dim3(dev::kPassThreads), 0, stream, cur,
+                         (long long)ldc, (int)width, M, dst, (long long)ldo, p.d_dtype, d);
     if (check_launch() != CODA_OK) return CODA_ERR_HIP;
     cur = dst;
     ldc = ldo;
